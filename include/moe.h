@@ -1,0 +1,235 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: forward pass of a data-sparse
+ * token-choice Mixture-of-Experts layer with zero-compute (null) experts, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (paper review "Improving MoE Compute Efficiency by Composing Weight
+ * and Data Sparsity", section 3 "Technical architecture"):
+ *   y = E_shared(x) + sum over the chosen real experts i of g_i(x) E_i(x)
+ * The router scores N real experts plus one null expert whose output is zero;
+ * the null logit is copied M times into the pool before top-K, so a real expert
+ * is used only when its logit is strictly larger than the null logit, and at
+ * most K are used. Weights are renormalised over the chosen real experts only.
+ * Null slots are sorted past the end of the expert-ordered slot list and cut
+ * off before the grouped GEMM ("implementation" paragraph), so they cost no
+ * compute. The layer also reports the load-balance statistics f_i, P_i, L_bal
+ * and the router z-loss over the N+M pool ("load-balance loss", "Z-loss").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer to a dense row-major buffer,
+ *     16-byte aligned. Structs (moe_dims, moe_layer_params, moe_aux_out) live
+ *     in host memory and are read during the call only.
+ *   - Element type of activations, expert weights, intermediates and outputs:
+ *     dims->dtype (MOE_BF16 = bf16 bit patterns, MOE_F32 = float). The router
+ *     weight, logits and routing weights are always float32.
+ *   - Weight layout follows the linear-layer convention [out, in] with the
+ *     reduction dimension contiguous: w_gate, w_up [N][d_ff][d_model];
+ *     w_down [N][d_model][d_ff]; the router [N+1][d_model], row N = null.
+ *   - Ownership: the caller allocates and frees all memory. The library never
+ *     allocates, frees or synchronises; it keeps no state between calls
+ *     except a per-device cache of the compute-unit count. Calls on distinct
+ *     buffers may run concurrently.
+ *   - Execution: every kernel is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream). MOE_OK means validated and enqueued. A launch
+ *     failure returns MOE_ERR_HIP. Nothing is launched when validation fails.
+ *   - Validation: N >= 1, M >= 0, 1 <= K <= N + M, K <= N when M = 0,
+ *     N <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK, N + M <= MOE_MAX_POOL,
+ *     0 <= T and T * K < 2^31, d_model and d_ff multiples of 8. T = 0 is a no-op.
+ *   - Pool ids: 0..N-1 are real experts, N..N+M-1 are the null copies.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_EXPERTS 255
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_POOL 4096
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,         /* bad dimension or NULL required pointer */
+  MOE_ERR_ALIGN = 2,       /* a device pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOE_ERR_UNSUPPORTED = 4, /* valid but outside this build's limits */
+  MOE_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+  int64_t T;           /* tokens */
+  int32_t d_model;
+  int32_t n_experts;   /* N real experts */
+  int32_t n_null;      /* M copies of the null logit in the pool */
+  int32_t top_k;       /* K slots per token */
+  int32_t d_ff;        /* routed expert hidden size */
+  int32_t d_ff_shared; /* shared expert hidden size, 0 = no shared expert */
+  int32_t dtype;       /* moe_dtype */
+} moe_dims;
+
+/* Which workspace size moe_workspace_bytes() returns. */
+enum { MOE_WS_LAYER = 0, MOE_WS_ROUTE = 1, MOE_WS_PERMUTE = 2, MOE_WS_AUX = 3 };
+
+typedef void* moe_stream; /* hipStream_t */
+
+/*
+ * moe_route -- router GEMM + null-threshold top-K + renormalisation.
+ * Paper review section 3, "Null Expert mechanism" and "threshold
+ * interpretation"; quant67 MoE primer section 3 (router softmax, top-k,
+ * renormalise among the chosen).
+ *   logits s = x W^T (float32; column N gets + null_bias + null_bias_tok[t]).
+ *   c = #{j < N : s_j > s_N};  r = min(K, max(c, K - M))   (r = K when M = 0)
+ *   topk_idx[t, 0..r-1] = the r largest real logits, by (value desc, index asc)
+ *   topk_idx[t, r..K-1] = null copies N, N+1, ... (lowest copy ids first)
+ *   topk_w = softmax over the chosen real logits (computed in float64 from the
+ *            float32 logits, rounded once); 0 on null slots.
+ *   n_real[t] = r.
+ * x: [T][d_model] dtype; w_router: [N+1][d_model] float32.
+ * logits_in: optional [T][N+1] float32 whose column N is already the effective
+ *   null logit; when given, x, w_router and the biases are ignored (may be NULL)
+ *   and no GEMM runs (routing from identical logits is bit-exact).
+ * logits_out: optional [T][N+1] float32 output (column N effective).
+ * null_bias_tok: optional [T] float32 per-token null bias.
+ * topk_idx [T][K] int32, topk_w [T][K] float32 required; n_real [T] optional.
+ * ws: MOE_WS_ROUTE bytes (router weight split into three bf16 parts for the
+ *   MFMA GEMM); may be NULL when logits_in is given or dtype is MOE_F32.
+ */
+moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
+                     float null_bias, const float* null_bias_tok, const float* logits_in,
+                     float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* n_real,
+                     void* ws, size_t ws_bytes, moe_stream stream);
+
+/*
+ * moe_permute -- counting-sort dispatch of the token slots into expert order.
+ * Paper review section 3 "implementation": an argsort sends the null indices
+ * (>= N) to the end and the sorted list is truncated before the grouped GEMM.
+ * Equivalent to a stable argsort of the flat slot ids f = t*K + k by expert id,
+ * null slots removed. Any topk_idx value outside [0, N) counts as null. A token
+ * should name each real expert at most once (moe_route guarantees it); if
+ * not, R can exceed T*min(K,N) and the slots past that capacity are dropped
+ * (their slot_pos still holds the position, which moe_combine then skips).
+ *   counts[e]   = number of slots routed to real expert e              [N]
+ *   offsets[e]  = exclusive prefix sum of counts; offsets[N] = R        [N+1]
+ *   perm_token[p] = token of the p-th slot in expert order, p < R      [T*min(K,N)]
+ *                 (entries from R on are left unwritten)
+ *   slot_pos[t][k] = position p of slot (t,k) or -1 for a null slot   [T][K]
+ *   x_perm[p] = x[perm_token[p]] when x and x_perm are both non-NULL   [T*min(K,N)][d]
+ * ws: MOE_WS_PERMUTE bytes (per-chunk expert histograms).
+ * R stays on the device; nothing is copied to the host.
+ */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void* x,
+                       int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                       int32_t* slot_pos, void* x_perm, void* ws, size_t ws_bytes,
+                       moe_stream stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU expert FFN over variable-length segments
+ * (the grouped GEMM of the paper review's "implementation" paragraph; the
+ * per-token FFN of the quant67 primer section 2, in SwiGLU form):
+ *   for each group e and row p in [offsets[e], offsets[e+1]):
+ *     h = silu(W_gate[e] a_p) * (W_up[e] a_p),  silu(z) = z / (1 + exp(-z))
+ *     out_p = W_down[e] h
+ * a, out: [max_rows][d_model] dtype; w_gate, w_up: [n_groups][d_ff][d_model];
+ * w_down: [n_groups][d_model][d_ff]. offsets: DEVICE [n_groups+1] int32,
+ * read on the device only. Segment e is [a, b) with a = clamp(offsets[e], 0,
+ * max_rows) and b = clamp(offsets[e+1], a, max_rows), so any offsets stay in
+ * bounds; overlapping segments (decreasing offsets) are not meaningful.
+ * offsets may be NULL when n_groups == 1 (one segment of max_rows rows).
+ * Rows outside the segments are not written.
+ * bf16: MFMA with float32 accumulation, h stored as bf16; float32: float FMA.
+ * ws: moe_expert_ffn_workspace_bytes() bytes (holds h).
+ */
+moe_status moe_expert_ffn(const moe_dims* dims, int32_t n_groups, int32_t d_ff, int64_t max_rows,
+                          const void* a, const int32_t* offsets, const void* w_gate,
+                          const void* w_up, const void* w_down, void* out, void* ws,
+                          size_t ws_bytes, moe_stream stream);
+
+size_t moe_expert_ffn_workspace_bytes(const moe_dims* dims, int32_t d_ff, int64_t max_rows);
+
+/*
+ * moe_combine -- y_t = y_shared_t + sum_k topk_w[t,k] * y_perm[slot_pos[t,k]]
+ * (paper review section 3, core formula; a null slot contributes E_null = 0).
+ * Summed in slot order in float32 with one rounding to dtype; no atomics, so
+ * the result is bitwise reproducible. Slots with slot_pos outside
+ * [0, T*min(K,N)) are skipped. y_shared [T][d] may be NULL (no shared expert).
+ * y_perm: [T*min(K,N)][d] dtype; y: [T][d] dtype.
+ */
+moe_status moe_combine(const moe_dims* dims, const void* y_perm, const int32_t* slot_pos,
+                       const float* topk_w, const void* y_shared, void* y, moe_stream stream);
+
+/*
+ * moe_aux_stats -- load-balance and z-loss statistics over the N+M pool
+ * (paper review section 3, "load-balance loss" and "Z-loss"):
+ *   p_t = softmax over [s_0..s_{N-1}, s_null repeated M times]
+ *   P[i] = mean_t p_t,i;  counts[i] = #slots with topk_idx == i;  f[i] = counts[i] / T
+ *   scalars[0] = L_bal = N * sum_{i < N+M} f[i] P[i]
+ *   scalars[1] = L_z   = mean_t (log sum_i exp v_t,i)^2
+ *   scalars[2] = mean_t n_real[t]  (mean number of chosen real experts)
+ * With M = 0 the pool is the N reals (column N ignored). Reductions run in
+ * float64 in a fixed order (bitwise reproducible), rounded once to float32.
+ * logits: [T][N+1] float32 (column N effective); topk_idx: [T][K] int32.
+ * f, P: [N+M] float32; counts: [N+M] int32 or NULL; scalars: [3] float32.
+ * ws: MOE_WS_AUX bytes.
+ */
+moe_status moe_aux_stats(const moe_dims* dims, const float* logits, const int32_t* topk_idx,
+                         float* f, float* P, int32_t* counts, float* scalars, void* ws,
+                         size_t ws_bytes, moe_stream stream);
+
+/* Device pointers of the layer's inputs. */
+typedef struct {
+  const void* x;               /* [T][d_model] dtype */
+  const float* w_router;       /* [N+1][d_model] float32, row N = null */
+  float null_bias;             /* added to the null logit */
+  const float* null_bias_tok;  /* [T] float32 or NULL */
+  const void* w_gate;          /* [N][d_ff][d_model] */
+  const void* w_up;            /* [N][d_ff][d_model] */
+  const void* w_down;          /* [N][d_model][d_ff] */
+  const void* ws_gate;         /* [d_ff_shared][d_model] or NULL when d_ff_shared = 0 */
+  const void* ws_up;           /* [d_ff_shared][d_model] */
+  const void* ws_down;         /* [d_model][d_ff_shared] */
+} moe_layer_params;
+
+/* Optional device outputs of moe_layer_forward; any member may be NULL. */
+typedef struct {
+  float* logits;      /* [T][N+1] */
+  int32_t* topk_idx;  /* [T][K] */
+  float* topk_w;      /* [T][K] */
+  int32_t* n_real;    /* [T] */
+  int32_t* offsets;   /* [N+1] expert segment offsets, offsets[N] = R */
+  int32_t* counts;    /* [N+M] pool slot counts */
+  float* f;           /* [N+M] */
+  float* P;           /* [N+M] */
+  float* scalars;     /* [3] L_bal, L_z, mean n_real */
+} moe_aux_out;
+
+/*
+ * moe_layer_forward -- the whole layer: route -> permute -> gather ->
+ * grouped SwiGLU GEMMs -> shared expert -> combine -> statistics, all enqueued
+ * on `stream` with no host synchronisation. y: [T][d_model] dtype.
+ * aux may be NULL; the statistics kernels run only when aux requests
+ * counts, f, P or scalars. ws: moe_workspace_bytes(dims, MOE_WS_LAYER) bytes,
+ * sized for the worst case of T*min(K,N) real slots.
+ */
+moe_status moe_layer_forward(const moe_dims* dims, const moe_layer_params* params, void* y,
+                             const moe_aux_out* aux, void* ws, size_t ws_bytes,
+                             moe_stream stream);
+
+/* Workspace bytes for MOE_WS_LAYER / ROUTE / PERMUTE / AUX; 0 on invalid dims. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t which);
+
+/* Static, NUL-terminated description of a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

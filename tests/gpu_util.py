@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests (marshalling and tolerance checks)."""
+import sys
+
+import numpy as np
+import torch
+
+import token_choice_routing_amd as tcr
+from token_choice_routing_amd.layer import to_device, to_host
+from workloads import bf16_bits_to_f32
+
+# Tolerances of the layer output: max-abs error relative to the oracle's RMS.
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+FLIP_GAP = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def vals(a):
+    """float64 values of a host array (uint16 = bf16 bit patterns)."""
+    a = np.asarray(a)
+    return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def rms(a):
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
+
+
+def assert_close_rms(got, ref, tol, what=""):
+    got, ref = vals(got), np.asarray(ref, dtype=np.float64)
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    scale = rms(ref)
+    say(f"  {what}: max|err| = {err:.3e}, RMS(ref) = {scale:.3e}, ratio = {err / max(scale, 1e-300):.3e} (tol {tol:g})")
+    assert err <= tol * scale, f"{what}: max abs error {err} > {tol} * RMS {scale}"
+
+
+def bf16_tensor(a_f32):
+    from workloads import bf16_round
+    return to_device(bf16_round(np.asarray(a_f32, dtype=np.float32)))
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+def route_from_logits(logits_f32, N, M, K):
+    T = logits_f32.shape[0]
+    dims = tcr.make_dims(T, 64, N, M, K, 64, 0, tcr.MOE_F32)
+    topk = empty((T, K), torch.int32)
+    w = empty((T, K), torch.float32)
+    nr = empty((T,), torch.int32)
+    tcr.moe_route(dims, None, None, logits_in=to_device(np.ascontiguousarray(logits_f32, dtype=np.float32)),
+                  topk_idx=topk, topk_w=w, n_real=nr)
+    torch.cuda.synchronize()
+    return to_host(topk), to_host(w), to_host(nr)

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments with the documented
+status before anything reaches the GPU (these calls never launch a kernel, so
+they run without a GPU)."""
+import ctypes
+
+import pytest
+
+import token_choice_routing_amd as tcr
+from token_choice_routing_amd import (MOE_BF16, MOE_ERR_ALIGN, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED,
+                                      MOE_ERR_WORKSPACE, MOE_F32, MOE_OK, MOE_WS_AUX, MOE_WS_LAYER,
+                                      MOE_WS_PERMUTE, MOE_WS_ROUTE, make_dims)
+from workloads import CONFIGS
+
+FAKE = 0x7f0000001000        # 16-byte aligned, never dereferenced: validation fails first
+MIS = FAKE + 4               # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tcr.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = tcr.header_functions()
+    assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_aux_stats",
+            "moe_layer_forward", "moe_workspace_bytes", "moe_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert tcr.version() >= 100
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert tcr.status_str(s)
+    assert tcr.status_str(99) == "unknown status"
+
+
+def test_workspace_sizes_cover_the_worst_case():
+    for cfg in CONFIGS.values():
+        d = tcr.dims_from_config(cfg)
+        e = 2 if cfg.dtype == "bf16" else 4
+        R = cfg.T * min(cfg.top_k, cfg.n_experts)
+        total = tcr.workspace_bytes(d, MOE_WS_LAYER)
+        assert total >= R * cfg.d_model * e * 2 + R * cfg.d_ff * e
+        assert tcr.workspace_bytes(d, MOE_WS_PERMUTE) > 0
+        assert tcr.workspace_bytes(d, MOE_WS_AUX) > 0
+        assert (tcr.workspace_bytes(d, MOE_WS_ROUTE) > 0) == (cfg.dtype == "bf16")
+        assert tcr.expert_ffn_workspace_bytes(d, cfg.d_ff, R) == R * cfg.d_ff * e
+
+
+BAD_DIMS = [
+    dict(T=-1), dict(n_experts=0), dict(n_null=-1), dict(top_k=0), dict(top_k=17, n_null=8),
+    dict(n_null=0, top_k=9), dict(d_model=12), dict(d_ff=4), dict(d_ff_shared=-8), dict(dtype=7),
+]
+UNSUPPORTED_DIMS = [dict(n_experts=256, top_k=2), dict(top_k=33, n_null=64), dict(n_null=5000),
+                    dict(T=1 << 30, top_k=2)]
+
+
+def _dims(**kw):
+    base = dict(T=64, d_model=64, n_experts=8, n_null=8, top_k=2, d_ff=64, d_ff_shared=0, dtype=MOE_BF16)
+    base.update(kw)
+    return make_dims(**base)
+
+
+@pytest.mark.parametrize("kw", BAD_DIMS)
+def test_invalid_dims_rejected(lib, kw):
+    d = _dims(**kw)
+    assert tcr.workspace_bytes(d, MOE_WS_LAYER) == 0
+    st = lib.moe_route(ctypes.byref(d), FAKE, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == MOE_ERR_ARG
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED_DIMS)
+def test_unsupported_dims_rejected(lib, kw):
+    d = _dims(**kw)
+    st = lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None)
+    assert st == MOE_ERR_UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers(lib):
+    d = _dims()
+    b = ctypes.byref(d)
+    big = 1 << 34
+    assert lib.moe_route(b, FAKE, FAKE, 0.0, None, None, None, None, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_route(b, FAKE, FAKE, 0.0, None, None, None, MIS, FAKE, None, FAKE, big, None) == MOE_ERR_ALIGN
+    assert lib.moe_route(b, None, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_permute(b, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_permute(b, FAKE, MIS, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ALIGN
+    assert lib.moe_combine(b, FAKE, FAKE, FAKE, MIS, FAKE, None) == MOE_ERR_ALIGN
+    assert lib.moe_combine(b, None, FAKE, FAKE, None, FAKE, None) == MOE_ERR_ARG
+    assert lib.moe_aux_stats(b, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_expert_ffn(b, 0, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_expert_ffn(b, 2, 64, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_expert_ffn(b, 2, 60, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_ARG
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, None, None, None, None)
+    assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    assert lib.moe_layer_forward(b, None, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    ds = _dims(d_ff_shared=64)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_layer_forward(ctypes.byref(ds), ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+
+
+def test_short_workspace(lib):
+    d = _dims()
+    b = ctypes.byref(d)
+    need = tcr.workspace_bytes(d, MOE_WS_LAYER)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, FAKE, need - 1, None) == MOE_ERR_WORKSPACE
+    assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, None, need, None) == MOE_ERR_WORKSPACE
+    assert lib.moe_route(b, FAKE, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE,
+                         tcr.workspace_bytes(d, MOE_WS_ROUTE) - 1, None) == MOE_ERR_WORKSPACE
+    assert lib.moe_permute(b, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == MOE_ERR_WORKSPACE
+    assert lib.moe_aux_stats(b, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                             tcr.workspace_bytes(d, MOE_WS_AUX) - 1, None) == MOE_ERR_WORKSPACE
+    ffn_need = tcr.expert_ffn_workspace_bytes(d, 64, 10)
+    assert lib.moe_expert_ffn(b, 2, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ffn_need - 1,
+                              None) == MOE_ERR_WORKSPACE
+
+
+def test_empty_inputs_are_noops(lib):
+    """T = 0 and zero rows validate and return OK without launching anything."""
+    d = _dims(T=0)
+    b = ctypes.byref(d)
+    big = 1 << 34
+    assert lib.moe_route(b, FAKE, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE, big, None) == MOE_OK
+    assert lib.moe_combine(b, FAKE, FAKE, FAKE, None, FAKE, None) == MOE_OK
+    assert lib.moe_permute(b, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == MOE_OK
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_OK
+    d1 = _dims()
+    assert lib.moe_expert_ffn(ctypes.byref(d1), 3, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                              None) == MOE_OK
+    assert tcr.workspace_bytes(_dims(dtype=MOE_F32), MOE_WS_ROUTE) == 0

@@ -1,0 +1,194 @@
+"""End-to-end GPU parity of moe_layer_forward against the CPU oracle.
+
+Every config runs at full size. Configs the oracle finishes in seconds are
+compared on every output element; the large ones on a seeded sample of tokens
+(plus whole-array checks of routing, permutation and statistics, which are
+cheap). Also: determinism, solution-space preservation, null-routed tokens."""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import token_choice_routing_amd as tcr
+from oracle import moe_oracle as O
+from token_choice_routing_amd.layer import MoeLayer, to_device, to_host
+from workloads import CONFIGS, generate
+from workloads.configs import Config
+from tests.gpu_util import FLIP_GAP, TOL_BF16, TOL_F32, assert_close_rms, empty, say, vals
+
+pytestmark = pytest.mark.gpu
+
+
+def sub_workload(wl, rows):
+    """Same weights, a subset of the tokens (in the given order)."""
+    w2 = copy.copy(wl)
+    w2.x = np.ascontiguousarray(wl.x[rows])
+    if wl.null_bias_tok is not None:
+        w2.null_bias_tok = np.ascontiguousarray(wl.null_bias_tok[rows])
+    w2.cfg = copy.copy(wl.cfg)
+    object.__setattr__(w2.cfg, "T", len(rows))
+    return w2
+
+
+def run_layer(wl):
+    say(f"  layer forward T={wl.x.shape[0]} {wl.cfg.name}")
+    layer = MoeLayer(wl)
+    layer.forward()
+    return layer, layer.results()
+
+
+def check_routing(wl, out, rows=None, stats=True):
+    """Logits against float64, routing bit-exact from the GPU logits, flips only at tiny gaps."""
+    cfg = wl.cfg
+    N, M, K = cfg.n_experts, cfg.n_null, cfg.top_k
+    gl = out["logits"]
+    ot, ow, on = O.route(gl.astype(np.float64), N, M, K)
+    np.testing.assert_array_equal(out["topk_idx"], ot)
+    np.testing.assert_array_equal(out["n_real"], on)
+    np.testing.assert_allclose(out["topk_w"], ow, rtol=1e-6, atol=0)
+    rows = np.arange(gl.shape[0]) if rows is None else rows
+    btok = None if wl.null_bias_tok is None else wl.null_bias_tok[rows].astype(np.float64)
+    ref = O.router_logits(wl.values("x")[rows], wl.values("w_router"), wl.null_bias, btok)
+    fin = np.isfinite(ref)
+    err = np.abs(gl[rows][fin] - ref[fin]).max()
+    say(f"  max |logit err| = {err:.3e}")
+    assert err < 2e-6
+    ft, _, _ = O.route(ref, N, M, K)
+    flips = np.nonzero((np.sort(ft, 1) != np.sort(ot[rows], 1)).any(1))[0]
+    gap = O.decisive_gap(ref, N, M, K)
+    say(f"  tokens routed differently from the float64 logits: {len(flips)}")
+    assert (gap[flips] < FLIP_GAP).all()
+    # permutation offsets and the statistics from the same routing
+    _, off, _, _ = O.permute(out["topk_idx"], N)
+    np.testing.assert_array_equal(out["offsets"], off)
+    if not stats:
+        return gl
+    a = O.aux_stats(gl.astype(np.float64), out["topk_idx"], N, M, K)
+    np.testing.assert_array_equal(out["counts"], a["counts"])
+    np.testing.assert_allclose(out["P"], a["P"], rtol=1e-4, atol=1e-12)
+    np.testing.assert_allclose(out["f"], a["f"], rtol=1e-6)
+    for i, key in enumerate(("L_bal", "L_z", "mean_r")):
+        assert abs(out["scalars"][i] - a[key]) <= 1e-4 * abs(a[key]) + 1e-12, key
+    return gl
+
+
+def tol(cfg):
+    return TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
+
+
+def check_full(wl, stats=True):
+    layer, out = run_layer(wl)
+    gl = check_routing(wl, out, stats=stats)
+    ref = O.layer_forward(wl, logits=gl.astype(np.float64))
+    assert_close_rms(out["y"], ref["y"], tol(wl.cfg), f"y {wl.cfg.name}")
+    nul = out["n_real"] == 0
+    if nul.any() and not wl.cfg.d_ff_shared:
+        assert (vals(out["y"])[nul] == 0).all()
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "qwen3_0p6b_rho1"])
+def test_layer_full_compare(name):
+    say(f"layer full compare {name}")
+    check_full(generate(CONFIGS[name]))
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("qwen3_0p6b_rho0p5", np.arange(1500)),
+    ("qwen3_1p7b_rho0p25", np.arange(777)),
+    ("modality_skew_rho0p5", np.r_[0:500, 16384 - 524:16384]),   # both token classes
+])
+def test_layer_token_subset_full_compare(name, rows):
+    say(f"layer subset compare {name} T={len(rows)}")
+    check_full(sub_workload(generate(CONFIGS[name]), rows))
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_rho0p5", "qwen3_1p7b_rho0p25", "modality_skew_rho0p5"])
+def test_layer_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    say(f"layer full size, sampled rows: {name}")
+    wl = generate(cfg)
+    layer, out = run_layer(wl)
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(cfg.T, size=384, replace=False))
+    gl = check_routing(wl, out, rows=rows)
+    if cfg.bias_mode == "calibrated":
+        assert abs(out["n_real"].mean() - cfg.target_mean_r) <= 0.05
+    yd, _, _ = O.layer_dense(wl, logits=gl.astype(np.float64), tokens=rows)
+    assert_close_rms(vals(out["y"])[rows], yd, TOL_BF16, f"y sampled {name}")
+    # second run in the same launch configuration is bitwise identical
+    y1 = out["y"].copy()
+    layer.forward()
+    np.testing.assert_array_equal(to_host(layer.y), y1)
+
+
+def _small(**kw):
+    base = dict(name="small_bf16", T=600, d_model=256, n_experts=16, n_null=16, top_k=4, d_ff=128,
+                d_ff_shared=64, dtype="bf16", w_std=0.05)
+    base.update(kw)
+    return Config(**base)
+
+
+def test_solution_space_preservation_bitwise():
+    """K=4 with the null logit put between each token's 2nd and 3rd real logit
+    gives the K=2, M=0 layer output bit for bit."""
+    say("solution-space preservation on the GPU")
+    wl4 = generate(_small(top_k=4, n_null=2))
+    s = O.router_logits(wl4.values("x"), wl4.values("w_router"))
+    srt = np.sort(s[:, :16], axis=1)[:, ::-1]
+    wl4.null_bias_tok = (0.5 * (srt[:, 1] + srt[:, 2]) - s[:, 16]).astype(np.float32)
+    _, o4 = run_layer(wl4)
+    assert (o4["n_real"] == 2).all()
+    _, o2 = run_layer(generate(_small(top_k=2, n_null=0)))
+    np.testing.assert_array_equal(o4["y"], o2["y"])
+    np.testing.assert_array_equal(o4["topk_w"][:, :2], o2["topk_w"])
+
+
+@pytest.mark.parametrize("shared", [64, 0])
+def test_null_routed_tokens_give_shared_output(shared):
+    say(f"null-routed tokens, shared={shared}")
+    wl = generate(_small(d_ff_shared=shared))
+    btok = np.zeros(wl.cfg.T, dtype=np.float32)
+    btok[::3] = np.inf
+    wl.null_bias_tok = btok
+    layer, out = run_layer(wl)
+    nul = np.isinf(btok)
+    assert (out["n_real"][nul] == 0).all()
+    if shared:
+        dims = layer.dims
+        ys = empty((wl.cfg.T, wl.cfg.d_model), torch.bfloat16)
+        ws = empty((tcr.expert_ffn_workspace_bytes(dims, shared, wl.cfg.T),), torch.uint8)
+        tcr.moe_expert_ffn(dims, 1, shared, wl.cfg.T, layer.x, None, layer.ws_gate, layer.ws_up,
+                           layer.ws_down, ys, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out["y"][nul], to_host(ys)[nul])
+    else:
+        assert (vals(out["y"])[nul] == 0).all()
+    check_routing(wl, out, stats=False)
+
+
+@pytest.mark.parametrize("shared", [64, 0])
+def test_every_token_null(shared):
+    say(f"every token null (R = 0), shared={shared}")
+    wl = generate(_small(d_ff_shared=shared))
+    wl.null_bias_tok = np.full(wl.cfg.T, np.inf, dtype=np.float32)
+    _, out = run_layer(wl)
+    assert out["offsets"][-1] == 0
+    if not shared:
+        assert (vals(out["y"]) == 0).all()
+
+
+def test_one_expert_takes_every_slot():
+    say("one expert holds every real slot")
+    wl = generate(_small(top_k=1, n_null=0, T=700))
+    wl.x[:, 0] = 0x3F80                      # bf16 1.0 in column 0 of every token
+    wl.w_router[5, 0] = 100.0                # expert 5 wins every token
+    out = check_full(wl)
+    assert (out["topk_idx"][:, 0] == 5).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 129])
+def test_tiny_token_counts(T):
+    say(f"T = {T}")
+    check_full(sub_workload(generate(_small()), np.arange(T)))

@@ -1,0 +1,199 @@
+"""Python binding of libmoe_mi355x.so (C ABI in include/moe.h).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers and torch's current HIP stream to the C entry point of the same name
+and raises ``MoeError`` on a non-zero status. No step of the layer runs here.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (one runtime per process: streams and
+pointers are shared). The library must have been built
+(``python -m token_choice_routing_amd.build``); importing the package does not
+fall back to anything when it is missing.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(6)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_AUX = range(4)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_null", ctypes.c_int32), ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w_router", ctypes.c_void_p), ("null_bias", ctypes.c_float),
+                ("null_bias_tok", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("ws_gate", ctypes.c_void_p),
+                ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p)]
+
+
+class AuxOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logits", "topk_idx", "topk_w", "n_real", "offsets", "counts", "f", "P", "scalars")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m token_choice_routing_amd.build`")
+    lib = ctypes.CDLL(path)
+    D = ctypes.POINTER(Dims)
+    sig = {
+        "moe_route": [D, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+        "moe_permute": [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+        "moe_expert_ffn": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
+                           _P, ctypes.c_size_t, _P],
+        "moe_combine": [D, _P, _P, _P, _P, _P, _P],
+        "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+        "moe_layer_forward": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P,
+                              ctypes.c_size_t, _P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.moe_workspace_bytes.argtypes = [D, ctypes.c_int32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_expert_ffn_workspace_bytes.argtypes = [D, ctypes.c_int32, ctypes.c_int64]
+    lib.moe_expert_ffn_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/moe.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)) - {"moe_stream"})
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    if isinstance(ws, tuple):
+        return ws
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(int(status)).decode()
+
+
+def version() -> int:
+    return load_library().moe_version()
+
+
+def make_dims(T, d_model, n_experts, n_null, top_k, d_ff, d_ff_shared=0, dtype=MOE_BF16) -> Dims:
+    return Dims(int(T), int(d_model), int(n_experts), int(n_null), int(top_k), int(d_ff),
+                int(d_ff_shared), int(dtype))
+
+
+def dims_from_config(cfg, T=None) -> Dims:
+    return make_dims(cfg.T if T is None else T, cfg.d_model, cfg.n_experts, cfg.n_null, cfg.top_k,
+                     cfg.d_ff, cfg.d_ff_shared, MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+
+
+def workspace_bytes(dims: Dims, which: int = MOE_WS_LAYER) -> int:
+    return load_library().moe_workspace_bytes(ctypes.byref(dims), which)
+
+
+def expert_ffn_workspace_bytes(dims: Dims, d_ff: int, max_rows: int) -> int:
+    return load_library().moe_expert_ffn_workspace_bytes(ctypes.byref(dims), d_ff, max_rows)
+
+
+def moe_route(dims, x, w_router, null_bias=0.0, null_bias_tok=None, logits_in=None,
+              logits_out=None, topk_idx=None, topk_w=None, n_real=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), float(null_bias),
+                                     _ptr(null_bias_tok), _ptr(logits_in), _ptr(logits_out),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(n_real), wp, wb,
+                                     _stream(stream)), "moe_route")
+
+
+def moe_permute(dims, topk_idx, x, counts, offsets, perm_token, slot_pos, x_perm, ws, stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_permute(ctypes.byref(dims), _ptr(topk_idx), _ptr(x), _ptr(counts),
+                                       _ptr(offsets), _ptr(perm_token), _ptr(slot_pos),
+                                       _ptr(x_perm), wp, wb, _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn(dims, n_groups, d_ff, max_rows, a, offsets, w_gate, w_up, w_down, out, ws,
+                   stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_expert_ffn(ctypes.byref(dims), int(n_groups), int(d_ff), int(max_rows),
+                                          _ptr(a), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+                                          _ptr(w_down), _ptr(out), wp, wb, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(dims, y_perm, slot_pos, topk_w, y_shared, y, stream=None):
+    _check(load_library().moe_combine(ctypes.byref(dims), _ptr(y_perm), _ptr(slot_pos),
+                                       _ptr(topk_w), _ptr(y_shared), _ptr(y), _stream(stream)),
+           "moe_combine")
+
+
+def moe_aux_stats(dims, logits, topk_idx, f, P, counts, scalars, ws, stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_aux_stats(ctypes.byref(dims), _ptr(logits), _ptr(topk_idx), _ptr(f),
+                                         _ptr(P), _ptr(counts), _ptr(scalars), wp, wb,
+                                         _stream(stream)), "moe_aux_stats")
+
+
+def moe_layer_forward(dims, params: LayerParams, y, aux: AuxOut = None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(params), _ptr(y),
+                                             ctypes.byref(aux) if aux is not None else None, wp, wb,
+                                             _stream(stream)), "moe_layer_forward")
+
+
+from .layer import MoeLayer  # noqa: E402,F401

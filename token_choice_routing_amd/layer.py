@@ -1,0 +1,80 @@
+"""Device-side holder for one layer call: uploads a workload's tensors once,
+owns the workspace and output buffers, and calls ``moe_layer_forward``.
+Marshalling only; the layer itself runs in the HIP library."""
+import numpy as np
+import torch
+
+from . import (AuxOut, LayerParams, MOE_BF16, MOE_WS_LAYER, dims_from_config, moe_layer_forward,
+               workspace_bytes)
+
+
+def to_device(a, device="cuda"):
+    """numpy storage array (uint16 bf16 bit patterns or float32/int32) -> torch tensor."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t):
+    """torch tensor -> numpy (bf16 becomes uint16 bit patterns)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class MoeLayer:
+    def __init__(self, workload, device="cuda", T=None):
+        cfg = workload.cfg
+        self.cfg = cfg
+        self.T = cfg.T if T is None else T
+        self.dims = dims_from_config(cfg, self.T)
+        self.bf16 = self.dims.dtype == MOE_BF16
+        dt = torch.bfloat16 if self.bf16 else torch.float32
+        dev = device
+        self.x = to_device(workload.x[: self.T], dev)
+        self.w_router = to_device(workload.w_router, dev)
+        self.null_bias = float(workload.null_bias)
+        self.null_bias_tok = (to_device(workload.null_bias_tok[: self.T], dev)
+                              if workload.null_bias_tok is not None else None)
+        self.w_gate = to_device(workload.w_gate, dev)
+        self.w_up = to_device(workload.w_up, dev)
+        self.w_down = to_device(workload.w_down, dev)
+        self.ws_gate = to_device(workload.ws_gate, dev)
+        self.ws_up = to_device(workload.ws_up, dev)
+        self.ws_down = to_device(workload.ws_down, dev)
+        N, M, K = cfg.n_experts, cfg.n_null, cfg.top_k
+        T_ = self.T
+        self.y = torch.empty((T_, cfg.d_model), dtype=dt, device=dev)
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty((T_, N + 1), dtype=f32, device=dev)
+        self.topk_idx = torch.empty((T_, K), dtype=i32, device=dev)
+        self.topk_w = torch.empty((T_, K), dtype=f32, device=dev)
+        self.n_real = torch.empty((T_,), dtype=i32, device=dev)
+        self.offsets = torch.empty((N + 1,), dtype=i32, device=dev)
+        self.counts = torch.empty((N + M,), dtype=i32, device=dev)
+        self.f = torch.empty((N + M,), dtype=f32, device=dev)
+        self.P = torch.empty((N + M,), dtype=f32, device=dev)
+        self.scalars = torch.empty((3,), dtype=f32, device=dev)
+        self.ws = torch.empty((max(workspace_bytes(self.dims, MOE_WS_LAYER), 256),), dtype=torch.uint8,
+                              device=dev)
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        self.params = LayerParams(p(self.x), p(self.w_router), self.null_bias, p(self.null_bias_tok),
+                                  p(self.w_gate), p(self.w_up), p(self.w_down), p(self.ws_gate),
+                                  p(self.ws_up), p(self.ws_down))
+        self.aux_full = AuxOut(p(self.logits), p(self.topk_idx), p(self.topk_w), p(self.n_real),
+                               p(self.offsets), p(self.counts), p(self.f), p(self.P), p(self.scalars))
+
+    def forward(self, aux=True, stream=None):
+        moe_layer_forward(self.dims, self.params, self.y, self.aux_full if aux else None, self.ws,
+                          stream=stream)
+        return self.y
+
+    def results(self):
+        """Host copies of every output (synchronises)."""
+        torch.cuda.synchronize()
+        names = ("y", "logits", "topk_idx", "topk_w", "n_real", "offsets", "counts", "f", "P", "scalars")
+        return {n: to_host(getattr(self, n)) for n in names}
