@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Throughput of the null-expert token-choice MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sweep] [--no-cpu]
+
+A step is one moe_layer_forward call (route, permute, gather, grouped SwiGLU
+GEMMs, shared expert, combine, statistics) over one batch of synthetic tokens
+already resident in HBM. The headline workload is the Qwen3-0.6B-shaped layer
+(T=2048, d_model=1024, N=64 experts of d_ff=768, shared expert d_ff=768, K=2,
+M=0). Real-expert FLOPs count only the slots routed to real experts
+(6 d d_ff per slot) plus the shared expert (6 d d_ff_shared per token).
+
+Besides the JSON line's required fields it reports, per kernel, the average
+launch time measured with HIP events on the launch stream and the algorithmic
+bytes / FLOPs per launch; the rho sweep at the Qwen3-1.7B shape and the other
+workloads (timed only); and the CPU oracle's throughput on a bounded sample.
+Prints exactly one JSON line on stdout.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the rho sweep and other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every entry point is given)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters, warmup=2):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        s = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(s)
+        for _ in range(iters):
+            fn()
+        b.record(s)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters   # microseconds per call
+
+
+def layer_flops(cfg, R, T):
+    return 6.0 * cfg.d_model * cfg.d_ff * R + 6.0 * cfg.d_model * cfg.d_ff_shared * T
+
+
+def time_layer(torch, layer, steps, warmup):
+    for _ in range(warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(s)
+    for _ in range(steps):
+        layer.forward()
+    b.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall * 1e3 / steps
+
+
+def kernel_table(torch, tcr, layer, iters):
+    """Each stage through its own entry point, on the layer's own inputs."""
+    cfg, dims = layer.cfg, layer.dims
+    T, d, N, M, K, f, fs = layer.T, cfg.d_model, cfg.n_experts, cfg.n_null, cfg.top_k, cfg.d_ff, cfg.d_ff_shared
+    Rmax = T * min(K, N)
+    dev, i32, f32, bf = "cuda", torch.int32, torch.float32, torch.bfloat16
+    E = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+    logits, topk, tw, nr = E((T, N + 1), f32), E((T, K), i32), E((T, K), f32), E((T,), i32)
+    ws_r = E((max(tcr.workspace_bytes(dims, tcr.MOE_WS_ROUTE), 16),), torch.uint8)
+    counts, offsets = E((N,), i32), E((N + 1,), i32)
+    perm, slot = E((Rmax,), i32), E((T, K), i32)
+    xp = E((Rmax, d), bf)
+    ws_p = E((max(tcr.workspace_bytes(dims, tcr.MOE_WS_PERMUTE), 16),), torch.uint8)
+    h, yp = E((Rmax, f), bf), E((Rmax, d), f32)
+    hs = E((T, max(fs, 8)), bf)
+    ys = E((T, d), f32) if fs else None
+    y = E((T, d), bf)
+    P = N + M
+    fo, Po, co, sc = E((P,), f32), E((P,), f32), E((P,), i32), E((3,), f32)
+    ws_a = E((tcr.workspace_bytes(dims, tcr.MOE_WS_AUX),), torch.uint8)
+
+    def route():
+        tcr.moe_route(dims, layer.x, layer.w_router, layer.null_bias, layer.null_bias_tok, None, logits,
+                      topk, tw, nr, ws_r)
+
+    def permute():
+        tcr.moe_permute(dims, topk, None, counts, offsets, perm, slot, None, ws_p)
+
+    def permute_gather():
+        tcr.moe_permute(dims, topk, layer.x, counts, offsets, perm, slot, xp, ws_p)
+
+    def gemm1():
+        tcr.moe_grouped_gemm(dims, tcr.MOE_GEMM_GATE_UP, N, f, d, Rmax, xp, offsets, layer.w_gate,
+                             layer.w_up, h)
+
+    def gemm2():
+        tcr.moe_grouped_gemm(dims, tcr.MOE_GEMM_DOWN, N, d, f, Rmax, h, offsets, layer.w_down, None, yp)
+
+    def sgemm1():
+        tcr.moe_grouped_gemm(dims, tcr.MOE_GEMM_GATE_UP, 1, fs, d, T, layer.x, None, layer.ws_gate,
+                             layer.ws_up, hs)
+
+    def sgemm2():
+        tcr.moe_grouped_gemm(dims, tcr.MOE_GEMM_DOWN, 1, d, fs, T, hs, None, layer.ws_down, None, ys)
+
+    def combine():
+        tcr.moe_combine(dims, yp, slot, tw, ys, y)
+
+    def aux():
+        tcr.moe_aux_stats(dims, logits, topk, fo, Po, co, sc, ws_a)
+
+    tm = Timer(torch)
+    route()
+    permute_gather()
+    torch.cuda.synchronize()
+    off_h = offsets.cpu().numpy()
+    R = int(off_h[-1])
+    active = int((off_h[1:] > off_h[:-1]).sum())
+    rows = {}
+
+    def add(name, us, nbytes, flops=0.0, launches=1):
+        rows[name] = {"us": round(us, 3), "bytes": int(nbytes), "flops": float(flops),
+                      "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
+                      "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4), "launches": launches}
+
+    t_route = tm.run(route, iters)
+    add("route", t_route, T * d * 2 + 4 * (N + 1) * d + 4 * T * (N + 1) + 8 * T * K + 4 * T,
+        2.0 * T * d * (N + 1), 2)
+    t_perm = tm.run(permute, iters)
+    add("permute", t_perm, 4 * T * K + 4 * R + 4 * T * K + 4 * (2 * N + 1), 0, 3)
+    t_pg = tm.run(permute_gather, iters)
+    add("gather", max(t_pg - t_perm, 1e-3), 2 * R * d * 2 + 4 * R)
+    add("gemm_gate_up", tm.run(gemm1, iters), R * d * 2 + active * 2 * f * d * 2 + R * f * 2, 4.0 * R * d * f)
+    add("gemm_down", tm.run(gemm2, iters), R * f * 2 + active * d * f * 2 + R * d * 4, 2.0 * R * d * f)
+    if fs:
+        add("shared_gate_up", tm.run(sgemm1, iters), T * d * 2 + 2 * fs * d * 2 + T * fs * 2, 4.0 * T * d * fs)
+        add("shared_down", tm.run(sgemm2, iters), T * fs * 2 + d * fs * 2 + T * d * 4, 2.0 * T * d * fs)
+    add("combine", tm.run(combine, iters), R * d * 4 + (T * d * 4 if fs else 0) + T * d * 2 + 8 * T * K)
+    add("aux_stats", tm.run(aux, iters), 4 * T * (N + 1) + 4 * T * K, 0, 2)
+    return rows, R
+
+
+def roofline(k):
+    """Dominant-kernel roofline object from one kernel_table row."""
+    ai = k["flops"] / max(k["bytes"], 1)
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai >= ridge:
+        return {"bound": "mfma", "achieved": k["TFLOP_s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(k["TFLOP_s"] / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    return {"bound": "hbm", "achieved": k["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(k["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None}
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, when a summary for this
+    kernel and workload is committed under profiles/ (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        tab = json.load(open(path))
+        ent = tab.get(f"{kernel}@{workload}")
+        return None if ent is None else ent.get("bytes_per_launch")
+    except (ValueError, OSError):
+        return None
+
+
+def cpu_baseline(budget_s=12.0):
+    """The CPU oracle as it stands, on the first 512 tokens of the headline
+    workload, repeated until about budget_s seconds of CPU work."""
+    import numpy as np  # noqa: F401
+    from oracle import moe_oracle as O
+    from workloads import CONFIGS, generate
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    cfg = CONFIGS["qwen3_0p6b_rho1"]
+    Ts = 512
+    wl = generate(cfg, T=Ts)
+    O.layer_forward(wl)            # warm caches
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        O.layer_forward(wl)
+        n += 1
+    el = time.perf_counter() - t0
+    return {"value": round(n * Ts / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {Ts} tokens of the headline workload (same weights), float64 NumPy oracle, "
+                      f"{n} full layer forwards in {el:.1f} s"}
+
+
+def sweep(torch, tcr, steps, warmup):
+    """Other workloads, timed only: the rho sweep at the Qwen3-1.7B shape, the
+    matched-FLOPs pair at T=8192, and the modality-skewed mix."""
+    import copy
+    from token_choice_routing_amd.layer import MoeLayer
+    from workloads import CONFIGS, MATCHED_PAIR, SWEEP, generate
+    from workloads.gen import null_bias_for
+    out = []
+    base = generate(CONFIGS["qwen3_1p7b_rho0p25"])
+    base_layer = None
+    names = list(SWEEP) + ["modality_skew_rho0p5"]
+    for name in names:
+        cfg = SWEEP.get(name) or CONFIGS[name]
+        if cfg.x_kind == "modality":
+            wl = generate(cfg, experts=False)
+            wl.w_gate, wl.w_up, wl.w_down = base.w_gate, base.w_up, base.w_down
+        else:
+            wl = copy.copy(base)
+            wl.cfg = cfg
+            wl.null_bias, wl.null_bias_tok = null_bias_for(cfg)
+        layer = MoeLayer(wl, weights_from=base_layer)
+        if base_layer is None:
+            base_layer = layer
+        out.append(measure(torch, layer, steps, warmup))
+        log(f"  {name}: {out[-1]}")
+    c1 = generate(CONFIGS["qwen3_0p6b_rho0p5"])
+    l1 = None
+    for name in ("matched_k2_rho1", "matched_k4_rho0p5"):
+        cfg = MATCHED_PAIR[name]
+        wl = copy.copy(c1)
+        wl.cfg = cfg
+        wl.null_bias, wl.null_bias_tok = null_bias_for(cfg)
+        layer = MoeLayer(wl, weights_from=l1)
+        l1 = l1 or layer
+        out.append(measure(torch, layer, steps, warmup))
+        log(f"  {name}: {out[-1]}")
+    return out
+
+
+def measure(torch, layer, steps, warmup):
+    ms, _ = time_layer(torch, layer, steps, warmup)
+    cfg = layer.cfg
+    R = int(layer.offsets[-1].item())
+    fl = layer_flops(cfg, R, layer.T)
+    return {"workload": cfg.name, "T": layer.T, "K": cfg.top_k, "M": cfg.n_null,
+            "rho_nominal": round(cfg.rho_nominal, 4), "rho_realised": round(R / (layer.T * cfg.top_k), 4),
+            "real_slots": R, "ms": round(ms, 4), "tokens_per_s": round(layer.T / ms * 1e3, 1),
+            "real_expert_tflops": round(fl / ms / 1e9, 2),
+            "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is built and measured for one GPU's share).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import token_choice_routing_amd as tcr
+    from token_choice_routing_amd.layer import MoeLayer
+    from workloads import CONFIGS, generate
+
+    tcr.load_library()
+    torch.cuda.set_device(0)
+    cfg = CONFIGS["qwen3_0p6b_rho1"]
+    log(f"bench: generating {cfg.name}")
+    wl = generate(cfg)
+    layer = MoeLayer(wl)
+    log("bench: warmup + timed steps")
+    ms, wall_ms = time_layer(torch, layer, args.steps, args.warmup)
+    R = int(layer.offsets[-1].item())
+    T = layer.T
+    tok_s = T / ms * 1e3
+    fl = layer_flops(cfg, R, T)
+    log(f"bench: {ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (wall), R={R}")
+    log("bench: per-kernel timing")
+    kernels, _ = kernel_table(torch, tcr, layer, args.kernel_iters)
+    dom = "gemm_gate_up"
+    rl = roofline(kernels[dom])
+    rl["kernel"] = "grouped_gemm_bf16_kernel<gate/up SwiGLU> (routed)"
+    rl["traffic"] = traffic_from_profiles("gemm_gate_up", cfg.name)
+    line = {
+        "metric": "MoE-layer tokens/s + real-expert TFLOP/s (% bf16 MFMA peak) vs rho",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, fp32 router)",
+        "config": {"workload": f"{cfg.name}: T={T}, d_model={cfg.d_model}, N={cfg.n_experts}, "
+                               f"M={cfg.n_null}, K={cfg.top_k}, d_ff={cfg.d_ff}, shared d_ff={cfg.d_ff_shared}",
+                   "T": T, "d_model": cfg.d_model, "n_experts": cfg.n_experts, "n_null": cfg.n_null,
+                   "top_k": cfg.top_k, "d_ff": cfg.d_ff, "d_ff_shared": cfg.d_ff_shared,
+                   "parallelism": "single GPU"},
+        "real_slots": R,
+        "real_expert_tflops": round(fl / ms / 1e9, 2),
+        "real_expert_mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": rl,
+        "kernels": kernels,
+    }
+    if not args.no_sweep:
+        log("bench: rho sweep and other workloads")
+        line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

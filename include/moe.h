@@ -135,14 +135,17 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void
  *   for each group e and row p in [offsets[e], offsets[e+1]):
  *     h = silu(W_gate[e] a_p) * (W_up[e] a_p),  silu(z) = z / (1 + exp(-z))
  *     out_p = W_down[e] h
- * a, out: [max_rows][d_model] dtype; w_gate, w_up: [n_groups][d_ff][d_model];
+ * a: [max_rows][d_model] dtype; out: [max_rows][d_model] FLOAT32 (expert outputs
+ * stay float32 so the combine rounds the layer output once);
+ * w_gate, w_up: [n_groups][d_ff][d_model];
  * w_down: [n_groups][d_model][d_ff]. offsets: DEVICE [n_groups+1] int32,
  * read on the device only. Segment e is [a, b) with a = clamp(offsets[e], 0,
  * max_rows) and b = clamp(offsets[e+1], a, max_rows), so any offsets stay in
  * bounds; overlapping segments (decreasing offsets) are not meaningful.
  * offsets may be NULL when n_groups == 1 (one segment of max_rows rows).
  * Rows outside the segments are not written.
- * bf16: MFMA with float32 accumulation, h stored as bf16; float32: float FMA.
+ * bf16: MFMA with float32 accumulation, h stored as bf16 (the input type of
+ * the down projection's MFMA); float32: float FMA throughout.
  * ws: moe_expert_ffn_workspace_bytes() bytes (holds h).
  */
 moe_status moe_expert_ffn(const moe_dims* dims, int32_t n_groups, int32_t d_ff, int64_t max_rows,
@@ -153,12 +156,26 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t n_groups, int32_t d_ff, 
 size_t moe_expert_ffn_workspace_bytes(const moe_dims* dims, int32_t d_ff, int64_t max_rows);
 
 /*
+ * moe_grouped_gemm -- one of the two GEMMs of moe_expert_ffn on its own (same
+ * passage and segment rules as moe_expert_ffn; offsets NULL = one segment):
+ *   op = MOE_GEMM_GATE_UP: out[p] = silu(b0[e] a_p) * (b1[e] a_p)   out dtype, [rows][n_out]
+ *                          a: [rows][k_dim]; b0, b1: [n_groups][n_out][k_dim]
+ *   op = MOE_GEMM_DOWN:    out[p] = b0[e] a_p                        out float32, [rows][n_out]
+ *                          a: [rows][k_dim] dtype; b0: [n_groups][n_out][k_dim]; b1 unused
+ * n_out and k_dim multiples of 8. No workspace.
+ */
+enum { MOE_GEMM_GATE_UP = 0, MOE_GEMM_DOWN = 1 };
+moe_status moe_grouped_gemm(const moe_dims* dims, int32_t op, int32_t n_groups, int32_t n_out,
+                            int32_t k_dim, int64_t rows, const void* a, const int32_t* offsets,
+                            const void* b0, const void* b1, void* out, moe_stream stream);
+
+/*
  * moe_combine -- y_t = y_shared_t + sum_k topk_w[t,k] * y_perm[slot_pos[t,k]]
  * (paper review section 3, core formula; a null slot contributes E_null = 0).
  * Summed in slot order in float32 with one rounding to dtype; no atomics, so
  * the result is bitwise reproducible. Slots with slot_pos outside
- * [0, T*min(K,N)) are skipped. y_shared [T][d] may be NULL (no shared expert).
- * y_perm: [T*min(K,N)][d] dtype; y: [T][d] dtype.
+ * [0, T*min(K,N)) are skipped. y_shared [T][d] float32, may be NULL (no shared
+ * expert). y_perm: [T*min(K,N)][d] float32; y: [T][d] dtype.
  */
 moe_status moe_combine(const moe_dims* dims, const void* y_perm, const int32_t* slot_pos,
                        const float* topk_w, const void* y_shared, void* y, moe_stream stream);

@@ -38,6 +38,25 @@ def assert_close_rms(got, ref, tol, what=""):
     assert err <= tol * scale, f"{what}: max abs error {err} > {tol} * RMS {scale}"
 
 
+def assert_rows_close(got, ref, tol, what=""):
+    """Layer-output tolerance, one token row at a time: max_j |got - ref| <= tol * RMS_j(ref)
+    for every row; a row whose reference is exactly zero must be exactly zero. The
+    whole-tensor ratio max|err| / RMS(ref) is printed as well."""
+    got, ref = vals(got), np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return
+    err = np.abs(got - ref)
+    row_rms = np.sqrt((ref * ref).mean(axis=1))
+    row_err = err.max(axis=1)
+    zero = row_rms == 0
+    assert (row_err[zero] == 0).all(), f"{what}: an all-zero reference row is not exactly zero"
+    ratio = np.where(zero, 0.0, row_err / np.where(zero, 1.0, row_rms))
+    worst = int(np.argmax(ratio))
+    say(f"  {what}: per-row max|err|/RMS(row) = {ratio.max():.3e} (row {worst}), "
+        f"whole-tensor max|err|/RMS = {err.max() / max(rms(ref), 1e-300):.3e} (tol {tol:g})")
+    assert ratio.max() <= tol, f"{what}: row {worst} error {row_err[worst]} > {tol} * RMS(row) {row_rms[worst]}"
+
+
 def bf16_tensor(a_f32):
     from workloads import bf16_round
     return to_device(bf16_round(np.asarray(a_f32, dtype=np.float32)))

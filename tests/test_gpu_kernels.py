@@ -10,8 +10,8 @@ import token_choice_routing_amd as tcr
 from oracle import moe_oracle as O
 from token_choice_routing_amd.layer import to_device, to_host
 from workloads import CONFIGS, bf16_round, generate
-from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close_rms, empty, route_from_logits, say,
-                            vals)
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close_rms, assert_rows_close, empty,
+                            route_from_logits, say, vals)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +80,9 @@ def test_route_gemm_logits_and_flip_rule(T, d, N, M, K, dtype):
     torch.cuda.synchronize()
     gl, gt, gw, gn = to_host(logits), to_host(topk), to_host(tw), to_host(nr)
     ref = O.router_logits(xv, w.astype(np.float64), b, btok.astype(np.float64))
-    err = np.abs(gl - ref).max()
-    say(f"  max |logit err| = {err:.3e}")
-    assert err < 2e-6
+    err = (np.abs(gl - ref) / np.maximum(1.0, np.abs(ref))).max()
+    say(f"  max |logit err| / max(1, |logit|) = {err:.3e}")
+    assert err < 1e-6
     # routing from the GPU's own logits is the oracle's routing of those logits, bit for bit
     ot, ow, on = O.route(gl.astype(np.float64), N, M, K)
     np.testing.assert_array_equal(gt, ot)
@@ -165,8 +165,7 @@ def _ffn_run(lengths, d, f, dtype="bf16", seed=0, slack=7, offsets=None):
     A, Wg, Wu, Wd = conv(a), conv(wg), conv(wu), conv(wd)
     off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32) if offsets is None else offsets
     dims = tcr.make_dims(max(rows, 1), d, max(G, 1), 0, 1, f, 0, tcr.MOE_BF16 if dtype == "bf16" else tcr.MOE_F32)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    out = torch.full((rows, d), 3.0, dtype=tdt, device="cuda")     # sentinel outside the segments
+    out = torch.full((rows, d), 3.0, dtype=torch.float32, device="cuda")  # sentinel outside the segments
     ws = empty((max(tcr.expert_ffn_workspace_bytes(dims, f, rows), 16),), torch.uint8)
     tcr.moe_expert_ffn(dims, G, f, rows, to_device(A), to_device(off), to_device(Wg), to_device(Wu),
                        to_device(Wd), out, ws)
@@ -189,14 +188,14 @@ def test_expert_ffn_segments_bf16(lengths, d, f):
     say(f"expert_ffn bf16 lengths={lengths[:8]} d={d} d_ff={f}")
     got, ref, R, rows = _ffn_run(lengths, d, f, "bf16", seed=d + f)
     if R:
-        assert_close_rms(got[:R], ref[:R], TOL_BF16, "segments")
+        assert_rows_close(got[:R], ref[:R], TOL_BF16, "segments")
     assert (got[R:] == 3.0).all(), "rows outside the segments were written"
 
 
 def test_expert_ffn_f32():
     say("expert_ffn f32 (tiny workload shape)")
     got, ref, R, rows = _ffn_run([27, 0, 31, 26, 30, 1, 60, 38], 64, 128, "f32", seed=3)
-    assert_close_rms(got[:R], ref[:R], TOL_F32, "segments f32")
+    assert_rows_close(got[:R], ref[:R], TOL_F32, "segments f32")
     assert (got[R:] == 3.0).all()
 
 
@@ -205,7 +204,7 @@ def test_expert_ffn_clamps_bad_offsets():
     off = np.array([0, 40, 10_000_000], dtype=np.int32)
     got, ref, R, rows = _ffn_run([40, 10], 128, 64, "bf16", seed=5, slack=0, offsets=off)
     assert rows == 50
-    assert_close_rms(got, ref, TOL_BF16, "clamped segments")   # numpy slicing clamps the same way
+    assert_rows_close(got, ref, TOL_BF16, "clamped segments")   # numpy slicing clamps the same way
 
 
 @pytest.mark.parametrize("T,K,d,shared", [(1000, 4, 1024, True), (333, 8, 2048, False), (64, 2, 64, False)])
@@ -218,16 +217,17 @@ def test_combine(T, K, d, shared):
     topk, w, _ = O.route(s, N, M, K)
     _, off, _, slot = O.permute(topk, N)
     Rmax = T * min(K, N)
-    yp = bf16_round(rng.standard_normal((Rmax, d)).astype(np.float32))
-    ys = bf16_round(rng.standard_normal((T, d)).astype(np.float32)) if shared else None
+    yp = rng.standard_normal((Rmax, d)).astype(np.float32)
+    ys = rng.standard_normal((T, d)).astype(np.float32) if shared else None
     w32 = w.astype(np.float32)
     dims = tcr.make_dims(T, d, N, M, K, 64, 64 if shared else 0, tcr.MOE_BF16)
     y = empty((T, d), torch.bfloat16)
     tcr.moe_combine(dims, to_device(yp), to_device(slot), to_device(w32), to_device(ys) if shared else None, y)
     torch.cuda.synchronize()
-    ref = O.combine(vals(yp), slot, w32.astype(np.float64), vals(ys) if shared else None, d_model=d)
+    ref = O.combine(yp.astype(np.float64), slot, w32.astype(np.float64),
+                    ys.astype(np.float64) if shared else None, d_model=d)
     got = vals(to_host(y))
-    assert_close_rms(got, ref, TOL_BF16, "combine")
+    assert_rows_close(got, ref, TOL_BF16, "combine")
     # float32 accumulation + one bf16 rounding: within one bf16 half-ulp plus accumulation noise
     assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
 

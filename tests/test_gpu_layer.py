@@ -15,7 +15,8 @@ from oracle import moe_oracle as O
 from token_choice_routing_amd.layer import MoeLayer, to_device, to_host
 from workloads import CONFIGS, generate
 from workloads.configs import Config
-from tests.gpu_util import FLIP_GAP, TOL_BF16, TOL_F32, assert_close_rms, empty, say, vals
+from tests.gpu_util import FLIP_GAP, TOL_BF16, TOL_F32, assert_rows_close, empty, say, vals
+from workloads import bf16_round
 
 pytestmark = pytest.mark.gpu
 
@@ -51,9 +52,9 @@ def check_routing(wl, out, rows=None, stats=True):
     btok = None if wl.null_bias_tok is None else wl.null_bias_tok[rows].astype(np.float64)
     ref = O.router_logits(wl.values("x")[rows], wl.values("w_router"), wl.null_bias, btok)
     fin = np.isfinite(ref)
-    err = np.abs(gl[rows][fin] - ref[fin]).max()
-    say(f"  max |logit err| = {err:.3e}")
-    assert err < 2e-6
+    err = (np.abs(gl[rows][fin] - ref[fin]) / np.maximum(1.0, np.abs(ref[fin]))).max()
+    say(f"  max |logit err| / max(1, |logit|) = {err:.3e}")
+    assert err < 1e-6
     ft, _, _ = O.route(ref, N, M, K)
     flips = np.nonzero((np.sort(ft, 1) != np.sort(ot[rows], 1)).any(1))[0]
     gap = O.decisive_gap(ref, N, M, K)
@@ -81,7 +82,7 @@ def check_full(wl, stats=True):
     layer, out = run_layer(wl)
     gl = check_routing(wl, out, stats=stats)
     ref = O.layer_forward(wl, logits=gl.astype(np.float64))
-    assert_close_rms(out["y"], ref["y"], tol(wl.cfg), f"y {wl.cfg.name}")
+    assert_rows_close(out["y"], ref["y"], tol(wl.cfg), f"y {wl.cfg.name}")
     nul = out["n_real"] == 0
     if nul.any() and not wl.cfg.d_ff_shared:
         assert (vals(out["y"])[nul] == 0).all()
@@ -116,7 +117,7 @@ def test_layer_full_size_sampled(name):
     if cfg.bias_mode == "calibrated":
         assert abs(out["n_real"].mean() - cfg.target_mean_r) <= 0.05
     yd, _, _ = O.layer_dense(wl, logits=gl.astype(np.float64), tokens=rows)
-    assert_close_rms(vals(out["y"])[rows], yd, TOL_BF16, f"y sampled {name}")
+    assert_rows_close(vals(out["y"])[rows], yd, TOL_BF16, f"y sampled {name}")
     # second run in the same launch configuration is bitwise identical
     y1 = out["y"].copy()
     layer.forward()
@@ -157,12 +158,12 @@ def test_null_routed_tokens_give_shared_output(shared):
     assert (out["n_real"][nul] == 0).all()
     if shared:
         dims = layer.dims
-        ys = empty((wl.cfg.T, wl.cfg.d_model), torch.bfloat16)
+        ys = empty((wl.cfg.T, wl.cfg.d_model), torch.float32)
         ws = empty((tcr.expert_ffn_workspace_bytes(dims, shared, wl.cfg.T),), torch.uint8)
         tcr.moe_expert_ffn(dims, 1, shared, wl.cfg.T, layer.x, None, layer.ws_gate, layer.ws_up,
                            layer.ws_down, ys, ws)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(out["y"][nul], to_host(ys)[nul])
+        np.testing.assert_array_equal(out["y"][nul], bf16_round(to_host(ys)[nul]))
     else:
         assert (vals(out["y"])[nul] == 0).all()
     check_routing(wl, out, stats=False)

@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_AUX = range(4)
+MOE_GEMM_GATE_UP, MOE_GEMM_DOWN = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -67,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_expert_ffn": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
                            _P, ctypes.c_size_t, _P],
         "moe_combine": [D, _P, _P, _P, _P, _P, _P],
+        "moe_grouped_gemm": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_int64, _P, _P, _P, _P, _P, _P],
         "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
         "moe_layer_forward": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P,
                               ctypes.c_size_t, _P],
@@ -174,6 +177,12 @@ def moe_expert_ffn(dims, n_groups, d_ff, max_rows, a, offsets, w_gate, w_up, w_d
                                           _ptr(a), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
                                           _ptr(w_down), _ptr(out), wp, wb, _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_grouped_gemm(dims, op, n_groups, n_out, k_dim, rows, a, offsets, b0, b1, out, stream=None):
+    _check(load_library().moe_grouped_gemm(ctypes.byref(dims), int(op), int(n_groups), int(n_out),
+                                            int(k_dim), int(rows), _ptr(a), _ptr(offsets), _ptr(b0),
+                                            _ptr(b1), _ptr(out), _stream(stream)), "moe_grouped_gemm")
 
 
 def moe_combine(dims, y_perm, slot_pos, topk_w, y_shared, y, stream=None):

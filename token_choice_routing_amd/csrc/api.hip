@@ -93,8 +93,8 @@ LayerWs layer_ws(const moe_dims* d) {
   w.permute = take(permute_ws_bytes(TK, N));
   w.xp = take((size_t)R * d->d_model * e);
   w.h = take(std::max((size_t)R * d->d_ff, (size_t)T * d->d_ff_shared) * e);
-  w.yp = take((size_t)R * d->d_model * e);
-  w.ys = take(d->d_ff_shared ? (size_t)T * d->d_model * e : 0);
+  w.yp = take((size_t)R * d->d_model * 4);
+  w.ys = take(d->d_ff_shared ? (size_t)T * d->d_model * 4 : 0);
   w.aux = take(aux_ws_bytes(T, N, M));
   w.total = o;
   return w;
@@ -209,6 +209,28 @@ moe_status moe_expert_ffn(const moe_dims* d, int32_t n_groups, int32_t d_ff, int
   FfnArgs f{d->dtype == MOE_BF16, n_groups, d->d_model, d_ff, rows, a, offsets, w_gate, w_up,
             w_down, ws, out, cu_count()};
   HIP_TRY(launch_expert_ffn(f, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int32_t n_out,
+                            int32_t k_dim, int64_t rows, const void* a, const int32_t* offsets,
+                            const void* b0, const void* b1, void* out, moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (op != MOE_GEMM_GATE_UP && op != MOE_GEMM_DOWN) return MOE_ERR_ARG;
+  if (n_groups < 1 || n_groups > MOE_MAX_EXPERTS + 1 || n_out < 8 || n_out % 8 || k_dim < 8 ||
+      k_dim % 8 || rows < 0)
+    return MOE_ERR_ARG;
+  if (!offsets && n_groups != 1) return MOE_ERR_ARG;
+  MOE_TRY(need(a));
+  MOE_TRY(maybe(offsets));
+  MOE_TRY(need(b0));
+  if (op == MOE_GEMM_GATE_UP) MOE_TRY(need(b1));
+  MOE_TRY(need(out));
+  if (rows == 0) return MOE_OK;
+  (void)hipGetLastError();
+  GemmArgs g{d->dtype == MOE_BF16, op, n_groups, n_out, k_dim, rows, a, offsets, b0,
+             op == MOE_GEMM_GATE_UP ? b1 : nullptr, out, cu_count()};
+  HIP_TRY(launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 

@@ -6,9 +6,10 @@
 // E_null(x) = 0 and is skipped (slot_pos = -1).
 //
 // One wavefront per token row: the K (position, weight) pairs are loaded once
-// by lanes 0..K-1 and broadcast with shuffles; each lane owns 16-byte vectors
-// of the row and accumulates in float32 in slot order, then rounds once. No
-// atomics, so repeated runs are bitwise identical.
+// by lanes 0..K-1 and broadcast with shuffles; each lane owns 8-element
+// vectors of the row and accumulates the float32 expert outputs in float32 in
+// slot order, then rounds once to the output type. No atomics, so repeated
+// runs are bitwise identical.
 #include <algorithm>
 
 #include "common.hpp"
@@ -50,10 +51,11 @@ struct Vec8<float> {
   }
 };
 
+// y_perm and y_shared are float32; y is ET (bf16 or float32).
 template <typename ET, int VPL>  // VPL: 8-element vectors per lane per pass
 __global__ void __launch_bounds__(256)
-combine_kernel(const ET* __restrict__ y_perm, const int32_t* __restrict__ slot_pos,
-               const float* __restrict__ topk_w, const ET* __restrict__ y_shared,
+combine_kernel(const float* __restrict__ y_perm, const int32_t* __restrict__ slot_pos,
+               const float* __restrict__ topk_w, const float* __restrict__ y_shared,
                ET* __restrict__ y, int64_t T, int K, int d, int64_t max_rows) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
@@ -73,7 +75,7 @@ combine_kernel(const ET* __restrict__ y_perm, const int32_t* __restrict__ slot_p
       for (int u = 0; u < VPL; ++u) {
         const int v = v0 + u * kWave + lane;
         if (y_shared && v < vpr) {
-          Vec8<ET>::load(y_shared + t * d + v * 8, acc[u]);
+          Vec8<float>::load(y_shared + t * d + v * 8, acc[u]);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[u][j] = 0.0f;
@@ -88,7 +90,7 @@ combine_kernel(const ET* __restrict__ y_perm, const int32_t* __restrict__ slot_p
           const int v = v0 + u * kWave + lane;
           if (v < vpr) {
             float r[8];
-            Vec8<ET>::load(y_perm + (int64_t)p * d + v * 8, r);
+            Vec8<float>::load(y_perm + (int64_t)p * d + v * 8, r);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[u][j] = fmaf(w, r[j], acc[u][j]);
           }
@@ -107,19 +109,18 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((a.T + 3) / 4, 65536);
   const int vpr = a.d / 8;
+  const float* yp = static_cast<const float*>(a.y_perm);
+  const float* ys = static_cast<const float*>(a.y_shared);
   if (a.bf16) {
     if (vpr >= 4 * kWave)
       combine_kernel<bf16_t, 4><<<(unsigned)blocks, 256, 0, stream>>>(
-          static_cast<const bf16_t*>(a.y_perm), a.slot_pos, a.topk_w,
-          static_cast<const bf16_t*>(a.y_shared), static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
+          yp, a.slot_pos, a.topk_w, ys, static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
     else
       combine_kernel<bf16_t, 2><<<(unsigned)blocks, 256, 0, stream>>>(
-          static_cast<const bf16_t*>(a.y_perm), a.slot_pos, a.topk_w,
-          static_cast<const bf16_t*>(a.y_shared), static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
+          yp, a.slot_pos, a.topk_w, ys, static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
   } else {
     combine_kernel<float, 1><<<(unsigned)blocks, 256, 0, stream>>>(
-        static_cast<const float*>(a.y_perm), a.slot_pos, a.topk_w,
-        static_cast<const float*>(a.y_shared), static_cast<float*>(a.y), a.T, a.K, a.d, a.max_rows);
+        yp, a.slot_pos, a.topk_w, ys, static_cast<float*>(a.y), a.T, a.K, a.d, a.max_rows);
   }
   return hipGetLastError();
 }

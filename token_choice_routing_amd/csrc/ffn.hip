@@ -10,7 +10,10 @@
 // bf16 path, MI355X design:
 //  * v_mfma_f32_32x32x16_bf16 with float32 accumulation. The MFMA "A" operand
 //    is the weight tile and "B" the activation tile, so each lane ends up with
-//    four consecutive output columns of one row: 8-byte bf16 stores.
+//    four consecutive output columns of one row (8-byte bf16 / 16-byte fp32
+//    stores). h is stored in bf16 because the down projection's MFMA reads
+//    bf16; the expert output stays float32 so that the combine rounds the
+//    layer output only once.
 //  * Workgroup tile: 128 rows x 128 weight rows x 64 K, four wavefronts of
 //    64 x 64. For the gate/up pass the 128 weight rows are 64 gate + 64 up rows
 //    of the same output columns, so a lane holds gate and up values of the same
@@ -97,12 +100,15 @@ __device__ void build_tile_table(TileTable& tt, const int32_t* offsets, int grou
   __syncthreads();
 }
 
-template <int MODE>
+// MODE kSwiGLU writes h as bf16 (the next MFMA's input); kPlain writes float32.
+// DENSE = 1 is the same code instantiated for the single-segment (shared
+// expert) launches, so profiles report the two uses separately.
+template <int MODE, int DENSE>
 __global__ void __launch_bounds__(kFfnThreads)
 grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                          int groups, int64_t max_rows, const bf16_t* __restrict__ B0,
                          const bf16_t* __restrict__ B1, int Nout, int Kdim,
-                         bf16_t* __restrict__ C) {
+                         void* __restrict__ Cout) {
   __shared__ TileTable tt;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][kBM * kBK];  // [buf][A|B][tile]
   constexpr int OC = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
@@ -217,8 +223,8 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
     for (int ms = 0; ms < 2; ++ms) {
       const int rl = wm * 64 + ms * 32 + l32;
       if (rl >= rows_valid) continue;
-      bf16_t* crow = C + (int64_t)(m0 + rl) * Nout;
       if (MODE == kSwiGLU) {
+        bf16_t* crow = static_cast<bf16_t*>(Cout) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = ntile * OC + wn * 32 + 8 * g + 4 * half;
@@ -230,6 +236,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
           }
         }
       } else {
+        float* crow = static_cast<float*>(Cout) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -237,8 +244,8 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
             const int col = ntile * OC + wn * 64 + ns * 32 + 8 * g + 4 * half;
             if (col < Nout) {
               const f32x16_t& v = acc[ns][ms];
-              *reinterpret_cast<u32x2_t*>(crow + col) =
-                  u32x2_t{pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+              *reinterpret_cast<f32x4_t*>(crow + col) =
+                  f32x4_t{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
             }
           }
       }
@@ -284,36 +291,58 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
   }
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
-  if (a.max_rows <= 0) return hipSuccess;
-  if (a.bf16) {
-    // persistent grid: 2 workgroups per CU (64 KiB LDS each), a multiple of 8
-    const int64_t upper_m = a.max_rows / kBM + a.groups;
-    const int64_t t1 = upper_m * ((a.d_ff + kBN / 2 - 1) / (kBN / 2));
-    const int64_t t2 = upper_m * ((a.d_model + kBN - 1) / kBN);
-    const int cap = std::max(8, a.num_cus * 2 / 8 * 8);
-    const unsigned g1 = (unsigned)std::min<int64_t>(cap, (t1 + 7) / 8 * 8);
-    const unsigned g2 = (unsigned)std::min<int64_t>(cap, (t2 + 7) / 8 * 8);
-    grouped_gemm_bf16_kernel<kSwiGLU><<<g1, kFfnThreads, 0, stream>>>(
-        static_cast<const bf16_t*>(a.a), a.offsets, a.groups, a.max_rows,
-        static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), a.d_ff,
-        a.d_model, static_cast<bf16_t*>(a.h));
-    grouped_gemm_bf16_kernel<kPlain><<<g2, kFfnThreads, 0, stream>>>(
-        static_cast<const bf16_t*>(a.h), a.offsets, a.groups, a.max_rows,
-        static_cast<const bf16_t*>(a.w_down), nullptr, a.d_model, a.d_ff,
-        static_cast<bf16_t*>(a.out));
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
+  if (g.max_rows <= 0) return hipSuccess;
+  if (g.bf16) {
+    // persistent grid: 2 workgroups per CU (about 68 KiB LDS each), a multiple of 8
+    const int oc = g.op == 0 ? kBN / 2 : kBN;
+    const int64_t upper = (g.max_rows / kBM + g.groups) * ((g.n_out + oc - 1) / oc);
+    const int cap = std::max(8, g.num_cus * 2 / 8 * 8);
+    const unsigned grid = (unsigned)std::min<int64_t>(cap, (upper + 7) / 8 * 8);
+    const bf16_t* A = static_cast<const bf16_t*>(g.a);
+    const bf16_t* B0 = static_cast<const bf16_t*>(g.b0);
+    const bf16_t* B1 = static_cast<const bf16_t*>(g.b1);
+    const bool dense = g.offsets == nullptr;
+    if (g.op == 0) {
+      if (dense)
+        grouped_gemm_bf16_kernel<kSwiGLU, 1><<<grid, kFfnThreads, 0, stream>>>(
+            A, g.offsets, g.groups, g.max_rows, B0, B1, g.n_out, g.k_dim, g.out);
+      else
+        grouped_gemm_bf16_kernel<kSwiGLU, 0><<<grid, kFfnThreads, 0, stream>>>(
+            A, g.offsets, g.groups, g.max_rows, B0, B1, g.n_out, g.k_dim, g.out);
+    } else {
+      if (dense)
+        grouped_gemm_bf16_kernel<kPlain, 1><<<grid, kFfnThreads, 0, stream>>>(
+            A, g.offsets, g.groups, g.max_rows, B0, nullptr, g.n_out, g.k_dim, g.out);
+      else
+        grouped_gemm_bf16_kernel<kPlain, 0><<<grid, kFfnThreads, 0, stream>>>(
+            A, g.offsets, g.groups, g.max_rows, B0, nullptr, g.n_out, g.k_dim, g.out);
+    }
   } else {
-    const int64_t n1 = a.max_rows * a.d_ff, n2 = a.max_rows * a.d_model;
-    grouped_gemm_f32_kernel<kSwiGLU><<<(unsigned)((n1 + 255) / 256), 256, 0, stream>>>(
-        static_cast<const float*>(a.a), a.offsets, a.groups, a.max_rows,
-        static_cast<const float*>(a.w_gate), static_cast<const float*>(a.w_up), a.d_ff, a.d_model,
-        static_cast<float*>(a.h));
-    grouped_gemm_f32_kernel<kPlain><<<(unsigned)((n2 + 255) / 256), 256, 0, stream>>>(
-        static_cast<const float*>(a.h), a.offsets, a.groups, a.max_rows,
-        static_cast<const float*>(a.w_down), nullptr, a.d_model, a.d_ff,
-        static_cast<float*>(a.out));
+    const int64_t n = g.max_rows * g.n_out;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (g.op == 0)
+      grouped_gemm_f32_kernel<kSwiGLU><<<grid, 256, 0, stream>>>(
+          static_cast<const float*>(g.a), g.offsets, g.groups, g.max_rows,
+          static_cast<const float*>(g.b0), static_cast<const float*>(g.b1), g.n_out, g.k_dim,
+          static_cast<float*>(g.out));
+    else
+      grouped_gemm_f32_kernel<kPlain><<<grid, 256, 0, stream>>>(
+          static_cast<const float*>(g.a), g.offsets, g.groups, g.max_rows,
+          static_cast<const float*>(g.b0), nullptr, g.n_out, g.k_dim, static_cast<float*>(g.out));
   }
   return hipGetLastError();
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
+  if (a.max_rows <= 0) return hipSuccess;
+  GemmArgs g1{a.bf16, 0, a.groups, a.d_ff, a.d_model, a.max_rows, a.a, a.offsets, a.w_gate,
+              a.w_up, a.h, a.num_cus};
+  hipError_t e = launch_grouped_gemm(g1, stream);
+  if (e != hipSuccess) return e;
+  GemmArgs g2{a.bf16, 1, a.groups, a.d_model, a.d_ff, a.max_rows, a.h, a.offsets, a.w_down,
+              nullptr, a.out, a.num_cus};
+  return launch_grouped_gemm(g2, stream);
 }
 
 }  // namespace moe

@@ -57,6 +57,21 @@ struct FfnArgs {
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
 
+struct GemmArgs {
+  bool bf16;
+  int op;              // 0: h = silu(a b0^T) * (a b1^T) -> dtype; 1: out = a b0^T -> float32
+  int groups;
+  int n_out, k_dim;
+  int64_t max_rows;
+  const void* a;       // [max_rows][k_dim]
+  const int32_t* offsets;  // [groups+1] device, or NULL: one segment of max_rows rows
+  const void* b0;      // [groups][n_out][k_dim]
+  const void* b1;
+  void* out;           // [max_rows][n_out]
+  int num_cus;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
+
 struct CombineArgs {
   bool bf16;
   int64_t T;

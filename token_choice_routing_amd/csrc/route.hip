@@ -17,9 +17,12 @@
 // MI355X design. x is bf16 and the router weight float32. Every bf16 x bf16
 // product is exact in float32, and an fp32 weight splits exactly into three
 // bf16 parts (hi + mid + lo, each the bf16 rounding of what is left), so three
-// bf16 MFMAs give the float32-accurate logits at MFMA rate instead of the
-// slower float32 path. The null row is a plain float32 dot product on the
-// vector ALUs. Each workgroup scores 64 tokens; the logits go through LDS to
+// bf16 MFMAs give the products exactly at MFMA rate instead of the slower
+// float32 path. MFMA partial sums over 64-wide K blocks are accumulated across
+// blocks in fp64, which keeps the logits within a few 1e-7 of the exact value
+// (fp32 accumulation over d = 2048 terms drifts by a few 1e-6, too close to the
+// 1e-5 near-tie margin of the routing parity rule). The null row is an fp64
+// dot product on the vector ALUs. Each workgroup scores 64 tokens; the logits go through LDS to
 // the epilogue, where one wavefront handles one token with a lane per expert.
 #include <algorithm>
 
@@ -148,54 +151,62 @@ route_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3,
     const bf16x8_t* b0 = reinterpret_cast<const bf16x8_t*>(w3 + (int64_t)erow * d);
     const bf16x8_t* b1 = reinterpret_cast<const bf16x8_t*>(w3 + plane + (int64_t)erow * d);
     const bf16x8_t* b2 = reinterpret_cast<const bf16x8_t*>(w3 + 2 * plane + (int64_t)erow * d);
-    f32x16_t acc = {};
-    int ks = 0;
-#pragma unroll 8
-    for (; ks < nch / 2; ++ks) {
-      const int cidx = 2 * ks + half;
-      const bf16x8_t a = ap[cidx];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0[cidx], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1[cidx], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b2[cidx], acc, 0, 0, 0);
-    }
-    if (ks < nsteps) {  // odd number of chunks: the upper half-wave contributes zeros
-      const int cidx = 2 * ks + half;
-      bf16x8_t a = {}, v0 = {}, v1 = {}, v2 = {};
-      if (cidx < nch) { a = ap[cidx]; v0 = b0[cidx]; v1 = b1[cidx]; v2 = b2[cidx]; }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v1, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v2, acc, 0, 0, 0);
+    // fp32 MFMA partial sums over 64-wide K blocks, accumulated across blocks in fp64
+    double acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+    for (int kb = 0; kb < nsteps; kb += 4) {
+      f32x16_t part = {};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cidx = 2 * (kb + u) + half;
+        bf16x8_t a = {}, v0 = {}, v1 = {}, v2 = {};
+        if (kb + u < nsteps && cidx < nch) {
+          a = ap[cidx];
+          v0 = b0[cidx];
+          v1 = b1[cidx];
+          v2 = b2[cidx];
+        }
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v2, part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v1, part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v0, part, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += (double)part[i];
     }
     const int e = et * 32 + (lane & 31);
     if (e < N) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tl = wt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        sl[tl * ld + e] = acc[i];
+        sl[tl * ld + e] = (float)acc[i];
       }
     }
   }
-  // Null row: float32 dot product, 4 threads per token, combined in a fixed order.
+  // Null row: x (bf16) times the float32 row, each product exact in fp64, summed in
+  // fp64 by 4 threads per token and combined in a fixed order.
   {
     const int tl = threadIdx.x >> 2, part = threadIdx.x & 3;
     const int64_t t = min<int64_t>(t0 + tl, T - 1);
     const bf16_t* xr = x + t * d;
-    float acc = 0.0f;
+    double acc = 0.0;
     for (int c = part; c < nch; c += 4) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
-      const float* wn = w_null + c * 8;
+      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(w_null + c * 8);
+      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(w_null + c * 8 + 4);
+      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        acc = fmaf(__uint_as_float(v[h] << 16), wn[2 * h], acc);
-        acc = fmaf(__uint_as_float(v[h] & 0xffff0000u), wn[2 * h + 1], acc);
+        acc = fma((double)__uint_as_float(v[h] << 16), (double)wv[2 * h], acc);
+        acc = fma((double)__uint_as_float(v[h] & 0xffff0000u), (double)wv[2 * h + 1], acc);
       }
     }
-    const float a01 = acc + __shfl_xor(acc, 1, kWave);
-    const float sum = a01 + __shfl_xor(a01, 2, kWave);
+    const double a01 = acc + __shfl_xor(acc, 1, kWave);
+    const double sum = a01 + __shfl_xor(a01, 2, kWave);
     if (part == 0 && tl < nt) {
-      float v = sum + null_bias;
-      if (null_bias_tok) v += null_bias_tok[t0 + tl];
-      sl[tl * ld + N] = v;
+      double v = sum + (double)null_bias;
+      if (null_bias_tok) v += (double)null_bias_tok[t0 + tl];
+      sl[tl * ld + N] = (float)v;
     }
   }
   __syncthreads();

@@ -27,7 +27,10 @@ def to_host(t):
 
 
 class MoeLayer:
-    def __init__(self, workload, device="cuda", T=None):
+    WEIGHTS = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+
+    def __init__(self, workload, device="cuda", T=None, weights_from=None):
+        """weights_from: another MoeLayer whose device weights are reused (same arrays)."""
         cfg = workload.cfg
         self.cfg = cfg
         self.T = cfg.T if T is None else T
@@ -36,16 +39,17 @@ class MoeLayer:
         dt = torch.bfloat16 if self.bf16 else torch.float32
         dev = device
         self.x = to_device(workload.x[: self.T], dev)
-        self.w_router = to_device(workload.w_router, dev)
         self.null_bias = float(workload.null_bias)
         self.null_bias_tok = (to_device(workload.null_bias_tok[: self.T], dev)
                               if workload.null_bias_tok is not None else None)
-        self.w_gate = to_device(workload.w_gate, dev)
-        self.w_up = to_device(workload.w_up, dev)
-        self.w_down = to_device(workload.w_down, dev)
-        self.ws_gate = to_device(workload.ws_gate, dev)
-        self.ws_up = to_device(workload.ws_up, dev)
-        self.ws_down = to_device(workload.ws_down, dev)
+        for name in self.WEIGHTS:
+            arr = getattr(workload, name)
+            if weights_from is not None and arr is not None:
+                t = getattr(weights_from, name)
+                assert t is not None and tuple(t.shape) == arr.shape
+            else:
+                t = to_device(arr, dev)
+            setattr(self, name, t)
         N, M, K = cfg.n_experts, cfg.n_null, cfg.top_k
         T_ = self.T
         self.y = torch.empty((T_, cfg.d_model), dtype=dt, device=dev)
