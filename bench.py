@@ -64,6 +64,22 @@ class Timer:
         b.synchronize()
         return a.elapsed_time(b) * 1e3 / iters   # microseconds per call
 
+    def run_cold(self, fn, iters, flush):
+        """Average of single launches, each after a write of a buffer larger than the
+        256 MB last-level cache (the flush is outside the timed events)."""
+        torch = self.torch
+        fn()
+        s = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            flush.zero_()
+            a.record(s)
+            fn()
+            b.record(s)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) * 1e3 / iters
+
 
 def layer_flops(cfg, R, T):
     return 6.0 * cfg.d_model * cfg.d_ff * R + 6.0 * cfg.d_model * cfg.d_ff_shared * T
@@ -137,6 +153,7 @@ def kernel_table(torch, tcr, layer, iters):
         tcr.moe_aux_stats(dims, logits, topk, fo, Po, co, sc, ws_a)
 
     tm = Timer(torch)
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
     route()
     permute_gather()
     torch.cuda.synchronize()
@@ -158,8 +175,10 @@ def kernel_table(torch, tcr, layer, iters):
     add("permute", t_perm, 4 * T * K + 4 * R + 4 * T * K + 4 * (2 * N + 1), 0, 3)
     t_pg = tm.run(permute_gather, iters)
     add("gather", max(t_pg - t_perm, 1e-3), 2 * R * d * 2 + 4 * R)
-    add("gemm_gate_up", tm.run(gemm1, iters), R * d * 2 + active * 2 * f * d * 2 + R * f * 2, 4.0 * R * d * f)
-    add("gemm_down", tm.run(gemm2, iters), R * f * 2 + active * d * f * 2 + R * d * 4, 2.0 * R * d * f)
+    add("gemm_gate_up", tm.run_cold(gemm1, iters, flush), R * d * 2 + active * 2 * f * d * 2 + R * f * 2,
+        4.0 * R * d * f)
+    add("gemm_down", tm.run_cold(gemm2, iters, flush), R * f * 2 + active * d * f * 2 + R * d * 4,
+        2.0 * R * d * f)
     if fs:
         add("shared_gate_up", tm.run(sgemm1, iters), T * d * 2 + 2 * fs * d * 2 + T * fs * 2, 4.0 * T * d * fs)
         add("shared_down", tm.run(sgemm2, iters), T * fs * 2 + d * fs * 2 + T * d * 4, 2.0 * T * d * fs)
@@ -298,7 +317,8 @@ def main():
     kernels, _ = kernel_table(torch, tcr, layer, args.kernel_iters)
     dom = "gemm_gate_up"
     rl = roofline(kernels[dom])
-    rl["kernel"] = "grouped_gemm_bf16_kernel<gate/up SwiGLU> (routed)"
+    rl["kernel"] = ("grouped_gemm_bf16_kernel<0, 0>: routed gate/up + SwiGLU, standalone launch on "
+                    "the layer's permuted rows, last-level cache flushed before each timed launch")
     rl["traffic"] = traffic_from_profiles("gemm_gate_up", cfg.name)
     line = {
         "metric": "MoE-layer tokens/s + real-expert TFLOP/s (% bf16 MFMA peak) vs rho",

@@ -42,7 +42,7 @@ def test_workspace_sizes_cover_the_worst_case():
         e = 2 if cfg.dtype == "bf16" else 4
         R = cfg.T * min(cfg.top_k, cfg.n_experts)
         total = tcr.workspace_bytes(d, MOE_WS_LAYER)
-        assert total >= R * cfg.d_model * e * 2 + R * cfg.d_ff * e
+        assert total >= R * cfg.d_model * 4 + R * cfg.d_ff * e   # float32 expert outputs + h
         assert tcr.workspace_bytes(d, MOE_WS_PERMUTE) > 0
         assert tcr.workspace_bytes(d, MOE_WS_AUX) > 0
         assert (tcr.workspace_bytes(d, MOE_WS_ROUTE) > 0) == (cfg.dtype == "bf16")

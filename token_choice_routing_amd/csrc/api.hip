@@ -67,7 +67,7 @@ int cu_count() {
 // Layer workspace layout (byte offsets, 256-byte aligned pieces).
 struct LayerWs {
   size_t logits, topk_idx, topk_w, n_real, counts, offsets, perm_token, slot_pos, route, permute,
-      xp, h, yp, ys, aux, total;
+      h, hs, yp, ys, acc, pool_counts, total;
 };
 
 LayerWs layer_ws(const moe_dims* d) {
@@ -90,12 +90,13 @@ LayerWs layer_ws(const moe_dims* d) {
   w.perm_token = take((size_t)R * 4);
   w.slot_pos = take((size_t)TK * 4);
   w.route = take(d->dtype == MOE_BF16 ? route_split_bytes(N, d->d_model) : 0);
-  w.permute = take(permute_ws_bytes(TK, N));
-  w.xp = take((size_t)R * d->d_model * e);
-  w.h = take(std::max((size_t)R * d->d_ff, (size_t)T * d->d_ff_shared) * e);
+  w.permute = take(permute_ws_bytes(T, N));
+  w.h = take((size_t)R * d->d_ff * e);
+  w.hs = take((size_t)T * d->d_ff_shared * e);
   w.yp = take((size_t)R * d->d_model * 4);
   w.ys = take(d->d_ff_shared ? (size_t)T * d->d_model * 4 : 0);
-  w.aux = take(aux_ws_bytes(T, N, M));
+  w.acc = take((size_t)(N + 3) * 8);
+  w.pool_counts = take((size_t)(N + M) * 4);
   w.total = o;
   return w;
 }
@@ -123,8 +124,8 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t which) {
   switch (which) {
     case MOE_WS_LAYER: return layer_ws(d).total;
     case MOE_WS_ROUTE: return d->dtype == MOE_BF16 ? route_split_bytes(d->n_experts, d->d_model) : 0;
-    case MOE_WS_PERMUTE: return permute_ws_bytes(d->T * d->top_k, d->n_experts);
-    case MOE_WS_AUX: return aux_ws_bytes(d->T, d->n_experts, d->n_null);
+    case MOE_WS_PERMUTE: return permute_ws_bytes(d->T, d->n_experts);
+    case MOE_WS_AUX: return aux_ws_bytes(d->n_experts, d->n_null);
   }
   return 0;
 }
@@ -157,9 +158,9 @@ moe_status moe_route(const moe_dims* d, const void* x, const float* w_router, fl
   }
   if (d->T == 0) return MOE_OK;
   (void)hipGetLastError();
-  RouteArgs a{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, x, w_router, null_bias,
-              null_bias_tok, logits_in, logits_out, topk_idx, topk_w, n_real,
-              static_cast<uint16_t*>(ws)};
+  RouteArgs a{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, false, x, w_router,
+              null_bias, null_bias_tok, logits_in, logits_out, topk_idx, topk_w, n_real,
+              static_cast<uint16_t*>(ws), nullptr, nullptr, nullptr};
   HIP_TRY(launch_route(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -175,13 +176,14 @@ moe_status moe_permute(const moe_dims* d, const int32_t* topk_idx, const void* x
   MOE_TRY(need(slot_pos));
   MOE_TRY(maybe(x));
   MOE_TRY(maybe(x_perm));
-  const size_t need_ws = permute_ws_bytes(d->T * d->top_k, d->n_experts);
+  const size_t need_ws = permute_ws_bytes(d->T, d->n_experts);
   if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   MOE_TRY(maybe(ws));
   if (d->T == 0) return MOE_OK;
   (void)hipGetLastError();
-  PermuteArgs a{d->T, d->top_k, d->n_experts, d->d_model, (int)elt_bytes(d), topk_idx, x, counts,
-                offsets, perm_token, slot_pos, x_perm, static_cast<int32_t*>(ws)};
+  PermuteArgs a{d->T, d->top_k, d->n_experts, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx,
+                x, counts, offsets, perm_token, slot_pos, x_perm, static_cast<int32_t*>(ws),
+                false, nullptr};
   HIP_TRY(launch_permute(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -228,9 +230,12 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
   MOE_TRY(need(out));
   if (rows == 0) return MOE_OK;
   (void)hipGetLastError();
-  GemmArgs g{d->dtype == MOE_BF16, op, n_groups, n_out, k_dim, rows, a, offsets, b0,
-             op == MOE_GEMM_GATE_UP ? b1 : nullptr, out, cu_count()};
-  HIP_TRY(launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+  GemmProblem g{static_cast<const uint16_t*>(a), nullptr, rows, offsets, n_groups, rows,
+                static_cast<const uint16_t*>(b0),
+                op == MOE_GEMM_GATE_UP ? static_cast<const uint16_t*>(b1) : nullptr, n_out, k_dim,
+                out};
+  HIP_TRY(launch_gemm_pair(d->dtype == MOE_BF16, op, g, GemmProblem{}, cu_count(),
+                           static_cast<hipStream_t>(stream), offsets ? 0 : 1));
   return MOE_OK;
 }
 
@@ -260,7 +265,7 @@ moe_status moe_aux_stats(const moe_dims* d, const float* logits, const int32_t* 
   MOE_TRY(need(P));
   MOE_TRY(maybe(counts));
   MOE_TRY(need(scalars));
-  const size_t need_ws = aux_ws_bytes(d->T, d->n_experts, d->n_null);
+  const size_t need_ws = aux_ws_bytes(d->n_experts, d->n_null);
   if (!ws || ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
   MOE_TRY(maybe(ws));
   if (d->T == 0) return MOE_OK;
@@ -310,41 +315,57 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   float* topk_w = ao.topk_w ? ao.topk_w : static_cast<float*>(at(L.topk_w));
   int32_t* n_real = ao.n_real ? ao.n_real : static_cast<int32_t*>(at(L.n_real));
   int32_t* offsets = ao.offsets ? ao.offsets : static_cast<int32_t*>(at(L.offsets));
+  int32_t* pool_counts = ao.counts ? ao.counts : static_cast<int32_t*>(at(L.pool_counts));
+  uint64_t* acc = static_cast<uint64_t*>(at(L.acc));
+  int32_t* perm_token = static_cast<int32_t*>(at(L.perm_token));
+  int32_t* slot_pos = static_cast<int32_t*>(at(L.slot_pos));
+  int32_t* permute_ws = static_cast<int32_t*>(at(L.permute));
   const bool want_stats = ao.counts || ao.f || ao.P || ao.scalars;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = d->dtype == MOE_BF16;
   const int64_t R = max_rows(d);
+  const int N = d->n_experts;
   (void)hipGetLastError();
 
-  RouteArgs ra{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, p->x, p->w_router,
+  // 1. scores, selection, weights; per-chunk expert histogram; statistics sums
+  RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
                p->null_bias, p->null_bias_tok, nullptr, logits, topk_idx, topk_w, n_real,
-               static_cast<uint16_t*>(at(L.route))};
+               static_cast<uint16_t*>(at(L.route)), permute_ws, acc, pool_counts};
   HIP_TRY(launch_route(ra, s));
 
-  PermuteArgs pa{d->T, d->top_k, d->n_experts, d->d_model, (int)elt_bytes(d), topk_idx, p->x,
-                 static_cast<int32_t*>(at(L.counts)), offsets,
-                 static_cast<int32_t*>(at(L.perm_token)), static_cast<int32_t*>(at(L.slot_pos)),
-                 at(L.xp), static_cast<int32_t*>(at(L.permute))};
+  // 2. counting sort (histograms already written) + statistics finalisation
+  AuxFinal af{acc, pool_counts, ao.f, ao.P, ao.counts, ao.scalars};
+  PermuteArgs pa{d->T, d->top_k, N, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx, nullptr,
+                 static_cast<int32_t*>(at(L.counts)), offsets, perm_token, slot_pos, nullptr,
+                 permute_ws, true, want_stats ? &af : nullptr};
   HIP_TRY(launch_permute(pa, s));
 
+  // 3. gate/up + SwiGLU: routed experts read x through perm_token (the gather), and the
+  //    shared expert runs in the same launch
   const int cus = cu_count();
-  FfnArgs fr{bf16, d->n_experts, d->d_model, d->d_ff, R, at(L.xp), offsets, p->w_gate, p->w_up,
-             p->w_down, at(L.h), at(L.yp), cus};
-  HIP_TRY(launch_expert_ffn(fr, s));
-  if (d->d_ff_shared) {
-    FfnArgs fs{bf16, 1, d->d_model, d->d_ff_shared, d->T, p->x, nullptr, p->ws_gate, p->ws_up,
-               p->ws_down, at(L.h), at(L.ys), cus};
-    HIP_TRY(launch_expert_ffn(fs, s));
-  }
-  CombineArgs ca{bf16, d->T, d->top_k, d->d_model, R, at(L.yp),
-                 static_cast<int32_t*>(at(L.slot_pos)), topk_w,
+  const uint16_t* x16 = static_cast<const uint16_t*>(p->x);
+  GemmProblem r1{x16, perm_token, d->T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate),
+                 static_cast<const uint16_t*>(p->w_up), d->d_ff, d->d_model, at(L.h)};
+  GemmProblem s1{};
+  if (d->d_ff_shared)
+    s1 = GemmProblem{x16, nullptr, d->T, nullptr, 1, d->T, static_cast<const uint16_t*>(p->ws_gate),
+                     static_cast<const uint16_t*>(p->ws_up), d->d_ff_shared, d->d_model, at(L.hs)};
+  HIP_TRY(launch_gemm_pair(bf16, 0, r1, s1, cus, s, 2));
+
+  // 4. down projection, routed and shared, float32 outputs
+  GemmProblem r2{static_cast<const uint16_t*>(at(L.h)), nullptr, R, offsets, N, R,
+                 static_cast<const uint16_t*>(p->w_down), nullptr, d->d_model, d->d_ff, at(L.yp)};
+  GemmProblem s2{};
+  if (d->d_ff_shared)
+    s2 = GemmProblem{static_cast<const uint16_t*>(at(L.hs)), nullptr, d->T, nullptr, 1, d->T,
+                     static_cast<const uint16_t*>(p->ws_down), nullptr, d->d_model,
+                     d->d_ff_shared, at(L.ys)};
+  HIP_TRY(launch_gemm_pair(bf16, 1, r2, s2, cus, s, 2));
+
+  // 5. weighted combine in slot order, one rounding
+  CombineArgs ca{bf16, d->T, d->top_k, d->d_model, R, at(L.yp), slot_pos, topk_w,
                  d->d_ff_shared ? at(L.ys) : nullptr, y};
   HIP_TRY(launch_combine(ca, s));
-  if (want_stats) {
-    AuxArgs xa{d->T, d->n_experts, d->n_null, d->top_k, logits, topk_idx, ao.f, ao.P, ao.counts,
-               ao.scalars, at(L.aux)};
-    HIP_TRY(launch_aux(xa, s));
-  }
   return MOE_OK;
 }
 

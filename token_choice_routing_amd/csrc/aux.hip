@@ -1,4 +1,5 @@
-// Load-balance and z-loss statistics over the N+M pool.
+// Load-balance and z-loss statistics over the N+M pool (standalone entry point;
+// the fused layer path computes the same sums in the router's epilogue).
 //
 // Paper review "Improving MoE Compute Efficiency by Composing Weight and Data
 // Sparsity", section 3, "load-balance loss" and "Z-loss":
@@ -8,56 +9,56 @@
 // The M null copies share one probability, so the pool softmax needs N+1
 // exponentials per token.
 //
-// Two kernels: each workgroup reduces a contiguous token range in float64 (one
-// wavefront per token, lanes over experts, tokens in order), then one
-// workgroup adds the per-workgroup partials in workgroup order. Pool-slot counts
-// use LDS integer atomics (order-free). Everything is bitwise reproducible.
+// Three small kernels: clear the accumulators; one wavefront per token, lanes
+// over experts, each workgroup summing its 64 tokens and adding them into
+// fixed-point integer accumulators (order-free, so bitwise reproducible); one
+// workgroup turns the sums into f, P, counts and the scalars.
 #include <algorithm>
 
+#include "aux_final.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 constexpr int kAuxThreads = 256;
-constexpr int kAuxMaxBlocks = 512;
-constexpr int kQ = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
+constexpr int kAuxBT = 64;
+constexpr int kQa = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
 
-static int aux_blocks(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>((T + 63) / 64, kAuxMaxBlocks)); }
+size_t aux_ws_bytes(int N, int M) {
+  return (size_t)(N + 3) * sizeof(uint64_t) + (size_t)(N + M) * sizeof(int32_t);
+}
 
-// per-block record: [N] real P sums, null P sum, sum lse^2, sum n_real (doubles), then counts
-__host__ __device__ inline size_t aux_rec_doubles(int N) { return (size_t)N + 3; }
-
-size_t aux_ws_bytes(int64_t T, int N, int M) {
-  const int nb = aux_blocks(T);
-  return (size_t)nb * aux_rec_doubles(N) * sizeof(double) + (size_t)nb * (N + M) * sizeof(int32_t);
+__global__ void aux_clear_kernel(uint64_t* __restrict__ acc, int nacc, int32_t* __restrict__ cnt,
+                                 int ncnt) {
+  for (int i = threadIdx.x; i < nacc; i += blockDim.x) acc[i] = 0;
+  for (int i = threadIdx.x; i < ncnt; i += blockDim.x) cnt[i] = 0;
 }
 
 __global__ void __launch_bounds__(kAuxThreads)
 aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
-                   int64_t T, int N, int M, int K, double* __restrict__ rec,
-                   int32_t* __restrict__ rec_counts) {
-  extern __shared__ double smd[];
+                   int64_t T, int N, int M, int K, uint64_t* __restrict__ acc,
+                   int32_t* __restrict__ cnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int nw = kAuxThreads / kWave;
-  double* wacc = smd;                                           // [nw][N+3]
-  int* cnt = reinterpret_cast<int*>(smd + nw * aux_rec_doubles(N));  // [N+M]
-  const int P = N + M;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) cnt[i] = 0;
+  const int rd = N + 3, P = N + M;
+  double* wacc = reinterpret_cast<double*>(smem_raw);          // [nw][N+3]
+  int* cnt_lds = reinterpret_cast<int*>(wacc + nw * rd);       // [N+M]
+  for (int i = threadIdx.x; i < P; i += blockDim.x) cnt_lds[i] = 0;
+  __syncthreads();
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int64_t per = (T + gridDim.x - 1) / gridDim.x;
-  const int64_t tb = blockIdx.x * per, te = min<int64_t>(T, tb + per);
-  double psum[kQ];
+  const int64_t tb = (int64_t)blockIdx.x * kAuxBT, te = min<int64_t>(T, tb + kAuxBT);
+  double psum[kQa];
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) psum[q] = 0.0;
+  for (int q = 0; q < kQa; ++q) psum[q] = 0.0;
   double pnull = 0.0, lz = 0.0;
   int nreal = 0;
-  __syncthreads();
   for (int64_t t = tb + wave; t < te; t += nw) {
     const float* s = logits + t * (N + 1);
-    float v[kQ];
+    float v[kQa];
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
+    for (int q = 0; q < kQa; ++q) {
       const int j = lane + q * kWave;
       v[q] = (j < N) ? s[j] : -INFINITY;
       m = fmaxf(m, v[q]);
@@ -65,96 +66,68 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
     const float sn = s[N];
     m = wave_max(m);
     if (M > 0) m = fmaxf(m, sn);
-    double ex[kQ], part = 0.0;
+    float ex[kQa];
+    double part = 0.0;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int j = lane + q * kWave;
-      ex[q] = (j < N) ? exp((double)v[q] - (double)m) : 0.0;
-      part += ex[q];
+    for (int q = 0; q < kQa; ++q) {
+      ex[q] = (lane + q * kWave < N) ? expf(v[q] - m) : 0.0f;
+      part += (double)ex[q];
     }
-    const double en = M > 0 ? exp((double)sn - (double)m) : 0.0;
-    const double z = wave_sum_double(part) + (double)M * en;
+    const float en = M > 0 ? expf(sn - m) : 0.0f;
+    const double z = wave_sum_double(part) + (double)M * (double)en;
+    const double iz = 1.0 / z;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) psum[q] += ex[q] / z;
-    pnull += en / z;
-    const double lse = (double)m + log(z);
-    lz += lse * lse;
+    for (int q = 0; q < kQa; ++q) psum[q] += (double)ex[q] * iz;
+    if (lane == 0) {
+      pnull += (double)en * iz;
+      const double lse = (double)m + log(z);
+      lz += lse * lse;
+    }
     if (lane < K) {
       const int id = topk_idx[t * K + lane];
-      if (id >= 0 && id < P) atomicAdd(&cnt[id], 1);
+      if (id >= 0 && id < P) atomicAdd(&cnt_lds[id], 1);
       nreal += (id >= 0 && id < N);
     }
   }
-  // per-wave totals into LDS, then the block record in wave order
-  const int rd = (int)aux_rec_doubles(N);
+  nreal = wave_sum_int(nreal);
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    const int j = lane + q * kWave;
-    if (j < N) wacc[wave * rd + j] = psum[q];
-  }
-  const double nr = (double)wave_sum_int(nreal);
+  for (int q = 0; q < kQa; ++q)
+    if (lane + q * kWave < N) wacc[wave * rd + lane + q * kWave] = psum[q];
   if (lane == 0) {
     wacc[wave * rd + N] = pnull;
     wacc[wave * rd + N + 1] = lz;
-    wacc[wave * rd + N + 2] = nr;
+    wacc[wave * rd + N + 2] = (double)nreal;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < rd; i += blockDim.x) {
-    double acc = 0.0;
-    for (int w = 0; w < nw; ++w) acc += wacc[w * rd + i];
-    rec[(int64_t)blockIdx.x * rd + i] = acc;
+    double s = 0.0;
+    for (int w = 0; w < nw; ++w) s += wacc[w * rd + i];
+    const double scale = (i == N + 1) ? kAuxZScale : (i == N + 2 ? 1.0 : kAuxPScale);
+    const uint64_t q = (uint64_t)(s * scale + 0.5);
+    if (q) atomicAdd(reinterpret_cast<unsigned long long*>(&acc[i]), (unsigned long long)q);
   }
-  for (int i = threadIdx.x; i < P; i += blockDim.x) rec_counts[(int64_t)blockIdx.x * P + i] = cnt[i];
+  for (int i = threadIdx.x; i < P; i += blockDim.x)
+    if (cnt_lds[i]) atomicAdd(&cnt[i], cnt_lds[i]);
 }
 
 __global__ void __launch_bounds__(kAuxThreads)
-aux_final_kernel(const double* __restrict__ rec, const int32_t* __restrict__ rec_counts, int nb,
-                 int64_t T, int N, int M, float* __restrict__ f, float* __restrict__ Pout,
-                 int32_t* __restrict__ counts, float* __restrict__ scalars) {
-  extern __shared__ double sfin[];
-  const int rd = (int)aux_rec_doubles(N);
-  const int P = N + M;
-  double* tot = sfin;            // [rd]
-  double* term = sfin + rd;      // [P]
-  for (int i = threadIdx.x; i < rd; i += blockDim.x) {
-    double acc = 0.0;
-    for (int b = 0; b < nb; ++b) acc += rec[(int64_t)b * rd + i];
-    tot[i] = acc;
-  }
-  __syncthreads();
-  const double invT = 1.0 / (double)T;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    long long c = 0;
-    for (int b = 0; b < nb; ++b) c += rec_counts[(int64_t)b * P + i];
-    const double Pi = (i < N ? tot[i] : tot[N]) * invT;
-    const double fi = (double)c * invT;
-    term[i] = fi * Pi;
-    if (f) f[i] = (float)fi;
-    if (Pout) Pout[i] = (float)Pi;
-    if (counts) counts[i] = (int32_t)c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && scalars) {
-    double lb = 0.0;
-    for (int i = 0; i < P; ++i) lb += term[i];
-    scalars[0] = (float)((double)N * lb);
-    scalars[1] = (float)(tot[N + 1] * invT);
-    scalars[2] = (float)(tot[N + 2] * invT);
-  }
+aux_final_kernel(AuxFinal a, int64_t T, int N, int M) {
+  extern __shared__ double terms[];
+  aux_finalize(a, T, N, M, terms);
 }
 
 hipError_t launch_aux(const AuxArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
-  const int nb = aux_blocks(a.T);
-  const int rd = (int)aux_rec_doubles(a.N);
-  double* rec = static_cast<double*>(a.ws);
-  int32_t* rec_counts = reinterpret_cast<int32_t*>(rec + (size_t)nb * rd);
-  const size_t lds1 = (size_t)(kAuxThreads / kWave) * rd * sizeof(double) + (size_t)(a.N + a.M) * sizeof(int);
+  uint64_t* acc = static_cast<uint64_t*>(a.ws);
+  int32_t* cnt = reinterpret_cast<int32_t*>(acc + (a.N + 3));
+  const int P = a.N + a.M;
+  aux_clear_kernel<<<1, 256, 0, stream>>>(acc, a.N + 3, cnt, P);
+  const unsigned nb = (unsigned)((a.T + kAuxBT - 1) / kAuxBT);
+  const size_t lds1 = (size_t)(kAuxThreads / kWave) * (a.N + 3) * sizeof(double) + (size_t)P * sizeof(int);
   aux_partial_kernel<<<nb, kAuxThreads, lds1, stream>>>(a.logits, a.topk_idx, a.T, a.N, a.M, a.K,
-                                                        rec, rec_counts);
-  const size_t lds2 = ((size_t)rd + a.N + a.M) * sizeof(double);
-  aux_final_kernel<<<1, kAuxThreads, lds2, stream>>>(rec, rec_counts, nb, a.T, a.N, a.M, a.f, a.P,
-                                                     a.counts, a.scalars);
+                                                        acc, cnt);
+  AuxFinal f{acc, cnt, a.f, a.P, a.counts, a.scalars};
+  aux_final_kernel<<<1, kAuxThreads, (size_t)P * sizeof(double), stream>>>(f, a.T, a.N, a.M);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@
 namespace moe {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64, kFfnThreads = 256;
-constexpr int kMaxGroups = 256;
+constexpr int kMaxGroups = 320;   // routed groups (<= 256) + the dense shared-expert problem
 
 enum { kSwiGLU = 0, kPlain = 1 };
 
@@ -48,39 +48,47 @@ struct TileTable {
   int start[kMaxGroups + 1];
   int len[kMaxGroups + 1];
   int mt[kMaxGroups + 1];
+  int nt[kMaxGroups + 1];
   int prefix[kMaxGroups + 1];
 };
 
-// Segment e = [a, b) with a = clamp(offsets[e], 0, max_rows) and
-// b = clamp(offsets[e+1], a, max_rows): always inside the buffers, and exactly the
-// requested segment for valid (non-decreasing, <= max_rows) offsets.
-// Counts row tiles per segment and their exclusive prefix (times column tiles).
-__device__ void build_tile_table(TileTable& tt, const int32_t* offsets, int groups,
-                                 int64_t max_rows, int ntiles_n) {
+// Table of (group, column tile, row tile) over problem 0's groups followed by
+// problem 1's single dense group. Segment e of a grouped problem is [a, b) with
+// a = clamp(offsets[e], 0, max_rows), b = clamp(offsets[e+1], a, max_rows):
+// always inside the buffers, exactly the requested segment for valid offsets.
+__device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const GemmProblem& p1,
+                                 int oc) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int cnt[4], local = 0;
+    const int G0 = p0.groups, G = p0.groups + p1.groups;
+    constexpr int kPer = (kMaxGroups + kWave - 1) / kWave;
+    int cnt[kPer], local = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      int s = 0, l = 0;
-      if (e < groups) {
-        if (offsets) {
-          int64_t a = offsets[e], b = offsets[e + 1];
-          a = min<int64_t>(max<int64_t>(a, 0), max_rows);
-          b = min<int64_t>(max<int64_t>(b, a), max_rows);
+    for (int q = 0; q < kPer; ++q) {
+      const int e = lane * kPer + q;
+      int s = 0, l = 0, nt = 0;
+      if (e < G) {
+        const GemmProblem& pr = e < G0 ? p0 : p1;
+        const int ge = e < G0 ? e : e - G0;
+        if (pr.offsets) {
+          int64_t a = pr.offsets[ge], b = pr.offsets[ge + 1];
+          a = min<int64_t>(max<int64_t>(a, 0), pr.max_rows);
+          b = min<int64_t>(max<int64_t>(b, a), pr.max_rows);
           s = (int)a;
           l = (int)(b - a);
         } else {
-          s = 0;
-          l = (int)max_rows;
+          l = (int)pr.max_rows;
         }
+        nt = (pr.n_out + oc - 1) / oc;
       }
-      tt.start[e] = s;
-      tt.len[e] = l;
       const int m = (l + kBM - 1) / kBM;
-      tt.mt[e] = m;
-      cnt[q] = m * ntiles_n;
+      if (e <= kMaxGroups) {
+        tt.start[e] = s;
+        tt.len[e] = l;
+        tt.mt[e] = m;
+        tt.nt[e] = nt;
+      }
+      cnt[q] = m * nt;
       local += cnt[q];
     }
     int incl = local;
@@ -91,8 +99,9 @@ __device__ void build_tile_table(TileTable& tt, const int32_t* offsets, int grou
     }
     int run = incl - local;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tt.prefix[lane * 4 + q] = run;
+    for (int q = 0; q < kPer; ++q) {
+      const int e = lane * kPer + q;
+      if (e <= kMaxGroups) tt.prefix[e] = run;
       run += cnt[q];
     }
     if (lane == kWave - 1) tt.prefix[kMaxGroups] = incl;
@@ -101,25 +110,21 @@ __device__ void build_tile_table(TileTable& tt, const int32_t* offsets, int grou
 }
 
 // MODE kSwiGLU writes h as bf16 (the next MFMA's input); kPlain writes float32.
-// DENSE = 1 is the same code instantiated for the single-segment (shared
-// expert) launches, so profiles report the two uses separately.
-template <int MODE, int DENSE>
+// ROLE only names the launch in profiles (the code is identical): 0 standalone
+// grouped, 1 standalone single segment, 2 the layer's routed + shared launch.
+template <int MODE, int ROLE>
 __global__ void __launch_bounds__(kFfnThreads)
-grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                         int groups, int64_t max_rows, const bf16_t* __restrict__ B0,
-                         const bf16_t* __restrict__ B1, int Nout, int Kdim,
-                         void* __restrict__ Cout) {
+grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   __shared__ TileTable tt;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][kBM * kBK];  // [buf][A|B][tile]
   constexpr int OC = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
-  const int ntiles_n = (Nout + OC - 1) / OC;
-  build_tile_table(tt, offsets, groups, max_rows, ntiles_n);
+  build_tile_table(tt, p0, p1, OC);
+  const int G0 = p0.groups, G = p0.groups + p1.groups;
   const int total = tt.prefix[kMaxGroups];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5, l32 = lane & 31;
-  const int nk = (Kdim + kBK - 1) / kBK;
   const int ld_chunk = tid & 7, ld_row = tid >> 3;  // + 32 * i
 
   // XCD-contiguous tile ranges
@@ -130,13 +135,18 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
   const int r_begin = xcd * S, r_end = min(total, r_begin + S);
 
   for (int L = r_begin + slot; L < r_end; L += per_xcd_blocks) {
-    // locate (expert, column tile, row tile)
-    int lo = 0, hi = groups;  // prefix[lo] <= L < prefix[hi]
+    // locate (group, column tile, row tile)
+    int lo = 0, hi = G;  // prefix[lo] <= L < prefix[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tt.prefix[mid] <= L) lo = mid; else hi = mid;
     }
     const int e = lo;
+    const bool second = e >= G0;
+    const GemmProblem& pr = second ? p1 : p0;
+    const int ge = second ? e - G0 : e;
+    const int Nout = pr.n_out, Kdim = pr.k_dim;
+    const int nk = (Kdim + kBK - 1) / kBK;
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
     const int ntile = local / mt, mtile = local - ntile * mt;
@@ -149,17 +159,23 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = ld_row + 32 * i;
-      asrc[i] = r < rows_valid ? A + (int64_t)(m0 + r) * Kdim : nullptr;
+      if (r < rows_valid) {
+        int64_t row = m0 + r;
+        if (pr.a_rows) row = min<int64_t>(max<int64_t>(pr.a_rows[row], 0), pr.a_nrows - 1);
+        asrc[i] = pr.a + row * Kdim;
+      } else {
+        asrc[i] = nullptr;
+      }
       int n;
       const bf16_t* base;
       if (MODE == kSwiGLU) {
         n = ntile * OC + (r & (OC - 1));
-        base = r < OC ? B0 : B1;
+        base = r < OC ? pr.b0 : pr.b1;
       } else {
         n = ntile * OC + r;
-        base = B0;
+        base = pr.b0;
       }
-      bsrc[i] = n < Nout ? base + ((int64_t)e * Nout + n) * Kdim : nullptr;
+      bsrc[i] = n < Nout ? base + ((int64_t)ge * Nout + n) * Kdim : nullptr;
     }
     u32x4_t ra[4], rb[4];
     auto fetch = [&](int kt) {
@@ -224,7 +240,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
       const int rl = wm * 64 + ms * 32 + l32;
       if (rl >= rows_valid) continue;
       if (MODE == kSwiGLU) {
-        bf16_t* crow = static_cast<bf16_t*>(Cout) + (int64_t)(m0 + rl) * Nout;
+        bf16_t* crow = static_cast<bf16_t*>(pr.out) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = ntile * OC + wn * 32 + 8 * g + 4 * half;
@@ -236,7 +252,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
           }
         }
       } else {
-        float* crow = static_cast<float*>(Cout) + (int64_t)(m0 + rl) * Nout;
+        float* crow = static_cast<float*>(pr.out) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -256,8 +272,9 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
 // float32 path: one thread per output element, plain FMA loops (small workloads).
 template <int MODE>
 __global__ void __launch_bounds__(256)
-grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ offsets,
-                        int groups, int64_t max_rows, const float* __restrict__ B0,
+grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ a_rows,
+                        int64_t a_nrows, const int32_t* __restrict__ offsets, int groups,
+                        int64_t max_rows, const float* __restrict__ B0,
                         const float* __restrict__ B1, int Nout, int Kdim, float* __restrict__ C) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= max_rows * Nout) return;
@@ -274,7 +291,8 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
     }
   }
   if (e < 0) return;
-  const float* arow = A + p * Kdim;
+  const int64_t src = a_rows ? min<int64_t>(max<int64_t>(a_rows[p], 0), a_nrows - 1) : p;
+  const float* arow = A + src * Kdim;
   const float* b0 = B0 + ((int64_t)e * Nout + n) * Kdim;
   float s0 = 0.0f;
   if (MODE == kSwiGLU) {
@@ -291,58 +309,70 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
   }
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
-  if (g.max_rows <= 0) return hipSuccess;
-  if (g.bf16) {
-    // persistent grid: 2 workgroups per CU (about 68 KiB LDS each), a multiple of 8
-    const int oc = g.op == 0 ? kBN / 2 : kBN;
-    const int64_t upper = (g.max_rows / kBM + g.groups) * ((g.n_out + oc - 1) / oc);
-    const int cap = std::max(8, g.num_cus * 2 / 8 * 8);
-    const unsigned grid = (unsigned)std::min<int64_t>(cap, (upper + 7) / 8 * 8);
-    const bf16_t* A = static_cast<const bf16_t*>(g.a);
-    const bf16_t* B0 = static_cast<const bf16_t*>(g.b0);
-    const bf16_t* B1 = static_cast<const bf16_t*>(g.b1);
-    const bool dense = g.offsets == nullptr;
-    if (g.op == 0) {
-      if (dense)
-        grouped_gemm_bf16_kernel<kSwiGLU, 1><<<grid, kFfnThreads, 0, stream>>>(
-            A, g.offsets, g.groups, g.max_rows, B0, B1, g.n_out, g.k_dim, g.out);
-      else
-        grouped_gemm_bf16_kernel<kSwiGLU, 0><<<grid, kFfnThreads, 0, stream>>>(
-            A, g.offsets, g.groups, g.max_rows, B0, B1, g.n_out, g.k_dim, g.out);
+static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int oc, int num_cus) {
+  auto upper = [&](const GemmProblem& p) -> int64_t {
+    if (p.groups == 0 || p.max_rows <= 0) return 0;
+    return (p.max_rows / kBM + p.groups) * ((p.n_out + oc - 1) / oc);
+  };
+  const int64_t tiles = upper(p0) + upper(p1);
+  // persistent grid: 2 workgroups per CU (about 68 KiB LDS each), a multiple of 8
+  const int cap = std::max(8, num_cus * 2 / 8 * 8);
+  return (unsigned)std::max<int64_t>(8, std::min<int64_t>(cap, (tiles + 7) / 8 * 8));
+}
+
+hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
+                            int num_cus, hipStream_t stream, int role) {
+  const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
+  if (!any0 && !any1) return hipSuccess;
+  if (bf16) {
+    const int oc = op == 0 ? kBN / 2 : kBN;
+    GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
+    const unsigned grid = gemm_grid(q0, q1, oc, num_cus);
+#define MOE_GEMM_LAUNCH(M_, R_) grouped_gemm_bf16_kernel<M_, R_><<<grid, kFfnThreads, 0, stream>>>(q0, q1)
+    if (op == 0) {
+      if (role == 2) MOE_GEMM_LAUNCH(kSwiGLU, 2);
+      else if (role == 1) MOE_GEMM_LAUNCH(kSwiGLU, 1);
+      else MOE_GEMM_LAUNCH(kSwiGLU, 0);
     } else {
-      if (dense)
-        grouped_gemm_bf16_kernel<kPlain, 1><<<grid, kFfnThreads, 0, stream>>>(
-            A, g.offsets, g.groups, g.max_rows, B0, nullptr, g.n_out, g.k_dim, g.out);
-      else
-        grouped_gemm_bf16_kernel<kPlain, 0><<<grid, kFfnThreads, 0, stream>>>(
-            A, g.offsets, g.groups, g.max_rows, B0, nullptr, g.n_out, g.k_dim, g.out);
+      if (role == 2) MOE_GEMM_LAUNCH(kPlain, 2);
+      else if (role == 1) MOE_GEMM_LAUNCH(kPlain, 1);
+      else MOE_GEMM_LAUNCH(kPlain, 0);
     }
+#undef MOE_GEMM_LAUNCH
   } else {
-    const int64_t n = g.max_rows * g.n_out;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    if (g.op == 0)
-      grouped_gemm_f32_kernel<kSwiGLU><<<grid, 256, 0, stream>>>(
-          static_cast<const float*>(g.a), g.offsets, g.groups, g.max_rows,
-          static_cast<const float*>(g.b0), static_cast<const float*>(g.b1), g.n_out, g.k_dim,
-          static_cast<float*>(g.out));
-    else
-      grouped_gemm_f32_kernel<kPlain><<<grid, 256, 0, stream>>>(
-          static_cast<const float*>(g.a), g.offsets, g.groups, g.max_rows,
-          static_cast<const float*>(g.b0), nullptr, g.n_out, g.k_dim, static_cast<float*>(g.out));
+    for (const GemmProblem* p : {&p0, &p1}) {
+      if (p->groups == 0 || p->max_rows <= 0) continue;
+      const int64_t n = p->max_rows * p->n_out;
+      const unsigned grid = (unsigned)((n + 255) / 256);
+      const float* A = reinterpret_cast<const float*>(p->a);
+      if (op == 0)
+        grouped_gemm_f32_kernel<kSwiGLU><<<grid, 256, 0, stream>>>(
+            A, p->a_rows, p->a_nrows, p->offsets, p->groups, p->max_rows,
+            reinterpret_cast<const float*>(p->b0), reinterpret_cast<const float*>(p->b1), p->n_out,
+            p->k_dim, static_cast<float*>(p->out));
+      else
+        grouped_gemm_f32_kernel<kPlain><<<grid, 256, 0, stream>>>(
+            A, p->a_rows, p->a_nrows, p->offsets, p->groups, p->max_rows,
+            reinterpret_cast<const float*>(p->b0), nullptr, p->n_out, p->k_dim,
+            static_cast<float*>(p->out));
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   if (a.max_rows <= 0) return hipSuccess;
-  GemmArgs g1{a.bf16, 0, a.groups, a.d_ff, a.d_model, a.max_rows, a.a, a.offsets, a.w_gate,
-              a.w_up, a.h, a.num_cus};
-  hipError_t e = launch_grouped_gemm(g1, stream);
+  GemmProblem none{};
+  GemmProblem g1{static_cast<const bf16_t*>(a.a), nullptr, a.max_rows, a.offsets, a.groups,
+                 a.max_rows, static_cast<const bf16_t*>(a.w_gate),
+                 static_cast<const bf16_t*>(a.w_up), a.d_ff, a.d_model, a.h};
+  const int role = a.offsets ? 0 : 1;
+  hipError_t e = launch_gemm_pair(a.bf16, 0, g1, none, a.num_cus, stream, role);
   if (e != hipSuccess) return e;
-  GemmArgs g2{a.bf16, 1, a.groups, a.d_model, a.d_ff, a.max_rows, a.h, a.offsets, a.w_down,
-              nullptr, a.out, a.num_cus};
-  return launch_grouped_gemm(g2, stream);
+  GemmProblem g2{static_cast<const bf16_t*>(a.h), nullptr, a.max_rows, a.offsets, a.groups,
+                 a.max_rows, static_cast<const bf16_t*>(a.w_down), nullptr, a.d_model, a.d_ff,
+                 a.out};
+  return launch_gemm_pair(a.bf16, 1, g2, none, a.num_cus, stream, role);
 }
 
 }  // namespace moe

@@ -7,10 +7,15 @@
 
 namespace moe {
 
+// Fixed-point scales of the fused statistics accumulators (probability sums, lse^2 sums).
+constexpr double kAuxPScale = 4294967296.0;  // 2^32
+constexpr double kAuxZScale = 1048576.0;     // 2^20
+
 struct RouteArgs {
   int64_t T;
   int d, N, M, K;
   bool bf16;
+  bool fused;         // also emit per-block expert histogram + statistics accumulators
   const void* x;
   const float* w_router;
   float null_bias;
@@ -21,13 +26,27 @@ struct RouteArgs {
   float* topk_w;
   int32_t* n_real;
   uint16_t* w_split;  // [3][Np][d] bf16 scratch, bf16 path only
+  int32_t* chunk_hist; // fused: [blocks][N]
+  uint64_t* acc;       // fused: [N + 3] accumulators (cleared by the launch)
+  int32_t* counts;     // fused: [N + M] pool slot counts (cleared by the launch)
 };
+int route_tokens_per_block();
 size_t route_split_bytes(int N, int d);
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
+// Statistics finalisation done by the permutation's scan kernel in the fused layer path.
+struct AuxFinal {
+  const uint64_t* acc;   // [N + 3]
+  const int32_t* cnt;    // [N + M]
+  float* f;
+  float* P;
+  int32_t* counts;
+  float* scalars;
+};
+
 struct PermuteArgs {
   int64_t T;
-  int K, N, d, elt_bytes;
+  int K, N, M, d, elt_bytes;
   const int32_t* topk_idx;
   const void* x;
   int32_t* counts;
@@ -35,10 +54,12 @@ struct PermuteArgs {
   int32_t* perm_token;
   int32_t* slot_pos;
   void* x_perm;
-  int32_t* ws;
+  int32_t* ws;                    // chunk_hist [nchunks][N] then chunk_base [nchunks][N]
+  bool hist_ready;                // chunk_hist already written (by the fused router)
+  const AuxFinal* aux;            // optional statistics finalisation (fused path)
 };
-int permute_nchunks(int64_t TK);
-size_t permute_ws_bytes(int64_t TK, int N);
+int permute_nchunks(int64_t T);
+size_t permute_ws_bytes(int64_t T, int N);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
 struct FfnArgs {
@@ -57,20 +78,26 @@ struct FfnArgs {
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
 
-struct GemmArgs {
-  bool bf16;
-  int op;              // 0: h = silu(a b0^T) * (a b1^T) -> dtype; 1: out = a b0^T -> float32
-  int groups;
-  int n_out, k_dim;
+// One GEMM problem of a grouped launch: rows of segment g (from offsets, or one
+// segment of max_rows rows) times weight group g. a_rows optionally redirects
+// row p of A to a[a_rows[p]] (the permutation's gather, fused into the loads).
+struct GemmProblem {
+  const uint16_t* a;        // [a_nrows][k_dim] (bf16 bits, or float for the f32 path)
+  const int32_t* a_rows;    // [max_rows] or NULL
+  int64_t a_nrows;
+  const int32_t* offsets;   // [groups+1] device, or NULL
+  int groups;               // 0 = absent
   int64_t max_rows;
-  const void* a;       // [max_rows][k_dim]
-  const int32_t* offsets;  // [groups+1] device, or NULL: one segment of max_rows rows
-  const void* b0;      // [groups][n_out][k_dim]
-  const void* b1;
-  void* out;           // [max_rows][n_out]
-  int num_cus;
+  const uint16_t* b0;       // [groups][n_out][k_dim]
+  const uint16_t* b1;       // gate/up: the up weights
+  int n_out, k_dim;
+  void* out;                // [max_rows][n_out]: bf16 h (op 0) or float32 (op 1)
 };
-hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
+// op 0: out = silu(a b0^T) * (a b1^T); op 1: out = a b0^T. Both problems in one launch.
+// role names the launch in profiles: 0 standalone grouped, 1 standalone single
+// segment, 2 the layer's fused launch.
+hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
+                            int num_cus, hipStream_t stream, int role);
 
 struct CombineArgs {
   bool bf16;
@@ -96,7 +123,7 @@ struct AuxArgs {
   float* scalars;
   void* ws;
 };
-size_t aux_ws_bytes(int64_t T, int N, int M);
+size_t aux_ws_bytes(int N, int M);
 hipError_t launch_aux(const AuxArgs& a, hipStream_t stream);
 
 }  // namespace moe

@@ -9,33 +9,37 @@
 //   perm_token[p] (token of the p-th slot in expert order),
 //   slot_pos[t][k] (position of the slot, -1 for a null slot).
 //
-// Three kernels: (a) per-chunk expert histogram, (b) one workgroup turns the
-// histograms into counts, offsets and per-chunk bases, (c) each chunk ranks
-// its slots stably (wavefront ballots find the lanes holding the same expert)
-// and scatters. Histogram counts use LDS integer atomics, whose result does
-// not depend on their order, so the permutation is deterministic.
-// A fourth kernel gathers x_perm[p] = x[perm_token[p]].
+// The slots are cut into chunks of 64 tokens (64*K slots), the same chunks the
+// router's workgroups score, so in the fused layer path the router has already
+// written each chunk's expert histogram. Kernels: (a) per-chunk histogram
+// (standalone path only), (b) one workgroup turns the histograms into counts,
+// offsets and per-chunk bases (and, in the fused path, finalises the
+// statistics), (c) each chunk ranks its slots stably -- wavefront ballots find
+// the lanes holding the same expert -- and scatters. Counts use LDS integer
+// atomics, whose result does not depend on their order, so the permutation is
+// deterministic. A fourth kernel gathers x_perm[p] = x[perm_token[p]].
 #include <algorithm>
 
+#include "aux_final.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kChunk = 2048;          // flat slots per chunk
-constexpr int kPermThreads = 256;     // 4 wavefronts, 512 slots each
-constexpr int kPerWave = kChunk / (kPermThreads / kWave);
+constexpr int kTokChunk = 64;         // tokens per chunk (= router tokens per workgroup)
+constexpr int kPermThreads = 256;     // 4 wavefronts
+constexpr int kMaxGroupsPerWave = (MOE_MAX_TOPK * kTokChunk / kWave + 3) / 4;
 
 __device__ __forceinline__ int slot_key(int32_t v, int N) { return (v >= 0 && v < N) ? v : N; }
 
 __global__ void __launch_bounds__(kPermThreads)
-permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int N,
+permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
                     int32_t* __restrict__ chunk_hist) {
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e < N; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int64_t f0 = (int64_t)blockIdx.x * kChunk;
-  const int64_t f1 = min<int64_t>(f0 + kChunk, TK);
+  const int64_t f0 = (int64_t)blockIdx.x * kTokChunk * K;
+  const int64_t f1 = min<int64_t>(f0 + (int64_t)kTokChunk * K, TK);
   for (int64_t f = f0 + threadIdx.x; f < f1; f += blockDim.x) {
     const int k = slot_key(topk_idx[f], N);
     if (k < N) atomicAdd(&hist[k], 1);
@@ -47,15 +51,17 @@ permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int N,
 // One workgroup of 1024 threads: counts[e] = sum over chunks, offsets = exclusive
 // scan over e, chunk_base[c][e] = offsets[e] + sum_{c' < c} hist[c'][e].
 // Thread (e, g) owns expert e for the g-th contiguous group of chunks (N <= 255,
-// so there are at least 4 groups).
+// so there are at least 4 groups). In the fused path it also finalises the
+// statistics accumulated by the router.
 __global__ void __launch_bounds__(1024)
 permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                    int32_t* __restrict__ chunk_base) {
-  extern __shared__ int sm[];
+                    int32_t* __restrict__ chunk_base, AuxFinal aux, int64_t T, int M) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int groups = blockDim.x / N;
-  int* part = sm;                    // [groups][N]
-  int* off = sm + groups * N;        // [N + 1]
+  double* terms = reinterpret_cast<double*>(smem_raw);               // [N + M] (fused)
+  int* part = reinterpret_cast<int*>(terms + (aux.acc ? N + M : 0));  // [groups][N]
+  int* off = part + groups * N;                                      // [N + 1]
   const int per = (nchunks + groups - 1) / groups;
   const int e = threadIdx.x % N, g = threadIdx.x / N;
   const bool active = g < groups;
@@ -110,28 +116,36 @@ permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
       base += chunk_hist[(int64_t)c * N + e];
     }
   }
+  if (aux.acc) aux_finalize(aux, T, N, M, terms);
 }
 
+// One workgroup per chunk of 64 tokens: 64*K slots in K groups of 64; each
+// wavefront takes a contiguous run of groups, in order.
 __global__ void __launch_bounds__(kPermThreads)
 permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
                        const int32_t* __restrict__ chunk_base, int64_t max_rows,
                        int32_t* __restrict__ perm_token, int32_t* __restrict__ slot_pos) {
   extern __shared__ int sm[];
   const int nkeys = N + 1;
-  int* wcnt = sm;                                   // [4][N+1] running count per wave
-  int* wbase = sm + (kPermThreads / kWave) * nkeys; // [4][N]
+  constexpr int nw = kPermThreads / kWave;
+  int* wcnt = sm;                  // [4][N+1] running count per wave
+  int* wbase = sm + nw * nkeys;    // [4][N]
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  for (int i = threadIdx.x; i < (kPermThreads / kWave) * nkeys; i += blockDim.x) wcnt[i] = 0;
+  for (int i = threadIdx.x; i < nw * nkeys; i += blockDim.x) wcnt[i] = 0;
   __syncthreads();
   int nbits = 1;
   while ((1 << nbits) <= N) ++nbits;  // enough bits for keys 0..N
-  const int64_t fw = (int64_t)blockIdx.x * kChunk + (int64_t)wave * kPerWave;
-  constexpr int G = kPerWave / kWave;
-  int key[G], lrank[G];
+  const int gpw = (K + nw - 1) / nw;  // groups (of 64 slots) per wave
+  const int64_t fc = (int64_t)blockIdx.x * kTokChunk * K;
+  int key[kMaxGroupsPerWave], lrank[kMaxGroupsPerWave];
   int* mycnt = wcnt + wave * nkeys;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int64_t f = fw + gi * kWave + lane;
+  for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
+    key[gi] = N;
+    lrank[gi] = 0;
+    const int grp = wave * gpw + gi;
+    if (gi >= gpw || grp >= K) continue;  // uniform across the wave
+    const int64_t f = fc + (int64_t)grp * kWave + lane;
     const int k = f < TK ? slot_key(topk_idx[f], N) : N;
     uint64_t peers = ~0ull;
     for (int b = 0; b < nbits; ++b) {
@@ -147,7 +161,6 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, 
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  const int nw = kPermThreads / kWave;
   for (int i = threadIdx.x; i < nw * N; i += blockDim.x) {
     const int w = i / N, e = i % N;
     int b = chunk_base[(int64_t)blockIdx.x * N + e];
@@ -156,14 +169,16 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, 
   }
   __syncthreads();
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int64_t f = fw + gi * kWave + lane;
+  for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
+    const int grp = wave * gpw + gi;
+    if (gi >= gpw || grp >= K) continue;
+    const int64_t f = fc + (int64_t)grp * kWave + lane;
     if (f < TK) {
       const int k = key[gi];
       if (k < N) {
         const int p = wbase[wave * N + k] + lrank[gi];
         slot_pos[f] = p;
-        if (p < max_rows) perm_token[p] = (int32_t)(f / K);  // rows past capacity: dropped
+        if (p < max_rows) perm_token[p] = (int32_t)(f / K);  // past capacity: dropped
       } else {
         slot_pos[f] = -1;
       }
@@ -205,31 +220,35 @@ gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ pe
   }
 }
 
-int permute_nchunks(int64_t TK) { return (int)((TK + kChunk - 1) / kChunk); }
+int permute_nchunks(int64_t T) { return (int)((T + kTokChunk - 1) / kTokChunk); }
 
-size_t permute_ws_bytes(int64_t TK, int N) {
-  return (size_t)2 * permute_nchunks(TK) * N * sizeof(int32_t);
+size_t permute_ws_bytes(int64_t T, int N) {
+  return (size_t)2 * permute_nchunks(T) * N * sizeof(int32_t);
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int64_t TK = a.T * a.K;
-  const int nchunks = permute_nchunks(TK);
+  const int nchunks = permute_nchunks(a.T);
   int32_t* chunk_hist = a.ws;
   int32_t* chunk_base = a.ws + (int64_t)nchunks * a.N;
-  permute_hist_kernel<<<nchunks, kPermThreads, a.N * sizeof(int), stream>>>(a.topk_idx, TK, a.N,
-                                                                           chunk_hist);
-  const size_t scan_lds = ((size_t)(1024 / a.N) * a.N + a.N + 1) * sizeof(int);
-  permute_scan_kernel<<<1, 1024, scan_lds, stream>>>(chunk_hist, nchunks, a.N, a.counts,
-                                                     a.offsets, chunk_base);
+  if (!a.hist_ready)
+    permute_hist_kernel<<<nchunks, kPermThreads, a.N * sizeof(int), stream>>>(a.topk_idx, TK, a.K,
+                                                                             a.N, chunk_hist);
+  AuxFinal af{};
+  if (a.aux) af = *a.aux;
+  const int groups = 1024 / a.N;
+  const size_t scan_lds = (af.acc ? (size_t)(a.N + a.M) * sizeof(double) : 0) +
+                          ((size_t)groups * a.N + a.N + 1) * sizeof(int);
+  permute_scan_kernel<<<1, 1024, scan_lds, stream>>>(chunk_hist, nchunks, a.N, a.counts, a.offsets,
+                                                     chunk_base, af, a.T, a.M);
   const size_t sc_lds = ((size_t)(kPermThreads / kWave) * (a.N + 1) +
                          (size_t)(kPermThreads / kWave) * a.N) * sizeof(int);
+  const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);
   permute_scatter_kernel<<<nchunks, kPermThreads, sc_lds, stream>>>(
-      a.topk_idx, TK, a.K, a.N, chunk_base, a.T * (int64_t)std::min(a.K, a.N), a.perm_token,
-      a.slot_pos);
+      a.topk_idx, TK, a.K, a.N, chunk_base, max_rows, a.perm_token, a.slot_pos);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.x && a.x_perm) {
-    const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);
     const int row_bytes = a.d * a.elt_bytes;
     const int64_t vecs = max_rows * (row_bytes / 16);
     const unsigned gblk = (unsigned)std::max<int64_t>(1, std::min<int64_t>((vecs + 255) / 256, 4096));
