@@ -153,19 +153,30 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     const int m0 = tt.start[e] + mtile * kBM;
     const int rows_valid = min(kBM, tt.start[e] + tt.len[e] - m0);
 
-    // global sources of this thread's 4 A rows and 4 B rows
+    // global sources of this thread's 4 A rows and 4 B rows: always a valid row
+    // (clamped). Rows past the segment and columns past n_out only produce outputs
+    // that are never stored, so their loads need no masking; columns past k_dim
+    // (last K tile only) are zeroed at stash. No branch or select sits between a
+    // load and the MFMAs, so all eight loads of the next tile stay in flight.
     const bf16_t* asrc[4];
     const bf16_t* bsrc[4];
+    int64_t arow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = ld_row + 32 * i;
-      if (r < rows_valid) {
-        int64_t row = m0 + r;
-        if (pr.a_rows) row = min<int64_t>(max<int64_t>(pr.a_rows[row], 0), pr.a_nrows - 1);
-        asrc[i] = pr.a + row * Kdim;
-      } else {
-        asrc[i] = nullptr;
-      }
+      arow[i] = m0 + (r < rows_valid ? r : 0);
+    }
+    if (pr.a_rows) {
+      int32_t src_row[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) src_row[i] = pr.a_rows[arow[i]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) arow[i] = min<int64_t>(max<int64_t>(src_row[i], 0), pr.a_nrows - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ld_row + 32 * i;
+      asrc[i] = pr.a + arow[i] * Kdim;
       int n;
       const bf16_t* base;
       if (MODE == kSwiGLU) {
@@ -175,19 +186,23 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
         n = ntile * OC + r;
         base = pr.b0;
       }
-      bsrc[i] = n < Nout ? base + ((int64_t)ge * Nout + n) * Kdim : nullptr;
+      bsrc[i] = base + ((int64_t)ge * Nout + (n < Nout ? n : 0)) * Kdim;
     }
     u32x4_t ra[4], rb[4];
     auto fetch = [&](int kt) {
       const int k = kt * kBK + ld_chunk * 8;
-      const bool kin = k < Kdim;
+      const int kc = k < Kdim ? k : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ra[i] = (asrc[i] && kin) ? *reinterpret_cast<const u32x4_t*>(asrc[i] + k) : u32x4_t{0, 0, 0, 0};
-        rb[i] = (bsrc[i] && kin) ? *reinterpret_cast<const u32x4_t*>(bsrc[i] + k) : u32x4_t{0, 0, 0, 0};
+        ra[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + kc);
+        rb[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + kc);
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, int kt) {
+      if ((kt + 1) * kBK > Kdim && kt * kBK + ld_chunk * 8 >= Kdim) {  // K tail only
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = rb[i] = u32x4_t{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = ld_row + 32 * i;
@@ -203,7 +218,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
 
     fetch(0);
-    stash(0);
+    stash(0, 0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
@@ -230,7 +245,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
           for (int ms = 0; ms < 2; ++ms)
             acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], af[ms], acc[ns][ms], 0, 0, 0);
       }
-      if (kt + 1 < nk) stash(buf ^ 1);
+      if (kt + 1 < nk) stash(buf ^ 1, kt + 1);
       __syncthreads();
     }
 

@@ -24,14 +24,16 @@
 //    accumulation over d = 2048 terms drifts by a few 1e-6, too close to the
 //    1e-5 near-tie margin of routing parity). The null row is an fp64 dot
 //    product on the vector ALUs.
-//  * A workgroup scores 64 tokens. Its four wavefronts split the work into
-//    (32-expert tile, K slice) pairs; the K slices are added in a fixed order
-//    through LDS. Fragment loads for the next K block are issued before the
-//    MFMAs of the current one.
-//  * Epilogue: one wavefront per token. The chosen reals are found by r rounds
-//    of a wavefront arg-max over 64-bit keys (order-preserving bits of the
-//    logit, then the complemented expert index, so ties go to the lower index);
-//    no sort and no O(N) loop per lane.
+//  * A workgroup scores 64 tokens. K tiles of x and of the three weight planes
+//    are staged through two swizzled LDS buffers by all 256 threads (the next
+//    tile is fetched into registers while the current one feeds the MFMAs);
+//    wavefront w takes token half w & 1 against every other 32-expert tile.
+//  * Epilogue: one lane per token. Each lane walks its token's logits row in
+//    LDS once and keeps the best K reals in registers with a branch-free
+//    insertion network over 64-bit keys (order-preserving bits of the logit,
+//    then the complemented expert index, so ties go to the lower index). This
+//    costs a few instructions per (token, expert) instead of wavefront-wide
+//    reductions per token.
 //  * Fused layer mode additionally writes the per-workgroup expert histogram
 //    (the first pass of the permutation's counting sort) and accumulates the
 //    load-balance / z-loss sums of its 64 tokens into fixed-point integer
@@ -46,6 +48,9 @@ namespace moe {
 
 constexpr int kRouteBT = 64;       // tokens per workgroup
 constexpr int kRouteThreads = 256;
+// 16-byte loads per thread per K tile of the MFMA router: ((64 + 3 Np) BK / 8 + BK / 4)
+// chunks over 256 threads, at most 9 for every (Np, BK) pair route_bk() picks.
+constexpr int kRouteMaxLoads = 9;
 constexpr int kQ = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
 
 int route_tokens_per_block() { return kRouteBT; }
@@ -93,92 +98,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-struct AuxPartial {  // per-lane running sums of one wavefront (fused mode)
-  double psum[kQ];
-  double pnull, lz;
-  int nreal;
-};
-
-// One wavefront selects one token from its logits row s[0..N] (LDS).
-template <bool FUSED>
-__device__ void select_token(const float* s, int N, int M, int K, int64_t t,
-                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                             int32_t* __restrict__ n_real, AuxPartial& ap, int* cnt_lds) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float snull = s[N];
-  float v[kQ];
-  uint64_t key[kQ];
-  int c = 0;
-  float vmax = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    const int j = lane + q * kWave;
-    const bool valid = j < N;
-    v[q] = valid ? s[j] : -INFINITY;
-    key[q] = valid ? (((uint64_t)ordered_bits(v[q]) << 32) | (0xffffffffu - (uint32_t)j)) : 0ull;
-    if (q * kWave < N) {
-      c += __popcll(ballot(valid && v[q] > snull));
-      vmax = fmaxf(vmax, v[q]);
-    }
-  }
-  vmax = wave_max(vmax);
-  const int r = (M == 0) ? K : min(K, max(c, K - M));
-  int my_idx = 0;
-  float my_v = 0.0f;
-  for (int i = 0; i < r; ++i) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) best = key[q] > best ? key[q] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      if (key[q] == best) key[q] = 0;
-    if (lane == i) {
-      my_idx = (int)(0xffffffffu - (uint32_t)best);
-      my_v = from_ordered_bits((uint32_t)(best >> 32));
-    }
-  }
-  // weights: softmax over the chosen reals in fp64 from the fp32 logits (max = vmax)
-  const double e = lane < r ? exp((double)my_v - (double)vmax) : 0.0;
-  const double tot = wave_sum_double(e);
-  int32_t* idx_row = topk_idx + t * K;
-  float* w_row = topk_w + t * K;
-  if (lane < r) {
-    idx_row[lane] = my_idx;
-    w_row[lane] = (float)(e / tot);
-  } else if (lane < K) {
-    idx_row[lane] = N + (lane - r);
-    w_row[lane] = 0.0f;
-  }
-  if (lane == 0 && n_real) n_real[t] = r;
-  if (FUSED) {
-    // pool softmax over [reals, null x M] in fp32, accumulated per lane in fp64
-    const float mp = M > 0 ? fmaxf(vmax, snull) : vmax;
-    float ex[kQ];
-    double part = 0.0;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      ex[q] = (lane + q * kWave < N) ? expf(v[q] - mp) : 0.0f;
-      part += (double)ex[q];
-    }
-    const float en = M > 0 ? expf(snull - mp) : 0.0f;
-    const double z = wave_sum_double(part) + (double)M * (double)en;
-    const double iz = 1.0 / z;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) ap.psum[q] += (double)ex[q] * iz;
-    if (lane == 0) {
-      ap.pnull += (double)en * iz;
-      const double lse = (double)mp + log(z);
-      ap.lz += lse * lse;
-      ap.nreal += r;
-    }
-    if (lane < r)
-      atomicAdd(&cnt_lds[my_idx], 1);
-    else if (lane < K)
-      atomicAdd(&cnt_lds[N + (lane - r)], 1);
-  }
-}
-
 struct RouteKernelArgs {
   const bf16_t* x;
   const bf16_t* w3;
@@ -186,7 +105,7 @@ struct RouteKernelArgs {
   float null_bias;
   const float* null_bias_tok;
   int64_t T;
-  int d, N, Np, M, K, ks;  // ks: K slices per expert tile
+  int d, N, Np, M, K, ks;  // ks: unused (1)
   float* logits_out;
   int32_t* topk_idx;
   float* topk_w;
@@ -196,41 +115,121 @@ struct RouteKernelArgs {
   int32_t* counts;         // fused: [N + M] pool slot counts
 };
 
-template <bool FUSED>
+// Lane-per-token selection for the (up to 64) tokens of one workgroup, run by
+// wavefront 0 with lane t owning token t. Each lane walks its logits row once,
+// keeping the best KMAX reals in a register list sorted by 64-bit keys (the
+// order-preserving bits of the logit, then the complemented index: a larger key
+// is a larger logit, or the lower index at equal logits). An insertion is a
+// fixed compare-and-swap chain, so no lane diverges. In fused mode the row is
+// then overwritten with its pool-softmax probabilities for the column sums.
+template <int KMAX, bool FUSED>
+__device__ void select_lanes(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
+                             int* cnt_lds, double* lane_acc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int N = a.N, M = a.M, K = a.K;
+  const bool live = lane < nt;
+  float* s = sl + (live ? lane : 0) * ld;
+  const float snull = s[N];
+  uint64_t lk[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) lk[i] = 0ull;
+  int c = 0;
+  float vmax = -INFINITY;
+#pragma unroll 2
+  for (int j = 0; j < N; ++j) {
+    const float v = s[j];
+    c += v > snull;
+    vmax = fmaxf(vmax, v);
+    uint64_t key = ((uint64_t)ordered_bits(v) << 32) | (0xffffffffu - (uint32_t)j);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      const bool gt = key > lk[i];
+      const uint64_t old = lk[i];
+      lk[i] = gt ? key : old;
+      key = gt ? old : key;
+    }
+  }
+  const int r = (M == 0) ? K : min(K, max(c, K - M));
+  // weights: softmax over the chosen reals in fp64, summed in rank order
+  double e[KMAX];
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    e[i] = i < r ? exp((double)from_ordered_bits((uint32_t)(lk[i] >> 32)) - (double)vmax) : 0.0;
+    tot += e[i];
+  }
+  if (live) {
+    const int64_t t = t0 + lane;
+    int32_t* idx_row = a.topk_idx + t * K;
+    float* w_row = a.topk_w + t * K;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < K) {
+        const int id = i < r ? (int)(0xffffffffu - (uint32_t)lk[i]) : N + (i - r);
+        idx_row[i] = id;
+        w_row[i] = i < r ? (float)(e[i] / tot) : 0.0f;
+        if (FUSED) atomicAdd(&cnt_lds[id], 1);
+      }
+    }
+    if (a.n_real) a.n_real[t] = r;
+  }
+  if (FUSED) {
+    // pool softmax [reals, null x M]: p_j written over the logits row
+    const float mp = M > 0 ? fmaxf(vmax, snull) : vmax;
+    double z = 0.0;
+#pragma unroll 4
+    for (int j = 0; j < N; ++j) z += (double)expf(s[j] - mp);
+    const float en = M > 0 ? expf(snull - mp) : 0.0f;
+    z += (double)M * (double)en;
+    const float iz = (float)(1.0 / z);
+    if (live) {
+#pragma unroll 4
+      for (int j = 0; j < N; ++j) s[j] = expf(s[j] - mp) * iz;
+      s[N] = en * iz;
+      const double lse = (double)mp + log(z);
+      lane_acc[0] = lse * lse;
+      lane_acc[1] = (double)r;
+    } else {
+      lane_acc[0] = lane_acc[1] = 0.0;
+    }
+  }
+}
+
+template <bool FUSED, int KMAX>
 __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
                                int* cnt_lds, double* wacc) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int N = a.N, M = a.M, P = N + M;
   if (a.logits_out) {
     const int w = N + 1;
     for (int i = threadIdx.x; i < nt * w; i += blockDim.x)
       a.logits_out[(t0 + i / w) * w + i % w] = sl[(i / w) * ld + i % w];
+    if (FUSED) __syncthreads();  // the fused selection overwrites the rows
   }
-  AuxPartial ap;
-#pragma unroll
-  for (int q = 0; q < kQ; ++q) ap.psum[q] = 0.0;
-  ap.pnull = ap.lz = 0.0;
-  ap.nreal = 0;
-  for (int tl = wave; tl < nt; tl += kRouteThreads / kWave)
-    select_token<FUSED>(sl + tl * ld, N, M, a.K, t0 + tl, a.topk_idx, a.topk_w, a.n_real, ap,
-                        cnt_lds);
+  double lane_acc[2];
+  if (wave == 0) select_lanes<KMAX, FUSED>(a, sl, ld, nt, t0, cnt_lds, lane_acc);
   if (!FUSED) return;
+  // per-block sums in a fixed order: probability columns over the block's tokens,
+  // and lse^2 / n_real over wavefront 0's lanes
   const int rd = N + 3;
-#pragma unroll
-  for (int q = 0; q < kQ; ++q)
-    if (lane + q * kWave < N) wacc[wave * rd + lane + q * kWave] = ap.psum[q];
-  if (lane == 0) {
-    wacc[wave * rd + N] = ap.pnull;
-    wacc[wave * rd + N + 1] = ap.lz;
-    wacc[wave * rd + N + 2] = (double)ap.nreal;
+  if (wave == 0) {
+    const double lz = wave_sum_double(lane_acc[0]);
+    const double nr = wave_sum_double(lane_acc[1]);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      wacc[N + 1] = lz;
+      wacc[N + 2] = nr;
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j <= N; j += blockDim.x) {
+    double sum = 0.0;
+    for (int tl = 0; tl < nt; ++tl) sum += (double)sl[tl * ld + j];
+    wacc[j] = sum;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < rd; i += blockDim.x) {
-    double s = 0.0;
-    for (int w = 0; w < kRouteThreads / kWave; ++w) s += wacc[w * rd + i];
     const double scale = (i == N + 1) ? kAuxZScale : (i == N + 2 ? 1.0 : kAuxPScale);
-    const uint64_t q = (uint64_t)(s * scale + 0.5);
+    const uint64_t q = (uint64_t)(wacc[i] * scale + 0.5);
     if (q) atomicAdd(reinterpret_cast<unsigned long long*>(&a.acc[i]), (unsigned long long)q);
   }
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
@@ -241,163 +240,195 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
 }
 
 // bf16 x: three-way split MFMA scoring of the N real rows + fp64 null row.
-template <bool FUSED>
+// K tiles of BK columns of x (64 tokens) and of the three weight planes (Np rows)
+// are staged through two LDS buffers by all 256 threads; wavefront w computes
+// token half (w & 1) against expert tiles (w >> 1), (w >> 1) + 2, ...
+template <int BK>
+__device__ __forceinline__ int rt_off(int row, int chunk) {
+  constexpr int CPR = BK / 8;  // 16-byte chunks per row
+  return row * BK + ((chunk ^ (row & (CPR - 1))) << 3);
+}
+
+template <bool FUSED, int BK, int TPW, int KMAX>  // TPW: 32-expert tiles per wavefront
 __global__ void __launch_bounds__(kRouteThreads)
 route_mfma_kernel(RouteKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  const int N = a.N, d = a.d, Np = a.Np, ks = a.ks;
+  constexpr int CPR = BK / 8;
+  const int N = a.N, d = a.d, Np = a.Np;
   const int ld = N + 1;
   const int n_et = Np / 32;
-  // LDS: partial K-slice sums [ks-1][64][Np] doubles, logits [64][ld] floats,
-  // fused: wave partials [4][N+3] doubles and pool counts [N+M] ints
-  double* part = reinterpret_cast<double*>(smem_raw);
-  float* sl = reinterpret_cast<float*>(part + (size_t)(ks - 1) * kRouteBT * Np);
+  // LDS: 2 x { x tile [64][BK], weight tile [3][Np][BK] bf16, null-row tile [BK] float },
+  // logits [64][ld] float, fused: [N+3] doubles and pool counts [N+M] ints
+  const int xt_elems = kRouteBT * BK, wt_elems = 3 * Np * BK;
+  const int buf_elems = xt_elems + wt_elems + 2 * BK;  // bf16 units; the null tile is BK floats
+  bf16_t* tiles = reinterpret_cast<bf16_t*>(smem_raw);
+  float* sl = reinterpret_cast<float*>(tiles + 2 * buf_elems);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? 4 * (N + 3) : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
   if (FUSED)
     for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
 
   const int64_t T = a.T;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, T - t0);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int half = lane >> 5, l32 = lane & 31;
-  const int nch = d / 8;               // 16-byte chunks per row
-  const int nsteps = (nch + 1) / 2;    // 16-wide K steps
-  const int steps_per_slice = (nsteps + ks - 1) / ks;
-  const bf16x8_t* ap0 = reinterpret_cast<const bf16x8_t*>(a.x + min<int64_t>(t0 + l32, T - 1) * d);
-  const bf16x8_t* ap1 =
-      reinterpret_cast<const bf16x8_t*>(a.x + min<int64_t>(t0 + 32 + l32, T - 1) * d);
+  const int th = wave & 1, eg = wave >> 1;
+  const int nk = (d + BK - 1) / BK;
   const int64_t plane = (int64_t)Np * d;
 
-  // With ks > 1 there are exactly four (tile, slice) items, one per wavefront, and
-  // every wavefront passes the one barrier below; with ks == 1 there is none.
-  for (int item = wave; item < n_et * ks; item += kRouteThreads / kWave) {
-    const int et = item % n_et, kq = item / n_et;
-    const int erow = et * 32 + l32;
-    const bf16x8_t* b0 = reinterpret_cast<const bf16x8_t*>(a.w3 + (int64_t)erow * d);
-    const bf16x8_t* b1 = reinterpret_cast<const bf16x8_t*>(a.w3 + plane + (int64_t)erow * d);
-    const bf16x8_t* b2 = reinterpret_cast<const bf16x8_t*>(a.w3 + 2 * plane + (int64_t)erow * d);
-    const int s_begin = kq * steps_per_slice, s_end = min(nsteps, s_begin + steps_per_slice);
-    double acc0[16], acc1[16];
+  // loader assignment: x chunks [64 rows][CPR], weight chunks [3*Np rows][CPR]
+  const int x_chunks = kRouteBT * CPR, w_chunks = 3 * Np * CPR, n_chunks = BK / 4;
+  constexpr int kMaxLoads = kRouteMaxLoads;
+  const int n_loads = (x_chunks + w_chunks + n_chunks + kRouteThreads - 1) / kRouteThreads;
+  u32x4_t rbuf[kMaxLoads];
+  // Every load is issued unconditionally from a clamped, valid address, with no
+  // branch or select between it and the MFMAs, so the whole next tile stays in
+  // flight while the current one is used. Rows past T read row T-1 and padded
+  // expert rows are zero in the split weight; neither reaches a stored logit. Only
+  // columns past d (the last tile when BK does not divide d) are zeroed, at stash.
+  (void)n_loads;
+  auto fetch = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0;
-    // fragments of 2 K steps, double-buffered in registers
-    bf16x8_t fa0[2], fa1[2], fb0[2], fb1[2], fb2[2];
-    auto fetch = [&](int s, bf16x8_t* xa0, bf16x8_t* xa1, bf16x8_t* xb0, bf16x8_t* xb1,
-                     bf16x8_t* xb2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int cidx = 2 * (s + u) + half;
-        if (s + u < s_end && cidx < nch) {
-          xa0[u] = ap0[cidx];
-          xa1[u] = ap1[cidx];
-          xb0[u] = b0[cidx];
-          xb1[u] = b1[cidx];
-          xb2[u] = b2[cidx];
-        } else {
-          xa0[u] = xa1[u] = xb0[u] = xb1[u] = xb2[u] = bf16x8_t{};
-        }
+    for (int u = 0; u < kMaxLoads; ++u) {
+      const int id = tid + u * kRouteThreads;
+      const bool is_x = id < x_chunks;
+      const bool is_w = !is_x && id < x_chunks + w_chunks;
+      const bool is_n = !is_x && !is_w && id < x_chunks + w_chunks + n_chunks;
+      const int wid = is_w ? id - x_chunks : 0;
+      const int nid = is_n ? id - x_chunks - w_chunks : 0;
+      const int ch = is_x ? id % CPR : wid % CPR;
+      const int k = kt * BK + (is_n ? nid * 4 : ch * 8);
+      const int kc = k < d ? k : 0;
+      const bf16_t* src;
+      if (is_x) {
+        src = a.x + min<int64_t>(t0 + id / CPR, T - 1) * d + kc;
+      } else if (is_w) {
+        const int row = wid / CPR;
+        src = a.w3 + (row / Np) * plane + (int64_t)(row % Np) * d + kc;
+      } else {
+        src = reinterpret_cast<const bf16_t*>(a.w_null + kc);
       }
-    };
-    if (s_begin < s_end) fetch(s_begin, fa0, fa1, fb0, fb1, fb2);
-    for (int s = s_begin; s < s_end; s += 2) {
-      bf16x8_t na0[2], na1[2], nb0[2], nb1[2], nb2[2];
-      if (s + 2 < s_end) fetch(s + 2, na0, na1, nb0, nb1, nb2);
-      f32x16_t p0 = {}, p1 = {};
+      rbuf[u] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+  };
+  auto stash = [&](int buf, int kt) {
+    bf16_t* xt = tiles + buf * buf_elems;
+    bf16_t* wt = xt + xt_elems;
+    float* nt_ = reinterpret_cast<float*>(wt + wt_elems);
+    const bool tail = (kt + 1) * BK > d;  // uniform
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[u], fb2[u], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[u], fb2[u], p1, 0, 0, 0);
-        p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[u], fb1[u], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[u], fb1[u], p1, 0, 0, 0);
-        p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[u], fb0[u], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[u], fb0[u], p1, 0, 0, 0);
+    for (int u = 0; u < kMaxLoads; ++u) {
+      const int id = tid + u * kRouteThreads;
+      u32x4_t v = rbuf[u];
+      if (id < x_chunks) {
+        if (tail && kt * BK + (id % CPR) * 8 >= d) v = u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(&xt[rt_off<BK>(id / CPR, id % CPR)]) = v;
+      } else if (id < x_chunks + w_chunks) {
+        const int wid = id - x_chunks;
+        if (tail && kt * BK + (wid % CPR) * 8 >= d) v = u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(&wt[rt_off<BK>(wid / CPR, wid % CPR)]) = v;
+      } else if (id < x_chunks + w_chunks + n_chunks) {
+        const int nid = id - x_chunks - w_chunks;
+        if (tail && kt * BK + nid * 4 >= d) v = u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(&nt_[nid * 4]) = v;
+      }
+    }
+  };
+
+  constexpr int kMaxTilesPerWave = TPW;
+  double acc[kMaxTilesPerWave][16];
+#pragma unroll
+  for (int e = 0; e < kMaxTilesPerWave; ++e)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[e][i] = 0.0;
+  // null row: thread (token tid/4, part tid%4), fp64
+  const int nl_tok = tid >> 2, nl_part = tid & 3;
+  double nacc = 0.0;
+
+  fetch(0);
+  stash(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) fetch(kt + 1);
+    const bf16_t* xt = tiles + buf * buf_elems;
+    const bf16_t* wt = xt + xt_elems;
+    const float* wn = reinterpret_cast<const float*>(wt + wt_elems);
+#pragma unroll
+    for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
+      const int et = eg + 2 * ti;
+      if (et >= n_et) break;
+      f32x16_t part = {};
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int ch = ks * 2 + half;
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xt[rt_off<BK>(th * 32 + l32, ch)]);
+        const int er = et * 32 + l32;
+        const bf16x8_t b2 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(2 * Np + er, ch)]);
+        const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(Np + er, ch)]);
+        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(er, ch)]);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc0[i] += (double)p0[i];
-        acc1[i] += (double)p1[i];
-      }
-      if (s + 2 < s_end) {
+      for (int i = 0; i < 16; ++i) acc[ti][i] += (double)part[i];
+    }
+    // null row over this K tile (zero-padded past d): 16 columns per thread for BK = 64
+    {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          fa0[u] = na0[u];
-          fa1[u] = na1[u];
-          fb0[u] = nb0[u];
-          fb1[u] = nb1[u];
-          fb2[u] = nb2[u];
+      for (int c = nl_part; c < CPR; c += 4) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&xt[rt_off<BK>(nl_tok, c)]);
+        const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(wn + c * 8);
+        const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(wn + c * 8 + 4);
+        const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          nacc = fma((double)__uint_as_float(xv[h] << 16), (double)wv[2 * h], nacc);
+          nacc = fma((double)__uint_as_float(xv[h] & 0xffff0000u), (double)wv[2 * h + 1], nacc);
         }
       }
     }
-    // lane holds expert column erow, token rows 8*(i/4) + 4*half + i%4 (+32 for acc1)
-    if (kq > 0) {
-      double* pp = part + (size_t)(kq - 1) * kRouteBT * Np;
+    if (kt + 1 < nk) stash(buf ^ 1, kt + 1);
+    __syncthreads();
+  }
+  // logits to LDS: lane holds expert column et*32 + l32, token rows 8*(i/4) + 4*half + i%4
+#pragma unroll
+  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
+    const int et = eg + 2 * ti;
+    if (et >= n_et) break;
+    const int er = et * 32 + l32;
+    if (er < N) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int tr = 8 * (i / 4) + 4 * half + (i % 4);
-        pp[tr * Np + erow] = acc0[i];
-        pp[(tr + 32) * Np + erow] = acc1[i];
-      }
-      __syncthreads();
-    } else {
-      if (ks > 1) __syncthreads();  // the other slices of this tile are in LDS
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tr = 8 * (i / 4) + 4 * half + (i % 4);
-        double s0 = acc0[i], s1 = acc1[i];
-        for (int k2 = 1; k2 < ks; ++k2) {
-          const double* pp = part + (size_t)(k2 - 1) * kRouteBT * Np;
-          s0 += pp[tr * Np + erow];
-          s1 += pp[(tr + 32) * Np + erow];
-        }
-        if (erow < N) {
-          sl[tr * ld + erow] = (float)s0;
-          sl[(tr + 32) * ld + erow] = (float)s1;
-        }
+        const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        sl[tr * ld + er] = (float)acc[ti][i];
       }
     }
   }
-  // Null row: x (bf16) times the float32 row, each product exact in fp64, summed
-  // in fp64 by 4 threads per token and combined in a fixed order.
   {
-    const int tl = threadIdx.x >> 2, prt = threadIdx.x & 3;
-    const int64_t t = min<int64_t>(t0 + tl, T - 1);
-    const bf16_t* xr = a.x + t * d;
-    double acc = 0.0;
-    for (int c = prt; c < nch; c += 4) {
-      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
-      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(a.w_null + c * 8);
-      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(a.w_null + c * 8 + 4);
-      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        acc = fma((double)__uint_as_float(xv[h] << 16), (double)wv[2 * h], acc);
-        acc = fma((double)__uint_as_float(xv[h] & 0xffff0000u), (double)wv[2 * h + 1], acc);
-      }
-    }
-    const double a01 = acc + __shfl_xor(acc, 1, kWave);
+    const double a01 = nacc + __shfl_xor(nacc, 1, kWave);
     const double sum = a01 + __shfl_xor(a01, 2, kWave);
-    if (prt == 0 && tl < nt) {
+    if (nl_part == 0 && nl_tok < nt) {
       double vv = sum + (double)a.null_bias;
-      if (a.null_bias_tok) vv += (double)a.null_bias_tok[t0 + tl];
-      sl[tl * ld + N] = (float)vv;
+      if (a.null_bias_tok) vv += (double)a.null_bias_tok[t0 + nl_tok];
+      sl[nl_tok * ld + N] = (float)vv;
     }
   }
   __syncthreads();
-  route_epilogue<FUSED>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
 }
 
 // float32 x: plain dot products (small workloads), then the same epilogue.
-template <bool FUSED>
+template <bool FUSED, int KMAX>
 __global__ void __launch_bounds__(kRouteThreads)
 route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* __restrict__ w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int N = a.N, d = a.d, ld = N + 1;
   float* sl = reinterpret_cast<float*>(smem_raw);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? 4 * (N + 3) : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
   if (FUSED)
     for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
@@ -414,24 +445,24 @@ route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* 
     sl[tl * ld + j] = (float)acc;
   }
   __syncthreads();
-  route_epilogue<FUSED>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
 }
 
-template <bool FUSED>
+template <bool FUSED, int KMAX>
 __global__ void __launch_bounds__(kRouteThreads)
 route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int N = a.N, ld = N + 1;
   float* sl = reinterpret_cast<float*>(smem_raw);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? 4 * (N + 3) : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
   if (FUSED)
     for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) sl[i] = logits[t0 * ld + i];
   __syncthreads();
-  route_epilogue<FUSED>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
 }
 
 size_t route_split_bytes(int N, int d) {
@@ -439,18 +470,16 @@ size_t route_split_bytes(int N, int d) {
   return (size_t)3 * Np * d * sizeof(bf16_t);
 }
 
-static int route_ks(int Np) {
-  const int n_et = Np / 32;
-  return n_et >= 3 ? 1 : 4 / n_et;
-}
+// K tile width of the MFMA router: keeps two buffers of the weight tile in LDS.
+static int route_bk(int Np) { return Np <= 64 ? 64 : (Np <= 128 ? 32 : 16); }
 
 static size_t route_lds_bytes(const RouteArgs& r, bool mfma) {
   const int Np = (r.N + 31) / 32 * 32;
   const int ld = r.N + 1;
   size_t b = 0;
-  if (mfma) b += (size_t)(route_ks(Np) - 1) * kRouteBT * Np * sizeof(double);
+  if (mfma) b += (size_t)2 * ((kRouteBT + 3 * Np) * route_bk(Np) + 2 * route_bk(Np)) * sizeof(bf16_t);
   b += (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
-  if (r.fused) b += (size_t)4 * (r.N + 3) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
+  if (r.fused) b += (size_t)(r.N + 3) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
   return b;
 }
 
@@ -467,7 +496,7 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
   const bool mfma = !r.logits_in && r.bf16;
   RouteKernelArgs a{static_cast<const bf16_t*>(r.x), r.w_split,
                     r.w_router ? r.w_router + (int64_t)r.N * r.d : nullptr, r.null_bias,
-                    r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, route_ks(Np), r.logits_out,
+                    r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, 1, r.logits_out,
                     r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.acc, r.counts};
   const size_t lds = route_lds_bytes(r, mfma);
   // prep: split the router weight (bf16 scoring) and clear the fused accumulators
@@ -478,32 +507,53 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
     route_prep_kernel<<<sblk, 256, 0, stream>>>(r.w_router, mfma ? r.w_split : nullptr, r.N, Np,
                                                 r.d, r.acc, nacc, r.counts, ncnt);
   }
+  const int kmax = r.K <= 2 ? 2 : (r.K <= 8 ? 8 : 32);
+#define MOE_KMAX_SWITCH(MACRO, ...)                 \
+  do {                                              \
+    if (kmax == 2) MACRO(__VA_ARGS__, 2);           \
+    else if (kmax == 8) MACRO(__VA_ARGS__, 8);      \
+    else MACRO(__VA_ARGS__, 32);                    \
+  } while (0)
+#define MOE_LOGITS_LAUNCH(F_, KM_)                                                        \
+  do {                                                                                    \
+    allow_lds(route_from_logits_kernel<F_, KM_>, lds);                                    \
+    route_from_logits_kernel<F_, KM_><<<nblk, kRouteThreads, lds, stream>>>(a, r.logits_in); \
+  } while (0)
+#define MOE_SIMT_LAUNCH(F_, KM_)                                                          \
+  do {                                                                                    \
+    allow_lds(route_simt_kernel<F_, KM_>, lds);                                           \
+    route_simt_kernel<F_, KM_><<<nblk, kRouteThreads, lds, stream>>>(                     \
+        a, static_cast<const float*>(r.x), r.w_router);                                   \
+  } while (0)
+#define MOE_ROUTE_LAUNCH(F_, BK_, TPW_, KM_)                                              \
+  do {                                                                                    \
+    allow_lds(route_mfma_kernel<F_, BK_, TPW_, KM_>, lds);                                \
+    route_mfma_kernel<F_, BK_, TPW_, KM_><<<nblk, kRouteThreads, lds, stream>>>(a);       \
+  } while (0)
   if (r.logits_in) {
-    if (r.fused) {
-      allow_lds(route_from_logits_kernel<true>, lds);
-      route_from_logits_kernel<true><<<nblk, kRouteThreads, lds, stream>>>(a, r.logits_in);
-    } else {
-      allow_lds(route_from_logits_kernel<false>, lds);
-      route_from_logits_kernel<false><<<nblk, kRouteThreads, lds, stream>>>(a, r.logits_in);
-    }
+    if (r.fused) MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, true);
+    else MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, false);
   } else if (r.bf16) {
+    const int bk = route_bk(Np);
+    const int chunks = (kRouteBT + 3 * Np) * bk / 8 + bk / 4;
+    if (chunks > kRouteMaxLoads * kRouteThreads) return hipErrorInvalidValue;
     if (r.fused) {
-      allow_lds(route_mfma_kernel<true>, lds);
-      route_mfma_kernel<true><<<nblk, kRouteThreads, lds, stream>>>(a);
+      if (bk == 64) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 64, 1);
+      else if (bk == 32) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 32, 2);
+      else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 16, 4);
     } else {
-      allow_lds(route_mfma_kernel<false>, lds);
-      route_mfma_kernel<false><<<nblk, kRouteThreads, lds, stream>>>(a);
+      if (bk == 64) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 64, 1);
+      else if (bk == 32) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 32, 2);
+      else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 16, 4);
     }
   } else {
-    const float* xf = static_cast<const float*>(r.x);
-    if (r.fused) {
-      allow_lds(route_simt_kernel<true>, lds);
-      route_simt_kernel<true><<<nblk, kRouteThreads, lds, stream>>>(a, xf, r.w_router);
-    } else {
-      allow_lds(route_simt_kernel<false>, lds);
-      route_simt_kernel<false><<<nblk, kRouteThreads, lds, stream>>>(a, xf, r.w_router);
-    }
+    if (r.fused) MOE_KMAX_SWITCH(MOE_SIMT_LAUNCH, true);
+    else MOE_KMAX_SWITCH(MOE_SIMT_LAUNCH, false);
   }
+#undef MOE_ROUTE_LAUNCH
+#undef MOE_SIMT_LAUNCH
+#undef MOE_LOGITS_LAUNCH
+#undef MOE_KMAX_SWITCH
   return hipGetLastError();
 }
 
