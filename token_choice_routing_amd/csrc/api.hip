@@ -89,7 +89,7 @@ LayerWs layer_ws(const moe_dims* d) {
   w.offsets = take((size_t)(N + 1) * 4);
   w.perm_token = take((size_t)R * 4);
   w.slot_pos = take((size_t)TK * 4);
-  w.route = take(d->dtype == MOE_BF16 ? route_split_bytes(N, d->d_model) : 0);
+  w.route = take(d->dtype == MOE_BF16 ? route_ws_bytes(T, N, d->d_model) : 0);
   w.permute = take(permute_ws_bytes(T, N));
   w.h = take((size_t)R * d->d_ff * e);
   w.hs = take((size_t)T * d->d_ff_shared * e);
@@ -123,7 +123,8 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t which) {
   if (check_dims(d) != MOE_OK) return 0;
   switch (which) {
     case MOE_WS_LAYER: return layer_ws(d).total;
-    case MOE_WS_ROUTE: return d->dtype == MOE_BF16 ? route_split_bytes(d->n_experts, d->d_model) : 0;
+    case MOE_WS_ROUTE:
+      return d->dtype == MOE_BF16 ? route_ws_bytes(d->T, d->n_experts, d->d_model) : 0;
     case MOE_WS_PERMUTE: return permute_ws_bytes(d->T, d->n_experts);
     case MOE_WS_AUX: return aux_ws_bytes(d->n_experts, d->n_null);
   }
@@ -152,7 +153,7 @@ moe_status moe_route(const moe_dims* d, const void* x, const float* w_router, fl
     MOE_TRY(need(w_router));
     MOE_TRY(maybe(null_bias_tok));
     if (bf16) {
-      if (!ws || ws_bytes < route_split_bytes(d->n_experts, d->d_model)) return MOE_ERR_WORKSPACE;
+      if (!ws || ws_bytes < route_ws_bytes(d->T, d->n_experts, d->d_model)) return MOE_ERR_WORKSPACE;
       MOE_TRY(maybe(ws));
     }
   }
@@ -160,7 +161,7 @@ moe_status moe_route(const moe_dims* d, const void* x, const float* w_router, fl
   (void)hipGetLastError();
   RouteArgs a{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, false, x, w_router,
               null_bias, null_bias_tok, logits_in, logits_out, topk_idx, topk_w, n_real,
-              static_cast<uint16_t*>(ws), nullptr, nullptr, nullptr};
+              ws, nullptr, nullptr, nullptr};
   HIP_TRY(launch_route(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -330,7 +331,7 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   // 1. scores, selection, weights; per-chunk expert histogram; statistics sums
   RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
                p->null_bias, p->null_bias_tok, nullptr, logits, topk_idx, topk_w, n_real,
-               static_cast<uint16_t*>(at(L.route)), permute_ws, acc, pool_counts};
+               at(L.route), permute_ws, acc, pool_counts};
   HIP_TRY(launch_route(ra, s));
 
   // 2. counting sort (histograms already written) + statistics finalisation

@@ -66,6 +66,36 @@ __device__ __forceinline__ double wave_sum_double(double v) {
   return v;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wavefront are outstanding (lgkmcnt and expcnt left alone).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+// 16-byte global -> LDS load (global_load_lds_dwordx4). The LDS address must be
+// uniform across the wavefront; lane l writes bytes [16 l, 16 l + 16) after it. The
+// builtin only exists in the device compilation pass, where it is kept.
+__device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#else
+  (void)g;
+  (void)l;
+#endif
+}
+
+// LDS-only workgroup barrier for tiles written by global->LDS loads: each wavefront
+// first retires its own LDS reads; the caller has already waited (vmcnt) for the
+// loads that filled the stage about to be read. The asm statement is also a
+// compiler memory barrier, so no LDS access moves across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace moe

@@ -14,27 +14,31 @@
 //    stores). h is stored in bf16 because the down projection's MFMA reads
 //    bf16; the expert output stays float32 so that the combine rounds the
 //    layer output only once.
-//  * Workgroup tile: 128 rows x 128 weight rows x 64 K, four wavefronts of
-//    64 x 64. For the gate/up pass the 128 weight rows are 64 gate + 64 up rows
-//    of the same output columns, so a lane holds gate and up values of the same
-//    (row, column) and applies SwiGLU in registers; h is written once in bf16.
-//  * LDS tiles are row-major with 16-byte chunks XOR-swizzled by (row mod 8),
-//    so the 32 rows a fragment read touches fall in distinct banks. Two LDS
-//    buffers; the next K tile is fetched into registers while the current one
-//    feeds the MFMAs, one barrier per K tile.
+//  * Workgroup tile BM rows x BN weight rows x 64 K (default 128 x 256 on eight
+//    wavefronts of 64 x 64). For the gate/up pass the BN weight rows are BN/2 gate
+//    + BN/2 up rows of the same output columns, so a lane holds gate and up values
+//    of the same (row, column) and applies SwiGLU in registers; h is written once.
+//  * K tiles stream through S LDS stages filled by global->LDS loads
+//    (global_load_lds_dwordx4): no staging registers, S-1 tiles in flight while
+//    one is multiplied, and the wait before each barrier counts only this
+//    wavefront's loads of the tile about to be read. LDS rows are 128 bytes with
+//    16-byte chunks XOR-swizzled by (row mod 8), so the 32 rows a fragment read
+//    touches fall in distinct banks; the swizzle is applied on the global side
+//    of each load.
 //  * Persistent grid. Each workgroup builds the tile table from the device
 //    offsets (no host round trip for R), and tiles are ordered
 //    (expert, column tile, row tile) and cut into 8 contiguous ranges, one per
 //    XCD (workgroups are dispatched round-robin over the 8 XCDs), so the row
 //    tiles that share one expert's weight panel run on the same L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kFfnThreads = 256;
+constexpr int kBK = 64;
 constexpr int kMaxGroups = 320;   // routed groups (<= 256) + the dense shared-expert problem
 
 enum { kSwiGLU = 0, kPlain = 1 };
@@ -57,7 +61,7 @@ struct TileTable {
 // a = clamp(offsets[e], 0, max_rows), b = clamp(offsets[e+1], a, max_rows):
 // always inside the buffers, exactly the requested segment for valid offsets.
 __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const GemmProblem& p1,
-                                 int oc) {
+                                 int oc, int bm) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const int G0 = p0.groups, G = p0.groups + p1.groups;
@@ -81,7 +85,7 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
         }
         nt = (pr.n_out + oc - 1) / oc;
       }
-      const int m = (l + kBM - 1) / kBM;
+      const int m = (l + bm - 1) / bm;
       if (e <= kMaxGroups) {
         tt.start[e] = s;
         tt.len[e] = l;
@@ -112,27 +116,47 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 // MODE kSwiGLU writes h as bf16 (the next MFMA's input); kPlain writes float32.
 // ROLE only names the launch in profiles (the code is identical): 0 standalone
 // grouped, 1 standalone single segment, 2 the layer's routed + shared launch.
-template <int MODE, int ROLE>
-__global__ void __launch_bounds__(kFfnThreads)
+//
+// Tile BM rows x BN weight rows x 64 K on WM x WN wavefronts; each wavefront owns
+// (BM/WM) x (BN/WN) outputs as 32x32 MFMA blocks. K tiles stream through S LDS
+// stages filled by global->LDS loads (global_load_lds_dwordx4): no staging
+// registers, S-1 stages in flight while one is multiplied. One wavefront load
+// instruction fills 8 consecutive tile rows (64 lanes x 16 bytes = 1 KB of LDS);
+// lane l writes physical chunk l%8 of row l/8, so it fetches the logical chunk
+// (l%8) ^ (row%8) from global memory, which realises the XOR swizzle that keeps
+// the MFMA fragment reads free of bank conflicts.
+template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S>
+__global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int J = (BM + BN) / (8 * NW);            // load instructions per stage per wavefront
+  constexpr int JA = BM / (8 * NW);                  // of which fill A rows
+  constexpr int STAGE = (BM + BN) * kBK;             // elements per stage
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split over the wavefronts");
+  static_assert(MODE != kSwiGLU || FN % 2 == 0, "gate/up tiles come in pairs");
+  static_assert(S >= 2 && S <= 5 && J * (S - 2) < 64, "stages in flight must fit the vmcnt counter");
   __shared__ TileTable tt;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][kBM * kBK];  // [buf][A|B][tile]
-  constexpr int OC = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
-  build_tile_table(tt, p0, p1, OC);
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // [S][BM + BN][kBK]
+  build_tile_table(tt, p0, p1, OC, BM);
   const int G0 = p0.groups, G = p0.groups + p1.groups;
   const int total = tt.prefix[kMaxGroups];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int half = lane >> 5, l32 = lane & 31;
-  const int ld_chunk = tid & 7, ld_row = tid >> 3;  // + 32 * i
+  // this lane's load: row 8 * (wave + NW * j) + lane / 8 of the stage, logical chunk lc
+  const int lrow = lane >> 3;
+  const int lc = (lane & 7) ^ lrow;
 
   // XCD-contiguous tile ranges
   const int P = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per_xcd_blocks = P >> 3;
-  const int S = (total + 7) / 8;
-  const int r_begin = xcd * S, r_end = min(total, r_begin + S);
+  const int Sx = (total + 7) / 8;
+  const int r_begin = xcd * Sx, r_end = min(total, r_begin + Sx);
 
   for (int L = r_begin + slot; L < r_end; L += per_xcd_blocks) {
     // locate (group, column tile, row tile)
@@ -150,133 +174,156 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
     const int ntile = local / mt, mtile = local - ntile * mt;
-    const int m0 = tt.start[e] + mtile * kBM;
-    const int rows_valid = min(kBM, tt.start[e] + tt.len[e] - m0);
+    const int m0 = tt.start[e] + mtile * BM;
+    const int rows_valid = min(BM, tt.start[e] + tt.len[e] - m0);
 
-    // global sources of this thread's 4 A rows and 4 B rows: always a valid row
-    // (clamped). Rows past the segment and columns past n_out only produce outputs
-    // that are never stored, so their loads need no masking; columns past k_dim
-    // (last K tile only) are zeroed at stash. No branch or select sits between a
-    // load and the MFMAs, so all eight loads of the next tile stay in flight.
-    const bf16_t* asrc[4];
-    const bf16_t* bsrc[4];
-    int64_t arow[4];
+    // Row sources, always a valid row: rows past the segment and columns past n_out
+    // only feed outputs that are never stored.
+    const bf16_t* src[J];
+    {
+      int64_t arow[JA > 0 ? JA : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ld_row + 32 * i;
-      arow[i] = m0 + (r < rows_valid ? r : 0);
-    }
-    if (pr.a_rows) {
-      int32_t src_row[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) src_row[i] = pr.a_rows[arow[i]];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) arow[i] = min<int64_t>(max<int64_t>(src_row[i], 0), pr.a_nrows - 1);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ld_row + 32 * i;
-      asrc[i] = pr.a + arow[i] * Kdim;
-      int n;
-      const bf16_t* base;
-      if (MODE == kSwiGLU) {
-        n = ntile * OC + (r & (OC - 1));
-        base = r < OC ? pr.b0 : pr.b1;
-      } else {
-        n = ntile * OC + r;
-        base = pr.b0;
+      for (int j = 0; j < JA; ++j) {
+        const int r = 8 * (wave + NW * j) + lrow;
+        arow[j] = m0 + (r < rows_valid ? r : 0);
       }
-      bsrc[i] = base + ((int64_t)ge * Nout + (n < Nout ? n : 0)) * Kdim;
+      if (pr.a_rows) {
+        int32_t sr[JA > 0 ? JA : 1];
+#pragma unroll
+        for (int j = 0; j < JA; ++j) sr[j] = pr.a_rows[arow[j]];
+#pragma unroll
+        for (int j = 0; j < JA; ++j) arow[j] = min<int64_t>(max<int64_t>(sr[j], 0), pr.a_nrows - 1);
+      }
+#pragma unroll
+      for (int j = 0; j < JA; ++j) src[j] = pr.a + arow[j] * Kdim;
+#pragma unroll
+      for (int j = JA; j < J; ++j) {
+        const int r = 8 * (wave + NW * j) + lrow - BM;
+        int n;
+        const bf16_t* base;
+        if (MODE == kSwiGLU) {
+          n = ntile * OC + (r % OC);
+          base = r < OC ? pr.b0 : pr.b1;
+        } else {
+          n = ntile * OC + r;
+          base = pr.b0;
+        }
+        src[j] = base + ((int64_t)ge * Nout + (n < Nout ? n : 0)) * Kdim;
+      }
     }
-    u32x4_t ra[4], rb[4];
-    auto fetch = [&](int kt) {
-      const int k = kt * kBK + ld_chunk * 8;
+    // K tile kt into stage st. Chunks past k_dim (last tile only) read column 0;
+    // their fragments are zeroed before the MFMAs.
+    auto issue = [&](int kt, int st) {
+      const int k = kt * kBK + lc * 8;
       const int kc = k < Kdim ? k : 0;
+      bf16_t* stage = smem + st * STAGE;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + kc);
-        rb[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + kc);
-      }
-    };
-    auto stash = [&](int buf, int kt) {
-      if ((kt + 1) * kBK > Kdim && kt * kBK + ld_chunk * 8 >= Kdim) {  // K tail only
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = rb[i] = u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = ld_row + 32 * i;
-        *reinterpret_cast<u32x4_t*>(&smem[buf][0][lds_off(r, ld_chunk)]) = ra[i];
-        *reinterpret_cast<u32x4_t*>(&smem[buf][1][lds_off(r, ld_chunk)]) = rb[i];
-      }
+      for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + 8 * (wave + NW * j) * kBK);
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[FN][FM];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int f = 0; f < FN; ++f)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
+      for (int g = 0; g < FM; ++g) acc[f][g] = f32x16_t{};
 
-    fetch(0);
-    stash(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) fetch(kt + 1);
-      const bf16_t* As = smem[buf][0];
-      const bf16_t* Bs = smem[buf][1];
+    // One K tile from stage st in four 16-wide steps; the fragments of step ks+1
+    // are read while step ks multiplies.
+    auto compute = [&](auto tail, int st, int kvalid) {
+      const bf16_t* As = smem + st * STAGE;
+      const bf16_t* Bs = As + BM * kBK;
+      bf16x8_t wf[2][FN], af[2][FM];
+      auto frags = [&](int ks, bf16x8_t* w, bf16x8_t* a) {
+        const int ch = ks * 2 + half;
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          int brow;
+          if (MODE == kSwiGLU)
+            brow = (f < FN / 2 ? 0 : BN / 2) + wn * (TN / 2) + (f % (FN / 2)) * 32 + l32;
+          else
+            brow = wn * TN + f * 32 + l32;
+          w[f] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, ch)]);
+        }
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          a[g] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * TM + g * 32 + l32, ch)]);
+        if constexpr (decltype(tail)::value) {  // last K tile: zero the chunks past k_dim
+          const bool z = ch * 8 >= kvalid;
+#pragma unroll
+          for (int f = 0; f < FN; ++f) w[f] = z ? bf16x8_t{} : w[f];
+#pragma unroll
+          for (int g = 0; g < FM; ++g) a[g] = z ? bf16x8_t{} : a[g];
+        }
+      };
+      frags(0, wf[0], af[0]);
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int ch = ks * 2 + half;
-        bf16x8_t wf[2], af[2];
+        const int cur = ks & 1;
+        if (ks + 1 < kBK / 16) frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-          const int brow = MODE == kSwiGLU ? ns * OC + wn * 32 + l32 : wn * 64 + ns * 32 + l32;
-          wf[ns] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, ch)]);
-        }
+        for (int f = 0; f < FN; ++f)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-          const int arow = wm * 64 + ms * 32 + l32;
-          af[ms] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(arow, ch)]);
-        }
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-          for (int ms = 0; ms < 2; ++ms)
-            acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ns], af[ms], acc[ns][ms], 0, 0, 0);
+          for (int g = 0; g < FM; ++g)
+            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][f], af[cur][g], acc[f][g], 0, 0, 0);
       }
-      if (kt + 1 < nk) stash(buf ^ 1, kt + 1);
-      __syncthreads();
+    };
+
+    // Pipeline. The previous tile's LDS reads finish before its stages are refilled.
+    // Stage kt % S holds K tile kt. Before reading it a wavefront waits until at
+    // most the loads of the later tiles already issued are outstanding; on a tile's
+    // first step it waits for everything, because the previous tile's output stores
+    // may retire out of order with the loads.
+    stage_barrier();
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(S - 2, nk - 1 - kt);  // tiles issued after kt
+      if (kt == 0 || ahead <= 0) wait_vmcnt<0>();
+      else if (S > 3 && ahead == 2) wait_vmcnt<J * (S > 3 ? 2 : 0)>();
+      else if (S > 4 && ahead == 3) wait_vmcnt<J * (S > 4 ? 3 : 0)>();
+      else wait_vmcnt<J>();
+      stage_barrier();
+      if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+      const int kvalid = Kdim - kt * kBK;
+      if (kvalid < kBK)
+        compute(std::true_type{}, kt % S, kvalid);
+      else
+        compute(std::false_type{}, kt % S, kvalid);
     }
 
-    // epilogue: lane owns row (l32) of each 32-row subtile, 4 consecutive columns per group
+    // epilogue: lane owns row l32 of each 32-row subtile, 4 consecutive columns per group
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int rl = wm * 64 + ms * 32 + l32;
+    for (int g = 0; g < FM; ++g) {
+      const int rl = wm * TM + g * 32 + l32;
       if (rl >= rows_valid) continue;
       if (MODE == kSwiGLU) {
         bf16_t* crow = static_cast<bf16_t*>(pr.out) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = ntile * OC + wn * 32 + 8 * g + 4 * half;
-          if (col < Nout) {
-            float h[4];
+        for (int f = 0; f < FN / 2; ++f)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = silu(acc[0][ms][4 * g + j]) * acc[1][ms][4 * g + j];
-            *reinterpret_cast<u32x2_t*>(crow + col) = u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+          for (int q = 0; q < 4; ++q) {
+            const int col = ntile * OC + wn * (TN / 2) + f * 32 + 8 * q + 4 * half;
+            if (col < Nout) {
+              float h[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                h[j] = silu(acc[f][g][4 * q + j]) * acc[f + FN / 2][g][4 * q + j];
+              *reinterpret_cast<u32x2_t*>(crow + col) =
+                  u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+            }
           }
-        }
       } else {
         float* crow = static_cast<float*>(pr.out) + (int64_t)(m0 + rl) * Nout;
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
+        for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = ntile * OC + wn * 64 + ns * 32 + 8 * g + 4 * half;
+          for (int q = 0; q < 4; ++q) {
+            const int col = ntile * OC + wn * TN + f * 32 + 8 * q + 4 * half;
             if (col < Nout) {
-              const f32x16_t& v = acc[ns][ms];
+              const f32x16_t& v = acc[f][g];
               *reinterpret_cast<f32x4_t*>(crow + col) =
-                  f32x4_t{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+                  f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
             }
           }
       }
@@ -324,15 +371,64 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
   }
 }
 
-static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int oc, int num_cus) {
+// Tile shapes (BM x BN, wavefronts, stages). The default, 128 x 256 on eight
+// wavefronts with three stages, measured fastest on both short (~64-row, weight
+// streaming) and long (~512-row) segments; the others remain selectable at build
+// time with MOE_GEMM_VARIANT for tuning.
+struct GemmShape {
+  int bm, bn, threads;
+  size_t lds;
+};
+template <int BM, int BN, int WM, int WN, int S>
+constexpr GemmShape shape_of() {
+  return GemmShape{BM, BN, 64 * WM * WN, (size_t)S * (BM + BN) * kBK * sizeof(bf16_t)};
+}
+
+#ifndef MOE_GEMM_VARIANT
+#define MOE_GEMM_VARIANT 0
+#endif
+
+static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int bm, int oc,
+                          int num_cus, int per_cu) {
   auto upper = [&](const GemmProblem& p) -> int64_t {
     if (p.groups == 0 || p.max_rows <= 0) return 0;
-    return (p.max_rows / kBM + p.groups) * ((p.n_out + oc - 1) / oc);
+    return (p.max_rows / bm + p.groups) * ((p.n_out + oc - 1) / oc);
   };
   const int64_t tiles = upper(p0) + upper(p1);
-  // persistent grid: 2 workgroups per CU (about 68 KiB LDS each), a multiple of 8
-  const int cap = std::max(8, num_cus * 2 / 8 * 8);
+  // persistent grid, a multiple of 8 (one contiguous tile range per XCD)
+  const int cap = std::max(8, num_cus * per_cu / 8 * 8);
   return (unsigned)std::max<int64_t>(8, std::min<int64_t>(cap, (tiles + 7) / 8 * 8));
+}
+
+template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S>
+static void launch_variant(const GemmProblem& q0, const GemmProblem& q1, int num_cus,
+                           hipStream_t stream) {
+  constexpr GemmShape sh = shape_of<BM, BN, WM, WN, S>();
+  static_assert(sh.lds + sizeof(TileTable) <= 160 * 1024, "LDS budget of one CU");
+  constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;
+  auto kern = grouped_gemm_bf16_kernel<MODE, ROLE, BM, BN, WM, WN, S>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
+  // resident workgroups per CU (registers and LDS), queried once per instantiation
+  static const int per_cu = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, sh.threads, sh.lds) != hipSuccess)
+      n = 1;
+    return std::max(1, std::min(n, 2));
+  }();
+  const unsigned grid = gemm_grid(q0, q1, BM, OC, num_cus, per_cu);
+  kern<<<grid, sh.threads, sh.lds, stream>>>(q0, q1);
+}
+
+template <int MODE, int ROLE>
+static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& q1, int num_cus,
+                         hipStream_t stream) {
+  switch (variant) {
+    case 1: launch_variant<MODE, ROLE, 128, 128, 2, 2, 4>(q0, q1, num_cus, stream); break;
+    case 2: launch_variant<MODE, ROLE, 128, 256, 2, 2, 3>(q0, q1, num_cus, stream); break;
+    case 4: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3>(q0, q1, num_cus, stream); break;
+    default: launch_variant<MODE, ROLE, 64, 256, 1, 4, 3>(q0, q1, num_cus, stream); break;
+  }
 }
 
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
@@ -340,20 +436,21 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
   if (!any0 && !any1) return hipSuccess;
   if (bf16) {
-    const int oc = op == 0 ? kBN / 2 : kBN;
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
-    const unsigned grid = gemm_grid(q0, q1, oc, num_cus);
-#define MOE_GEMM_LAUNCH(M_, R_) grouped_gemm_bf16_kernel<M_, R_><<<grid, kFfnThreads, 0, stream>>>(q0, q1)
-    if (op == 0) {
-      if (role == 2) MOE_GEMM_LAUNCH(kSwiGLU, 2);
-      else if (role == 1) MOE_GEMM_LAUNCH(kSwiGLU, 1);
-      else MOE_GEMM_LAUNCH(kSwiGLU, 0);
-    } else {
-      if (role == 2) MOE_GEMM_LAUNCH(kPlain, 2);
-      else if (role == 1) MOE_GEMM_LAUNCH(kPlain, 1);
-      else MOE_GEMM_LAUNCH(kPlain, 0);
-    }
-#undef MOE_GEMM_LAUNCH
+    // worst-case rows per group decides the tile shape
+    const int64_t rows = std::max<int64_t>(any0 ? q0.max_rows / q0.groups : 0,
+                                           any1 ? q1.max_rows / q1.groups : 0);
+    int variant = MOE_GEMM_VARIANT;
+    if (variant == 0) variant = 4;
+#define MOE_GEMM_DISPATCH(M_)                                                  \
+  do {                                                                         \
+    if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream);      \
+    else if (role == 1) launch_shape<M_, 1>(variant, q0, q1, num_cus, stream); \
+    else launch_shape<M_, 0>(variant, q0, q1, num_cus, stream);                \
+  } while (0)
+    if (op == 0) MOE_GEMM_DISPATCH(kSwiGLU);
+    else MOE_GEMM_DISPATCH(kPlain);
+#undef MOE_GEMM_DISPATCH
   } else {
     for (const GemmProblem* p : {&p0, &p1}) {
       if (p->groups == 0 || p->max_rows <= 0) continue;

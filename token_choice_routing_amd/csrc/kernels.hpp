@@ -25,13 +25,13 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   int32_t* n_real;
-  uint16_t* w_split;  // [3][Np][d] bf16 scratch, bf16 path only
+  void* ws;           // bf16 scoring scratch of route_ws_bytes(T, N, d) bytes
   int32_t* chunk_hist; // fused: [blocks][N]
   uint64_t* acc;       // fused: [N + 3] accumulators (cleared by the launch)
   int32_t* counts;     // fused: [N + M] pool slot counts (cleared by the launch)
 };
 int route_tokens_per_block();
-size_t route_split_bytes(int N, int d);
+size_t route_ws_bytes(int64_t T, int N, int d);
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 // Statistics finalisation done by the permutation's scan kernel in the fused layer path.

@@ -24,10 +24,12 @@
 //    accumulation over d = 2048 terms drifts by a few 1e-6, too close to the
 //    1e-5 near-tie margin of routing parity). The null row is an fp64 dot
 //    product on the vector ALUs.
-//  * A workgroup scores 64 tokens. K tiles of x and of the three weight planes
-//    are staged through two swizzled LDS buffers by all 256 threads (the next
-//    tile is fetched into registers while the current one feeds the MFMAs);
-//    wavefront w takes token half w & 1 against every other 32-expert tile.
+//  * A workgroup scores 64 tokens against one or two 32-expert tiles (all of
+//    them when N <= 64). K tiles of x, of the three weight planes and of the null
+//    row stream through 4-6 swizzled LDS stages filled by global->LDS loads, so
+//    several tiles are in flight while one feeds the MFMAs. When N > 64 the
+//    expert tiles of a token tile are spread over several workgroups and the last
+//    one to finish runs the selection.
 //  * Epilogue: one lane per token. Each lane walks its token's logits row in
 //    LDS once and keeps the best K reals in registers with a branch-free
 //    insertion network over 64-bit keys (order-preserving bits of the logit,
@@ -48,18 +50,15 @@ namespace moe {
 
 constexpr int kRouteBT = 64;       // tokens per workgroup
 constexpr int kRouteThreads = 256;
-// 16-byte loads per thread per K tile of the MFMA router: ((64 + 3 Np) BK / 8 + BK / 4)
-// chunks over 256 threads, at most 9 for every (Np, BK) pair route_bk() picks.
-constexpr int kRouteMaxLoads = 9;
-constexpr int kQ = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
 
 int route_tokens_per_block() { return kRouteBT; }
 
-// Prep: split W into bf16 (hi, mid, lo) planes [3][Np][d] (rows >= N zero) and
-// clear the fused-statistics accumulators.
+// Prep: split W into bf16 (hi, mid, lo) planes [3][Np][d] (rows >= N zero), clear
+// the fused-statistics accumulators and the token-tile counters.
 __global__ void route_prep_kernel(const float* __restrict__ w, bf16_t* __restrict__ w3, int N,
                                   int Np, int d, uint64_t* __restrict__ acc, int nacc,
-                                  int32_t* __restrict__ cnt, int ncnt) {
+                                  int32_t* __restrict__ cnt, int ncnt, uint32_t* __restrict__ tiles,
+                                  int64_t ntiles) {
   const int64_t total = w3 ? (int64_t)Np * d : 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -76,6 +75,7 @@ __global__ void route_prep_kernel(const float* __restrict__ w, bf16_t* __restric
   }
   for (int64_t i = i0; i < nacc; i += stride) acc[i] = 0;
   for (int64_t i = i0; i < ncnt; i += stride) cnt[i] = 0;
+  for (int64_t i = i0; i < ntiles; i += stride) tiles[i] = 0;
 }
 
 // total order of float32 values as unsigned keys (-0.0 and +0.0 equal)
@@ -113,6 +113,8 @@ struct RouteKernelArgs {
   int32_t* chunk_hist;     // fused: [blocks][N]
   uint64_t* acc;           // fused: [N + 3] fixed-point sums
   int32_t* counts;         // fused: [N + M] pool slot counts
+  float* lbuf;             // bf16 scoring: [T][N + 1] logits of the expert-tile workgroups
+  uint32_t* tile_cnt;      // bf16 scoring: [token tiles] finished expert tiles (kept at 0)
 };
 
 // Lane-per-token selection for the (up to 64) tokens of one workgroup, run by
@@ -197,10 +199,10 @@ __device__ void select_lanes(const RouteKernelArgs& a, float* sl, int ld, int nt
 
 template <bool FUSED, int KMAX>
 __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
-                               int* cnt_lds, double* wacc) {
+                               int64_t tile, bool copy_logits, int* cnt_lds, double* wacc) {
   const int wave = threadIdx.x / kWave;
   const int N = a.N, M = a.M, P = N + M;
-  if (a.logits_out) {
+  if (copy_logits) {
     const int w = N + 1;
     for (int i = threadIdx.x; i < nt * w; i += blockDim.x)
       a.logits_out[(t0 + i / w) * w + i % w] = sl[(i / w) * ld + i % w];
@@ -234,152 +236,138 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
   }
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
     const int cval = cnt_lds[i];
-    if (i < N) a.chunk_hist[(int64_t)blockIdx.x * N + i] = cval;
+    if (i < N) a.chunk_hist[tile * N + i] = cval;
     if (cval) atomicAdd(&a.counts[i], cval);
   }
 }
 
-// bf16 x: three-way split MFMA scoring of the N real rows + fp64 null row.
-// K tiles of BK columns of x (64 tokens) and of the three weight planes (Np rows)
-// are staged through two LDS buffers by all 256 threads; wavefront w computes
-// token half (w & 1) against expert tiles (w >> 1), (w >> 1) + 2, ...
-template <int BK>
+// bf16 x: three-way split MFMA scoring. Workgroup (token tile tt, expert group eg)
+// scores 64 tokens against ETW 32-expert tiles over the whole of d; the EG = Np /
+// (32 ETW) groups of a token tile are dispatched to one XCD, where they share the
+// x tile in L2. K tiles of 64 columns (x rows, the three weight planes of the
+// group and the null row's float32 weights) stream through S LDS stages filled by
+// global->LDS loads, S-1 of them in flight. Wavefront w multiplies token half
+// w & 1 over the 16-wide K steps 2 (w >> 1) and 2 (w >> 1) + 1 of each tile; the
+// two K halves are added in a fixed order at the end. Group 0 also computes the
+// null row as an fp64 dot product. With one group per token tile the logits go
+// straight to LDS for the selection epilogue; otherwise each group writes its
+// columns and the last group of the token tile to finish (an atomic counter,
+// release/acquire fenced) reads the whole tile back and selects.
+constexpr int kRouteRedOff = 84 * 1024;  // LDS byte offset of the K-half exchange buffer
+
+template <int ETW>
+struct RouteTile {
+  static constexpr int rows = kRouteBT + 3 * 32 * ETW;   // x rows + weight rows per stage
+  static constexpr int stage = rows * 64 + 512;          // bf16 elements (+ 1 KB null slot)
+  static constexpr int loads = rows / 8 / 4;             // row loads per stage per wavefront
+  static constexpr int stages = ETW == 1 ? 6 : 4;
+  static constexpr size_t lds = (size_t)stages * stage * sizeof(bf16_t);
+  static_assert(lds <= 160 * 1024 - 256, "LDS budget of one CU");
+  static_assert(kRouteRedOff + 2 * ETW * 16 * kWave * sizeof(double) <= lds, "exchange buffer");
+};
+
 __device__ __forceinline__ int rt_off(int row, int chunk) {
-  constexpr int CPR = BK / 8;  // 16-byte chunks per row
-  return row * BK + ((chunk ^ (row & (CPR - 1))) << 3);
+  return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
 
-template <bool FUSED, int BK, int TPW, int KMAX>  // TPW: 32-expert tiles per wavefront
+template <bool FUSED, int KMAX, int ETW>
 __global__ void __launch_bounds__(kRouteThreads)
-route_mfma_kernel(RouteKernelArgs a) {
+route_tile_kernel(RouteKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  constexpr int CPR = BK / 8;
-  const int N = a.N, d = a.d, Np = a.Np;
+  using TL = RouteTile<ETW>;
+  constexpr int S = TL::stages, J = TL::loads;
+  static_assert(kRouteBT == 64 && kRouteThreads == 256, "tile shape");
+  static_assert((J + 1) * (S - 2) < 64, "stages in flight must fit the vmcnt counter");
+  const int N = a.N, d = a.d, Np = a.Np, n_et = Np / 32, EG = (n_et + ETW - 1) / ETW;
   const int ld = N + 1;
-  const int n_et = Np / 32;
-  // LDS: 2 x { x tile [64][BK], weight tile [3][Np][BK] bf16, null-row tile [BK] float },
-  // logits [64][ld] float, fused: [N+3] doubles and pool counts [N+M] ints
-  const int xt_elems = kRouteBT * BK, wt_elems = 3 * Np * BK;
-  const int buf_elems = xt_elems + wt_elems + 2 * BK;  // bf16 units; the null tile is BK floats
-  bf16_t* tiles = reinterpret_cast<bf16_t*>(smem_raw);
-  float* sl = reinterpret_cast<float*>(tiles + 2 * buf_elems);
-  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
-  if (FUSED)
-    for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
+  bf16_t* stages = reinterpret_cast<bf16_t*>(smem_raw);
 
+  const int b = blockIdx.x, xcd = b & 7, q = b >> 3;
+  const int64_t tt = (int64_t)(q / EG) * 8 + xcd;
+  const int eg = q % EG;
   const int64_t T = a.T;
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
+  if (tt * kRouteBT >= T) return;  // padding of the grid to whole XCD rounds
+  const int64_t t0 = tt * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, T - t0);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int half = lane >> 5, l32 = lane & 31;
-  const int th = wave & 1, eg = wave >> 1;
-  const int nk = (d + BK - 1) / BK;
+  const int th = wave & 1, kp = wave >> 1;
+  const int nk = (d + 63) / 64;
   const int64_t plane = (int64_t)Np * d;
+  const int lrow = lane >> 3, lc = (lane & 7) ^ lrow;
 
-  // loader assignment: x chunks [64 rows][CPR], weight chunks [3*Np rows][CPR]
-  const int x_chunks = kRouteBT * CPR, w_chunks = 3 * Np * CPR, n_chunks = BK / 4;
-  constexpr int kMaxLoads = kRouteMaxLoads;
-  const int n_loads = (x_chunks + w_chunks + n_chunks + kRouteThreads - 1) / kRouteThreads;
-  u32x4_t rbuf[kMaxLoads];
-  // Every load is issued unconditionally from a clamped, valid address, with no
-  // branch or select between it and the MFMAs, so the whole next tile stays in
-  // flight while the current one is used. Rows past T read row T-1 and padded
-  // expert rows are zero in the split weight; neither reaches a stored logit. Only
-  // columns past d (the last tile when BK does not divide d) are zeroed, at stash.
-  (void)n_loads;
-  auto fetch = [&](int kt) {
+  // Stage row 8 (wave + 4 j) + lane / 8 comes from x (rows < 64, clamped to T - 1;
+  // those rows are never stored) or, at 64 + 32 (3 u + p) + i, from weight plane p,
+  // expert 32 (ETW eg + u) + i (a tile past Np reads tile 0 and is never stored).
+  const bf16_t* src[J];
 #pragma unroll
-    for (int u = 0; u < kMaxLoads; ++u) {
-      const int id = tid + u * kRouteThreads;
-      const bool is_x = id < x_chunks;
-      const bool is_w = !is_x && id < x_chunks + w_chunks;
-      const bool is_n = !is_x && !is_w && id < x_chunks + w_chunks + n_chunks;
-      const int wid = is_w ? id - x_chunks : 0;
-      const int nid = is_n ? id - x_chunks - w_chunks : 0;
-      const int ch = is_x ? id % CPR : wid % CPR;
-      const int k = kt * BK + (is_n ? nid * 4 : ch * 8);
-      const int kc = k < d ? k : 0;
-      const bf16_t* src;
-      if (is_x) {
-        src = a.x + min<int64_t>(t0 + id / CPR, T - 1) * d + kc;
-      } else if (is_w) {
-        const int row = wid / CPR;
-        src = a.w3 + (row / Np) * plane + (int64_t)(row % Np) * d + kc;
-      } else {
-        src = reinterpret_cast<const bf16_t*>(a.w_null + kc);
-      }
-      rbuf[u] = *reinterpret_cast<const u32x4_t*>(src);
+  for (int j = 0; j < J; ++j) {
+    const int r = 8 * (wave + 4 * j) + lrow;
+    if (j < kRouteBT / 32) {
+      src[j] = a.x + min<int64_t>(t0 + r, T - 1) * d;
+    } else {
+      const int wr = r - kRouteBT, u = wr / 96, p = (wr / 32) % 3;
+      const int et = ETW * eg + u < n_et ? ETW * eg + u : 0;
+      src[j] = a.w3 + p * plane + (int64_t)(et * 32 + wr % 32) * d;
     }
-  };
-  auto stash = [&](int buf, int kt) {
-    bf16_t* xt = tiles + buf * buf_elems;
-    bf16_t* wt = xt + xt_elems;
-    float* nt_ = reinterpret_cast<float*>(wt + wt_elems);
-    const bool tail = (kt + 1) * BK > d;  // uniform
+  }
+  // null slot: lane l loads floats [4 (l % 16), 4 (l % 16) + 4) of the tile (four copies)
+  const int nl_col = 4 * (lane & 15);
+  // Loads of K tile kt into stage st; chunks past d read column 0 and are zeroed
+  // at use.
+  auto issue = [&](int kt, int st) {
+    const int k = kt * 64 + lc * 8;
+    const int kc = k < d ? k : 0;
+    bf16_t* stage = stages + st * TL::stage;
 #pragma unroll
-    for (int u = 0; u < kMaxLoads; ++u) {
-      const int id = tid + u * kRouteThreads;
-      u32x4_t v = rbuf[u];
-      if (id < x_chunks) {
-        if (tail && kt * BK + (id % CPR) * 8 >= d) v = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(&xt[rt_off<BK>(id / CPR, id % CPR)]) = v;
-      } else if (id < x_chunks + w_chunks) {
-        const int wid = id - x_chunks;
-        if (tail && kt * BK + (wid % CPR) * 8 >= d) v = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(&wt[rt_off<BK>(wid / CPR, wid % CPR)]) = v;
-      } else if (id < x_chunks + w_chunks + n_chunks) {
-        const int nid = id - x_chunks - w_chunks;
-        if (tail && kt * BK + nid * 4 >= d) v = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(&nt_[nid * 4]) = v;
-      }
-    }
+    for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + 8 * (wave + 4 * j) * 64);
+    const int kn = kt * 64 + nl_col;
+    load_lds16(reinterpret_cast<const bf16_t*>(a.w_null + (kn + 4 <= d ? kn : 0)),
+               stage + TL::rows * 64);
   };
 
-  constexpr int kMaxTilesPerWave = TPW;
-  double acc[kMaxTilesPerWave][16];
+  double acc[ETW][16];
 #pragma unroll
-  for (int e = 0; e < kMaxTilesPerWave; ++e)
+  for (int u = 0; u < ETW; ++u)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[e][i] = 0.0;
-  // null row: thread (token tid/4, part tid%4), fp64
+    for (int i = 0; i < 16; ++i) acc[u][i] = 0.0;
+  const bool do_null = eg == 0;
   const int nl_tok = tid >> 2, nl_part = tid & 3;
   double nacc = 0.0;
 
-  fetch(0);
-  stash(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) fetch(kt + 1);
-    const bf16_t* xt = tiles + buf * buf_elems;
-    const bf16_t* wt = xt + xt_elems;
-    const float* wn = reinterpret_cast<const float*>(wt + wt_elems);
+  auto compute = [&](auto tail, int st, int kvalid) {
+    const bf16_t* xs = stages + st * TL::stage;
+    const float* wn = reinterpret_cast<const float*>(xs + TL::rows * 64);
+    f32x16_t part[ETW];
 #pragma unroll
-    for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
-      const int et = eg + 2 * ti;
-      if (et >= n_et) break;
-      f32x16_t part = {};
+    for (int u = 0; u < ETW; ++u) part[u] = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ks * 2 + half;
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xt[rt_off<BK>(th * 32 + l32, ch)]);
-        const int er = et * 32 + l32;
-        const bf16x8_t b2 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(2 * Np + er, ch)]);
-        const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(Np + er, ch)]);
-        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&wt[rt_off<BK>(er, ch)]);
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part, 0, 0, 0);
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ch = (2 * kp + s2) * 2 + half;
+      bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(th * 32 + l32, ch)]);
+      if constexpr (decltype(tail)::value) {
+        if (ch * 8 >= kvalid) af = bf16x8_t{};
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[ti][i] += (double)part[i];
+      for (int u = 0; u < ETW; ++u) {
+        const int wr = kRouteBT + 96 * u + l32;
+        bf16x8_t b2 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr + 64, ch)]);
+        bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr + 32, ch)]);
+        bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr, ch)]);
+        if constexpr (decltype(tail)::value) {
+          if (ch * 8 >= kvalid) b2 = b1 = b0 = bf16x8_t{};
+        }
+        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part[u], 0, 0, 0);
+        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part[u], 0, 0, 0);
+        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part[u], 0, 0, 0);
+      }
     }
-    // null row over this K tile (zero-padded past d): 16 columns per thread for BK = 64
-    {
+    if (do_null) {
 #pragma unroll
-      for (int c = nl_part; c < CPR; c += 4) {
-        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&xt[rt_off<BK>(nl_tok, c)]);
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = nl_part + 4 * cc;
+        if (decltype(tail)::value && c * 8 >= kvalid) continue;
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&xs[rt_off(nl_tok, c)]);
         const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(wn + c * 8);
         const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(wn + c * 8 + 4);
         const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
@@ -390,34 +378,107 @@ route_mfma_kernel(RouteKernelArgs a) {
         }
       }
     }
-    if (kt + 1 < nk) stash(buf ^ 1, kt + 1);
-    __syncthreads();
-  }
-  // logits to LDS: lane holds expert column et*32 + l32, token rows 8*(i/4) + 4*half + i%4
 #pragma unroll
-  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
-    const int et = eg + 2 * ti;
-    if (et >= n_et) break;
-    const int er = et * 32 + l32;
-    if (er < N) {
+    for (int u = 0; u < ETW; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][i] += (double)part[u][i];
+  };
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(S - 2, nk - 1 - kt);  // K tiles issued after kt
+    switch (ahead) {
+      case 4: wait_vmcnt<(S > 5 ? 4 : 0) * (J + 1)>(); break;
+      case 3: wait_vmcnt<(S > 4 ? 3 : 0) * (J + 1)>(); break;
+      case 2: wait_vmcnt<2 * (J + 1)>(); break;
+      case 1: wait_vmcnt<J + 1>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+    stage_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    const int kvalid = d - kt * 64;
+    if (kvalid < 64) compute(std::true_type{}, kt % S, kvalid);
+    else compute(std::false_type{}, kt % S, kvalid);
+  }
+
+  // LDS after the K loop: selection tile [64][ld] floats at 0, then the epilogue's
+  // statistics scratch, and the K-half exchange buffer at kRouteRedOff.
+  stage_barrier();
+  float* sl = reinterpret_cast<float*>(smem_raw);
+  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
+  double* red = reinterpret_cast<double*>(smem_raw + kRouteRedOff);  // [2][ETW][16][64]
+  if (kp == 1) {
+#pragma unroll
+    for (int u = 0; u < ETW; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[((th * ETW + u) * 16 + i) * kWave + lane] = acc[u][i];
+  }
+  if (FUSED && EG == 1)
+    for (int i = tid; i < N + a.M; i += kRouteThreads) cnt_lds[i] = 0;
+  __syncthreads();
+  // EG == 1: the tile's logits go to LDS; otherwise to the staging buffer
+  float* out = EG == 1 ? sl : a.lbuf + t0 * ld;
+  if (kp == 0) {
+#pragma unroll
+    for (int u = 0; u < ETW; ++u) {
+      const int e = (ETW * eg + u) * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
         const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        sl[tr * ld + er] = (float)acc[ti][i];
+        if (e < N && tr < nt) out[tr * ld + e] = (float)v;
       }
     }
   }
-  {
+  if (do_null) {
     const double a01 = nacc + __shfl_xor(nacc, 1, kWave);
     const double sum = a01 + __shfl_xor(a01, 2, kWave);
     if (nl_part == 0 && nl_tok < nt) {
       double vv = sum + (double)a.null_bias;
       if (a.null_bias_tok) vv += (double)a.null_bias_tok[t0 + nl_tok];
-      sl[nl_tok * ld + N] = (float)vv;
+      out[nl_tok * ld + N] = (float)vv;
     }
   }
+  if (EG == 1) {
+    __syncthreads();
+    route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out != nullptr, cnt_lds, wacc);
+    return;
+  }
+
+  // the last group of the token tile to finish selects
+  __shared__ int last;
+  __threadfence();
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  if (tid == 0) last = atomicAdd(&a.tile_cnt[tt], 1u) == (unsigned)(EG - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  if (tid == 0) a.tile_cnt[tt] = 0u;
+  {
+    const int n = nt * ld;
+    const float* src_l = a.lbuf + t0 * ld;
+    for (int i0 = tid; i0 < n; i0 += 8 * kRouteThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        v[u] = i < n ? src_l[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        if (i < n) sl[i] = v[u];
+      }
+    }
+  }
+  if (FUSED)
+    for (int i = tid; i < N + a.M; i += kRouteThreads) cnt_lds[i] = 0;
+  __syncthreads();
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out && a.logits_out != a.lbuf,
+                              cnt_lds, wacc);
 }
 
 // float32 x: plain dot products (small workloads), then the same epilogue.
@@ -445,7 +506,8 @@ route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* 
     sl[tl * ld + j] = (float)acc;
   }
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds,
+                              wacc);
 }
 
 template <bool FUSED, int KMAX>
@@ -462,24 +524,36 @@ route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) sl[i] = logits[t0 * ld + i];
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds,
+                              wacc);
 }
 
-size_t route_split_bytes(int N, int d) {
+// bf16 scoring workspace: split weight planes, the logits staging buffer and the
+// token-tile counters, each 256-byte aligned.
+struct RouteWs {
+  size_t split, lbuf, tiles, total;
+};
+static RouteWs route_ws(int64_t T, int N, int d) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const int Np = (N + 31) / 32 * 32;
-  return (size_t)3 * Np * d * sizeof(bf16_t);
+  RouteWs w;
+  w.split = 0;
+  w.lbuf = up((size_t)3 * Np * d * sizeof(bf16_t));
+  w.tiles = w.lbuf + up((size_t)T * (N + 1) * sizeof(float));
+  w.total = w.tiles + up((size_t)((T + kRouteBT - 1) / kRouteBT) * sizeof(uint32_t));
+  return w;
 }
+size_t route_ws_bytes(int64_t T, int N, int d) { return route_ws(T, N, d).total; }
 
-// K tile width of the MFMA router: keeps two buffers of the weight tile in LDS.
-static int route_bk(int Np) { return Np <= 64 ? 64 : (Np <= 128 ? 32 : 16); }
+// 32-expert tiles per scoring workgroup: all of them when N <= 64 (no cross-workgroup
+// step), else pairs.
+static int route_etw(int N) { return N <= 32 ? 1 : 2; }
 
 static size_t route_lds_bytes(const RouteArgs& r, bool mfma) {
-  const int Np = (r.N + 31) / 32 * 32;
   const int ld = r.N + 1;
-  size_t b = 0;
-  if (mfma) b += (size_t)2 * ((kRouteBT + 3 * Np) * route_bk(Np) + 2 * route_bk(Np)) * sizeof(bf16_t);
-  b += (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
+  size_t b = (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
   if (r.fused) b += (size_t)(r.N + 3) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
+  if (mfma) b = std::max(b, route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds);
   return b;
 }
 
@@ -491,21 +565,29 @@ static void allow_lds(F* kernel, size_t lds) {
 }
 
 hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
-  const unsigned nblk = (unsigned)((r.T + kRouteBT - 1) / kRouteBT);
+  const int64_t ntt = (r.T + kRouteBT - 1) / kRouteBT;
+  const unsigned nblk = (unsigned)ntt;
   const int Np = (r.N + 31) / 32 * 32;
   const bool mfma = !r.logits_in && r.bf16;
-  RouteKernelArgs a{static_cast<const bf16_t*>(r.x), r.w_split,
+  const RouteWs rw = route_ws(r.T, r.N, r.d);
+  unsigned char* ws = static_cast<unsigned char*>(r.ws);
+  bf16_t* w3 = mfma ? reinterpret_cast<bf16_t*>(ws + rw.split) : nullptr;
+  float* lbuf = mfma ? (r.logits_out ? r.logits_out : reinterpret_cast<float*>(ws + rw.lbuf)) : nullptr;
+  uint32_t* tiles = mfma ? reinterpret_cast<uint32_t*>(ws + rw.tiles) : nullptr;
+  RouteKernelArgs a{static_cast<const bf16_t*>(r.x), w3,
                     r.w_router ? r.w_router + (int64_t)r.N * r.d : nullptr, r.null_bias,
                     r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, 1, r.logits_out,
-                    r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.acc, r.counts};
+                    r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.acc, r.counts, lbuf, tiles};
   const size_t lds = route_lds_bytes(r, mfma);
-  // prep: split the router weight (bf16 scoring) and clear the fused accumulators
+  // prep: split the router weight (bf16 scoring), clear the fused accumulators and
+  // the token-tile counters
   const int nacc = r.fused ? r.N + 3 : 0, ncnt = r.fused ? r.N + r.M : 0;
   if (mfma || r.fused) {
-    const int64_t n = mfma ? (int64_t)Np * r.d : std::max(nacc, ncnt);
+    const int64_t n = std::max<int64_t>(mfma ? (int64_t)Np * r.d : 0,
+                                        std::max<int64_t>(std::max(nacc, ncnt), mfma ? ntt : 0));
     const unsigned sblk = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1024));
-    route_prep_kernel<<<sblk, 256, 0, stream>>>(r.w_router, mfma ? r.w_split : nullptr, r.N, Np,
-                                                r.d, r.acc, nacc, r.counts, ncnt);
+    route_prep_kernel<<<sblk, 256, 0, stream>>>(r.w_router, w3, r.N, Np, r.d, r.acc, nacc,
+                                                r.counts, ncnt, tiles, mfma ? ntt : 0);
   }
   const int kmax = r.K <= 2 ? 2 : (r.K <= 8 ? 8 : 32);
 #define MOE_KMAX_SWITCH(MACRO, ...)                 \
@@ -525,27 +607,26 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
     route_simt_kernel<F_, KM_><<<nblk, kRouteThreads, lds, stream>>>(                     \
         a, static_cast<const float*>(r.x), r.w_router);                                   \
   } while (0)
-#define MOE_ROUTE_LAUNCH(F_, BK_, TPW_, KM_)                                              \
+#define MOE_ROUTE_LAUNCH(F_, KM_)                                                         \
   do {                                                                                    \
-    allow_lds(route_mfma_kernel<F_, BK_, TPW_, KM_>, lds);                                \
-    route_mfma_kernel<F_, BK_, TPW_, KM_><<<nblk, kRouteThreads, lds, stream>>>(a);       \
+    if (etw == 1) {                                                                       \
+      allow_lds(route_tile_kernel<F_, KM_, 1>, lds);                                      \
+      route_tile_kernel<F_, KM_, 1><<<grid, kRouteThreads, lds, stream>>>(a);             \
+    } else {                                                                              \
+      allow_lds(route_tile_kernel<F_, KM_, 2>, lds);                                      \
+      route_tile_kernel<F_, KM_, 2><<<grid, kRouteThreads, lds, stream>>>(a);             \
+    }                                                                                     \
   } while (0)
   if (r.logits_in) {
     if (r.fused) MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, true);
     else MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, false);
   } else if (r.bf16) {
-    const int bk = route_bk(Np);
-    const int chunks = (kRouteBT + 3 * Np) * bk / 8 + bk / 4;
-    if (chunks > kRouteMaxLoads * kRouteThreads) return hipErrorInvalidValue;
-    if (r.fused) {
-      if (bk == 64) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 64, 1);
-      else if (bk == 32) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 32, 2);
-      else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true, 16, 4);
-    } else {
-      if (bk == 64) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 64, 1);
-      else if (bk == 32) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 32, 2);
-      else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false, 16, 4);
-    }
+    // token tiles padded to whole rounds of the 8 XCDs, times the expert groups
+    const int etw = route_etw(r.N);
+    const int eg = (Np / 32 + etw - 1) / etw;
+    const unsigned grid = (unsigned)((ntt + 7) / 8 * 8 * eg);
+    if (r.fused) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true);
+    else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false);
   } else {
     if (r.fused) MOE_KMAX_SWITCH(MOE_SIMT_LAUNCH, true);
     else MOE_KMAX_SWITCH(MOE_SIMT_LAUNCH, false);
