@@ -193,3 +193,12 @@ def test_one_expert_takes_every_slot():
 def test_tiny_token_counts(T):
     say(f"T = {T}")
     check_full(sub_workload(generate(_small()), np.arange(T)))
+
+
+@pytest.mark.parametrize("N,M,K,T", [(100, 28, 6, 300), (255, 1, 8, 130), (24, 0, 3, 200)])
+def test_expert_counts_across_router_tilings(N, M, K, T):
+    """Full layer where the router spreads a token tile over several scoring
+    workgroups (N > 64, up to the 255-expert limit) and where one 32-expert
+    tile covers every expert (N <= 32)."""
+    say(f"layer with N={N} M={M} K={K} T={T}")
+    check_full(generate(_small(n_experts=N, n_null=M, top_k=K, T=T)))

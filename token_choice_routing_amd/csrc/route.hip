@@ -117,39 +117,62 @@ struct RouteKernelArgs {
   uint32_t* tile_cnt;      // bf16 scoring: [token tiles] finished expert tiles (kept at 0)
 };
 
-// Lane-per-token selection for the (up to 64) tokens of one workgroup, run by
-// wavefront 0 with lane t owning token t. Each lane walks its logits row once,
-// keeping the best KMAX reals in a register list sorted by 64-bit keys (the
-// order-preserving bits of the logit, then the complemented index: a larger key
-// is a larger logit, or the lower index at equal logits). An insertion is a
-// fixed compare-and-swap chain, so no lane diverges. In fused mode the row is
-// then overwritten with its pool-softmax probabilities for the column sums.
+// Selection for the (up to 64) tokens of one workgroup: four consecutive lanes
+// own a token, lane q walking experts q, q + 4, ... of its logits row. Each lane
+// keeps the best KMAX reals it has seen in a register list sorted by 64-bit keys
+// (the order-preserving bits of the logit, then the complemented index: a larger
+// key is a larger logit, or the lower index at equal logits); an insertion is a
+// fixed compare-and-swap chain, so no lane diverges. The four lists are merged
+// with two rounds of shuffles, after which every lane of the token holds the
+// same top-KMAX list. In fused mode the row is then overwritten with its
+// pool-softmax probabilities for the column sums, and lane 0 of the token leaves
+// lse^2 and r in tok_acc[0][t] and tok_acc[1][t].
+template <int KMAX>
+__device__ __forceinline__ void insert_key(uint64_t (&lk)[KMAX], uint64_t key) {
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const bool gt = key > lk[i];
+    const uint64_t old = lk[i];
+    lk[i] = gt ? key : old;
+    key = gt ? old : key;
+  }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 template <int KMAX, bool FUSED>
-__device__ void select_lanes(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
-                             int* cnt_lds, double* lane_acc) {
-  const int lane = threadIdx.x & (kWave - 1);
+__device__ void select_quads(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
+                             int* cnt_lds, double* tok_acc) {
+  const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
   const int N = a.N, M = a.M, K = a.K;
-  const bool live = lane < nt;
-  float* s = sl + (live ? lane : 0) * ld;
+  const bool live = tl < nt;
+  float* s = sl + (live ? tl : 0) * ld;
   const float snull = s[N];
   uint64_t lk[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) lk[i] = 0ull;
   int c = 0;
   float vmax = -INFINITY;
-#pragma unroll 2
-  for (int j = 0; j < N; ++j) {
+#pragma unroll 4
+  for (int j = q; j < N; j += 4) {
     const float v = s[j];
     c += v > snull;
     vmax = fmaxf(vmax, v);
-    uint64_t key = ((uint64_t)ordered_bits(v) << 32) | (0xffffffffu - (uint32_t)j);
+    insert_key(lk, ((uint64_t)ordered_bits(v) << 32) | (0xffffffffu - (uint32_t)j));
+  }
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const bool gt = key > lk[i];
-      const uint64_t old = lk[i];
-      lk[i] = gt ? key : old;
-      key = gt ? old : key;
-    }
+  for (int o = 1; o <= 2; o <<= 1) {
+    uint64_t other[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) other[i] = shfl_xor_u64(lk[i], o);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) insert_key(lk, other[i]);
+    c += __shfl_xor(c, o, kWave);
+    vmax = fmaxf(vmax, __shfl_xor(vmax, o, kWave));
   }
   const int r = (M == 0) ? K : min(K, max(c, K - M));
   // weights: softmax over the chosen reals in fp64, summed in rank order
@@ -161,78 +184,93 @@ __device__ void select_lanes(const RouteKernelArgs& a, float* sl, int ld, int nt
     tot += e[i];
   }
   if (live) {
-    const int64_t t = t0 + lane;
+    const int64_t t = t0 + tl;
     int32_t* idx_row = a.topk_idx + t * K;
     float* w_row = a.topk_w + t * K;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-      if (i < K) {
+      if (i < K && (i & 3) == q) {
         const int id = i < r ? (int)(0xffffffffu - (uint32_t)lk[i]) : N + (i - r);
         idx_row[i] = id;
         w_row[i] = i < r ? (float)(e[i] / tot) : 0.0f;
         if (FUSED) atomicAdd(&cnt_lds[id], 1);
       }
     }
-    if (a.n_real) a.n_real[t] = r;
+    if (a.n_real && q == 0) a.n_real[t] = r;
   }
   if (FUSED) {
     // pool softmax [reals, null x M]: p_j written over the logits row
     const float mp = M > 0 ? fmaxf(vmax, snull) : vmax;
-    double z = 0.0;
+    double zq = 0.0;
 #pragma unroll 4
-    for (int j = 0; j < N; ++j) z += (double)expf(s[j] - mp);
+    for (int j = q; j < N; j += 4) {
+      const float ej = expf(s[j] - mp);
+      if (live) s[j] = ej;
+      zq += (double)ej;
+    }
+    const double z01 = zq + __shfl_xor(zq, 1, kWave);
+    double z = z01 + __shfl_xor(z01, 2, kWave);
     const float en = M > 0 ? expf(snull - mp) : 0.0f;
     z += (double)M * (double)en;
     const float iz = (float)(1.0 / z);
     if (live) {
 #pragma unroll 4
-      for (int j = 0; j < N; ++j) s[j] = expf(s[j] - mp) * iz;
-      s[N] = en * iz;
+      for (int j = q; j < N; j += 4) s[j] *= iz;
+      if (q == 0) s[N] = en * iz;
+    }
+    if (q == 0) {
       const double lse = (double)mp + log(z);
-      lane_acc[0] = lse * lse;
-      lane_acc[1] = (double)r;
-    } else {
-      lane_acc[0] = lane_acc[1] = 0.0;
+      tok_acc[tl] = live ? lse * lse : 0.0;
+      tok_acc[kRouteBT + tl] = live ? (double)r : 0.0;
     }
   }
 }
 
+// fp64 LDS scratch of the fused epilogue: block sums [N + 3], per-token lse^2 and r
+// [2][64], column quarters [4][N + 1]
+__host__ __device__ constexpr int epi_doubles(int N) { return (N + 3) + 2 * 64 + 4 * (N + 1); }
+
 template <bool FUSED, int KMAX>
 __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
                                int64_t tile, bool copy_logits, int* cnt_lds, double* wacc) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int N = a.N, M = a.M, P = N + M;
   if (copy_logits) {
     const int w = N + 1;
     for (int i = threadIdx.x; i < nt * w; i += blockDim.x)
       a.logits_out[(t0 + i / w) * w + i % w] = sl[(i / w) * ld + i % w];
-    if (FUSED) __syncthreads();  // the fused selection overwrites the rows
+    __syncthreads();  // the fused selection overwrites the rows
   }
-  double lane_acc[2];
-  if (wave == 0) select_lanes<KMAX, FUSED>(a, sl, ld, nt, t0, cnt_lds, lane_acc);
+  double* tok_acc = wacc + N + 3;  // [2][64]
+  select_quads<KMAX, FUSED>(a, sl, ld, nt, t0, cnt_lds, tok_acc);
   if (!FUSED) return;
-  // per-block sums in a fixed order: probability columns over the block's tokens,
-  // and lse^2 / n_real over wavefront 0's lanes
-  const int rd = N + 3;
+  __syncthreads();
+  // per-block sums in a fixed order: lse^2 / n_real over the block's tokens, and
+  // the probability columns in four interleaved quarters added in order
   if (wave == 0) {
-    const double lz = wave_sum_double(lane_acc[0]);
-    const double nr = wave_sum_double(lane_acc[1]);
-    if ((threadIdx.x & (kWave - 1)) == 0) {
+    const double lz = wave_sum_double(tok_acc[lane]);
+    const double nr = wave_sum_double(tok_acc[kRouteBT + lane]);
+    if (lane == 0) {
       wacc[N + 1] = lz;
       wacc[N + 2] = nr;
     }
   }
-  __syncthreads();
-  for (int j = threadIdx.x; j <= N; j += blockDim.x) {
+  double* colq = tok_acc + 2 * kRouteBT;  // [4][N + 1]
+  for (int i = threadIdx.x; i < 4 * (N + 1); i += blockDim.x) {
+    const int j = i % (N + 1), qq = i / (N + 1);
     double sum = 0.0;
-    for (int tl = 0; tl < nt; ++tl) sum += (double)sl[tl * ld + j];
-    wacc[j] = sum;
+    for (int tl = qq; tl < nt; tl += 4) sum += (double)sl[tl * ld + j];
+    colq[qq * (N + 1) + j] = sum;
   }
   __syncthreads();
+  for (int j = threadIdx.x; j <= N; j += blockDim.x)
+    wacc[j] = (colq[j] + colq[(N + 1) + j]) + (colq[2 * (N + 1) + j] + colq[3 * (N + 1) + j]);
+  __syncthreads();
+  const int rd = N + 3;
   for (int i = threadIdx.x; i < rd; i += blockDim.x) {
     const double scale = (i == N + 1) ? kAuxZScale : (i == N + 2 ? 1.0 : kAuxPScale);
-    const uint64_t q = (uint64_t)(wacc[i] * scale + 0.5);
-    if (q) atomicAdd(reinterpret_cast<unsigned long long*>(&a.acc[i]), (unsigned long long)q);
+    const uint64_t qv = (uint64_t)(wacc[i] * scale + 0.5);
+    if (qv) atomicAdd(reinterpret_cast<unsigned long long*>(&a.acc[i]), (unsigned long long)qv);
   }
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
     const int cval = cnt_lds[i];
@@ -334,6 +372,9 @@ route_tile_kernel(RouteKernelArgs a) {
   const bool do_null = eg == 0;
   const int nl_tok = tid >> 2, nl_part = tid & 3;
   double nacc = 0.0;
+  // per-token null bias, loaded before the K loop so its latency is hidden
+  const float nbias_tok =
+      (do_null && a.null_bias_tok && nl_part == 0 && nl_tok < nt) ? a.null_bias_tok[t0 + nl_tok] : 0.0f;
 
   auto compute = [&](auto tail, int st, int kvalid) {
     const bf16_t* xs = stages + st * TL::stage;
@@ -408,7 +449,7 @@ route_tile_kernel(RouteKernelArgs a) {
   stage_barrier();
   float* sl = reinterpret_cast<float*>(smem_raw);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
   double* red = reinterpret_cast<double*>(smem_raw + kRouteRedOff);  // [2][ETW][16][64]
   if (kp == 1) {
 #pragma unroll
@@ -438,7 +479,7 @@ route_tile_kernel(RouteKernelArgs a) {
     const double sum = a01 + __shfl_xor(a01, 2, kWave);
     if (nl_part == 0 && nl_tok < nt) {
       double vv = sum + (double)a.null_bias;
-      if (a.null_bias_tok) vv += (double)a.null_bias_tok[t0 + nl_tok];
+      if (a.null_bias_tok) vv += (double)nbias_tok;
       out[nl_tok * ld + N] = (float)vv;
     }
   }
@@ -489,7 +530,7 @@ route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* 
   const int N = a.N, d = a.d, ld = N + 1;
   float* sl = reinterpret_cast<float*>(smem_raw);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
   if (FUSED)
     for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
@@ -517,7 +558,7 @@ route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   const int N = a.N, ld = N + 1;
   float* sl = reinterpret_cast<float*>(smem_raw);
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? N + 3 : 0));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
   if (FUSED)
     for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
@@ -552,7 +593,7 @@ static int route_etw(int N) { return N <= 32 ? 1 : 2; }
 static size_t route_lds_bytes(const RouteArgs& r, bool mfma) {
   const int ld = r.N + 1;
   size_t b = (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
-  if (r.fused) b += (size_t)(r.N + 3) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
+  if (r.fused) b += (size_t)epi_doubles(r.N) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
   if (mfma) b = std::max(b, route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds);
   return b;
 }
