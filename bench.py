@@ -37,7 +37,13 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the rho sweep and other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run three 256 MiB device copies: the reference that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters (token_choice_routing_amd.traffic)")
     return ap.parse_args()
+
+
+COPY_REF_BYTES = 256 << 20
 
 
 def log(*a):
@@ -313,6 +319,13 @@ def main():
     tok_s = T / ms * 1e3
     fl = layer_flops(cfg, R, T)
     log(f"bench: {ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (wall), R={R}")
+    if args.copy_ref:
+        src = torch.ones((COPY_REF_BYTES,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("bench: per-kernel timing")
     kernels, _ = kernel_table(torch, tcr, layer, args.kernel_iters)
     dom = "gemm_gate_up"

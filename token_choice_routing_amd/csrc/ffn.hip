@@ -387,6 +387,12 @@ constexpr GemmShape shape_of() {
 #ifndef MOE_GEMM_VARIANT
 #define MOE_GEMM_VARIANT 0
 #endif
+#ifndef MOE_GEMM_VARIANT_GU
+#define MOE_GEMM_VARIANT_GU 4
+#endif
+#ifndef MOE_GEMM_VARIANT_DOWN
+#define MOE_GEMM_VARIANT_DOWN 4
+#endif
 
 static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int bm, int oc,
                           int num_cus, int per_cu) {
@@ -441,7 +447,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     const int64_t rows = std::max<int64_t>(any0 ? q0.max_rows / q0.groups : 0,
                                            any1 ? q1.max_rows / q1.groups : 0);
     int variant = MOE_GEMM_VARIANT;
-    if (variant == 0) variant = 4;
+    if (variant == 0) variant = op == 0 ? MOE_GEMM_VARIANT_GU : MOE_GEMM_VARIANT_DOWN;
 #define MOE_GEMM_DISPATCH(M_)                                                  \
   do {                                                                         \
     if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream);      \
