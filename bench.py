@@ -168,11 +168,14 @@ def kernel_table(torch, tcr, layer, iters):
     active = int((off_h[1:] > off_h[:-1]).sum())
     rows = {}
 
-    def add(name, us, nbytes, flops=0.0, launches=1):
+    def add(name, us, nbytes, flops=0.0, launches=1, us_warm=None):
         rows[name] = {"us": round(us, 3), "bytes": int(nbytes), "flops": float(flops),
                       "GB_s": round(nbytes / us / 1e3, 1), "TFLOP_s": round(flops / us / 1e6, 2),
                       "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4), "launches": launches}
+        if us_warm is not None:
+            rows[name]["us_warm"] = round(us_warm, 3)
+            rows[name]["mfma_frac_warm"] = round(flops / us_warm / 1e6 / BF16_PEAK_TFLOPS, 4)
 
     t_route = tm.run(route, iters)
     add("route", t_route, T * d * 2 + 4 * (N + 1) * d + 4 * T * (N + 1) + 8 * T * K + 4 * T,
@@ -181,15 +184,18 @@ def kernel_table(torch, tcr, layer, iters):
     add("permute", t_perm, 4 * T * K + 4 * R + 4 * T * K + 4 * (2 * N + 1), 0, 3)
     t_pg = tm.run(permute_gather, iters)
     add("gather", max(t_pg - t_perm, 1e-3), 2 * R * d * 2 + 4 * R)
+    # GEMMs: "us" after a last-level-cache flush (the roofline figure), "us_warm" back to back
     add("gemm_gate_up", tm.run_cold(gemm1, iters, flush), R * d * 2 + active * 2 * f * d * 2 + R * f * 2,
-        4.0 * R * d * f)
+        4.0 * R * d * f, us_warm=tm.run(gemm1, iters))
     add("gemm_down", tm.run_cold(gemm2, iters, flush), R * f * 2 + active * d * f * 2 + R * d * 4,
-        2.0 * R * d * f)
+        2.0 * R * d * f, us_warm=tm.run(gemm2, iters))
     if fs:
-        add("shared_gate_up", tm.run(sgemm1, iters), T * d * 2 + 2 * fs * d * 2 + T * fs * 2, 4.0 * T * d * fs)
-        add("shared_down", tm.run(sgemm2, iters), T * fs * 2 + d * fs * 2 + T * d * 4, 2.0 * T * d * fs)
+        add("shared_gate_up", tm.run_cold(sgemm1, iters, flush), T * d * 2 + 2 * fs * d * 2 + T * fs * 2,
+            4.0 * T * d * fs, us_warm=tm.run(sgemm1, iters))
+        add("shared_down", tm.run_cold(sgemm2, iters, flush), T * fs * 2 + d * fs * 2 + T * d * 4,
+            2.0 * T * d * fs, us_warm=tm.run(sgemm2, iters))
     add("combine", tm.run(combine, iters), R * d * 4 + (T * d * 4 if fs else 0) + T * d * 2 + 8 * T * K)
-    add("aux_stats", tm.run(aux, iters), 4 * T * (N + 1) + 4 * T * K, 0, 2)
+    add("aux_stats", tm.run(aux, iters), 4 * T * (N + 1) + 4 * T * K, 0, 3)
     return rows, R
 
 
@@ -282,6 +288,56 @@ def sweep(torch, tcr, steps, warmup):
     return out
 
 
+def measured_peaks(torch):
+    """This GPU's attainable rates: a 1 GiB device copy (bytes read + written) and a
+    large bf16 GEMM through torch (hipBLASLt)."""
+    tm = Timer(torch)
+    n = 1 << 30
+    a = torch.ones((n,), dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    us_c = tm.run(lambda: b.copy_(a), 10)
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), device="cuda").to(torch.bfloat16).contiguous()
+    y = torch.randn((m, m), device="cuda").to(torch.bfloat16).contiguous()
+    us_g = tm.run(lambda: torch.matmul(x, y), 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_GB_s": round(2 * n / us_c / 1e3, 1), "copy": "1 GiB device-to-device copy, read + write",
+            "bf16_gemm_TFLOP_s": round(2.0 * m ** 3 / us_g / 1e6, 1),
+            "gemm": "8192 x 8192 x 8192 bf16 torch.matmul (hipBLASLt)",
+            "datasheet": {"hbm_GB_s": HBM_PEAK_GBS, "bf16_TFLOP_s": BF16_PEAK_TFLOPS}}
+
+
+def decode_sweep(torch, base, main_layer, steps):
+    """Small token counts at the headline shape (the decode regime): few rows per
+    expert, so the layer reads the weights of the experts it touches. Reported as
+    the rate on those weight bytes, with the last-level cache flushed before every
+    call (weights come from HBM, as when the other layers of a model ran in between)
+    and back to back."""
+    from token_choice_routing_amd.layer import MoeLayer
+    out = []
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    tm = Timer(torch)
+    cfg = base.cfg
+    for Ts in (1, 16, 64, 256):
+        layer = MoeLayer(base, T=Ts, weights_from=main_layer)
+        layer.forward()
+        torch.cuda.synchronize()
+        off = layer.offsets.cpu().numpy()
+        active = int((off[1:] > off[:-1]).sum())
+        wbytes = (active * 3 * cfg.d_model * cfg.d_ff + 3 * cfg.d_model * cfg.d_ff_shared) * 2 \
+            + 4 * (cfg.n_experts + 1) * cfg.d_model
+        cold = tm.run_cold(layer.forward, steps, flush)
+        warm = tm.run(layer.forward, steps)
+        out.append({"workload": f"decode_T{Ts}", "T": Ts, "active_experts": active,
+                    "weight_bytes": wbytes, "us_cold": round(cold, 2), "us_warm": round(warm, 2),
+                    "weight_GB_s_cold": round(wbytes / cold / 1e3, 1),
+                    "hbm_frac_cold": round(wbytes / cold / 1e3 / HBM_PEAK_GBS, 4)})
+        log(f"  decode T={Ts}: {out[-1]}")
+    return out
+
+
 def measure(torch, layer, steps, warmup):
     ms, _ = time_layer(torch, layer, steps, warmup)
     cfg = layer.cfg
@@ -361,6 +417,10 @@ def main():
     if not args.no_sweep:
         log("bench: rho sweep and other workloads")
         line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
+        log("bench: decode regime")
+        line["decode"] = decode_sweep(torch, wl, layer, max(5, args.steps // 2))
+        log("bench: measured peaks")
+        line["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline()

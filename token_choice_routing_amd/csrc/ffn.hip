@@ -38,14 +38,18 @@
 
 namespace moe {
 
-constexpr int kBK = 64;
 constexpr int kMaxGroups = 320;   // routed groups (<= 256) + the dense shared-expert problem
 
 enum { kSwiGLU = 0, kPlain = 1 };
 
-// element offset of (row, 16-byte chunk) in a [rows][kBK] bf16 LDS tile
+// Element offset of (row, 16-byte chunk) in a [rows][BK] bf16 LDS tile. 128-byte
+// rows (BK = 64) XOR the chunk with row % 8; 64-byte rows (BK = 32) with
+// (row / 4) % 4. Either way the 16-byte reads of 16 consecutive rows at one
+// logical chunk land on 16 distinct bank quads.
+template <int BK>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
+  if constexpr (BK == 64) return row * 64 + ((chunk ^ (row & 7)) << 3);
+  else return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
 struct TileTable {
@@ -117,29 +121,32 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 // ROLE only names the launch in profiles (the code is identical): 0 standalone
 // grouped, 1 standalone single segment, 2 the layer's routed + shared launch.
 //
-// Tile BM rows x BN weight rows x 64 K on WM x WN wavefronts; each wavefront owns
+// Tile BM rows x BN weight rows x BK K on WM x WN wavefronts; each wavefront owns
 // (BM/WM) x (BN/WN) outputs as 32x32 MFMA blocks. K tiles stream through S LDS
 // stages filled by global->LDS loads (global_load_lds_dwordx4): no staging
 // registers, S-1 stages in flight while one is multiplied. One wavefront load
-// instruction fills 8 consecutive tile rows (64 lanes x 16 bytes = 1 KB of LDS);
-// lane l writes physical chunk l%8 of row l/8, so it fetches the logical chunk
-// (l%8) ^ (row%8) from global memory, which realises the XOR swizzle that keeps
-// the MFMA fragment reads free of bank conflicts.
-template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S>
+// instruction fills 1 KB of LDS: 8 rows of 128 bytes (BK = 64) or 16 rows of 64
+// bytes (BK = 32), lane l writing physical chunk l % CPR of row l / CPR; it
+// fetches the logical chunk that lds_off() places there, which realises the XOR
+// swizzle that keeps the MFMA fragment reads free of bank conflicts.
+template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S, int BK>
 __global__ void __launch_bounds__(64 * WM * WN)
 grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
+  static_assert(BK == 32 || BK == 64, "K tile of 64- or 128-byte rows");
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
-  constexpr int J = (BM + BN) / (8 * NW);            // load instructions per stage per wavefront
-  constexpr int JA = BM / (8 * NW);                  // of which fill A rows
-  constexpr int STAGE = (BM + BN) * kBK;             // elements per stage
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must split over the wavefronts");
+  constexpr int CPR = BK / 8;                        // 16-byte chunks per tile row
+  constexpr int RPI = kWave / CPR;                   // tile rows filled by one load instruction
+  constexpr int J = (BM + BN) / (RPI * NW);          // load instructions per stage per wavefront
+  constexpr int JA = BM / (RPI * NW);                // of which fill A rows
+  constexpr int STAGE = (BM + BN) * BK;              // elements per stage
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows must split over the wavefronts");
   static_assert(MODE != kSwiGLU || FN % 2 == 0, "gate/up tiles come in pairs");
   static_assert(S >= 2 && S <= 5 && J * (S - 2) < 64, "stages in flight must fit the vmcnt counter");
   __shared__ TileTable tt;
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // [S][BM + BN][kBK]
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // [S][BM + BN][BK]
   build_tile_table(tt, p0, p1, OC, BM);
   const int G0 = p0.groups, G = p0.groups + p1.groups;
   const int total = tt.prefix[kMaxGroups];
@@ -147,9 +154,11 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave % WM, wn = wave / WM;
   const int half = lane >> 5, l32 = lane & 31;
-  // this lane's load: row 8 * (wave + NW * j) + lane / 8 of the stage, logical chunk lc
-  const int lrow = lane >> 3;
-  const int lc = (lane & 7) ^ lrow;
+  // this lane's load: row RPI (wave + NW j) + lane / CPR of the stage, physical chunk
+  // lane % CPR, so logical chunk lc (the swizzle of lds_off, which depends only on
+  // the row's offset within the instruction's RPI rows)
+  const int lrow = lane / CPR;
+  const int lc = (lane % CPR) ^ (BK == 64 ? lrow : (lrow >> 2) & 3);
 
   // XCD-contiguous tile ranges
   const int P = gridDim.x;
@@ -170,7 +179,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     const GemmProblem& pr = second ? p1 : p0;
     const int ge = second ? e - G0 : e;
     const int Nout = pr.n_out, Kdim = pr.k_dim;
-    const int nk = (Kdim + kBK - 1) / kBK;
+    const int nk = (Kdim + BK - 1) / BK;
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
     const int ntile = local / mt, mtile = local - ntile * mt;
@@ -184,7 +193,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       int64_t arow[JA > 0 ? JA : 1];
 #pragma unroll
       for (int j = 0; j < JA; ++j) {
-        const int r = 8 * (wave + NW * j) + lrow;
+        const int r = RPI * (wave + NW * j) + lrow;
         arow[j] = m0 + (r < rows_valid ? r : 0);
       }
       if (pr.a_rows) {
@@ -198,7 +207,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       for (int j = 0; j < JA; ++j) src[j] = pr.a + arow[j] * Kdim;
 #pragma unroll
       for (int j = JA; j < J; ++j) {
-        const int r = 8 * (wave + NW * j) + lrow - BM;
+        const int r = RPI * (wave + NW * j) + lrow - BM;
         int n;
         const bf16_t* base;
         if (MODE == kSwiGLU) {
@@ -214,11 +223,11 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     // K tile kt into stage st. Chunks past k_dim (last tile only) read column 0;
     // their fragments are zeroed before the MFMAs.
     auto issue = [&](int kt, int st) {
-      const int k = kt * kBK + lc * 8;
+      const int k = kt * BK + lc * 8;
       const int kc = k < Kdim ? k : 0;
       bf16_t* stage = smem + st * STAGE;
 #pragma unroll
-      for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + 8 * (wave + NW * j) * kBK);
+      for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + RPI * (wave + NW * j) * BK);
     };
 
     f32x16_t acc[FN][FM];
@@ -231,7 +240,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     // are read while step ks multiplies.
     auto compute = [&](auto tail, int st, int kvalid) {
       const bf16_t* As = smem + st * STAGE;
-      const bf16_t* Bs = As + BM * kBK;
+      const bf16_t* Bs = As + BM * BK;
       bf16x8_t wf[2][FN], af[2][FM];
       auto frags = [&](int ks, bf16x8_t* w, bf16x8_t* a) {
         const int ch = ks * 2 + half;
@@ -242,11 +251,11 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
             brow = (f < FN / 2 ? 0 : BN / 2) + wn * (TN / 2) + (f % (FN / 2)) * 32 + l32;
           else
             brow = wn * TN + f * 32 + l32;
-          w[f] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off(brow, ch)]);
+          w[f] = *reinterpret_cast<const bf16x8_t*>(&Bs[lds_off<BK>(brow, ch)]);
         }
 #pragma unroll
         for (int g = 0; g < FM; ++g)
-          a[g] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off(wm * TM + g * 32 + l32, ch)]);
+          a[g] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off<BK>(wm * TM + g * 32 + l32, ch)]);
         if constexpr (decltype(tail)::value) {  // last K tile: zero the chunks past k_dim
           const bool z = ch * 8 >= kvalid;
 #pragma unroll
@@ -255,11 +264,14 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
           for (int g = 0; g < FM; ++g) a[g] = z ? bf16x8_t{} : a[g];
         }
       };
+      // double-buffered fragments only while they are few (register pressure)
+      constexpr bool kDouble = FN + FM <= 6;
       frags(0, wf[0], af[0]);
 #pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < kBK / 16) frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int cur = kDouble ? (ks & 1) : 0;
+        if (kDouble && ks + 1 < BK / 16) frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+        if (!kDouble && ks > 0) frags(ks, wf[0], af[0]);
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -285,8 +297,8 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       else wait_vmcnt<J>();
       stage_barrier();
       if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-      const int kvalid = Kdim - kt * kBK;
-      if (kvalid < kBK)
+      const int kvalid = Kdim - kt * BK;
+      if (kvalid < BK)
         compute(std::true_type{}, kt % S, kvalid);
       else
         compute(std::false_type{}, kt % S, kvalid);
@@ -371,27 +383,22 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
   }
 }
 
-// Tile shapes (BM x BN, wavefronts, stages). The default, 128 x 256 on eight
-// wavefronts with three stages, measured fastest on both short (~64-row, weight
-// streaming) and long (~512-row) segments; the others remain selectable at build
-// time with MOE_GEMM_VARIANT for tuning.
+// Tile shape (BM x BN, wavefronts, stages, K tile): 128 x 256 on eight wavefronts,
+// three stages of 64-wide K tiles. It measured fastest at both ends of the
+// rows-per-expert range (64 and 512) among 128 x 128, 64 x 256, 128 x 384 (two
+// stages, or four of 32-wide K tiles) and 128 x 256 with five 32-wide stages;
+// those are compiled only for tuning builds (-DMOE_GEMM_VARIANT=k).
 struct GemmShape {
   int bm, bn, threads;
   size_t lds;
 };
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int BK>
 constexpr GemmShape shape_of() {
-  return GemmShape{BM, BN, 64 * WM * WN, (size_t)S * (BM + BN) * kBK * sizeof(bf16_t)};
+  return GemmShape{BM, BN, 64 * WM * WN, (size_t)S * (BM + BN) * BK * sizeof(bf16_t)};
 }
 
 #ifndef MOE_GEMM_VARIANT
 #define MOE_GEMM_VARIANT 0
-#endif
-#ifndef MOE_GEMM_VARIANT_GU
-#define MOE_GEMM_VARIANT_GU 4
-#endif
-#ifndef MOE_GEMM_VARIANT_DOWN
-#define MOE_GEMM_VARIANT_DOWN 4
 #endif
 
 static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int bm, int oc,
@@ -406,13 +413,13 @@ static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int bm, 
   return (unsigned)std::max<int64_t>(8, std::min<int64_t>(cap, (tiles + 7) / 8 * 8));
 }
 
-template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S, int BK>
 static void launch_variant(const GemmProblem& q0, const GemmProblem& q1, int num_cus,
                            hipStream_t stream) {
-  constexpr GemmShape sh = shape_of<BM, BN, WM, WN, S>();
+  constexpr GemmShape sh = shape_of<BM, BN, WM, WN, S, BK>();
   static_assert(sh.lds + sizeof(TileTable) <= 160 * 1024, "LDS budget of one CU");
   constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;
-  auto kern = grouped_gemm_bf16_kernel<MODE, ROLE, BM, BN, WM, WN, S>;
+  auto kern = grouped_gemm_bf16_kernel<MODE, ROLE, BM, BN, WM, WN, S, BK>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
   // resident workgroups per CU (registers and LDS), queried once per instantiation
@@ -430,10 +437,15 @@ template <int MODE, int ROLE>
 static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& q1, int num_cus,
                          hipStream_t stream) {
   switch (variant) {
-    case 1: launch_variant<MODE, ROLE, 128, 128, 2, 2, 4>(q0, q1, num_cus, stream); break;
-    case 2: launch_variant<MODE, ROLE, 128, 256, 2, 2, 3>(q0, q1, num_cus, stream); break;
-    case 4: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3>(q0, q1, num_cus, stream); break;
-    default: launch_variant<MODE, ROLE, 64, 256, 1, 4, 3>(q0, q1, num_cus, stream); break;
+#if MOE_GEMM_VARIANT
+    case 1: launch_variant<MODE, ROLE, 128, 128, 2, 2, 4, 64>(q0, q1, num_cus, stream); break;
+    case 2: launch_variant<MODE, ROLE, 128, 256, 2, 2, 3, 64>(q0, q1, num_cus, stream); break;
+    case 3: launch_variant<MODE, ROLE, 64, 256, 1, 4, 3, 64>(q0, q1, num_cus, stream); break;
+    case 5: launch_variant<MODE, ROLE, 128, 384, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
+    case 6: launch_variant<MODE, ROLE, 128, 384, 2, 2, 4, 32>(q0, q1, num_cus, stream); break;
+    case 7: launch_variant<MODE, ROLE, 128, 256, 2, 4, 5, 32>(q0, q1, num_cus, stream); break;
+#endif
+    default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
   }
 }
 
@@ -443,11 +455,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   if (!any0 && !any1) return hipSuccess;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
-    // worst-case rows per group decides the tile shape
-    const int64_t rows = std::max<int64_t>(any0 ? q0.max_rows / q0.groups : 0,
-                                           any1 ? q1.max_rows / q1.groups : 0);
-    int variant = MOE_GEMM_VARIANT;
-    if (variant == 0) variant = op == 0 ? MOE_GEMM_VARIANT_GU : MOE_GEMM_VARIANT_DOWN;
+    const int variant = MOE_GEMM_VARIANT;
 #define MOE_GEMM_DISPATCH(M_)                                                  \
   do {                                                                         \
     if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream);      \
