@@ -67,7 +67,7 @@ int cu_count() {
 // Layer workspace layout (byte offsets, 256-byte aligned pieces).
 struct LayerWs {
   size_t logits, topk_idx, topk_w, n_real, counts, offsets, perm_token, slot_pos, route, permute,
-      h, hs, yp, ys, acc, pool_counts, total;
+      h, hs, yp, ys, tstats, rhist, total;
 };
 
 LayerWs layer_ws(const moe_dims* d) {
@@ -95,8 +95,9 @@ LayerWs layer_ws(const moe_dims* d) {
   w.hs = take((size_t)T * d->d_ff_shared * e);
   w.yp = take((size_t)R * d->d_model * 4);
   w.ys = take(d->d_ff_shared ? (size_t)T * d->d_model * 4 : 0);
-  w.acc = take((size_t)(N + 3) * 8);
-  w.pool_counts = take((size_t)(N + M) * 4);
+  const int64_t tiles = permute_nchunks(T);  // 64-token tiles of the router and the sort
+  w.tstats = take((size_t)tiles * (N + 3) * 8);
+  w.rhist = take((size_t)tiles * (d->top_k + 1) * 4);
   w.total = o;
   return w;
 }
@@ -316,8 +317,8 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   float* topk_w = ao.topk_w ? ao.topk_w : static_cast<float*>(at(L.topk_w));
   int32_t* n_real = ao.n_real ? ao.n_real : static_cast<int32_t*>(at(L.n_real));
   int32_t* offsets = ao.offsets ? ao.offsets : static_cast<int32_t*>(at(L.offsets));
-  int32_t* pool_counts = ao.counts ? ao.counts : static_cast<int32_t*>(at(L.pool_counts));
-  uint64_t* acc = static_cast<uint64_t*>(at(L.acc));
+  double* tstats = static_cast<double*>(at(L.tstats));
+  int32_t* rhist = static_cast<int32_t*>(at(L.rhist));
   int32_t* perm_token = static_cast<int32_t*>(at(L.perm_token));
   int32_t* slot_pos = static_cast<int32_t*>(at(L.slot_pos));
   int32_t* permute_ws = static_cast<int32_t*>(at(L.permute));
@@ -331,11 +332,11 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   // 1. scores, selection, weights; per-chunk expert histogram; statistics sums
   RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
                p->null_bias, p->null_bias_tok, nullptr, logits, topk_idx, topk_w, n_real,
-               at(L.route), permute_ws, acc, pool_counts};
+               at(L.route), permute_ws, rhist, tstats};
   HIP_TRY(launch_route(ra, s));
 
   // 2. counting sort (histograms already written) + statistics finalisation
-  AuxFinal af{acc, pool_counts, ao.f, ao.P, ao.counts, ao.scalars};
+  AuxTiles af{tstats, rhist, ao.f, ao.P, ao.counts, ao.scalars};
   PermuteArgs pa{d->T, d->top_k, N, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx, nullptr,
                  static_cast<int32_t*>(at(L.counts)), offsets, perm_token, slot_pos, nullptr,
                  permute_ws, true, want_stats ? &af : nullptr};

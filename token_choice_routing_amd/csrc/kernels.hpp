@@ -15,7 +15,7 @@ struct RouteArgs {
   int64_t T;
   int d, N, M, K;
   bool bf16;
-  bool fused;         // also emit per-block expert histogram + statistics accumulators
+  bool fused;         // also emit per-tile histograms and statistic sums
   const void* x;
   const float* w_router;
   float null_bias;
@@ -25,19 +25,31 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   int32_t* n_real;
-  void* ws;           // bf16 scoring scratch of route_ws_bytes(T, N, d) bytes
-  int32_t* chunk_hist; // fused: [blocks][N]
-  uint64_t* acc;       // fused: [N + 3] accumulators (cleared by the launch)
-  int32_t* counts;     // fused: [N + M] pool slot counts (cleared by the launch)
+  void* ws;            // bf16 scoring scratch of route_ws_bytes(T, N, d) bytes
+  int32_t* chunk_hist; // fused: [tiles][N] real slots per expert and 64-token tile
+  int32_t* rhist;      // fused: [tiles][K + 1] tokens per number of chosen reals r
+  double* tstats;      // fused: [tiles][N + 3] sums of p_t,j (j <= N), lse_t^2 and r_t
 };
 int route_tokens_per_block();
 size_t route_ws_bytes(int64_t T, int N, int d);
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
-// Statistics finalisation done by the permutation's scan kernel in the fused layer path.
+// Statistics accumulated in fixed point by the standalone statistics kernels.
 struct AuxFinal {
   const uint64_t* acc;   // [N + 3]
   const int32_t* cnt;    // [N + M]
+  float* f;
+  float* P;
+  int32_t* counts;
+  float* scalars;
+};
+
+// Statistics finalised by the permutation's scan kernel in the fused layer path,
+// from the router's per-tile sums (added in tile order, so the result does not
+// depend on scheduling).
+struct AuxTiles {
+  const double* tstats;  // [tiles][N + 3]
+  const int32_t* rhist;  // [tiles][K + 1]
   float* f;
   float* P;
   int32_t* counts;
@@ -56,7 +68,7 @@ struct PermuteArgs {
   void* x_perm;
   int32_t* ws;                    // chunk_hist [nchunks][N] then chunk_base [nchunks][N]
   bool hist_ready;                // chunk_hist already written (by the fused router)
-  const AuxFinal* aux;            // optional statistics finalisation (fused path)
+  const AuxTiles* aux;            // optional statistics finalisation (fused path)
 };
 int permute_nchunks(int64_t T);
 size_t permute_ws_bytes(int64_t T, int N);

@@ -20,7 +20,6 @@
 // deterministic. A fourth kernel gathers x_perm[p] = x[perm_token[p]].
 #include <algorithm>
 
-#include "aux_final.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,27 +47,125 @@ permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int
   for (int e = threadIdx.x; e < N; e += blockDim.x) chunk_hist[(int64_t)blockIdx.x * N + e] = hist[e];
 }
 
+// Statistics of the fused layer path from the router's per-tile sums, added in
+// tile order (fixed, so the result does not depend on scheduling). Paper review
+// "Improving MoE Compute Efficiency by Composing Weight and Data Sparsity",
+// section 3, "load-balance loss" and "Z-loss": P_i = mean_t p_t,i (the M null
+// copies share P_null), f_i = counts_i / T, L_bal = N sum_{i < N+M} f_i P_i,
+// L_z = mean_t lse_t^2, plus mean r. A token with r chosen reals fills null copies
+// N .. N + K - r - 1, so copy N + j is used by the tokens with r < K - j.
+// Called by every thread of one workgroup; off[0..N] holds the expert offsets.
+__device__ void finalize_tiles(const AuxTiles& a, int tiles, int64_t T, int N, int M, int K,
+                               const int* off, double* part, double* tot, int* rsum,
+                               double* terms) {
+  const int C = N + 3;
+  const int G = max(1, (int)blockDim.x / C);
+  const int per = (tiles + G - 1) / G;
+  for (int r = threadIdx.x; r <= K; r += blockDim.x) rsum[r] = 0;
+  __syncthreads();
+  {
+    // thread (c, g) adds tiles [g per, (g + 1) per) of column c, eight loads at a time
+    const int c = threadIdx.x % C, g = threadIdx.x / C;
+    if (g < G) {
+      double s = 0.0;
+      const int t1 = min(tiles, (g + 1) * per);
+      for (int tb = g * per; tb < t1; tb += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = tb + u < t1 ? a.tstats[(int64_t)(tb + u) * C + c] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      part[g * C + c] = s;
+    }
+  }
+  {
+    // r histogram: integer sums, any order
+    const int R = K + 1, GR = max(1, (int)blockDim.x / R), pr = (tiles + GR - 1) / GR;
+    const int r = threadIdx.x % R, g = threadIdx.x / R;
+    if (g < GR) {
+      int s = 0;
+      const int t1 = min(tiles, (g + 1) * pr);
+      for (int tb = g * pr; tb < t1; tb += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = tb + u < t1 ? a.rhist[(int64_t)(tb + u) * R + r] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      if (s) atomicAdd(&rsum[r], s);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    double s = 0.0;
+    for (int g = 0; g < G; ++g) s += part[g * C + c];
+    tot[c] = s;
+  }
+  __syncthreads();
+  const int P = N + M;
+  const double invT = 1.0 / (double)T;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    int cnt = 0;
+    if (i < N) {
+      cnt = off[i + 1] - off[i];
+    } else {
+      const int j = i - N;
+      for (int r = 0; r < K - j; ++r) cnt += rsum[r];
+    }
+    const double Pi = tot[i < N ? i : N] * invT;
+    const double fi = (double)cnt * invT;
+    terms[i] = fi * Pi;
+    if (a.f) a.f[i] = (float)fi;
+    if (a.P) a.P[i] = (float)Pi;
+    if (a.counts) a.counts[i] = cnt;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < P; i += kWave) s += terms[i];
+    s = wave_sum_double(s);
+    if (threadIdx.x == 0 && a.scalars) {
+      a.scalars[0] = (float)((double)N * s);
+      a.scalars[1] = (float)(tot[N + 1] * invT);
+      a.scalars[2] = (float)(tot[N + 2] * invT);
+    }
+  }
+}
+
 // One workgroup of 1024 threads: counts[e] = sum over chunks, offsets = exclusive
 // scan over e, chunk_base[c][e] = offsets[e] + sum_{c' < c} hist[c'][e].
 // Thread (e, g) owns expert e for the g-th contiguous group of chunks (N <= 255,
 // so there are at least 4 groups). In the fused path it also finalises the
-// statistics accumulated by the router.
+// statistics from the router's per-tile sums.
 __global__ void __launch_bounds__(1024)
 permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                    int32_t* __restrict__ chunk_base, AuxFinal aux, int64_t T, int M) {
+                    int32_t* __restrict__ chunk_base, AuxTiles aux, int64_t T, int M, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int groups = blockDim.x / N;
-  double* terms = reinterpret_cast<double*>(smem_raw);               // [N + M] (fused)
-  int* part = reinterpret_cast<int*>(terms + (aux.acc ? N + M : 0));  // [groups][N]
+  const bool stats = aux.tstats != nullptr;
+  // fused: terms [N + M], tile-group partials [G][N + 3], totals [N + 3] (doubles)
+  const int C = N + 3, G = max(1, (int)blockDim.x / C);
+  double* terms = reinterpret_cast<double*>(smem_raw);
+  double* spart = terms + (stats ? N + M : 0);
+  double* stot = spart + (stats ? G * C : 0);
+  int* part = reinterpret_cast<int*>(stot + (stats ? C : 0));        // [groups][N]
   int* off = part + groups * N;                                      // [N + 1]
+  int* rsum = off + N + 1;                                           // [K + 1]
   const int per = (nchunks + groups - 1) / groups;
   const int e = threadIdx.x % N, g = threadIdx.x / N;
   const bool active = g < groups;
   const int c0 = g * per, c1 = min(nchunks, c0 + per);
   if (active) {
     int s = 0;
-    for (int c = c0; c < c1; ++c) s += chunk_hist[(int64_t)c * N + e];
+    for (int cb = c0; cb < c1; cb += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cb + u < c1 ? chunk_hist[(int64_t)(cb + u) * N + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
     part[g * N + e] = s;
   }
   __syncthreads();
@@ -116,7 +213,7 @@ permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
       base += chunk_hist[(int64_t)c * N + e];
     }
   }
-  if (aux.acc) aux_finalize(aux, T, N, M, terms);
+  if (stats) finalize_tiles(aux, nchunks, T, N, M, K, off, spart, stot, rsum, terms);
 }
 
 // One workgroup per chunk of 64 tokens: 64*K slots in K groups of 64; each
@@ -234,13 +331,15 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   if (!a.hist_ready)
     permute_hist_kernel<<<nchunks, kPermThreads, a.N * sizeof(int), stream>>>(a.topk_idx, TK, a.K,
                                                                              a.N, chunk_hist);
-  AuxFinal af{};
-  if (a.aux) af = *a.aux;
+  AuxTiles at{};
+  if (a.aux) at = *a.aux;
   const int groups = 1024 / a.N;
-  const size_t scan_lds = (af.acc ? (size_t)(a.N + a.M) * sizeof(double) : 0) +
-                          ((size_t)groups * a.N + a.N + 1) * sizeof(int);
+  const int C = a.N + 3, G = std::max(1, 1024 / C);
+  const size_t scan_lds =
+      (at.tstats ? ((size_t)(a.N + a.M) + (size_t)G * C + C) * sizeof(double) : 0) +
+      ((size_t)groups * a.N + a.N + 1 + a.K + 1) * sizeof(int);
   permute_scan_kernel<<<1, 1024, scan_lds, stream>>>(chunk_hist, nchunks, a.N, a.counts, a.offsets,
-                                                     chunk_base, af, a.T, a.M);
+                                                     chunk_base, at, a.T, a.M, a.K);
   const size_t sc_lds = ((size_t)(kPermThreads / kWave) * (a.N + 1) +
                          (size_t)(kPermThreads / kWave) * a.N) * sizeof(int);
   const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);

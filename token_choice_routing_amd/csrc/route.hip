@@ -25,22 +25,22 @@
 //    1e-5 near-tie margin of routing parity). The null row is an fp64 dot
 //    product on the vector ALUs.
 //  * A workgroup scores 64 tokens against one or two 32-expert tiles (all of
-//    them when N <= 64). K tiles of x, of the three weight planes and of the null
-//    row stream through 4-6 swizzled LDS stages filled by global->LDS loads, so
-//    several tiles are in flight while one feeds the MFMAs. When N > 64 the
-//    expert tiles of a token tile are spread over several workgroups and the last
-//    one to finish runs the selection.
-//  * Epilogue: one lane per token. Each lane walks its token's logits row in
-//    LDS once and keeps the best K reals in registers with a branch-free
-//    insertion network over 64-bit keys (order-preserving bits of the logit,
-//    then the complemented expert index, so ties go to the lower index). This
-//    costs a few instructions per (token, expert) instead of wavefront-wide
-//    reductions per token.
-//  * Fused layer mode additionally writes the per-workgroup expert histogram
-//    (the first pass of the permutation's counting sort) and accumulates the
-//    load-balance / z-loss sums of its 64 tokens into fixed-point integer
-//    accumulators; integer addition is associative, so the totals do not
-//    depend on the order in which workgroups finish.
+//    them when N <= 64). K tiles of x, of the float32 weight rows and of the
+//    null row stream through 5-7 swizzled LDS stages filled by global->LDS loads,
+//    so several tiles are in flight while one feeds the MFMAs; the weight is
+//    split into its three bf16 parts in registers. When N > 64 the expert tiles
+//    of a token tile are spread over several workgroups and the last one to
+//    finish runs the selection.
+//  * Epilogue: four lanes per token. Each lane walks a quarter of its token's
+//    logits row in LDS and keeps the best K reals in registers with a
+//    branch-free insertion network over 64-bit keys (order-preserving bits of
+//    the logit, then the complemented expert index, so ties go to the lower
+//    index); two shuffle rounds merge the four lists.
+//  * Fused layer mode additionally writes, per 64-token tile, the real slots
+//    per expert (the first pass of the permutation's counting sort), the
+//    histogram of r and the load-balance / z-loss sums; the permutation's scan
+//    adds them over tiles in tile order, so the totals do not depend on the
+//    order in which workgroups finish and no accumulator needs clearing.
 #include <algorithm>
 
 #include "common.hpp"
@@ -53,31 +53,6 @@ constexpr int kRouteThreads = 256;
 
 int route_tokens_per_block() { return kRouteBT; }
 
-// Prep: split W into bf16 (hi, mid, lo) planes [3][Np][d] (rows >= N zero), clear
-// the fused-statistics accumulators and the token-tile counters.
-__global__ void route_prep_kernel(const float* __restrict__ w, bf16_t* __restrict__ w3, int N,
-                                  int Np, int d, uint64_t* __restrict__ acc, int nacc,
-                                  int32_t* __restrict__ cnt, int ncnt, uint32_t* __restrict__ tiles,
-                                  int64_t ntiles) {
-  const int64_t total = w3 ? (int64_t)Np * d : 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  for (int64_t i = i0; i < total; i += stride) {
-    const int row = (int)(i / d);
-    const float v = row < N ? w[i] : 0.0f;
-    const bf16_t hi = f32_to_bf16(v);
-    const float r1 = v - bf16_to_f32(hi);
-    const bf16_t mid = f32_to_bf16(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
-    w3[i] = hi;
-    w3[total + i] = mid;
-    w3[2 * total + i] = f32_to_bf16(r2);
-  }
-  for (int64_t i = i0; i < nacc; i += stride) acc[i] = 0;
-  for (int64_t i = i0; i < ncnt; i += stride) cnt[i] = 0;
-  for (int64_t i = i0; i < ntiles; i += stride) tiles[i] = 0;
-}
-
 // total order of float32 values as unsigned keys (-0.0 and +0.0 equal)
 __device__ __forceinline__ uint32_t ordered_bits(float v) {
   const uint32_t u = __float_as_uint(v + 0.0f);
@@ -87,34 +62,24 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 struct RouteKernelArgs {
   const bf16_t* x;
-  const bf16_t* w3;
+  const float* w;          // [N + 1][d] float32, row N = null
   const float* w_null;
   float null_bias;
   const float* null_bias_tok;
   int64_t T;
-  int d, N, Np, M, K, ks;  // ks: unused (1)
+  int d, N, Np, M, K;
   float* logits_out;
   int32_t* topk_idx;
   float* topk_w;
   int32_t* n_real;
-  int32_t* chunk_hist;     // fused: [blocks][N]
-  uint64_t* acc;           // fused: [N + 3] fixed-point sums
-  int32_t* counts;         // fused: [N + M] pool slot counts
-  float* lbuf;             // bf16 scoring: [T][N + 1] logits of the expert-tile workgroups
-  uint32_t* tile_cnt;      // bf16 scoring: [token tiles] finished expert tiles (kept at 0)
+  int32_t* chunk_hist;     // fused: [tiles][N]
+  int32_t* rhist;          // fused: [tiles][K + 1]
+  double* tstats;          // fused: [tiles][N + 3]
+  int KS;                  // bf16 scoring: K splits (partials path)
+  int partials;            // bf16 scoring: 1 = write partial logits for route_select_kernel
+  double* lpart;           // bf16 scoring, partials path: [KS][T][N + 1] fp64 partial logits
 };
 
 // Selection for the (up to 64) tokens of one workgroup: four consecutive lanes
@@ -193,10 +158,11 @@ __device__ void select_quads(const RouteKernelArgs& a, float* sl, int ld, int nt
         const int id = i < r ? (int)(0xffffffffu - (uint32_t)lk[i]) : N + (i - r);
         idx_row[i] = id;
         w_row[i] = i < r ? (float)(e[i] / tot) : 0.0f;
-        if (FUSED) atomicAdd(&cnt_lds[id], 1);
+        if (FUSED && i < r) atomicAdd(&cnt_lds[id], 1);
       }
     }
     if (a.n_real && q == 0) a.n_real[t] = r;
+    if (FUSED && q == 0) atomicAdd(&cnt_lds[N + r], 1);
   }
   if (FUSED) {
     // pool softmax [reals, null x M]: p_j written over the logits row
@@ -234,7 +200,7 @@ template <bool FUSED, int KMAX>
 __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
                                int64_t tile, bool copy_logits, int* cnt_lds, double* wacc) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int N = a.N, M = a.M, P = N + M;
+  const int N = a.N;
   if (copy_logits) {
     const int w = N + 1;
     for (int i = threadIdx.x; i < nt * w; i += blockDim.x)
@@ -266,63 +232,71 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
   for (int j = threadIdx.x; j <= N; j += blockDim.x)
     wacc[j] = (colq[j] + colq[(N + 1) + j]) + (colq[2 * (N + 1) + j] + colq[3 * (N + 1) + j]);
   __syncthreads();
-  const int rd = N + 3;
-  for (int i = threadIdx.x; i < rd; i += blockDim.x) {
-    const double scale = (i == N + 1) ? kAuxZScale : (i == N + 2 ? 1.0 : kAuxPScale);
-    const uint64_t qv = (uint64_t)(wacc[i] * scale + 0.5);
-    if (qv) atomicAdd(reinterpret_cast<unsigned long long*>(&a.acc[i]), (unsigned long long)qv);
-  }
-  for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    const int cval = cnt_lds[i];
-    if (i < N) a.chunk_hist[tile * N + i] = cval;
-    if (cval) atomicAdd(&a.counts[i], cval);
-  }
+  // this tile's sums, real-slot histogram and r histogram; the permutation's scan
+  // adds them over tiles in order
+  double* ts = a.tstats + tile * (N + 3);
+  for (int i = threadIdx.x; i < N + 3; i += blockDim.x) ts[i] = wacc[i];
+  for (int i = threadIdx.x; i < N; i += blockDim.x) a.chunk_hist[tile * N + i] = cnt_lds[i];
+  for (int i = threadIdx.x; i <= a.K; i += blockDim.x) a.rhist[tile * (a.K + 1) + i] = cnt_lds[N + i];
 }
 
-// bf16 x: three-way split MFMA scoring. Workgroup (token tile tt, expert group eg)
-// scores 64 tokens against ETW 32-expert tiles over the whole of d; the EG = Np /
-// (32 ETW) groups of a token tile are dispatched to one XCD, where they share the
-// x tile in L2. K tiles of 64 columns (x rows, the three weight planes of the
-// group and the null row's float32 weights) stream through S LDS stages filled by
-// global->LDS loads, S-1 of them in flight. Wavefront w multiplies token half
-// w & 1 over the 16-wide K steps 2 (w >> 1) and 2 (w >> 1) + 1 of each tile; the
-// two K halves are added in a fixed order at the end. Group 0 also computes the
-// null row as an fp64 dot product. With one group per token tile the logits go
-// straight to LDS for the selection epilogue; otherwise each group writes its
-// columns and the last group of the token tile to finish (an atomic counter,
-// release/acquire fenced) reads the whole tile back and selects.
+// bf16 x: three-way split MFMA scoring. Workgroup (token tile tt, expert group eg,
+// K split ks) scores 64 tokens against ETW 32-expert tiles over its share of the
+// K tiles; the workgroups of a token tile are dispatched to one XCD, where they
+// share the x tile in L2. K tiles of 64 columns (x rows, the group's float32
+// weight rows and the null row) stream through S LDS stages filled by
+// global->LDS loads, S-1 of them in flight. Each weight fragment is split into its
+// bf16 (hi, mid, lo) parts in registers right before its three MFMAs (hardware
+// round-to-nearest-even; the two subtractions are exact), so the float32 weight is
+// read as it is. Wavefront w multiplies token half w & 1 over the 16-wide K steps
+// 2 (w >> 1) and 2 (w >> 1) + 1 of each tile; the two K halves are added in a
+// fixed order at the end. Group 0 also computes the null row as an fp64 dot
+// product. With one workgroup per token tile (many tokens, N <= 64) the logits go
+// straight to LDS for the selection epilogue. Otherwise each workgroup writes fp64
+// partial logits and route_select_kernel adds the K splits in order and selects:
+// with few tokens, splitting K spreads the latency-bound K loop over the CUs.
 constexpr int kRouteRedOff = 84 * 1024;  // LDS byte offset of the K-half exchange buffer
 
 template <int ETW>
 struct RouteTile {
-  static constexpr int rows = kRouteBT + 3 * 32 * ETW;   // x rows + weight rows per stage
-  static constexpr int stage = rows * 64 + 512;          // bf16 elements (+ 1 KB null slot)
-  static constexpr int loads = rows / 8 / 4;             // row loads per stage per wavefront
-  static constexpr int stages = ETW == 1 ? 6 : 4;
+  // stage: x [64][64] bf16 (128-byte rows), weights [32 ETW][64] float32 (256-byte
+  // rows), null row slot (1 KB: four copies of 64 floats); in bf16 elements
+  static constexpr int x_elems = kRouteBT * 64;
+  static constexpr int w_rows = 32 * ETW;
+  static constexpr int w_elems = w_rows * 128;
+  static constexpr int stage = x_elems + w_elems + 512;
+  static constexpr int loads = kRouteBT / 32 + w_rows / 16 + 1;  // per stage per wavefront
+  static constexpr int stages = ETW == 1 ? 7 : 5;
   static constexpr size_t lds = (size_t)stages * stage * sizeof(bf16_t);
   static_assert(lds <= 160 * 1024 - 256, "LDS budget of one CU");
   static_assert(kRouteRedOff + 2 * ETW * 16 * kWave * sizeof(double) <= lds, "exchange buffer");
+  static_assert(loads * (stages - 2) < 64, "stages in flight must fit the vmcnt counter");
 };
 
-__device__ __forceinline__ int rt_off(int row, int chunk) {
+__device__ __forceinline__ int rt_off(int row, int chunk) {  // x: 16-byte chunks, 8 per row
   return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
+__device__ __forceinline__ int wt_off(int row, int unit) {   // weights: floats, 16 units per row
+  return row * 64 + ((unit ^ (row & 15)) << 2);
+}
+
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 template <bool FUSED, int KMAX, int ETW>
 __global__ void __launch_bounds__(kRouteThreads)
 route_tile_kernel(RouteKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   using TL = RouteTile<ETW>;
-  constexpr int S = TL::stages, J = TL::loads;
+  constexpr int S = TL::stages, JN = TL::loads;
   static_assert(kRouteBT == 64 && kRouteThreads == 256, "tile shape");
-  static_assert((J + 1) * (S - 2) < 64, "stages in flight must fit the vmcnt counter");
   const int N = a.N, d = a.d, Np = a.Np, n_et = Np / 32, EG = (n_et + ETW - 1) / ETW;
+  const int KS = a.KS;
   const int ld = N + 1;
   bf16_t* stages = reinterpret_cast<bf16_t*>(smem_raw);
 
   const int b = blockIdx.x, xcd = b & 7, q = b >> 3;
-  const int64_t tt = (int64_t)(q / EG) * 8 + xcd;
-  const int eg = q % EG;
+  const int64_t tt = (int64_t)(q / (EG * KS)) * 8 + xcd;
+  const int eg = (q % (EG * KS)) % EG, ks = (q % (EG * KS)) / EG;
   const int64_t T = a.T;
   if (tt * kRouteBT >= T) return;  // padding of the grid to whole XCD rounds
   const int64_t t0 = tt * kRouteBT;
@@ -330,38 +304,48 @@ route_tile_kernel(RouteKernelArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int half = lane >> 5, l32 = lane & 31;
   const int th = wave & 1, kp = wave >> 1;
-  const int nk = (d + 63) / 64;
-  const int64_t plane = (int64_t)Np * d;
-  const int lrow = lane >> 3, lc = (lane & 7) ^ lrow;
+  const int nk_all = (d + 63) / 64;
+  const int per = (nk_all + KS - 1) / KS;       // the host makes every split non-empty
+  const int kt0 = ks * per;
+  const int nk = min(nk_all, kt0 + per) - kt0;  // this workgroup's K tiles kt0 .. kt0 + nk - 1
 
-  // Stage row 8 (wave + 4 j) + lane / 8 comes from x (rows < 64, clamped to T - 1;
-  // those rows are never stored) or, at 64 + 32 (3 u + p) + i, from weight plane p,
-  // expert 32 (ETW eg + u) + i (a tile past Np reads tile 0 and is never stored).
-  const bf16_t* src[J];
+  // x rows 8 (wave + 4 j) + lane / 8 (j < 2; clamped to T - 1, never stored), logical
+  // chunk (lane % 8) ^ (row % 8)
+  const int xr = lane >> 3, xc = (lane & 7) ^ xr;
+  const bf16_t* xsrc[2];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int r = 8 * (wave + 4 * j) + lrow;
-    if (j < kRouteBT / 32) {
-      src[j] = a.x + min<int64_t>(t0 + r, T - 1) * d;
-    } else {
-      const int wr = r - kRouteBT, u = wr / 96, p = (wr / 32) % 3;
-      const int et = ETW * eg + u < n_et ? ETW * eg + u : 0;
-      src[j] = a.w3 + p * plane + (int64_t)(et * 32 + wr % 32) * d;
-    }
+  for (int j = 0; j < 2; ++j) xsrc[j] = a.x + min<int64_t>(t0 + 8 * (wave + 4 * j) + xr, T - 1) * d;
+  // weight rows 4 (wave + 4 j) + lane / 16 of the group (expert 32 (ETW eg + u) + i;
+  // rows past N read row 0 and are never stored), logical unit (lane % 16) ^ (row % 16)
+  constexpr int JW = TL::w_rows / 16;
+  const float* wsrc[JW];
+  int wu[JW];
+#pragma unroll
+  for (int j = 0; j < JW; ++j) {
+    const int wr = 4 * (wave + 4 * j) + (lane >> 4);
+    const int e = (ETW * eg + wr / 32) * 32 + wr % 32;
+    wsrc[j] = a.w + (int64_t)(e < N ? e : 0) * d;
+    wu[j] = (lane & 15) ^ (wr & 15);
   }
   // null slot: lane l loads floats [4 (l % 16), 4 (l % 16) + 4) of the tile (four copies)
   const int nl_col = 4 * (lane & 15);
-  // Loads of K tile kt into stage st; chunks past d read column 0 and are zeroed
-  // at use.
-  auto issue = [&](int kt, int st) {
-    const int k = kt * 64 + lc * 8;
-    const int kc = k < d ? k : 0;
+  // Loads of K tile kt into stage st; chunks past d read column 0 and are zeroed at use.
+  auto issue = [&](int kl, int st) {
+    const int kt = kt0 + kl;
     bf16_t* stage = stages + st * TL::stage;
+    const int k = kt * 64 + xc * 8;
+    const int kc = k < d ? k : 0;
 #pragma unroll
-    for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + 8 * (wave + 4 * j) * 64);
+    for (int j = 0; j < 2; ++j) load_lds16(xsrc[j] + kc, stage + 8 * (wave + 4 * j) * 64);
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const int kw = kt * 64 + 4 * wu[j];
+      load_lds16(reinterpret_cast<const bf16_t*>(wsrc[j] + (kw < d ? kw : 0)),
+                 stage + TL::x_elems + 4 * (wave + 4 * j) * 128);
+    }
     const int kn = kt * 64 + nl_col;
     load_lds16(reinterpret_cast<const bf16_t*>(a.w_null + (kn + 4 <= d ? kn : 0)),
-               stage + TL::rows * 64);
+               stage + TL::x_elems + TL::w_elems);
   };
 
   double acc[ETW][16];
@@ -378,26 +362,29 @@ route_tile_kernel(RouteKernelArgs a) {
 
   auto compute = [&](auto tail, int st, int kvalid) {
     const bf16_t* xs = stages + st * TL::stage;
-    const float* wn = reinterpret_cast<const float*>(xs + TL::rows * 64);
+    const float* ws = reinterpret_cast<const float*>(xs + TL::x_elems);
+    const float* wn = reinterpret_cast<const float*>(xs + TL::x_elems + TL::w_elems);
     f32x16_t part[ETW];
 #pragma unroll
     for (int u = 0; u < ETW; ++u) part[u] = f32x16_t{};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int ch = (2 * kp + s2) * 2 + half;
+      const bool dead = decltype(tail)::value && ch * 8 >= kvalid;
       bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(th * 32 + l32, ch)]);
-      if constexpr (decltype(tail)::value) {
-        if (ch * 8 >= kvalid) af = bf16x8_t{};
-      }
+      if (dead) af = bf16x8_t{};
 #pragma unroll
       for (int u = 0; u < ETW; ++u) {
-        const int wr = kRouteBT + 96 * u + l32;
-        bf16x8_t b2 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr + 64, ch)]);
-        bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr + 32, ch)]);
-        bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(wr, ch)]);
-        if constexpr (decltype(tail)::value) {
-          if (ch * 8 >= kvalid) b2 = b1 = b0 = bf16x8_t{};
-        }
+        const int wr = 32 * u + l32;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch)]);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch + 1)]);
+        f32x8_t v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if (dead) v = f32x8_t{};
+        const bf16x8_t b0 = __builtin_convertvector(v, bf16x8_t);
+        const f32x8_t r1 = v - __builtin_convertvector(b0, f32x8_t);
+        const bf16x8_t b1 = __builtin_convertvector(r1, bf16x8_t);
+        const f32x8_t r2 = r1 - __builtin_convertvector(b1, f32x8_t);
+        const bf16x8_t b2 = __builtin_convertvector(r2, bf16x8_t);
         part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part[u], 0, 0, 0);
         part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part[u], 0, 0, 0);
         part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part[u], 0, 0, 0);
@@ -431,15 +418,16 @@ route_tile_kernel(RouteKernelArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(S - 2, nk - 1 - kt);  // K tiles issued after kt
     switch (ahead) {
-      case 4: wait_vmcnt<(S > 5 ? 4 : 0) * (J + 1)>(); break;
-      case 3: wait_vmcnt<(S > 4 ? 3 : 0) * (J + 1)>(); break;
-      case 2: wait_vmcnt<2 * (J + 1)>(); break;
-      case 1: wait_vmcnt<J + 1>(); break;
+      case 5: wait_vmcnt<(S > 6 ? 5 : 0) * JN>(); break;
+      case 4: wait_vmcnt<(S > 5 ? 4 : 0) * JN>(); break;
+      case 3: wait_vmcnt<(S > 4 ? 3 : 0) * JN>(); break;
+      case 2: wait_vmcnt<2 * JN>(); break;
+      case 1: wait_vmcnt<JN>(); break;
       default: wait_vmcnt<0>(); break;
     }
     stage_barrier();
     if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    const int kvalid = d - kt * 64;
+    const int kvalid = d - (kt0 + kt) * 64;
     if (kvalid < 64) compute(std::true_type{}, kt % S, kvalid);
     else compute(std::false_type{}, kt % S, kvalid);
   }
@@ -457,11 +445,39 @@ route_tile_kernel(RouteKernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) red[((th * ETW + u) * 16 + i) * kWave + lane] = acc[u][i];
   }
-  if (FUSED && EG == 1)
-    for (int i = tid; i < N + a.M; i += kRouteThreads) cnt_lds[i] = 0;
+  const bool direct = !a.partials;  // then EG == 1 and KS == 1
+  if (FUSED && direct)
+    for (int i = tid; i < N + a.K + 1; i += kRouteThreads) cnt_lds[i] = 0;
   __syncthreads();
-  // EG == 1: the tile's logits go to LDS; otherwise to the staging buffer
-  float* out = EG == 1 ? sl : a.lbuf + t0 * ld;
+  if (direct) {
+    // the tile's logits go to LDS, then the selection epilogue
+    if (kp == 0) {
+#pragma unroll
+      for (int u = 0; u < ETW; ++u) {
+        const int e = u * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
+          const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          if (e < N && tr < nt) sl[tr * ld + e] = (float)v;
+        }
+      }
+    }
+    if (do_null) {
+      const double a01 = nacc + __shfl_xor(nacc, 1, kWave);
+      const double sum = a01 + __shfl_xor(a01, 2, kWave);
+      if (nl_part == 0 && nl_tok < nt) {
+        double vv = sum + (double)a.null_bias;
+        if (a.null_bias_tok) vv += (double)nbias_tok;
+        sl[nl_tok * ld + N] = (float)vv;
+      }
+    }
+    __syncthreads();
+    route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out != nullptr, cnt_lds, wacc);
+    return;
+  }
+  // partials path: this split's fp64 sums (the null column without its biases)
+  double* lp = a.lpart + ((int64_t)ks * T + t0) * ld;
   if (kp == 0) {
 #pragma unroll
     for (int u = 0; u < ETW; ++u) {
@@ -470,56 +486,61 @@ route_tile_kernel(RouteKernelArgs a) {
       for (int i = 0; i < 16; ++i) {
         const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
         const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        if (e < N && tr < nt) out[tr * ld + e] = (float)v;
+        if (e < N && tr < nt) lp[tr * ld + e] = v;
       }
     }
   }
   if (do_null) {
     const double a01 = nacc + __shfl_xor(nacc, 1, kWave);
     const double sum = a01 + __shfl_xor(a01, 2, kWave);
-    if (nl_part == 0 && nl_tok < nt) {
-      double vv = sum + (double)a.null_bias;
-      if (a.null_bias_tok) vv += (double)nbias_tok;
-      out[nl_tok * ld + N] = (float)vv;
-    }
+    if (nl_part == 0 && nl_tok < nt) lp[nl_tok * ld + N] = sum;
   }
-  if (EG == 1) {
-    __syncthreads();
-    route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out != nullptr, cnt_lds, wacc);
-    return;
-  }
+}
 
-  // the last group of the token tile to finish selects
-  __shared__ int last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(&a.tile_cnt[tt], 1u) == (unsigned)(EG - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (tid == 0) a.tile_cnt[tt] = 0u;
-  {
-    const int n = nt * ld;
-    const float* src_l = a.lbuf + t0 * ld;
-    for (int i0 = tid; i0 < n; i0 += 8 * kRouteThreads) {
-      float v[8];
+// Partials path, second kernel: one workgroup per 64-token tile adds the K splits
+// of every logit in split order (fp64), adds the null biases, rounds to float32
+// and runs the selection epilogue.
+template <bool FUSED, int KMAX>
+__global__ void __launch_bounds__(kRouteThreads)
+route_select_kernel(RouteKernelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int kMaxSplits = 4;
+  const int N = a.N, ld = N + 1, KS = a.KS;
+  float* sl = reinterpret_cast<float*>(smem_raw);
+  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
+  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
+  if (FUSED)
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
+  const int64_t T = a.T, t0 = (int64_t)blockIdx.x * kRouteBT;
+  const int nt = (int)min<int64_t>(kRouteBT, T - t0);
+  const int n = nt * ld;
+  const double* lp = a.lpart + t0 * ld;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * kRouteThreads) {
+    double v[4][kMaxSplits];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k) {
         const int i = i0 + u * kRouteThreads;
-        v[u] = i < n ? src_l[i] : 0.0f;
+        v[u][k] = (i < n && k < KS) ? lp[(int64_t)k * T * ld + i] : 0.0;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kRouteThreads;
-        if (i < n) sl[i] = v[u];
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kRouteThreads;
+      if (i >= n) continue;
+      double sum = 0.0;
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k)
+        if (k < KS) sum += v[u][k];
+      if (i % ld == N) {
+        sum += (double)a.null_bias;
+        if (a.null_bias_tok) sum += (double)a.null_bias_tok[t0 + i / ld];
       }
+      sl[i] = (float)sum;
     }
   }
-  if (FUSED)
-    for (int i = tid; i < N + a.M; i += kRouteThreads) cnt_lds[i] = 0;
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out && a.logits_out != a.lbuf,
-                              cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds, wacc);
 }
 
 // float32 x: plain dot products (small workloads), then the same epilogue.
@@ -532,7 +553,7 @@ route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* 
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
   int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
   if (FUSED)
-    for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) {
@@ -560,7 +581,7 @@ route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
   int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
   if (FUSED)
-    for (int i = threadIdx.x; i < N + a.M; i += blockDim.x) cnt_lds[i] = 0;
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) sl[i] = logits[t0 * ld + i];
@@ -569,31 +590,44 @@ route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
                               wacc);
 }
 
-// bf16 scoring workspace: split weight planes, the logits staging buffer and the
-// token-tile counters, each 256-byte aligned.
-struct RouteWs {
-  size_t split, lbuf, tiles, total;
-};
-static RouteWs route_ws(int64_t T, int N, int d) {
-  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  const int Np = (N + 31) / 32 * 32;
-  RouteWs w;
-  w.split = 0;
-  w.lbuf = up((size_t)3 * Np * d * sizeof(bf16_t));
-  w.tiles = w.lbuf + up((size_t)T * (N + 1) * sizeof(float));
-  w.total = w.tiles + up((size_t)((T + kRouteBT - 1) / kRouteBT) * sizeof(uint32_t));
-  return w;
-}
-size_t route_ws_bytes(int64_t T, int N, int d) { return route_ws(T, N, d).total; }
-
-// 32-expert tiles per scoring workgroup: all of them when N <= 64 (no cross-workgroup
-// step), else pairs.
+// 32-expert tiles per scoring workgroup: all of them when N <= 64, else pairs.
 static int route_etw(int N) { return N <= 32 ? 1 : 2; }
 
+// bf16 scoring plan. Many tokens and N <= 64: one workgroup per token tile scores
+// and selects (no second kernel). Otherwise K is split so that the scoring grid
+// covers about 256 workgroups (at most 4 splits, each non-empty), fp64 partial
+// logits go to the workspace and route_select_kernel adds and selects.
+struct RoutePlan {
+  int etw, eg, ks;
+  bool partials;
+};
+static RoutePlan route_plan(int64_t T, int N, int d) {
+  const int etw = route_etw(N);
+  const int Np = (N + 31) / 32 * 32;
+  const int eg = (Np / 32 + etw - 1) / etw;
+  const int64_t ntt = std::max<int64_t>(1, (T + kRouteBT - 1) / kRouteBT);
+  if (eg == 1 && ntt >= 128) return {etw, 1, 1, false};
+  const int nk = (d + 63) / 64;
+  int ks = (int)std::min<int64_t>(4, std::max<int64_t>(1, (256 + ntt * eg - 1) / (ntt * eg)));
+  ks = std::min(ks, nk);
+  const int per = (nk + ks - 1) / ks;
+  ks = (nk + per - 1) / per;
+  return {etw, eg, ks, true};
+}
+
+// bf16 scoring workspace: the partial logits of the partials path (at least 256
+// bytes, so a bf16 call always passes one).
+size_t route_ws_bytes(int64_t T, int N, int d) {
+  const RoutePlan pl = route_plan(T, N, d);
+  const size_t part = pl.partials ? (size_t)pl.ks * T * (N + 1) * sizeof(double) : 0;
+  return std::max<size_t>(256, (part + 255) / 256 * 256);
+}
+
+// LDS of the selection epilogue, and of the scoring kernel (stages) when mfma
 static size_t route_lds_bytes(const RouteArgs& r, bool mfma) {
   const int ld = r.N + 1;
   size_t b = (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
-  if (r.fused) b += (size_t)epi_doubles(r.N) * sizeof(double) + (size_t)(r.N + r.M) * sizeof(int);
+  if (r.fused) b += (size_t)epi_doubles(r.N) * sizeof(double) + (size_t)(r.N + r.K + 1) * sizeof(int);
   if (mfma) b = std::max(b, route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds);
   return b;
 }
@@ -610,26 +644,15 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
   const unsigned nblk = (unsigned)ntt;
   const int Np = (r.N + 31) / 32 * 32;
   const bool mfma = !r.logits_in && r.bf16;
-  const RouteWs rw = route_ws(r.T, r.N, r.d);
-  unsigned char* ws = static_cast<unsigned char*>(r.ws);
-  bf16_t* w3 = mfma ? reinterpret_cast<bf16_t*>(ws + rw.split) : nullptr;
-  float* lbuf = mfma ? (r.logits_out ? r.logits_out : reinterpret_cast<float*>(ws + rw.lbuf)) : nullptr;
-  uint32_t* tiles = mfma ? reinterpret_cast<uint32_t*>(ws + rw.tiles) : nullptr;
-  RouteKernelArgs a{static_cast<const bf16_t*>(r.x), w3,
+  const RoutePlan pl = route_plan(r.T, r.N, r.d);
+  RouteKernelArgs a{static_cast<const bf16_t*>(r.x), r.w_router,
                     r.w_router ? r.w_router + (int64_t)r.N * r.d : nullptr, r.null_bias,
-                    r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, 1, r.logits_out,
-                    r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.acc, r.counts, lbuf, tiles};
-  const size_t lds = route_lds_bytes(r, mfma);
-  // prep: split the router weight (bf16 scoring), clear the fused accumulators and
-  // the token-tile counters
-  const int nacc = r.fused ? r.N + 3 : 0, ncnt = r.fused ? r.N + r.M : 0;
-  if (mfma || r.fused) {
-    const int64_t n = std::max<int64_t>(mfma ? (int64_t)Np * r.d : 0,
-                                        std::max<int64_t>(std::max(nacc, ncnt), mfma ? ntt : 0));
-    const unsigned sblk = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1024));
-    route_prep_kernel<<<sblk, 256, 0, stream>>>(r.w_router, w3, r.N, Np, r.d, r.acc, nacc,
-                                                r.counts, ncnt, tiles, mfma ? ntt : 0);
-  }
+                    r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, r.logits_out,
+                    r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.rhist, r.tstats,
+                    pl.ks, pl.partials ? 1 : 0, mfma ? static_cast<double*>(r.ws) : nullptr};
+  const size_t lds = route_lds_bytes(r, mfma && !pl.partials);
+  const size_t lds_score = route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds;
+  const size_t lds_select = route_lds_bytes(r, false);
   const int kmax = r.K <= 2 ? 2 : (r.K <= 8 ? 8 : 32);
 #define MOE_KMAX_SWITCH(MACRO, ...)                 \
   do {                                              \
@@ -650,22 +673,32 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
   } while (0)
 #define MOE_ROUTE_LAUNCH(F_, KM_)                                                         \
   do {                                                                                    \
-    if (etw == 1) {                                                                       \
-      allow_lds(route_tile_kernel<F_, KM_, 1>, lds);                                      \
-      route_tile_kernel<F_, KM_, 1><<<grid, kRouteThreads, lds, stream>>>(a);             \
+    if (!pl.partials) {                                                                   \
+      if (pl.etw == 1) {                                                                  \
+        allow_lds(route_tile_kernel<F_, KM_, 1>, lds);                                    \
+        route_tile_kernel<F_, KM_, 1><<<grid, kRouteThreads, lds, stream>>>(a);           \
+      } else {                                                                            \
+        allow_lds(route_tile_kernel<F_, KM_, 2>, lds);                                    \
+        route_tile_kernel<F_, KM_, 2><<<grid, kRouteThreads, lds, stream>>>(a);           \
+      }                                                                                   \
     } else {                                                                              \
-      allow_lds(route_tile_kernel<F_, KM_, 2>, lds);                                      \
-      route_tile_kernel<F_, KM_, 2><<<grid, kRouteThreads, lds, stream>>>(a);             \
+      if (pl.etw == 1) {                                                                  \
+        allow_lds(route_tile_kernel<false, 2, 1>, lds_score);                             \
+        route_tile_kernel<false, 2, 1><<<grid, kRouteThreads, lds_score, stream>>>(a);    \
+      } else {                                                                            \
+        allow_lds(route_tile_kernel<false, 2, 2>, lds_score);                             \
+        route_tile_kernel<false, 2, 2><<<grid, kRouteThreads, lds_score, stream>>>(a);    \
+      }                                                                                   \
+      allow_lds(route_select_kernel<F_, KM_>, lds_select);                                \
+      route_select_kernel<F_, KM_><<<nblk, kRouteThreads, lds_select, stream>>>(a);       \
     }                                                                                     \
   } while (0)
   if (r.logits_in) {
     if (r.fused) MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, true);
     else MOE_KMAX_SWITCH(MOE_LOGITS_LAUNCH, false);
   } else if (r.bf16) {
-    // token tiles padded to whole rounds of the 8 XCDs, times the expert groups
-    const int etw = route_etw(r.N);
-    const int eg = (Np / 32 + etw - 1) / etw;
-    const unsigned grid = (unsigned)((ntt + 7) / 8 * 8 * eg);
+    // token tiles padded to whole rounds of the 8 XCDs, times the groups and splits
+    const unsigned grid = (unsigned)((ntt + 7) / 8 * 8 * pl.eg * pl.ks);
     if (r.fused) MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, true);
     else MOE_KMAX_SWITCH(MOE_ROUTE_LAUNCH, false);
   } else {
