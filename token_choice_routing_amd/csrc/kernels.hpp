@@ -66,7 +66,7 @@ struct PermuteArgs {
   int32_t* perm_token;
   int32_t* slot_pos;
   void* x_perm;
-  int32_t* ws;                    // chunk_hist [nchunks][N] then chunk_base [nchunks][N]
+  int32_t* ws;                    // chunk_hist [nchunks][N]
   bool hist_ready;                // chunk_hist already written (by the fused router)
   const AuxTiles* aux;            // optional statistics finalisation (fused path)
 };

@@ -12,12 +12,14 @@
 // The slots are cut into chunks of 64 tokens (64*K slots), the same chunks the
 // router's workgroups score, so in the fused layer path the router has already
 // written each chunk's expert histogram. Kernels: (a) per-chunk histogram
-// (standalone path only), (b) one workgroup turns the histograms into counts,
-// offsets and per-chunk bases (and, in the fused path, finalises the
-// statistics), (c) each chunk ranks its slots stably -- wavefront ballots find
-// the lanes holding the same expert -- and scatters. Counts use LDS integer
-// atomics, whose result does not depend on their order, so the permutation is
-// deterministic. A fourth kernel gathers x_perm[p] = x[perm_token[p]].
+// (standalone path only); (b) one launch in which every chunk's workgroup adds the
+// histograms itself (all chunks for the expert totals and offsets, earlier chunks
+// for its base), ranks its slots stably -- wavefront ballots find the lanes
+// holding the same expert -- and scatters, while one more workgroup finalises the
+// statistics in the fused path. Counts use integer additions, whose result does
+// not depend on their order, so the permutation is deterministic. A further
+// kernel gathers x_perm[p] = x[perm_token[p]] (standalone path; the layer's
+// gate/up GEMM reads x through perm_token instead).
 #include <algorithm>
 
 #include "common.hpp"
@@ -63,10 +65,10 @@ __device__ void finalize_tiles(const AuxTiles& a, int tiles, int64_t T, int N, i
   const int per = (tiles + G - 1) / G;
   for (int r = threadIdx.x; r <= K; r += blockDim.x) rsum[r] = 0;
   __syncthreads();
-  {
-    // thread (c, g) adds tiles [g per, (g + 1) per) of column c, eight loads at a time
-    const int c = threadIdx.x % C, g = threadIdx.x / C;
-    if (g < G) {
+  for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x) {
+    // item (c, g) adds tiles [g per, (g + 1) per) of column c, eight loads at a time
+    const int c = idx % C, g = idx / C;
+    {
       double s = 0.0;
       const int t1 = min(tiles, (g + 1) * per);
       for (int tb = g * per; tb < t1; tb += 8) {
@@ -133,54 +135,85 @@ __device__ void finalize_tiles(const AuxTiles& a, int tiles, int64_t T, int N, i
   }
 }
 
-// One workgroup of 1024 threads: counts[e] = sum over chunks, offsets = exclusive
-// scan over e, chunk_base[c][e] = offsets[e] + sum_{c' < c} hist[c'][e].
-// Thread (e, g) owns expert e for the g-th contiguous group of chunks (N <= 255,
-// so there are at least 4 groups). In the fused path it also finalises the
-// statistics from the router's per-tile sums.
-__global__ void __launch_bounds__(1024)
-permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
-                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                    int32_t* __restrict__ chunk_base, AuxTiles aux, int64_t T, int M, int K) {
+// Counting sort of the token slots, one launch. Workgroup c < nchunks owns the
+// 64 tokens of chunk c: it adds the per-chunk expert histograms (all chunks for
+// the totals, chunks before c for its prefix), scans the totals into the expert
+// offsets, and scatters its 64 K slots at offsets[e] + prefix[e] + (rank within
+// the chunk), so the order is stable (token-major, then k). Workgroup nchunks,
+// when statistics are requested, finalises them from the router's per-tile sums.
+// K groups of 64 slots per chunk; each wavefront takes a contiguous run of groups.
+template <bool STATS>
+__global__ void __launch_bounds__(kPermThreads)
+permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
+               const int32_t* __restrict__ chunk_hist, int nchunks, int64_t max_rows,
+               int32_t* __restrict__ perm_token, int32_t* __restrict__ slot_pos,
+               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, AuxTiles aux,
+               int64_t T, int M) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  const int groups = blockDim.x / N;
-  const bool stats = aux.tstats != nullptr;
-  // fused: terms [N + M], tile-group partials [G][N + 3], totals [N + 3] (doubles)
-  const int C = N + 3, G = max(1, (int)blockDim.x / C);
-  double* terms = reinterpret_cast<double*>(smem_raw);
-  double* spart = terms + (stats ? N + M : 0);
-  double* stot = spart + (stats ? G * C : 0);
-  int* part = reinterpret_cast<int*>(stot + (stats ? C : 0));        // [groups][N]
-  int* off = part + groups * N;                                      // [N + 1]
-  int* rsum = off + N + 1;                                           // [K + 1]
-  const int per = (nchunks + groups - 1) / groups;
-  const int e = threadIdx.x % N, g = threadIdx.x / N;
-  const bool active = g < groups;
-  const int c0 = g * per, c1 = min(nchunks, c0 + per);
-  if (active) {
-    int s = 0;
-    for (int cb = c0; cb < c1; cb += 8) {
-      int v[8];
+  constexpr int nw = kPermThreads / kWave;
+  const int nkeys = N + 1;
+  const int c = blockIdx.x;
+  const bool stats_block = STATS && c == nchunks;
+  // LDS: off [N + 1], base [N] ints; then the reduction scratch and the scatter's
+  // per-wave counts, or the statistics scratch
+  int* off = reinterpret_cast<int*>(smem_raw);
+  int* cbase = off + (N + 1);
+  int* scratch = cbase + N;
+  const int N4 = (N + 3) / 4, RP = max(1, kPermThreads / N4);
+  {
+    // totals and prefix: thread (column quad q4, row phase r) adds rows r, r + RP, ...
+    int* ptot = scratch;             // [RP][N]
+    int* ppre = scratch + RP * N;    // [RP][N]
+    const int q4 = threadIdx.x % N4, r = threadIdx.x / N4;
+    if (r < RP) {
+      int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+      for (int rb = r; rb < nchunks; rb += 4 * RP) {
+        int v[4][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = cb + u < c1 ? chunk_hist[(int64_t)(cb + u) * N + e] : 0;
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+          for (int j = 0; j < 4; ++j) {
+            const int row = rb + u * RP, e = 4 * q4 + j;
+            v[u][j] = (row < nchunks && e < N) ? chunk_hist[(int64_t)row * N + e] : 0;
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            tot[j] += v[u][j];
+            if (rb + u * RP < c) pre[j] += v[u][j];
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * q4 + j;
+        if (e < N) {
+          ptot[r * N + e] = tot[j];
+          ppre[r * N + e] = pre[j];
+        }
+      }
     }
-    part[g * N + e] = s;
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += kPermThreads) {
+      int t = 0, p = 0;
+      for (int rr = 0; rr < RP; ++rr) {
+        t += ptot[rr * N + e];
+        p += ppre[rr * N + e];
+      }
+      off[e] = t;      // totals for now
+      cbase[e] = p;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (threadIdx.x < kWave) {
     // wave 0: exclusive scan of the per-expert totals, 4 experts per lane
     const int lane = threadIdx.x;
     int tot[4], local = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ee = lane * 4 + q;
-      int t = 0;
-      if (ee < N)
-        for (int gg = 0; gg < groups; ++gg) t += part[gg * N + ee];
-      tot[q] = t;
-      local += t;
+    for (int qq = 0; qq < 4; ++qq) {
+      const int ee = lane * 4 + qq;
+      tot[qq] = ee < N ? off[ee] : 0;
+      local += tot[qq];
     }
     int incl = local;
 #pragma unroll
@@ -190,50 +223,45 @@ permute_scan_kernel(const int32_t* __restrict__ chunk_hist, int nchunks, int N,
     }
     int run = incl - local;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ee = lane * 4 + q;
+    for (int qq = 0; qq < 4; ++qq) {
+      const int ee = lane * 4 + qq;
       if (ee < N) {
         off[ee] = run;
-        offsets[ee] = run;
-        counts[ee] = tot[q];
+        if (c == 0) {
+          offsets[ee] = run;
+          counts[ee] = tot[qq];
+        }
+        cbase[ee] += run;
       }
-      run += tot[q];
+      run += tot[qq];
     }
     if (lane == kWave - 1) {
       off[N] = incl;
-      offsets[N] = incl;
+      if (c == 0) offsets[N] = incl;
     }
   }
   __syncthreads();
-  if (active) {
-    int base = off[e];
-    for (int g2 = 0; g2 < g; ++g2) base += part[g2 * N + e];
-    for (int c = c0; c < c1; ++c) {
-      chunk_base[(int64_t)c * N + e] = base;
-      base += chunk_hist[(int64_t)c * N + e];
-    }
+  if (stats_block) {
+    // statistics scratch after off/cbase: terms [N + M], partials [G][N + 3], totals
+    // [N + 3] (doubles, 8-byte aligned), r sums [K + 1]
+    double* terms = reinterpret_cast<double*>(smem_raw + (((2 * N + 1) * sizeof(int) + 7) / 8) * 8);
+    const int C = N + 3, G = max(1, kPermThreads / C);
+    double* spart = terms + (N + M);
+    double* stot = spart + G * C;
+    int* rsum = reinterpret_cast<int*>(stot + C);
+    finalize_tiles(aux, nchunks, T, N, M, K, off, spart, stot, rsum, terms);
+    return;
   }
-  if (stats) finalize_tiles(aux, nchunks, T, N, M, K, off, spart, stot, rsum, terms);
-}
 
-// One workgroup per chunk of 64 tokens: 64*K slots in K groups of 64; each
-// wavefront takes a contiguous run of groups, in order.
-__global__ void __launch_bounds__(kPermThreads)
-permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
-                       const int32_t* __restrict__ chunk_base, int64_t max_rows,
-                       int32_t* __restrict__ perm_token, int32_t* __restrict__ slot_pos) {
-  extern __shared__ int sm[];
-  const int nkeys = N + 1;
-  constexpr int nw = kPermThreads / kWave;
-  int* wcnt = sm;                  // [4][N+1] running count per wave
-  int* wbase = sm + nw * nkeys;    // [4][N]
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  int* wcnt = scratch;               // [4][N+1] running count per wave
+  int* wbase = scratch + nw * nkeys; // [4][N]
   for (int i = threadIdx.x; i < nw * nkeys; i += blockDim.x) wcnt[i] = 0;
   __syncthreads();
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   int nbits = 1;
   while ((1 << nbits) <= N) ++nbits;  // enough bits for keys 0..N
   const int gpw = (K + nw - 1) / nw;  // groups (of 64 slots) per wave
-  const int64_t fc = (int64_t)blockIdx.x * kTokChunk * K;
+  const int64_t fc = (int64_t)c * kTokChunk * K;
   int key[kMaxGroupsPerWave], lrank[kMaxGroupsPerWave];
   int* mycnt = wcnt + wave * nkeys;
 #pragma unroll
@@ -260,7 +288,7 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, 
   __syncthreads();
   for (int i = threadIdx.x; i < nw * N; i += blockDim.x) {
     const int w = i / N, e = i % N;
-    int b = chunk_base[(int64_t)blockIdx.x * N + e];
+    int b = cbase[e];
     for (int w2 = 0; w2 < w; ++w2) b += wcnt[w2 * nkeys + e];
     wbase[w * N + e] = b;
   }
@@ -320,31 +348,40 @@ gather_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ pe
 int permute_nchunks(int64_t T) { return (int)((T + kTokChunk - 1) / kTokChunk); }
 
 size_t permute_ws_bytes(int64_t T, int N) {
-  return (size_t)2 * permute_nchunks(T) * N * sizeof(int32_t);
+  return (size_t)permute_nchunks(T) * N * sizeof(int32_t);
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int64_t TK = a.T * a.K;
   const int nchunks = permute_nchunks(a.T);
   int32_t* chunk_hist = a.ws;
-  int32_t* chunk_base = a.ws + (int64_t)nchunks * a.N;
   if (!a.hist_ready)
     permute_hist_kernel<<<nchunks, kPermThreads, a.N * sizeof(int), stream>>>(a.topk_idx, TK, a.K,
                                                                              a.N, chunk_hist);
   AuxTiles at{};
   if (a.aux) at = *a.aux;
-  const int groups = 1024 / a.N;
-  const int C = a.N + 3, G = std::max(1, 1024 / C);
-  const size_t scan_lds =
-      (at.tstats ? ((size_t)(a.N + a.M) + (size_t)G * C + C) * sizeof(double) : 0) +
-      ((size_t)groups * a.N + a.N + 1 + a.K + 1) * sizeof(int);
-  permute_scan_kernel<<<1, 1024, scan_lds, stream>>>(chunk_hist, nchunks, a.N, a.counts, a.offsets,
-                                                     chunk_base, at, a.T, a.M, a.K);
-  const size_t sc_lds = ((size_t)(kPermThreads / kWave) * (a.N + 1) +
-                         (size_t)(kPermThreads / kWave) * a.N) * sizeof(int);
+  const bool stats = at.tstats != nullptr;
+  constexpr int nw = kPermThreads / kWave;
+  const int N4 = (a.N + 3) / 4, RP = std::max(1, kPermThreads / N4);
+  const size_t head = (size_t)(2 * a.N + 1) * sizeof(int);
+  const size_t scat = std::max((size_t)2 * RP * a.N, (size_t)nw * (a.N + 1) + (size_t)nw * a.N) * sizeof(int);
+  size_t lds = head + scat;
+  if (stats) {
+    const int C = a.N + 3, G = std::max(1, kPermThreads / C);
+    const size_t st = (head + 7) / 8 * 8 + ((size_t)(a.N + a.M) + (size_t)G * C + C) * sizeof(double) +
+                      (size_t)(a.K + 1) * sizeof(int);
+    lds = std::max(lds, st);
+  }
   const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);
-  permute_scatter_kernel<<<nchunks, kPermThreads, sc_lds, stream>>>(
-      a.topk_idx, TK, a.K, a.N, chunk_base, max_rows, a.perm_token, a.slot_pos);
+  const unsigned grid = (unsigned)(nchunks + (stats ? 1 : 0));
+  if (stats)
+    permute_kernel<true><<<grid, kPermThreads, lds, stream>>>(
+        a.topk_idx, TK, a.K, a.N, chunk_hist, nchunks, max_rows, a.perm_token, a.slot_pos, a.counts,
+        a.offsets, at, a.T, a.M);
+  else
+    permute_kernel<false><<<grid, kPermThreads, lds, stream>>>(
+        a.topk_idx, TK, a.K, a.N, chunk_hist, nchunks, max_rows, a.perm_token, a.slot_pos, a.counts,
+        a.offsets, at, a.T, a.M);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.x && a.x_perm) {

@@ -79,7 +79,7 @@ struct RouteKernelArgs {
   double* tstats;          // fused: [tiles][N + 3]
   int KS;                  // bf16 scoring: K splits (partials path)
   int partials;            // bf16 scoring: 1 = write partial logits for route_select_kernel
-  double* lpart;           // bf16 scoring, partials path: [KS][T][N + 1] fp64 partial logits
+  float* lpart;            // bf16 scoring, partials path: [KS][T][N + 1] partial logits
 };
 
 // Selection for the (up to 64) tokens of one workgroup: four consecutive lanes
@@ -202,9 +202,16 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int N = a.N;
   if (copy_logits) {
-    const int w = N + 1;
-    for (int i = threadIdx.x; i < nt * w; i += blockDim.x)
-      a.logits_out[(t0 + i / w) * w + i % w] = sl[(i / w) * ld + i % w];
+    // the tile's rows are contiguous in both (ld = N + 1), 16-byte aligned (t0 % 64 == 0)
+    const int n = nt * ld;
+    float* dst = a.logits_out + t0 * ld;
+    for (int i = 4 * threadIdx.x; i < n; i += 4 * blockDim.x) {
+      if (i + 4 <= n) {
+        *reinterpret_cast<f32x4_t*>(dst + i) = *reinterpret_cast<const f32x4_t*>(sl + i);
+      } else {
+        for (int j = i; j < n; ++j) dst[j] = sl[j];
+      }
+    }
     __syncthreads();  // the fused selection overwrites the rows
   }
   double* tok_acc = wacc + N + 3;  // [2][64]
@@ -252,7 +259,7 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
 // 2 (w >> 1) and 2 (w >> 1) + 1 of each tile; the two K halves are added in a
 // fixed order at the end. Group 0 also computes the null row as an fp64 dot
 // product. With one workgroup per token tile (many tokens, N <= 64) the logits go
-// straight to LDS for the selection epilogue. Otherwise each workgroup writes fp64
+// straight to LDS for the selection epilogue. Otherwise each workgroup writes its
 // partial logits and route_select_kernel adds the K splits in order and selects:
 // with few tokens, splitting K spreads the latency-bound K loop over the CUs.
 constexpr int kRouteRedOff = 84 * 1024;  // LDS byte offset of the K-half exchange buffer
@@ -476,8 +483,10 @@ route_tile_kernel(RouteKernelArgs a) {
     route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out != nullptr, cnt_lds, wacc);
     return;
   }
-  // partials path: this split's fp64 sums (the null column without its biases)
-  double* lp = a.lpart + ((int64_t)ks * T + t0) * ld;
+  // partials path: this split's fp64 sums rounded once to float32 (the null column
+  // without its biases); split planes are padded to a multiple of 4 floats
+  const int64_t plane = (T * ld + 3) & ~int64_t(3);
+  float* lp = a.lpart + ks * plane + t0 * ld;
   if (kp == 0) {
 #pragma unroll
     for (int u = 0; u < ETW; ++u) {
@@ -486,20 +495,23 @@ route_tile_kernel(RouteKernelArgs a) {
       for (int i = 0; i < 16; ++i) {
         const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
         const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        if (e < N && tr < nt) lp[tr * ld + e] = v;
+        if (e < N && tr < nt) lp[tr * ld + e] = (float)v;
       }
     }
   }
   if (do_null) {
     const double a01 = nacc + __shfl_xor(nacc, 1, kWave);
     const double sum = a01 + __shfl_xor(a01, 2, kWave);
-    if (nl_part == 0 && nl_tok < nt) lp[nl_tok * ld + N] = sum;
+    if (nl_part == 0 && nl_tok < nt) lp[nl_tok * ld + N] = (float)sum;
   }
 }
 
 // Partials path, second kernel: one workgroup per 64-token tile adds the K splits
 // of every logit in split order (fp64), adds the null biases, rounds to float32
-// and runs the selection epilogue.
+// and runs the selection epilogue. Each split is an fp64 sum over its K range
+// rounded once to float32: at most 4 splits, so the logit moves by a few float32
+// ulps of the split sums (about 1e-7 of their size), far inside the 1e-5 near-tie
+// margin, while the workgroup reads half the bytes.
 template <bool FUSED, int KMAX>
 __global__ void __launch_bounds__(kRouteThreads)
 route_select_kernel(RouteKernelArgs a) {
@@ -514,29 +526,41 @@ route_select_kernel(RouteKernelArgs a) {
   const int64_t T = a.T, t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, T - t0);
   const int n = nt * ld;
-  const double* lp = a.lpart + t0 * ld;
-  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * kRouteThreads) {
-    double v[4][kMaxSplits];
+  const int64_t plane = (T * ld + 3) & ~int64_t(3);
+  const float* lp = a.lpart + t0 * ld;  // t0 * ld is a multiple of 4: 16-byte aligned quads
+  // element quads (4 i .. 4 i + 3), kQuads per thread at a time, every split's loads in
+  // flight together; the splits are added in order
+  constexpr int kQuads = 8;
+  const int nquad = (n + 3) / 4;
+  for (int p0 = threadIdx.x; p0 < nquad; p0 += kQuads * kRouteThreads) {
+    f32x4_t v[kQuads][kMaxSplits];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kQuads; ++u)
 #pragma unroll
       for (int k = 0; k < kMaxSplits; ++k) {
-        const int i = i0 + u * kRouteThreads;
-        v[u][k] = (i < n && k < KS) ? lp[(int64_t)k * T * ld + i] : 0.0;
+        const int pi = p0 + u * kRouteThreads;
+        v[u][k] = (pi < nquad && k < KS)
+                      ? *reinterpret_cast<const f32x4_t*>(lp + k * plane + 4 * (int64_t)pi)
+                      : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kRouteThreads;
-      if (i >= n) continue;
-      double sum = 0.0;
+    for (int u = 0; u < kQuads; ++u) {
+      const int pi = p0 + u * kRouteThreads;
+      if (pi >= nquad) continue;
 #pragma unroll
-      for (int k = 0; k < kMaxSplits; ++k)
-        if (k < KS) sum += v[u][k];
-      if (i % ld == N) {
-        sum += (double)a.null_bias;
-        if (a.null_bias_tok) sum += (double)a.null_bias_tok[t0 + i / ld];
+      for (int h = 0; h < 4; ++h) {
+        const int i = 4 * pi + h;
+        if (i >= n) continue;
+        double sum = 0.0;
+#pragma unroll
+        for (int k = 0; k < kMaxSplits; ++k)
+          if (k < KS) sum += (double)v[u][k][h];
+        if (i % ld == N) {
+          sum += (double)a.null_bias;
+          if (a.null_bias_tok) sum += (double)a.null_bias_tok[t0 + i / ld];
+        }
+        sl[i] = (float)sum;
       }
-      sl[i] = (float)sum;
     }
   }
   __syncthreads();
@@ -595,8 +619,8 @@ static int route_etw(int N) { return N <= 32 ? 1 : 2; }
 
 // bf16 scoring plan. Many tokens and N <= 64: one workgroup per token tile scores
 // and selects (no second kernel). Otherwise K is split so that the scoring grid
-// covers about 256 workgroups (at most 4 splits, each non-empty), fp64 partial
-// logits go to the workspace and route_select_kernel adds and selects.
+// covers about 256 workgroups (at most 4 splits, each non-empty), partial logits go
+// to the workspace and route_select_kernel adds and selects.
 struct RoutePlan {
   int etw, eg, ks;
   bool partials;
@@ -619,7 +643,8 @@ static RoutePlan route_plan(int64_t T, int N, int d) {
 // bytes, so a bf16 call always passes one).
 size_t route_ws_bytes(int64_t T, int N, int d) {
   const RoutePlan pl = route_plan(T, N, d);
-  const size_t part = pl.partials ? (size_t)pl.ks * T * (N + 1) * sizeof(double) : 0;
+  const size_t part =
+      pl.partials ? (size_t)pl.ks * (size_t)((T * (N + 1) + 3) & ~int64_t(3)) * sizeof(float) : 0;
   return std::max<size_t>(256, (part + 255) / 256 * 256);
 }
 
@@ -649,7 +674,7 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
                     r.w_router ? r.w_router + (int64_t)r.N * r.d : nullptr, r.null_bias,
                     r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, r.logits_out,
                     r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.rhist, r.tstats,
-                    pl.ks, pl.partials ? 1 : 0, mfma ? static_cast<double*>(r.ws) : nullptr};
+                    pl.ks, pl.partials ? 1 : 0, mfma ? static_cast<float*>(r.ws) : nullptr};
   const size_t lds = route_lds_bytes(r, mfma && !pl.partials);
   const size_t lds_score = route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds;
   const size_t lds_select = route_lds_bytes(r, false);
