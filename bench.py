@@ -51,40 +51,98 @@ def log(*a):
 
 
 class Timer:
-    """HIP events on torch's current stream (the stream every entry point is given)."""
+    """Launch timing with HIP events recorded on torch's current stream (the stream
+    every entry point is given). The events are created with
+    hipEventDisableSystemFence: a default timing event makes its release a
+    system-scope fence (L2 write-back and invalidate), which lands inside a
+    single-launch measurement. The runtime is the libamdhip64 that torch loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, torch):
+        import ctypes
         self.torch = torch
+        self.ct = ctypes
+        torch.cuda.init()
+        with open("/proc/self/maps") as f:
+            paths = [ln.split()[-1] for ln in f if "libamdhip64.so" in ln]
+        if not paths:
+            raise RuntimeError("libamdhip64 is not loaded")
+        self.hip = ctypes.CDLL(paths[0])
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def _events(self, n):
+        evs = []
+        for _ in range(n):
+            e = self.ct.c_void_p()
+            if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            evs.append(e)
+        return evs
+
+    def _elapsed_us(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def _record(self, e):
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def _free(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
 
     def run(self, fn, iters, warmup=2):
         torch = self.torch
         for _ in range(warmup):
             fn()
-        s = torch.cuda.current_stream()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = self._events(2)
         torch.cuda.synchronize()
-        a.record(s)
+        self._record(a)
         for _ in range(iters):
             fn()
-        b.record(s)
-        b.synchronize()
-        return a.elapsed_time(b) * 1e3 / iters   # microseconds per call
+        self._record(b)
+        torch.cuda.synchronize()
+        us = self._elapsed_us(a, b) / iters
+        self._free([a, b])
+        return us   # microseconds per call
 
     def run_cold(self, fn, iters, flush):
-        """Average of single launches, each after a write of a buffer larger than the
-        256 MB last-level cache (the flush is outside the timed events)."""
+        """Average of single launches, each after a flush (outside the timed events)."""
         torch = self.torch
         fn()
-        s = torch.cuda.current_stream()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for a, b in evs:
-            flush.zero_()
-            a.record(s)
+        evs = self._events(2 * iters)
+        for i in range(iters):
+            flush()
+            self._record(evs[2 * i])
             fn()
-            b.record(s)
+            self._record(evs[2 * i + 1])
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) * 1e3 / iters
+        us = sum(self._elapsed_us(evs[2 * i], evs[2 * i + 1]) for i in range(iters)) / iters
+        self._free(evs)
+        return us
+
+
+class Flush:
+    """Evicts earlier data from the caches by reading 512 MB, twice the 256 MB
+    last-level cache, with one reduction kernel. A read leaves clean lines behind; a
+    write flush would leave the last-level cache full of dirty lines, and the next
+    kernel would then pay for writing them back to HBM (measured: the routed gate/up
+    launch goes from ~53 us to ~89 us at 2048 tokens), which is not its own traffic."""
+
+    def __init__(self, torch):
+        self.buf = torch.ones((128 << 20,), dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+        self.torch = torch
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def layer_flops(cfg, R, T):
@@ -159,7 +217,7 @@ def kernel_table(torch, tcr, layer, iters):
         tcr.moe_aux_stats(dims, logits, topk, fo, Po, co, sc, ws_a)
 
     tm = Timer(torch)
-    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+    flush = Flush(torch)
     route()
     permute_gather()
     torch.cuda.synchronize()
@@ -317,7 +375,7 @@ def decode_sweep(torch, base, main_layer, steps):
     and back to back."""
     from token_choice_routing_amd.layer import MoeLayer
     out = []
-    flush = torch.empty((512 << 20,), dtype=torch.uint8, device="cuda")
+    flush = Flush(torch)
     tm = Timer(torch)
     cfg = base.cfg
     for Ts in (1, 16, 64, 256):
@@ -387,7 +445,7 @@ def main():
     dom = "gemm_gate_up"
     rl = roofline(kernels[dom])
     rl["kernel"] = ("grouped_gemm_bf16_kernel<0, 0>: routed gate/up + SwiGLU, standalone launch on "
-                    "the layer's permuted rows, last-level cache flushed before each timed launch")
+                    "the layer's permuted rows, caches flushed by a 512 MB read before each timed launch")
     rl["traffic"] = traffic_from_profiles("gemm_gate_up", cfg.name)
     line = {
         "metric": "MoE-layer tokens/s + real-expert TFLOP/s (% bf16 MFMA peak) vs rho",

@@ -76,6 +76,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
 }
 
+// Waits until at most n (wave-uniform, clamped to [0, MAX]) vector memory
+// operations of this wavefront are outstanding.
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (MAX > 0) {
+    if (n >= MAX) {
+      wait_vmcnt<MAX>();
+      return;
+    }
+    wait_vmcnt_upto<MAX - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // 16-byte global -> LDS load (global_load_lds_dwordx4). The LDS address must be
 // uniform across the wavefront; lane l writes bytes [16 l, 16 l + 16) after it. The
 // builtin only exists in the device compilation pass, where it is kept.

@@ -30,6 +30,12 @@
 //    (expert, column tile, row tile) and cut into 8 contiguous ranges, one per
 //    XCD (workgroups are dispatched round-robin over the 8 XCDs), so the row
 //    tiles that share one expert's weight panel run on the same L2.
+//  * When a range's last round has fewer tiles than the range has workgroups,
+//    those tiles are split by output columns into 2 or 4 sub-tiles, so every
+//    workgroup streams about the same weight bytes. Load instructions whose rows
+//    are all past the segment or outside the sub-tile are not issued. Each
+//    workgroup issues its next item's first stages before it stores the current
+//    item's outputs.
 #include <algorithm>
 #include <type_traits>
 
@@ -151,7 +157,8 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   const int G0 = p0.groups, G = p0.groups + p1.groups;
   const int total = tt.prefix[kMaxGroups];
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave % WM, wn = wave / WM;
   const int half = lane >> 5, l32 = lane & 31;
   // this lane's load: row RPI (wave + NW j) + lane / CPR of the stage, physical chunk
@@ -160,76 +167,122 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   const int lrow = lane / CPR;
   const int lc = (lane % CPR) ^ (BK == 64 ? lrow : (lrow >> 2) & 3);
 
-  // XCD-contiguous tile ranges
+  // XCD-contiguous tile ranges. When a range's last round would leave workgroups
+  // idle, its tiles are split by output columns into 2 or 4 sub-tiles, so that every
+  // workgroup of the range streams about the same number of weight bytes.
   const int P = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per_xcd_blocks = P >> 3;
+  const int Bx = P >> 3;
   const int Sx = (total + 7) / 8;
   const int r_begin = xcd * Sx, r_end = min(total, r_begin + Sx);
+  const int nx = max(0, r_end - r_begin);
+  const int full = nx / Bx * Bx, rem = nx - full;
+  const int split = rem == 0 ? 1 : (WN >= 4 && 4 * rem <= Bx) ? 4 : (WN >= 2 && 2 * rem <= Bx) ? 2 : 1;
+  const int items = full + rem * split;
 
-  for (int L = r_begin + slot; L < r_end; L += per_xcd_blocks) {
-    // locate (group, column tile, row tile)
+  // One work item: where its operands come from and where its outputs go.
+  struct Tile {
+    bool second, wact;
+    int ge, Kdim, nk, m0, rows_valid, col0, jn;
+    unsigned lmask;
+    const bf16_t* src[J];
+  };
+  // Locates work item it (group, column tile, row tile, sub-tile columns), decides
+  // which load instructions fetch something used (A rows before rows_valid, weight
+  // rows of the sub-tile's columns; wave-uniform and the same for every K tile, so
+  // each stage of the item holds jn of this wavefront's loads) and sets each load's
+  // row source, always a valid row: rows past the segment and columns past n_out
+  // only feed outputs that are never stored.
+  auto setup = [&](int it, Tile& t) {
+    int L = r_begin + it, part = 0, parts = 1;
+    if (it >= full) {
+      L = r_begin + full + (it - full) / split;
+      part = (it - full) % split;
+      parts = split;
+    }
     int lo = 0, hi = G;  // prefix[lo] <= L < prefix[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tt.prefix[mid] <= L) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const bool second = e >= G0;
-    const GemmProblem& pr = second ? p1 : p0;
-    const int ge = second ? e - G0 : e;
-    const int Nout = pr.n_out, Kdim = pr.k_dim;
-    const int nk = (Kdim + BK - 1) / BK;
+    t.second = e >= G0;
+    const GemmProblem pr = t.second ? p1 : p0;
+    t.ge = t.second ? e - G0 : e;
+    const int Nout = pr.n_out;
+    t.Kdim = pr.k_dim;
+    t.nk = (t.Kdim + BK - 1) / BK;
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
     const int ntile = local / mt, mtile = local - ntile * mt;
-    const int m0 = tt.start[e] + mtile * BM;
-    const int rows_valid = min(BM, tt.start[e] + tt.len[e] - m0);
-
-    // Row sources, always a valid row: rows past the segment and columns past n_out
-    // only feed outputs that are never stored.
-    const bf16_t* src[J];
-    {
-      int64_t arow[JA > 0 ? JA : 1];
+    t.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
+    t.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - t.m0));
+    const int ocp = OC / parts;  // output columns of this item
+    t.col0 = __builtin_amdgcn_readfirstlane(ntile * OC + part * ocp);
+    // wavefronts whose rows or columns all fall outside skip the MFMAs and the stores
+    t.wact = __builtin_amdgcn_readfirstlane(wn < WN / parts && wm * TM < t.rows_valid);
+    unsigned lmask = 0;
 #pragma unroll
-      for (int j = 0; j < JA; ++j) {
-        const int r = RPI * (wave + NW * j) + lrow;
-        arow[j] = m0 + (r < rows_valid ? r : 0);
-      }
-      if (pr.a_rows) {
-        int32_t sr[JA > 0 ? JA : 1];
-#pragma unroll
-        for (int j = 0; j < JA; ++j) sr[j] = pr.a_rows[arow[j]];
-#pragma unroll
-        for (int j = 0; j < JA; ++j) arow[j] = min<int64_t>(max<int64_t>(sr[j], 0), pr.a_nrows - 1);
-      }
-#pragma unroll
-      for (int j = 0; j < JA; ++j) src[j] = pr.a + arow[j] * Kdim;
-#pragma unroll
-      for (int j = JA; j < J; ++j) {
-        const int r = RPI * (wave + NW * j) + lrow - BM;
-        int n;
-        const bf16_t* base;
-        if (MODE == kSwiGLU) {
-          n = ntile * OC + (r % OC);
-          base = r < OC ? pr.b0 : pr.b1;
-        } else {
-          n = ntile * OC + r;
-          base = pr.b0;
-        }
-        src[j] = base + ((int64_t)ge * Nout + (n < Nout ? n : 0)) * Kdim;
-      }
+    for (int j = 0; j < J; ++j) {
+      const int r0 = RPI * (wave + NW * j);
+      const bool use = j < JA ? r0 < t.rows_valid : (MODE == kSwiGLU ? (r0 - BM) % OC : r0 - BM) < ocp;
+      lmask |= (unsigned)use << j;
     }
-    // K tile kt into stage st. Chunks past k_dim (last tile only) read column 0;
-    // their fragments are zeroed before the MFMAs.
-    auto issue = [&](int kt, int st) {
-      const int k = kt * BK + lc * 8;
-      const int kc = k < Kdim ? k : 0;
-      bf16_t* stage = smem + st * STAGE;
+    t.lmask = __builtin_amdgcn_readfirstlane(lmask);
+    t.jn = __builtin_popcount(t.lmask);
+    int64_t arow[JA > 0 ? JA : 1];
 #pragma unroll
-      for (int j = 0; j < J; ++j) load_lds16(src[j] + kc, stage + RPI * (wave + NW * j) * BK);
-    };
+    for (int j = 0; j < JA; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow;
+      arow[j] = t.m0 + (r < t.rows_valid ? r : 0);
+    }
+    if (pr.a_rows) {
+      int32_t sr[JA > 0 ? JA : 1];
+#pragma unroll
+      for (int j = 0; j < JA; ++j) sr[j] = pr.a_rows[arow[j]];
+#pragma unroll
+      for (int j = 0; j < JA; ++j) arow[j] = min<int64_t>(max<int64_t>(sr[j], 0), pr.a_nrows - 1);
+    }
+#pragma unroll
+    for (int j = 0; j < JA; ++j) t.src[j] = pr.a + arow[j] * t.Kdim;
+#pragma unroll
+    for (int j = JA; j < J; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow - BM;
+      int n;
+      const bf16_t* base;
+      if (MODE == kSwiGLU) {
+        n = t.col0 + (r % OC);
+        base = r < OC ? pr.b0 : pr.b1;
+      } else {
+        n = t.col0 + r;
+        base = pr.b0;
+      }
+      t.src[j] = base + ((int64_t)t.ge * Nout + (n < Nout ? n : 0)) * t.Kdim;
+    }
+  };
+  // K tile kt of item t into stage st. Chunks past k_dim (last tile only) read
+  // column 0; their fragments are zeroed before the MFMAs.
+  auto issue = [&](const Tile& t, int kt, int st) {
+    const int k = kt * BK + lc * 8;
+    const int kc = k < t.Kdim ? k : 0;
+    bf16_t* stage = smem + st * STAGE;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (t.lmask >> j & 1) load_lds16(t.src[j] + kc, stage + RPI * (wave + NW * j) * BK);
+  };
+  // the first S-1 K tiles of an item, into stages 0 .. S-2
+  auto prologue = [&](const Tile& t) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < t.nk) issue(t, s, s);
+  };
 
+  Tile cur;
+  if (slot < items) {
+    setup(slot, cur);
+    prologue(cur);
+  }
+  for (int it = slot; it < items; it += Bx) {
     f32x16_t acc[FN][FM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
@@ -269,41 +322,48 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       frags(0, wf[0], af[0]);
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        const int cur = kDouble ? (ks & 1) : 0;
-        if (kDouble && ks + 1 < BK / 16) frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+        const int cur_buf = kDouble ? (ks & 1) : 0;
+        if (kDouble && ks + 1 < BK / 16) frags(ks + 1, wf[cur_buf ^ 1], af[cur_buf ^ 1]);
         if (!kDouble && ks > 0) frags(ks, wf[0], af[0]);
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int g = 0; g < FM; ++g)
-            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][f], af[cur][g], acc[f][g], 0, 0, 0);
+            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur_buf][f], af[cur_buf][g], acc[f][g], 0, 0, 0);
       }
     };
 
-    // Pipeline. The previous tile's LDS reads finish before its stages are refilled.
-    // Stage kt % S holds K tile kt. Before reading it a wavefront waits until at
-    // most the loads of the later tiles already issued are outstanding; on a tile's
-    // first step it waits for everything, because the previous tile's output stores
-    // may retire out of order with the loads.
-    stage_barrier();
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nk) issue(s, s);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(S - 2, nk - 1 - kt);  // tiles issued after kt
+    // Stage kt % S holds K tile kt (the item's first S-1 tiles were issued before
+    // it started). Before reading a stage a wavefront waits until at most the loads
+    // of the later tiles already issued are outstanding; on the first tile it waits
+    // for everything, because the previous item's output stores may retire out of
+    // order with the loads.
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      const int ahead = min(S - 2, cur.nk - 1 - kt);  // tiles issued after kt
       if (kt == 0 || ahead <= 0) wait_vmcnt<0>();
-      else if (S > 3 && ahead == 2) wait_vmcnt<J * (S > 3 ? 2 : 0)>();
-      else if (S > 4 && ahead == 3) wait_vmcnt<J * (S > 4 ? 3 : 0)>();
-      else wait_vmcnt<J>();
+      else wait_vmcnt_upto<J * (S - 2)>(cur.jn * ahead);
       stage_barrier();
-      if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-      const int kvalid = Kdim - kt * BK;
+      if (kt + S - 1 < cur.nk) issue(cur, kt + S - 1, (kt + S - 1) % S);
+      const int kvalid = cur.Kdim - kt * BK;
+      if (!cur.wact) continue;
       if (kvalid < BK)
         compute(std::true_type{}, kt % S, kvalid);
       else
         compute(std::false_type{}, kt % S, kvalid);
     }
 
+    // Every wavefront is done with the stages: issue the next item's first tiles,
+    // then store this item's outputs while those loads are in flight.
+    const bool second = cur.second, wact = cur.wact;
+    const int m0 = cur.m0, rows_valid = cur.rows_valid, col0 = cur.col0;
+    stage_barrier();
+    if (it + Bx < items) {
+      setup(it + Bx, cur);
+      prologue(cur);
+    }
+    if (!wact) continue;
+    const GemmProblem pr = second ? p1 : p0;
+    const int Nout = pr.n_out;
     // epilogue: lane owns row l32 of each 32-row subtile, 4 consecutive columns per group
 #pragma unroll
     for (int g = 0; g < FM; ++g) {
@@ -315,7 +375,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
         for (int f = 0; f < FN / 2; ++f)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = ntile * OC + wn * (TN / 2) + f * 32 + 8 * q + 4 * half;
+            const int col = col0 + wn * (TN / 2) + f * 32 + 8 * q + 4 * half;
             if (col < Nout) {
               float h[4];
 #pragma unroll
@@ -331,7 +391,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = ntile * OC + wn * TN + f * 32 + 8 * q + 4 * half;
+            const int col = col0 + wn * TN + f * 32 + 8 * q + 4 * half;
             if (col < Nout) {
               const f32x16_t& v = acc[f][g];
               *reinterpret_cast<f32x4_t*>(crow + col) =

@@ -7,15 +7,18 @@ Usage:
 RESULTS_DB is the ``*_results.db`` that ``rocprofv3 --kernel-trace --stats -d <dir>
 -o run`` writes; COMMAND is the command that made it (printed into the summary).
 Besides the per-kernel totals this splits every kernel's dispatches into cold ones
-(the kernel dispatched right before it was the cache-flushing fill that bench.py
-issues before each timed GEMM launch of its kernel table) and warm ones (any other
-predecessor), because bench.py's roofline uses the cold launches.
+(the kernel dispatched right before it was the cache-flushing 512 MB sum that
+bench.py issues before each timed GEMM launch of its kernel table) and warm ones
+(any other predecessor), because bench.py's roofline uses the cold launches.
 """
 import sqlite3
 import statistics
 import sys
 
-FLUSH_PREFIX = "void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>"
+
+def is_flush(name):
+    """torch's reduction kernel for a float32 sum (bench.py's flush)."""
+    return name.startswith("void at::native::reduce_kernel<") and "sum_functor<float" in name
 
 
 def short(name):
@@ -29,7 +32,7 @@ def dispatches(db):
     con.close()
     out, prev = [], ""
     for name, _start, dur in rows:
-        out.append((name, dur, prev.startswith(FLUSH_PREFIX)))
+        out.append((name, dur, is_flush(prev)))
         prev = name
     return out
 
@@ -56,7 +59,7 @@ def main(argv):
     total = sum(sum(e["all"]) for e in per.values()) or 1
     print(f"# {title}\n\nCommand (run from /tmp with TMPDIR=/tmp on one MI355X):\n\n```\n{cmd}\n"
           f"python -m token_choice_routing_amd.profsummary <out>/run_results.db <title> <command>\n```\n")
-    print("Cold = dispatched directly after the cache-flushing fill; warm = any other dispatch.\n")
+    print("Cold = dispatched directly after the cache-flushing sum; warm = any other dispatch.\n")
     print("| kernel | calls | total us | average us | % | cold calls | cold avg us | warm calls | warm avg us |")
     print("|---|---|---|---|---|---|---|---|---|")
     for name, e in sorted(per.items(), key=lambda kv: -sum(kv[1]["all"])):
