@@ -28,20 +28,23 @@
 //    them when N <= 64). K tiles of x, of the float32 weight rows and of the
 //    null row stream through 5-7 swizzled LDS stages filled by global->LDS loads,
 //    so several tiles are in flight while one feeds the MFMAs; the weight is
-//    split into its three bf16 parts in registers. When N > 64 the expert tiles
-//    of a token tile are spread over several workgroups and the last one to
-//    finish runs the selection.
-//  * Epilogue: four lanes per token. Each lane walks a quarter of its token's
-//    logits row in LDS and keeps the best K reals in registers with a
-//    branch-free insertion network over 64-bit keys (order-preserving bits of
-//    the logit, then the complemented expert index, so ties go to the lower
-//    index); two shuffle rounds merge the four lists.
+//    split into its three bf16 parts in registers. With few tokens (or N > 64)
+//    K, and the expert tiles, are spread over several workgroups that write
+//    float32 partial logits, and a selection kernel adds them in a fixed order.
+//  * Epilogue: 4 lanes per token in the scoring kernel, 16 in the 1024-thread
+//    selection kernel. Each lane walks its share of the token's logits row in
+//    LDS and keeps the best K reals in registers with a branch-free insertion
+//    network over 64-bit keys (order-preserving bits of the logit, then the
+//    complemented expert index, so ties go to the lower index); DPP exchanges
+//    within the row merge the lists. One lane per token then does the per-token
+//    fp64 work (weights, log-sum-exp) once.
 //  * Fused layer mode additionally writes, per 64-token tile, the real slots
 //    per expert (the first pass of the permutation's counting sort), the
 //    histogram of r and the load-balance / z-loss sums; the permutation's scan
 //    adds them over tiles in tile order, so the totals do not depend on the
 //    order in which workgroups finish and no accumulator needs clearing.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -82,16 +85,53 @@ struct RouteKernelArgs {
   float* lpart;            // bf16 scoring, partials path: [KS][T][N + 1] partial logits
 };
 
-// Selection for the (up to 64) tokens of one workgroup: four consecutive lanes
-// own a token, lane q walking experts q, q + 4, ... of its logits row. Each lane
-// keeps the best KMAX reals it has seen in a register list sorted by 64-bit keys
-// (the order-preserving bits of the logit, then the complemented index: a larger
-// key is a larger logit, or the lower index at equal logits); an insertion is a
-// fixed compare-and-swap chain, so no lane diverges. The four lists are merged
-// with two rounds of shuffles, after which every lane of the token holds the
-// same top-KMAX list. In fused mode the row is then overwritten with its
-// pool-softmax probabilities for the column sums, and lane 0 of the token leaves
-// lse^2 and r in tok_acc[0][t] and tok_acc[1][t].
+// fp64 LDS scratch of the fused epilogue: block sums [N + 3], per-token lse^2 and r
+// [2][64], column parts [P][N + 1] (P = 4 or 16; sized for 16)
+__host__ __device__ constexpr int epi_doubles(int N) { return (N + 3) + 2 * 64 + 16 * (N + 1); }
+
+// threads of a selection-only workgroup: 16 lanes per token while the key lists
+// are short, else 4 (register budget of 1024-thread workgroups)
+template <int KMAX>
+constexpr int select_threads() { return KMAX <= 8 ? 1024 : 256; }
+
+// LDS of the selection epilogue: the logits tile [64][N + 1] float32, a per-token
+// hand-off of kTokSlots 8-byte slots (the top-KMAX keys at 0 .., then vmax and the
+// pool max at 32, r at 33, z at 34, 1/z at 35), and in fused mode the fp64
+// statistics scratch and the histogram counters [N + K + 1].
+constexpr int kTokSlots = 36;
+struct EpiLds {
+  float* sl;
+  uint64_t* tok;
+  double* wacc;
+  int* cnt;
+};
+__device__ __forceinline__ EpiLds epi_lds(unsigned char* smem, int N) {
+  EpiLds e;
+  e.sl = reinterpret_cast<float*>(smem);
+  e.tok = reinterpret_cast<uint64_t*>(e.sl + ((kRouteBT * (N + 1) + 1) & ~1));
+  e.wacc = reinterpret_cast<double*>(e.tok + kRouteBT * kTokSlots);
+  e.cnt = reinterpret_cast<int*>(e.wacc + epi_doubles(N));
+  return e;
+}
+static size_t epi_lds_bytes(int N, int K, bool fused) {
+  size_t b = (size_t)((kRouteBT * (N + 1) + 1) & ~1) * sizeof(float) +
+             (size_t)kRouteBT * kTokSlots * sizeof(uint64_t);
+  if (fused) b += (size_t)epi_doubles(N) * sizeof(double) + (size_t)(N + K + 1) * sizeof(int);
+  return b;
+}
+
+// Selection for the (up to 64) tokens of one workgroup, in two phases.
+// Phase 1: LPT consecutive lanes (4 or 16) own a token, lane q walking experts
+// q, q + LPT, ... of its logits row. Each lane keeps the best KMAX reals it has
+// seen in a register list sorted by 64-bit keys (the order-preserving bits of the
+// logit, then the complemented index: a larger key is a larger logit, or the lower
+// index at equal logits); an insertion is a fixed compare-and-swap chain, so no
+// lane diverges. The LPT lists are merged with log2(LPT) rounds of shuffles. In
+// fused mode the lanes also overwrite the row with the pool-softmax numerators and
+// add them up (z). Lane 0 hands the token's keys, maxima, r and z over in LDS.
+// Phase 2: one lane per token (wavefront 0) does the per-token fp64 work once:
+// the renormalised weights, the outputs, the histogram counts and, in fused mode,
+// 1/z (for the column sums), lse^2 and r in tok_acc[0][t] and tok_acc[1][t].
 template <int KMAX>
 __device__ __forceinline__ void insert_key(uint64_t (&lk)[KMAX], uint64_t key) {
 #pragma unroll
@@ -103,19 +143,34 @@ __device__ __forceinline__ void insert_key(uint64_t (&lk)[KMAX], uint64_t key) {
   }
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-  return ((uint64_t)hi << 32) | lo;
+// Partner exchange of round R of an all-reduce over the 4 (R < 2) or 16 lanes of a
+// DPP row: swap within pairs, swap pairs, mirror within halves of 8, mirror the
+// row. Each round combines two disjoint groups that already agree, so after
+// log2(lanes) rounds every lane holds the combination of all of them; for a
+// commutative combination every lane computes the same value.
+template <int R>
+__device__ __forceinline__ uint32_t dpp_xchg(uint32_t v) {
+  constexpr int kCtl[4] = {0xB1, 0x4E, 0x141, 0x140};  // quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtl[R], 0xF, 0xF, false);
+}
+template <int R>
+__device__ __forceinline__ uint64_t dpp_xchg64(uint64_t v) {
+  return ((uint64_t)dpp_xchg<R>((uint32_t)(v >> 32)) << 32) | dpp_xchg<R>((uint32_t)v);
+}
+template <int R>
+__device__ __forceinline__ double dpp_xchg_f64(double v) {
+  return __longlong_as_double((long long)dpp_xchg64<R>((uint64_t)__double_as_longlong(v)));
 }
 
-template <int KMAX, bool FUSED>
-__device__ void select_quads(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
-                             int* cnt_lds, double* tok_acc) {
-  const int tl = threadIdx.x >> 2, q = threadIdx.x & 3;
+template <int KMAX, bool FUSED, int LPT>
+__device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld, int nt, int64_t t0,
+                              double* tok_acc) {
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16, "lanes per token");
+  static_assert(KMAX <= 32, "key slots of the hand-off");
+  const int tl = threadIdx.x / LPT, q = threadIdx.x % LPT;
   const int N = a.N, M = a.M, K = a.K;
   const bool live = tl < nt;
-  float* s = sl + (live ? tl : 0) * ld;
+  float* s = L.sl + (live ? tl : 0) * ld;
   const float snull = s[N];
   uint64_t lk[KMAX];
 #pragma unroll
@@ -123,89 +178,114 @@ __device__ void select_quads(const RouteKernelArgs& a, float* sl, int ld, int nt
   int c = 0;
   float vmax = -INFINITY;
 #pragma unroll 4
-  for (int j = q; j < N; j += 4) {
+  for (int j = q; j < N; j += LPT) {
     const float v = s[j];
     c += v > snull;
     vmax = fmaxf(vmax, v);
     insert_key(lk, ((uint64_t)ordered_bits(v) << 32) | (0xffffffffu - (uint32_t)j));
   }
-#pragma unroll
-  for (int o = 1; o <= 2; o <<= 1) {
+  auto merge = [&](auto round) {
+    constexpr int R = decltype(round)::value;
     uint64_t other[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) other[i] = shfl_xor_u64(lk[i], o);
+    for (int i = 0; i < KMAX; ++i) other[i] = dpp_xchg64<R>(lk[i]);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) insert_key(lk, other[i]);
-    c += __shfl_xor(c, o, kWave);
-    vmax = fmaxf(vmax, __shfl_xor(vmax, o, kWave));
-  }
+    c += (int)dpp_xchg<R>((uint32_t)c);
+    vmax = fmaxf(vmax, __uint_as_float(dpp_xchg<R>(__float_as_uint(vmax))));
+  };
+  merge(std::integral_constant<int, 0>{});
+  merge(std::integral_constant<int, 1>{});
+  if constexpr (LPT >= 8) merge(std::integral_constant<int, 2>{});
+  if constexpr (LPT == 16) merge(std::integral_constant<int, 3>{});
   const int r = (M == 0) ? K : min(K, max(c, K - M));
+  const float mp = M > 0 ? fmaxf(vmax, snull) : vmax;  // pool maximum
+  uint64_t* tk = L.tok + tl * kTokSlots;
+  if (q == 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) tk[i] = lk[i];
+    tk[32] = ((uint64_t)__float_as_uint(mp) << 32) | __float_as_uint(vmax);
+    tk[33] = (uint64_t)r;
+  }
+  if (FUSED) {
+    // pool softmax [reals, null x M] numerators written over the logits row
+    double zq = 0.0;
+#pragma unroll 4
+    for (int j = q; j < N; j += LPT) {
+      const float ej = expf(s[j] - mp);
+      if (live) s[j] = ej;
+      zq += (double)ej;
+    }
+    // every lane adds the same operands in the same tree
+    zq += dpp_xchg_f64<0>(zq);
+    zq += dpp_xchg_f64<1>(zq);
+    if constexpr (LPT >= 8) zq += dpp_xchg_f64<2>(zq);
+    if constexpr (LPT == 16) zq += dpp_xchg_f64<3>(zq);
+    const float en = M > 0 ? expf(snull - mp) : 0.0f;
+    if (q == 0) {
+      tk[34] = (uint64_t)__double_as_longlong(zq + (double)M * (double)en);
+      if (live) s[N] = en;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= kRouteBT) return;
+  // phase 2: lane t of wavefront 0 finishes token t
+  const int t = threadIdx.x;
+  uint64_t* tt = L.tok + t * kTokSlots;
+  if (t >= nt) {
+    if (FUSED) {
+      tok_acc[t] = 0.0;
+      tok_acc[kRouteBT + t] = 0.0;
+    }
+    return;
+  }
+  const int rr = (int)tt[33];
+  const float vm = __uint_as_float((uint32_t)tt[32]), pm = __uint_as_float((uint32_t)(tt[32] >> 32));
   // weights: softmax over the chosen reals in fp64, summed in rank order
   double e[KMAX];
   double tot = 0.0;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    e[i] = i < r ? exp((double)from_ordered_bits((uint32_t)(lk[i] >> 32)) - (double)vmax) : 0.0;
+    e[i] = i < rr ? exp((double)from_ordered_bits((uint32_t)(tt[i] >> 32)) - (double)vm) : 0.0;
     tot += e[i];
   }
-  if (live) {
-    const int64_t t = t0 + tl;
-    int32_t* idx_row = a.topk_idx + t * K;
-    float* w_row = a.topk_w + t * K;
+  const int64_t tg = t0 + t;
+  int32_t* idx_row = a.topk_idx + tg * K;
+  float* w_row = a.topk_w + tg * K;
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if (i < K && (i & 3) == q) {
-        const int id = i < r ? (int)(0xffffffffu - (uint32_t)lk[i]) : N + (i - r);
-        idx_row[i] = id;
-        w_row[i] = i < r ? (float)(e[i] / tot) : 0.0f;
-        if (FUSED && i < r) atomicAdd(&cnt_lds[id], 1);
-      }
+  for (int i = 0; i < KMAX; ++i) {
+    if (i < K) {
+      const int id = i < rr ? (int)(0xffffffffu - (uint32_t)tt[i]) : N + (i - rr);
+      idx_row[i] = id;
+      w_row[i] = i < rr ? (float)(e[i] / tot) : 0.0f;
+      if (FUSED && i < rr) atomicAdd(&L.cnt[id], 1);
     }
-    if (a.n_real && q == 0) a.n_real[t] = r;
-    if (FUSED && q == 0) atomicAdd(&cnt_lds[N + r], 1);
   }
+  if (a.n_real) a.n_real[tg] = rr;
   if (FUSED) {
-    // pool softmax [reals, null x M]: p_j written over the logits row
-    const float mp = M > 0 ? fmaxf(vmax, snull) : vmax;
-    double zq = 0.0;
-#pragma unroll 4
-    for (int j = q; j < N; j += 4) {
-      const float ej = expf(s[j] - mp);
-      if (live) s[j] = ej;
-      zq += (double)ej;
-    }
-    const double z01 = zq + __shfl_xor(zq, 1, kWave);
-    double z = z01 + __shfl_xor(z01, 2, kWave);
-    const float en = M > 0 ? expf(snull - mp) : 0.0f;
-    z += (double)M * (double)en;
-    const float iz = (float)(1.0 / z);
-    if (live) {
-#pragma unroll 4
-      for (int j = q; j < N; j += 4) s[j] *= iz;
-      if (q == 0) s[N] = en * iz;
-    }
-    if (q == 0) {
-      const double lse = (double)mp + log(z);
-      tok_acc[tl] = live ? lse * lse : 0.0;
-      tok_acc[kRouteBT + tl] = live ? (double)r : 0.0;
-    }
+    atomicAdd(&L.cnt[N + rr], 1);
+    const double z = __longlong_as_double((long long)tt[34]);
+    reinterpret_cast<float*>(tt + 35)[0] = (float)(1.0 / z);
+    const double lse = (double)pm + log(z);
+    tok_acc[t] = lse * lse;
+    tok_acc[kRouteBT + t] = (double)rr;
   }
 }
 
-// fp64 LDS scratch of the fused epilogue: block sums [N + 3], per-token lse^2 and r
-// [2][64], column quarters [4][N + 1]
-__host__ __device__ constexpr int epi_doubles(int N) { return (N + 3) + 2 * 64 + 4 * (N + 1); }
-
-template <bool FUSED, int KMAX>
-__device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int nt, int64_t t0,
-                               int64_t tile, bool copy_logits, int* cnt_lds, double* wacc) {
+template <bool FUSED, int KMAX, int NT>
+__device__ void route_epilogue(const RouteKernelArgs& a, const EpiLds& L, int ld, int nt, int64_t t0,
+                               int64_t tile, bool copy_logits) {
+  constexpr int P = NT / kRouteBT;  // lanes per token, and column parts
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int N = a.N;
+  float* sl = L.sl;
+  double* wacc = L.wacc;
+  int* cnt_lds = L.cnt;
   if (copy_logits) {
     // the tile's rows are contiguous in both (ld = N + 1), 16-byte aligned (t0 % 64 == 0)
     const int n = nt * ld;
     float* dst = a.logits_out + t0 * ld;
-    for (int i = 4 * threadIdx.x; i < n; i += 4 * blockDim.x) {
+    for (int i = 4 * threadIdx.x; i < n; i += 4 * NT) {
       if (i + 4 <= n) {
         *reinterpret_cast<f32x4_t*>(dst + i) = *reinterpret_cast<const f32x4_t*>(sl + i);
       } else {
@@ -215,11 +295,12 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
     __syncthreads();  // the fused selection overwrites the rows
   }
   double* tok_acc = wacc + N + 3;  // [2][64]
-  select_quads<KMAX, FUSED>(a, sl, ld, nt, t0, cnt_lds, tok_acc);
+  select_tokens<KMAX, FUSED, P>(a, L, ld, nt, t0, tok_acc);
   if (!FUSED) return;
   __syncthreads();
   // per-block sums in a fixed order: lse^2 / n_real over the block's tokens, and
-  // the probability columns in four interleaved quarters added in order
+  // the probability columns (numerator x 1/z, rounded to float32) in P
+  // interleaved parts added pairwise
   if (wave == 0) {
     const double lz = wave_sum_double(tok_acc[lane]);
     const double nr = wave_sum_double(tok_acc[kRouteBT + lane]);
@@ -228,23 +309,33 @@ __device__ void route_epilogue(const RouteKernelArgs& a, float* sl, int ld, int 
       wacc[N + 2] = nr;
     }
   }
-  double* colq = tok_acc + 2 * kRouteBT;  // [4][N + 1]
-  for (int i = threadIdx.x; i < 4 * (N + 1); i += blockDim.x) {
+  double* colq = tok_acc + 2 * kRouteBT;  // [P][N + 1]
+  for (int i = threadIdx.x; i < P * (N + 1); i += NT) {
     const int j = i % (N + 1), qq = i / (N + 1);
     double sum = 0.0;
-    for (int tl = qq; tl < nt; tl += 4) sum += (double)sl[tl * ld + j];
+#pragma unroll 4
+    for (int tl = qq; tl < nt; tl += P)
+      sum += (double)(sl[tl * ld + j] * reinterpret_cast<const float*>(L.tok + tl * kTokSlots + 35)[0]);
     colq[qq * (N + 1) + j] = sum;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j <= N; j += blockDim.x)
-    wacc[j] = (colq[j] + colq[(N + 1) + j]) + (colq[2 * (N + 1) + j] + colq[3 * (N + 1) + j]);
+  for (int j = threadIdx.x; j <= N; j += NT) {
+    double v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) v[u] = colq[u * (N + 1) + j];
+#pragma unroll
+    for (int w = P / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int u = 0; u < w; ++u) v[u] += v[u + w];
+    wacc[j] = v[0];
+  }
   __syncthreads();
   // this tile's sums, real-slot histogram and r histogram; the permutation's scan
   // adds them over tiles in order
   double* ts = a.tstats + tile * (N + 3);
-  for (int i = threadIdx.x; i < N + 3; i += blockDim.x) ts[i] = wacc[i];
-  for (int i = threadIdx.x; i < N; i += blockDim.x) a.chunk_hist[tile * N + i] = cnt_lds[i];
-  for (int i = threadIdx.x; i <= a.K; i += blockDim.x) a.rhist[tile * (a.K + 1) + i] = cnt_lds[N + i];
+  for (int i = threadIdx.x; i < N + 3; i += NT) ts[i] = wacc[i];
+  for (int i = threadIdx.x; i < N; i += NT) a.chunk_hist[tile * N + i] = cnt_lds[i];
+  for (int i = threadIdx.x; i <= a.K; i += NT) a.rhist[tile * (a.K + 1) + i] = cnt_lds[N + i];
 }
 
 // bf16 x: three-way split MFMA scoring. Workgroup (token tile tt, expert group eg,
@@ -442,9 +533,8 @@ route_tile_kernel(RouteKernelArgs a) {
   // LDS after the K loop: selection tile [64][ld] floats at 0, then the epilogue's
   // statistics scratch, and the K-half exchange buffer at kRouteRedOff.
   stage_barrier();
-  float* sl = reinterpret_cast<float*>(smem_raw);
-  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
+  const EpiLds L = epi_lds(smem_raw, N);
+  float* sl = L.sl;
   double* red = reinterpret_cast<double*>(smem_raw + kRouteRedOff);  // [2][ETW][16][64]
   if (kp == 1) {
 #pragma unroll
@@ -454,7 +544,7 @@ route_tile_kernel(RouteKernelArgs a) {
   }
   const bool direct = !a.partials;  // then EG == 1 and KS == 1
   if (FUSED && direct)
-    for (int i = tid; i < N + a.K + 1; i += kRouteThreads) cnt_lds[i] = 0;
+    for (int i = tid; i < N + a.K + 1; i += kRouteThreads) L.cnt[i] = 0;
   __syncthreads();
   if (direct) {
     // the tile's logits go to LDS, then the selection epilogue
@@ -480,7 +570,7 @@ route_tile_kernel(RouteKernelArgs a) {
       }
     }
     __syncthreads();
-    route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, tt, a.logits_out != nullptr, cnt_lds, wacc);
+    route_epilogue<FUSED, KMAX, kRouteThreads>(a, L, ld, nt, t0, tt, a.logits_out != nullptr);
     return;
   }
   // partials path: this split's fp64 sums rounded once to float32 (the null column
@@ -513,16 +603,16 @@ route_tile_kernel(RouteKernelArgs a) {
 // ulps of the split sums (about 1e-7 of their size), far inside the 1e-5 near-tie
 // margin, while the workgroup reads half the bytes.
 template <bool FUSED, int KMAX>
-__global__ void __launch_bounds__(kRouteThreads)
+__global__ void __launch_bounds__(select_threads<KMAX>())
 route_select_kernel(RouteKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int NT = select_threads<KMAX>();
   constexpr int kMaxSplits = 4;
   const int N = a.N, ld = N + 1, KS = a.KS;
-  float* sl = reinterpret_cast<float*>(smem_raw);
-  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
+  const EpiLds L = epi_lds(smem_raw, N);
+  float* sl = L.sl;
   if (FUSED)
-    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) L.cnt[i] = 0;
   const int64_t T = a.T, t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, T - t0);
   const int n = nt * ld;
@@ -530,22 +620,22 @@ route_select_kernel(RouteKernelArgs a) {
   const float* lp = a.lpart + t0 * ld;  // t0 * ld is a multiple of 4: 16-byte aligned quads
   // element quads (4 i .. 4 i + 3), kQuads per thread at a time, every split's loads in
   // flight together; the splits are added in order
-  constexpr int kQuads = 8;
+  constexpr int kQuads = 8 * kRouteThreads / NT;
   const int nquad = (n + 3) / 4;
-  for (int p0 = threadIdx.x; p0 < nquad; p0 += kQuads * kRouteThreads) {
+  for (int p0 = threadIdx.x; p0 < nquad; p0 += kQuads * NT) {
     f32x4_t v[kQuads][kMaxSplits];
 #pragma unroll
     for (int u = 0; u < kQuads; ++u)
 #pragma unroll
       for (int k = 0; k < kMaxSplits; ++k) {
-        const int pi = p0 + u * kRouteThreads;
+        const int pi = p0 + u * NT;
         v[u][k] = (pi < nquad && k < KS)
                       ? *reinterpret_cast<const f32x4_t*>(lp + k * plane + 4 * (int64_t)pi)
                       : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
-      const int pi = p0 + u * kRouteThreads;
+      const int pi = p0 + u * NT;
       if (pi >= nquad) continue;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -564,7 +654,7 @@ route_select_kernel(RouteKernelArgs a) {
     }
   }
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds, wacc);
+  route_epilogue<FUSED, KMAX, NT>(a, L, ld, nt, t0, blockIdx.x, a.logits_out != nullptr);
 }
 
 // float32 x: plain dot products (small workloads), then the same epilogue.
@@ -573,11 +663,10 @@ __global__ void __launch_bounds__(kRouteThreads)
 route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* __restrict__ w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int N = a.N, d = a.d, ld = N + 1;
-  float* sl = reinterpret_cast<float*>(smem_raw);
-  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
+  const EpiLds L = epi_lds(smem_raw, N);
+  float* sl = L.sl;
   if (FUSED)
-    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) L.cnt[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) {
@@ -592,26 +681,23 @@ route_simt_kernel(RouteKernelArgs a, const float* __restrict__ xf, const float* 
     sl[tl * ld + j] = (float)acc;
   }
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds,
-                              wacc);
+  route_epilogue<FUSED, KMAX, kRouteThreads>(a, L, ld, nt, t0, blockIdx.x, a.logits_out != nullptr);
 }
 
 template <bool FUSED, int KMAX>
-__global__ void __launch_bounds__(kRouteThreads)
+__global__ void __launch_bounds__(select_threads<KMAX>())
 route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int N = a.N, ld = N + 1;
-  float* sl = reinterpret_cast<float*>(smem_raw);
-  double* wacc = reinterpret_cast<double*>(sl + ((kRouteBT * ld + 1) & ~1));
-  int* cnt_lds = reinterpret_cast<int*>(wacc + (FUSED ? epi_doubles(N) : 0));
+  const EpiLds L = epi_lds(smem_raw, N);
+  float* sl = L.sl;
   if (FUSED)
-    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) cnt_lds[i] = 0;
+    for (int i = threadIdx.x; i < N + a.K + 1; i += blockDim.x) L.cnt[i] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kRouteBT;
   const int nt = (int)min<int64_t>(kRouteBT, a.T - t0);
   for (int i = threadIdx.x; i < nt * ld; i += blockDim.x) sl[i] = logits[t0 * ld + i];
   __syncthreads();
-  route_epilogue<FUSED, KMAX>(a, sl, ld, nt, t0, blockIdx.x, a.logits_out != nullptr, cnt_lds,
-                              wacc);
+  route_epilogue<FUSED, KMAX, select_threads<KMAX>()>(a, L, ld, nt, t0, blockIdx.x, a.logits_out != nullptr);
 }
 
 // 32-expert tiles per scoring workgroup: all of them when N <= 64, else pairs.
@@ -650,9 +736,7 @@ size_t route_ws_bytes(int64_t T, int N, int d) {
 
 // LDS of the selection epilogue, and of the scoring kernel (stages) when mfma
 static size_t route_lds_bytes(const RouteArgs& r, bool mfma) {
-  const int ld = r.N + 1;
-  size_t b = (size_t)((kRouteBT * ld + 1) & ~1) * sizeof(float);
-  if (r.fused) b += (size_t)epi_doubles(r.N) * sizeof(double) + (size_t)(r.N + r.K + 1) * sizeof(int);
+  size_t b = epi_lds_bytes(r.N, r.K, r.fused);
   if (mfma) b = std::max(b, route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds);
   return b;
 }
@@ -688,7 +772,7 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
 #define MOE_LOGITS_LAUNCH(F_, KM_)                                                        \
   do {                                                                                    \
     allow_lds(route_from_logits_kernel<F_, KM_>, lds);                                    \
-    route_from_logits_kernel<F_, KM_><<<nblk, kRouteThreads, lds, stream>>>(a, r.logits_in); \
+    route_from_logits_kernel<F_, KM_><<<nblk, select_threads<KM_>(), lds, stream>>>(a, r.logits_in); \
   } while (0)
 #define MOE_SIMT_LAUNCH(F_, KM_)                                                          \
   do {                                                                                    \
@@ -715,7 +799,7 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
         route_tile_kernel<false, 2, 2><<<grid, kRouteThreads, lds_score, stream>>>(a);    \
       }                                                                                   \
       allow_lds(route_select_kernel<F_, KM_>, lds_select);                                \
-      route_select_kernel<F_, KM_><<<nblk, kRouteThreads, lds_select, stream>>>(a);       \
+      route_select_kernel<F_, KM_><<<nblk, select_threads<KM_>(), lds_select, stream>>>(a); \
     }                                                                                     \
   } while (0)
   if (r.logits_in) {
