@@ -19,8 +19,9 @@
 //    exact in float32, and an fp32 weight splits exactly into three bf16 parts
 //    (hi + mid + lo, each the bf16 rounding of what is left), so three bf16
 //    MFMAs give the products exactly at MFMA rate instead of the slower fp32
-//    path. MFMA partial sums over 32-wide K blocks are accumulated in fp64,
-//    which keeps the logits within a few 1e-7 of the exact value (plain fp32
+//    path. Each wavefront's float32 MFMA sums over 32 K columns (its half of
+//    a 64-wide K tile) are accumulated in fp64, which keeps the logits within
+//    a few 1e-7 of the exact value (plain fp32
 //    accumulation over d = 2048 terms drifts by a few 1e-6, too close to the
 //    1e-5 near-tie margin of routing parity). The null row is an fp64 dot
 //    product on the vector ALUs.
@@ -346,9 +347,11 @@ __device__ void route_epilogue(const RouteKernelArgs& a, const EpiLds& L, int ld
 // global->LDS loads, S-1 of them in flight. Each weight fragment is split into its
 // bf16 (hi, mid, lo) parts in registers right before its three MFMAs (hardware
 // round-to-nearest-even; the two subtractions are exact), so the float32 weight is
-// read as it is. Wavefront w multiplies token half w & 1 over the 16-wide K steps
-// 2 (w >> 1) and 2 (w >> 1) + 1 of each tile; the two K halves are added in a
-// fixed order at the end. Group 0 also computes the null row as an fp64 dot
+// read as it is. Each wavefront covers one K half (16-wide K steps 2 kp and
+// 2 kp + 1 of each tile): with two expert tiles wavefront w takes tile w >> 1 and
+// K half w & 1 for both token halves, so each weight fragment is split once per
+// workgroup; with one expert tile it takes token half w & 1 and K half w >> 1. The
+// two K halves are added in a fixed order at the end. Group 0 also computes the null row as an fp64 dot
 // product. With one workgroup per token tile (many tokens, N <= 64) the logits go
 // straight to LDS for the selection epilogue. Otherwise each workgroup writes its
 // partial logits and route_select_kernel adds the K splits in order and selects:
@@ -380,6 +383,18 @@ __device__ __forceinline__ int wt_off(int row, int unit) {   // weights: floats,
 
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
+// float32 values of eight packed bf16 (element 2 i is the low half of word i)
+__device__ __forceinline__ f32x8_t bf16x8_to_f32(bf16x8_t b) {
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, b);
+  f32x8_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = __uint_as_float(w[i] << 16);
+    r[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  return r;
+}
+
 template <bool FUSED, int KMAX, int ETW>
 __global__ void __launch_bounds__(kRouteThreads)
 route_tile_kernel(RouteKernelArgs a) {
@@ -401,7 +416,10 @@ route_tile_kernel(RouteKernelArgs a) {
   const int nt = (int)min<int64_t>(kRouteBT, T - t0);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int half = lane >> 5, l32 = lane & 31;
-  const int th = wave & 1, kp = wave >> 1;
+  constexpr int NTH = ETW;  // token halves per wavefront
+  const int kp = ETW == 2 ? (wave & 1) : (wave >> 1);
+  const int et = ETW == 2 ? (wave >> 1) : 0;     // expert tile of the group
+  const int th0 = ETW == 2 ? 0 : (wave & 1);     // first token half
   const int nk_all = (d + 63) / 64;
   const int per = (nk_all + KS - 1) / KS;       // the host makes every split non-empty
   const int kt0 = ks * per;
@@ -446,11 +464,11 @@ route_tile_kernel(RouteKernelArgs a) {
                stage + TL::x_elems + TL::w_elems);
   };
 
-  double acc[ETW][16];
+  double acc[NTH][16];
 #pragma unroll
-  for (int u = 0; u < ETW; ++u)
+  for (int h = 0; h < NTH; ++h)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[u][i] = 0.0;
+    for (int i = 0; i < 16; ++i) acc[h][i] = 0.0;
   const bool do_null = eg == 0;
   const int nl_tok = tid >> 2, nl_part = tid & 3;
   double nacc = 0.0;
@@ -462,30 +480,30 @@ route_tile_kernel(RouteKernelArgs a) {
     const bf16_t* xs = stages + st * TL::stage;
     const float* ws = reinterpret_cast<const float*>(xs + TL::x_elems);
     const float* wn = reinterpret_cast<const float*>(xs + TL::x_elems + TL::w_elems);
-    f32x16_t part[ETW];
+    f32x16_t part[NTH];
 #pragma unroll
-    for (int u = 0; u < ETW; ++u) part[u] = f32x16_t{};
+    for (int h = 0; h < NTH; ++h) part[h] = f32x16_t{};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int ch = (2 * kp + s2) * 2 + half;
       const bool dead = decltype(tail)::value && ch * 8 >= kvalid;
-      bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off(th * 32 + l32, ch)]);
-      if (dead) af = bf16x8_t{};
+      const int wr = 32 * et + l32;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch)]);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch + 1)]);
+      f32x8_t v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      if (dead) v = f32x8_t{};
+      const bf16x8_t b0 = __builtin_convertvector(v, bf16x8_t);
+      const f32x8_t r1 = v - bf16x8_to_f32(b0);
+      const bf16x8_t b1 = __builtin_convertvector(r1, bf16x8_t);
+      const f32x8_t r2 = r1 - bf16x8_to_f32(b1);
+      const bf16x8_t b2 = __builtin_convertvector(r2, bf16x8_t);
 #pragma unroll
-      for (int u = 0; u < ETW; ++u) {
-        const int wr = 32 * u + l32;
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch)]);
-        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(&ws[wt_off(wr, 2 * ch + 1)]);
-        f32x8_t v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        if (dead) v = f32x8_t{};
-        const bf16x8_t b0 = __builtin_convertvector(v, bf16x8_t);
-        const f32x8_t r1 = v - __builtin_convertvector(b0, f32x8_t);
-        const bf16x8_t b1 = __builtin_convertvector(r1, bf16x8_t);
-        const f32x8_t r2 = r1 - __builtin_convertvector(b1, f32x8_t);
-        const bf16x8_t b2 = __builtin_convertvector(r2, bf16x8_t);
-        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part[u], 0, 0, 0);
-        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part[u], 0, 0, 0);
-        part[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part[u], 0, 0, 0);
+      for (int h = 0; h < NTH; ++h) {
+        bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&xs[rt_off((th0 + h) * 32 + l32, ch)]);
+        if (dead) af = bf16x8_t{};
+        part[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b2, part[h], 0, 0, 0);
+        part[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, part[h], 0, 0, 0);
+        part[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, part[h], 0, 0, 0);
       }
     }
     if (do_null) {
@@ -505,9 +523,9 @@ route_tile_kernel(RouteKernelArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < ETW; ++u)
+    for (int h = 0; h < NTH; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[u][i] += (double)part[u][i];
+      for (int i = 0; i < 16; ++i) acc[h][i] += (double)part[h][i];
   };
 
 #pragma unroll
@@ -538,9 +556,9 @@ route_tile_kernel(RouteKernelArgs a) {
   double* red = reinterpret_cast<double*>(smem_raw + kRouteRedOff);  // [2][ETW][16][64]
   if (kp == 1) {
 #pragma unroll
-    for (int u = 0; u < ETW; ++u)
+    for (int h = 0; h < NTH; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[((th * ETW + u) * 16 + i) * kWave + lane] = acc[u][i];
+      for (int i = 0; i < 16; ++i) red[(((th0 + h) * ETW + et) * 16 + i) * kWave + lane] = acc[h][i];
   }
   const bool direct = !a.partials;  // then EG == 1 and KS == 1
   if (FUSED && direct)
@@ -549,12 +567,13 @@ route_tile_kernel(RouteKernelArgs a) {
   if (direct) {
     // the tile's logits go to LDS, then the selection epilogue
     if (kp == 0) {
+      const int e = et * 32 + l32;
 #pragma unroll
-      for (int u = 0; u < ETW; ++u) {
-        const int e = u * 32 + l32;
+      for (int h = 0; h < NTH; ++h) {
+        const int th = th0 + h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
+          const double v = acc[h][i] + red[((th * ETW + et) * 16 + i) * kWave + lane];
           const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
           if (e < N && tr < nt) sl[tr * ld + e] = (float)v;
         }
@@ -578,12 +597,13 @@ route_tile_kernel(RouteKernelArgs a) {
   const int64_t plane = (T * ld + 3) & ~int64_t(3);
   float* lp = a.lpart + ks * plane + t0 * ld;
   if (kp == 0) {
+    const int e = (ETW * eg + et) * 32 + l32;
 #pragma unroll
-    for (int u = 0; u < ETW; ++u) {
-      const int e = (ETW * eg + u) * 32 + l32;
+    for (int h = 0; h < NTH; ++h) {
+      const int th = th0 + h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const double v = acc[u][i] + red[((th * ETW + u) * 16 + i) * kWave + lane];
+        const double v = acc[h][i] + red[((th * ETW + et) * 16 + i) * kWave + lane];
         const int tr = th * 32 + 8 * (i / 4) + 4 * half + (i % 4);
         if (e < N && tr < nt) lp[tr * ld + e] = (float)v;
       }
