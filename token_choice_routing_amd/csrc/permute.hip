@@ -56,83 +56,94 @@ permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int
 // copies share P_null), f_i = counts_i / T, L_bal = N sum_{i < N+M} f_i P_i,
 // L_z = mean_t lse_t^2, plus mean r. A token with r chosen reals fills null copies
 // N .. N + K - r - 1, so copy N + j is used by the tokens with r < K - j.
-// Called by every thread of one workgroup; off[0..N] holds the expert offsets.
-__device__ void finalize_tiles(const AuxTiles& a, int tiles, int64_t T, int N, int M, int K,
-                               const int* off, double* part, double* tot, int* rsum,
-                               double* terms) {
-  const int C = N + 3;
-  const int G = max(1, (int)blockDim.x / C);
+// Called by every thread of one workgroup. All three per-tile tables (sums, expert
+// histograms, r histograms) are added column by column in one pass, so their loads
+// are in flight together. LDS: part [G][N + 3], tot [N + 3], terms [N + M] (doubles),
+// then cnt [N] and rsum [K + 1] (ints).
+__device__ void finalize_tiles(const AuxTiles& a, const int32_t* __restrict__ chunk_hist, int tiles,
+                               int64_t T, int N, int M, int K, unsigned char* lds) {
+  const int C = N + 3, R = K + 1, Q = C + N + R;
+  const int G = max(1, (int)blockDim.x / Q);
   const int per = (tiles + G - 1) / G;
-  for (int r = threadIdx.x; r <= K; r += blockDim.x) rsum[r] = 0;
+  double* part = reinterpret_cast<double*>(lds);
+  double* tot = part + G * C;
+  double* terms = tot + C;
+  int* cnt = reinterpret_cast<int*>(terms + N + M);
+  int* rsum = cnt + N;
+  for (int i = threadIdx.x; i < N + R; i += blockDim.x) cnt[i] = 0;  // cnt, then rsum
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x) {
-    // item (c, g) adds tiles [g per, (g + 1) per) of column c, eight loads at a time
-    const int c = idx % C, g = idx / C;
-    {
-      double s = 0.0;
-      const int t1 = min(tiles, (g + 1) * per);
-      for (int tb = g * per; tb < t1; tb += 8) {
-        double v[8];
+  for (int idx = threadIdx.x; idx < G * Q; idx += blockDim.x) {
+    // item (column q, group g) adds tiles [g per, (g + 1) per) of its column, 16
+    // loads at a time
+    const int q = idx % Q, g = idx / Q;
+    const int ta = g * per, tb = min(tiles, (g + 1) * per);
+    if (q < C) {
+      double sum = 0.0;
+#pragma unroll 2
+      for (int t = ta; t < tb; t += 16) {
+        double v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = tb + u < t1 ? a.tstats[(int64_t)(tb + u) * C + c] : 0.0;
+        for (int u = 0; u < 16; ++u) v[u] = t + u < tb ? a.tstats[(int64_t)(t + u) * C + q] : 0.0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < 16; ++u) sum += v[u];
       }
-      part[g * C + c] = s;
-    }
-  }
-  {
-    // r histogram: integer sums, any order
-    const int R = K + 1, GR = max(1, (int)blockDim.x / R), pr = (tiles + GR - 1) / GR;
-    const int r = threadIdx.x % R, g = threadIdx.x / R;
-    if (g < GR) {
-      int s = 0;
-      const int t1 = min(tiles, (g + 1) * pr);
-      for (int tb = g * pr; tb < t1; tb += 8) {
-        int v[8];
+      part[g * C + q] = sum;
+    } else {
+      // integer sums: any order
+      const bool hist = q < C + N;
+      const int col = hist ? q - C : q - C - N, width = hist ? N : R;
+      const int32_t* src = hist ? chunk_hist : a.rhist;
+      int sum = 0;
+#pragma unroll 2
+      for (int t = ta; t < tb; t += 16) {
+        int v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = tb + u < t1 ? a.rhist[(int64_t)(tb + u) * R + r] : 0;
+        for (int u = 0; u < 16; ++u) v[u] = t + u < tb ? src[(int64_t)(t + u) * width + col] : 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < 16; ++u) sum += v[u];
       }
-      if (s) atomicAdd(&rsum[r], s);
+      if (sum) atomicAdd(&cnt[q - C], sum);  // cnt[col] or rsum[col]
     }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    double s = 0.0;
-    for (int g = 0; g < G; ++g) s += part[g * C + c];
-    tot[c] = s;
+    double sum = 0.0;
+    for (int g = 0; g < G; ++g) sum += part[g * C + c];
+    tot[c] = sum;
   }
   __syncthreads();
   const int P = N + M;
   const double invT = 1.0 / (double)T;
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    int cnt = 0;
+    int c = 0;
     if (i < N) {
-      cnt = off[i + 1] - off[i];
+      c = cnt[i];
     } else {
       const int j = i - N;
-      for (int r = 0; r < K - j; ++r) cnt += rsum[r];
+      for (int r = 0; r < K - j; ++r) c += rsum[r];
     }
     const double Pi = tot[i < N ? i : N] * invT;
-    const double fi = (double)cnt * invT;
+    const double fi = (double)c * invT;
     terms[i] = fi * Pi;
     if (a.f) a.f[i] = (float)fi;
     if (a.P) a.P[i] = (float)Pi;
-    if (a.counts) a.counts[i] = cnt;
+    if (a.counts) a.counts[i] = c;
   }
   __syncthreads();
   if (threadIdx.x < kWave) {
-    double s = 0.0;
-    for (int i = threadIdx.x; i < P; i += kWave) s += terms[i];
-    s = wave_sum_double(s);
+    double sum = 0.0;
+    for (int i = threadIdx.x; i < P; i += kWave) sum += terms[i];
+    sum = wave_sum_double(sum);
     if (threadIdx.x == 0 && a.scalars) {
-      a.scalars[0] = (float)((double)N * s);
+      a.scalars[0] = (float)((double)N * sum);
       a.scalars[1] = (float)(tot[N + 1] * invT);
       a.scalars[2] = (float)(tot[N + 2] * invT);
     }
   }
+}
+
+__host__ __device__ constexpr int finalize_groups(int N, int K, int threads) {
+  return (threads / ((N + 3) + N + (K + 1))) > 1 ? threads / ((N + 3) + N + (K + 1)) : 1;
 }
 
 // Counting sort of the token slots, one launch. Workgroup c < nchunks owns the
@@ -153,61 +164,120 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
   constexpr int nw = kPermThreads / kWave;
   const int nkeys = N + 1;
   const int c = blockIdx.x;
-  const bool stats_block = STATS && c == nchunks;
-  // LDS: off [N + 1], base [N] ints; then the reduction scratch and the scatter's
-  // per-wave counts, or the statistics scratch
+  if (STATS && c == nchunks) {
+    finalize_tiles(aux, chunk_hist, nchunks, T, N, M, K, smem_raw);
+    return;
+  }
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int gpw = (K + nw - 1) / nw;  // groups (of 64 slots) per wave
+  const int64_t fc = (int64_t)c * kTokChunk * K;
+  // Loads first: this chunk's slots, then the first rows of the chunk histograms
+  // (thread (column quad q4, row phase r) adds rows r, r + RP, ...), so both
+  // latencies overlap and the ranking below waits only for the slots.
+  int kraw[kMaxGroupsPerWave];
+#pragma unroll
+  for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
+    const int grp = wave * gpw + gi;
+    const int64_t f = fc + (int64_t)grp * kWave + lane;
+    kraw[gi] = (gi < gpw && grp < K && f < TK) ? topk_idx[f] : -1;
+  }
+  const int N4 = (N + 3) / 4, RP = max(1, kPermThreads / N4);
+  const int q4 = threadIdx.x % N4, r = threadIdx.x / N4;
+  int v0[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = r + u * RP, e = 4 * q4 + j;
+      v0[u][j] = (r < RP && row < nchunks && e < N) ? chunk_hist[(int64_t)row * N + e] : 0;
+    }
+  // LDS: off [N + 1], base [N], per-wave counts [nw][N + 1], per-wave bases [nw][N],
+  // the histogram partials [2][RP][N] (ints)
   int* off = reinterpret_cast<int*>(smem_raw);
   int* cbase = off + (N + 1);
-  int* scratch = cbase + N;
-  const int N4 = (N + 3) / 4, RP = max(1, kPermThreads / N4);
-  {
-    // totals and prefix: thread (column quad q4, row phase r) adds rows r, r + RP, ...
-    int* ptot = scratch;             // [RP][N]
-    int* ppre = scratch + RP * N;    // [RP][N]
-    const int q4 = threadIdx.x % N4, r = threadIdx.x / N4;
-    if (r < RP) {
-      int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
-      for (int rb = r; rb < nchunks; rb += 4 * RP) {
-        int v[4][4];
+  int* wcnt = cbase + N;
+  int* wbase = wcnt + nw * nkeys;
+  int* ptot = wbase + nw * N;
+  int* ppre = ptot + RP * N;
+  for (int i = threadIdx.x; i < nw * nkeys; i += blockDim.x) wcnt[i] = 0;
+  __syncthreads();
+  // rank the slots: the lanes of a wavefront holding the same expert are found with
+  // ballots over the key bits; a slot's rank counts the equal keys in lower lanes and
+  // in the wavefront's earlier groups
+  int nbits = 1;
+  while ((1 << nbits) <= N) ++nbits;  // enough bits for keys 0..N
+  int key[kMaxGroupsPerWave], lrank[kMaxGroupsPerWave];
+  int* mycnt = wcnt + wave * nkeys;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+  for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
+    key[gi] = N;
+    lrank[gi] = 0;
+    const int grp = wave * gpw + gi;
+    if (gi >= gpw || grp >= K) continue;  // uniform across the wave
+    const int64_t f = fc + (int64_t)grp * kWave + lane;
+    const int k = f < TK ? slot_key(kraw[gi], N) : N;
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (k >> b) & 1;
+      const uint64_t bal = ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int before = __popcll(peers & lanemask_lt());
+    const int prev = mycnt[k];
+    key[gi] = k;
+    lrank[gi] = prev + before;
+    if (before == 0) mycnt[k] = prev + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // expert totals over all chunks and this chunk's prefix (chunks before c)
+  if (r < RP) {
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = rb + u * RP, e = 4 * q4 + j;
-            v[u][j] = (row < nchunks && e < N) ? chunk_hist[(int64_t)row * N + e] : 0;
-          }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            tot[j] += v[u][j];
-            if (rb + u * RP < c) pre[j] += v[u][j];
-          }
-      }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = 4 * q4 + j;
-        if (e < N) {
-          ptot[r * N + e] = tot[j];
-          ppre[r * N + e] = pre[j];
+        tot[j] += v0[u][j];
+        if (r + u * RP < c) pre[j] += v0[u][j];
+      }
+    for (int rb = r + 4 * RP; rb < nchunks; rb += 4 * RP) {
+      int v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = rb + u * RP, e = 4 * q4 + j;
+          v[u][j] = (row < nchunks && e < N) ? chunk_hist[(int64_t)row * N + e] : 0;
         }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tot[j] += v[u][j];
+          if (rb + u * RP < c) pre[j] += v[u][j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * q4 + j;
+      if (e < N) {
+        ptot[r * N + e] = tot[j];
+        ppre[r * N + e] = pre[j];
       }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < N; e += kPermThreads) {
-      int t = 0, p = 0;
-      for (int rr = 0; rr < RP; ++rr) {
-        t += ptot[rr * N + e];
-        p += ppre[rr * N + e];
-      }
-      off[e] = t;      // totals for now
-      cbase[e] = p;
-    }
-    __syncthreads();
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += kPermThreads) {
+    int t = 0, p = 0;
+    for (int rr = 0; rr < RP; ++rr) {
+      t += ptot[rr * N + e];
+      p += ppre[rr * N + e];
+    }
+    off[e] = t;  // totals for now
+    cbase[e] = p;
+  }
+  __syncthreads();
   if (threadIdx.x < kWave) {
     // wave 0: exclusive scan of the per-expert totals, 4 experts per lane
-    const int lane = threadIdx.x;
     int tot[4], local = 0;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -241,51 +311,6 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
     }
   }
   __syncthreads();
-  if (stats_block) {
-    // statistics scratch after off/cbase: terms [N + M], partials [G][N + 3], totals
-    // [N + 3] (doubles, 8-byte aligned), r sums [K + 1]
-    double* terms = reinterpret_cast<double*>(smem_raw + (((2 * N + 1) * sizeof(int) + 7) / 8) * 8);
-    const int C = N + 3, G = max(1, kPermThreads / C);
-    double* spart = terms + (N + M);
-    double* stot = spart + G * C;
-    int* rsum = reinterpret_cast<int*>(stot + C);
-    finalize_tiles(aux, nchunks, T, N, M, K, off, spart, stot, rsum, terms);
-    return;
-  }
-
-  int* wcnt = scratch;               // [4][N+1] running count per wave
-  int* wbase = scratch + nw * nkeys; // [4][N]
-  for (int i = threadIdx.x; i < nw * nkeys; i += blockDim.x) wcnt[i] = 0;
-  __syncthreads();
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  int nbits = 1;
-  while ((1 << nbits) <= N) ++nbits;  // enough bits for keys 0..N
-  const int gpw = (K + nw - 1) / nw;  // groups (of 64 slots) per wave
-  const int64_t fc = (int64_t)c * kTokChunk * K;
-  int key[kMaxGroupsPerWave], lrank[kMaxGroupsPerWave];
-  int* mycnt = wcnt + wave * nkeys;
-#pragma unroll
-  for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
-    key[gi] = N;
-    lrank[gi] = 0;
-    const int grp = wave * gpw + gi;
-    if (gi >= gpw || grp >= K) continue;  // uniform across the wave
-    const int64_t f = fc + (int64_t)grp * kWave + lane;
-    const int k = f < TK ? slot_key(topk_idx[f], N) : N;
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (k >> b) & 1;
-      const uint64_t bal = ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    const int before = __popcll(peers & lanemask_lt());
-    const int prev = mycnt[k];
-    key[gi] = k;
-    lrank[gi] = prev + before;
-    if (before == 0) mycnt[k] = prev + __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
   for (int i = threadIdx.x; i < nw * N; i += blockDim.x) {
     const int w = i / N, e = i % N;
     int b = cbase[e];
@@ -293,17 +318,19 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
     wbase[w * N + e] = b;
   }
   __syncthreads();
+  const int t0 = c * kTokChunk;
 #pragma unroll
   for (int gi = 0; gi < kMaxGroupsPerWave; ++gi) {
     const int grp = wave * gpw + gi;
     if (gi >= gpw || grp >= K) continue;
-    const int64_t f = fc + (int64_t)grp * kWave + lane;
+    const int local = grp * kWave + lane;  // slot within the chunk
+    const int64_t f = fc + local;
     if (f < TK) {
       const int k = key[gi];
       if (k < N) {
         const int p = wbase[wave * N + k] + lrank[gi];
         slot_pos[f] = p;
-        if (p < max_rows) perm_token[p] = (int32_t)(f / K);  // past capacity: dropped
+        if (p < max_rows) perm_token[p] = t0 + (int)((unsigned)local / (unsigned)K);  // past capacity: dropped
       } else {
         slot_pos[f] = -1;
       }
@@ -363,13 +390,12 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const bool stats = at.tstats != nullptr;
   constexpr int nw = kPermThreads / kWave;
   const int N4 = (a.N + 3) / 4, RP = std::max(1, kPermThreads / N4);
-  const size_t head = (size_t)(2 * a.N + 1) * sizeof(int);
-  const size_t scat = std::max((size_t)2 * RP * a.N, (size_t)nw * (a.N + 1) + (size_t)nw * a.N) * sizeof(int);
-  size_t lds = head + scat;
+  size_t lds = ((size_t)(2 * a.N + 1) + (size_t)nw * (a.N + 1) + (size_t)nw * a.N + (size_t)2 * RP * a.N) *
+               sizeof(int);
   if (stats) {
-    const int C = a.N + 3, G = std::max(1, kPermThreads / C);
-    const size_t st = (head + 7) / 8 * 8 + ((size_t)(a.N + a.M) + (size_t)G * C + C) * sizeof(double) +
-                      (size_t)(a.K + 1) * sizeof(int);
+    const int C = a.N + 3, G = finalize_groups(a.N, a.K, kPermThreads);
+    const size_t st = ((size_t)G * C + C + (size_t)(a.N + a.M)) * sizeof(double) +
+                      (size_t)(a.N + a.K + 1) * sizeof(int);
     lds = std::max(lds, st);
   }
   const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);
