@@ -192,6 +192,24 @@ def test_expert_ffn_segments_bf16(lengths, d, f):
     assert (got[R:] == 3.0).all(), "rows outside the segments were written"
 
 
+@pytest.mark.parametrize("lengths,d,f", [
+    ([0, 1, 17, 0, 5], 256, 192),               # a group over 16 rows: two row blocks
+    ([3, 16, 2], 136, 72),                      # K not a multiple of 32, n_out of 16
+    ([25], 2048, 1536),
+    ([1] * 20, 1024, 768),
+    ([0, 0, 1], 64, 8),
+])
+def test_expert_ffn_few_rows(lengths, d, f):
+    """At most 32 rows per group: the skinny kernel (16 x 16 blocks, K split over
+    the wavefronts, registers only)."""
+    say(f"expert_ffn few rows lengths={lengths[:8]} d={d} d_ff={f}")
+    got, ref, R, rows = _ffn_run(lengths, d, f, "bf16", seed=d + 2 * f)
+    assert rows <= 32
+    if R:
+        assert_rows_close(got[:R], ref[:R], TOL_BF16, "segments")
+    assert (got[R:] == 3.0).all(), "rows outside the segments were written"
+
+
 def test_expert_ffn_f32():
     say("expert_ffn f32 (tiny workload shape)")
     got, ref, R, rows = _ffn_run([27, 0, 31, 26, 30, 1, 60, 38], 64, 128, "f32", seed=3)

@@ -195,6 +195,14 @@ def test_tiny_token_counts(T):
     check_full(sub_workload(generate(_small()), np.arange(T)))
 
 
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_decode_token_counts_headline_shape(T):
+    """Decode-size batches at the Qwen3-0.6B shape (few rows per expert: the
+    grouped GEMMs take the skinny path up to 32 rows per group)."""
+    say(f"decode T = {T}")
+    check_full(sub_workload(generate(CONFIGS["qwen3_0p6b_rho1"]), np.arange(T)))
+
+
 @pytest.mark.parametrize("N,M,K,T", [(100, 28, 6, 300), (255, 1, 8, 130), (24, 0, 3, 200)])
 def test_expert_counts_across_router_tilings(N, M, K, T):
     """Full layer where the router spreads a token tile over several scoring
