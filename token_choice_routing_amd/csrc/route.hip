@@ -355,7 +355,8 @@ __device__ void route_epilogue(const RouteKernelArgs& a, const EpiLds& L, int ld
 // product. With one workgroup per token tile (many tokens, N <= 64) the logits go
 // straight to LDS for the selection epilogue. Otherwise each workgroup writes its
 // partial logits and route_select_kernel adds the K splits in order and selects:
-// with few tokens, splitting K spreads the latency-bound K loop over the CUs.
+// with few tokens, splitting K spreads the latency-bound K loop over the CUs (up to
+// 16 splits of one K tile each when the batch is a single token tile).
 constexpr int kRouteRedOff = 84 * 1024;  // LDS byte offset of the K-half exchange buffer
 
 template <int ETW>
@@ -619,15 +620,16 @@ route_tile_kernel(RouteKernelArgs a) {
 // Partials path, second kernel: one workgroup per 64-token tile adds the K splits
 // of every logit in split order (fp64), adds the null biases, rounds to float32
 // and runs the selection epilogue. Each split is an fp64 sum over its K range
-// rounded once to float32: at most 4 splits, so the logit moves by a few float32
+// rounded once to float32: at most 16 splits, so the logit moves by a few float32
 // ulps of the split sums (about 1e-7 of their size), far inside the 1e-5 near-tie
-// margin, while the workgroup reads half the bytes.
-template <bool FUSED, int KMAX>
+// margin, while the workgroup reads half the bytes. MAXKS (4 or 16) bounds the
+// splits a launch may have.
+template <bool FUSED, int KMAX, int MAXKS>
 __global__ void __launch_bounds__(select_threads<KMAX>())
 route_select_kernel(RouteKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   constexpr int NT = select_threads<KMAX>();
-  constexpr int kMaxSplits = 4;
+  constexpr int kMaxSplits = MAXKS;
   const int N = a.N, ld = N + 1, KS = a.KS;
   const EpiLds L = epi_lds(smem_raw, N);
   float* sl = L.sl;
@@ -640,7 +642,7 @@ route_select_kernel(RouteKernelArgs a) {
   const float* lp = a.lpart + t0 * ld;  // t0 * ld is a multiple of 4: 16-byte aligned quads
   // element quads (4 i .. 4 i + 3), kQuads per thread at a time, every split's loads in
   // flight together; the splits are added in order
-  constexpr int kQuads = 8 * kRouteThreads / NT;
+  constexpr int kQuads = std::max(1, 8 * kRouteThreads / NT * 4 / MAXKS);
   const int nquad = (n + 3) / 4;
   for (int p0 = threadIdx.x; p0 < nquad; p0 += kQuads * NT) {
     f32x4_t v[kQuads][kMaxSplits];
@@ -738,7 +740,10 @@ static RoutePlan route_plan(int64_t T, int N, int d) {
   const int64_t ntt = std::max<int64_t>(1, (T + kRouteBT - 1) / kRouteBT);
   if (eg == 1 && ntt >= 128) return {etw, 1, 1, false};
   const int nk = (d + 63) / 64;
-  int ks = (int)std::min<int64_t>(4, std::max<int64_t>(1, (256 + ntt * eg - 1) / (ntt * eg)));
+  // one token tile: up to 16 splits (one K tile each at d = 1024); else up to 4,
+  // which keeps the selection's partial-logit reads at twice the logits
+  const int64_t cap = ntt == 1 ? 16 : 4;
+  int ks = (int)std::min<int64_t>(cap, std::max<int64_t>(1, (256 + ntt * eg - 1) / (ntt * eg)));
   ks = std::min(ks, nk);
   const int per = (nk + ks - 1) / ks;
   ks = (nk + per - 1) / per;
@@ -818,8 +823,13 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
         allow_lds(route_tile_kernel<false, 2, 2>, lds_score);                             \
         route_tile_kernel<false, 2, 2><<<grid, kRouteThreads, lds_score, stream>>>(a);    \
       }                                                                                   \
-      allow_lds(route_select_kernel<F_, KM_>, lds_select);                                \
-      route_select_kernel<F_, KM_><<<nblk, select_threads<KM_>(), lds_select, stream>>>(a); \
+      if (pl.ks <= 4) {                                                                   \
+        allow_lds(route_select_kernel<F_, KM_, 4>, lds_select);                           \
+        route_select_kernel<F_, KM_, 4><<<nblk, select_threads<KM_>(), lds_select, stream>>>(a); \
+      } else {                                                                            \
+        allow_lds(route_select_kernel<F_, KM_, 16>, lds_select);                          \
+        route_select_kernel<F_, KM_, 16><<<nblk, select_threads<KM_>(), lds_select, stream>>>(a); \
+      }                                                                                   \
     }                                                                                     \
   } while (0)
   if (r.logits_in) {
