@@ -15,7 +15,14 @@ Readings where the pages leave a step open (each is listed in the design notes):
   * the K slots of a token list its chosen reals first, by (logit desc, index
     asc), then the null copies N, N+1, ... in copy-id order;
   * with M = 0 the null row is ignored and the pool is the N reals (plain top-K);
-  * the expert FFN is SwiGLU without biases: W_down (silu(W_gate a) * W_up a).
+  * the expert FFN is SwiGLU without biases: W_down (silu(W_gate a) * W_up a);
+  * zero-compute variants ([Review] "why null rather than copy experts" table and
+    the [MoE++] zero / copy / constant experts): a null slot outputs 0 (null),
+    the token x (copy) or a vector v (constant). For copy and constant slots the
+    gate weights are a softmax over all K chosen pool entries, null slots taking
+    the null logit, since a renormalisation over the reals alone would give the
+    null slots weight 0 and the layer could not become (1 - rho) x + rho y_dense
+    in expectation as the table says.
 """
 import numpy as np
 
@@ -117,9 +124,34 @@ def renorm_weights(logits, topk_idx, N):
     return w
 
 
-def route(logits, N, M, K):
+def chosen_weights(logits, topk_idx, N):
+    """Weights of the copy / constant variants: a softmax over all K chosen pool
+    entries, null slots taking the effective null logit (column N), max-shifted."""
+    s = np.asarray(logits, dtype=f64)
+    T, K = topk_idx.shape
+    vals = np.where(topk_idx < N, np.take_along_axis(s, np.minimum(topk_idx, N), axis=1), s[:, N:N + 1])
+    e = np.exp(vals - vals.max(axis=1, keepdims=True)) if K else vals
+    return e / e.sum(axis=1, keepdims=True) if K else e
+
+
+def route(logits, N, M, K, null_kind="zero"):
     topk, n_real = select(logits, N, M, K)
-    return topk, renorm_weights(logits, topk, N), n_real
+    w = renorm_weights(logits, topk, N) if null_kind == "zero" else chosen_weights(logits, topk, N)
+    return topk, w, n_real
+
+
+def null_source(wl, rows=None):
+    """Rows that a null slot adds (times its weight): None for null experts, the
+    tokens x for copy experts, the vector v (broadcast) for constant experts."""
+    kind = wl.cfg.null_kind
+    if kind == "zero":
+        return None
+    if kind == "copy":
+        x = wl.values("x")
+        return x if rows is None else x[rows]
+    if kind == "constant":
+        return wl.values("null_value")
+    raise ValueError(kind)
 
 
 # ---------------------------------------------------------------- dispatch
@@ -171,17 +203,22 @@ def expert_ffn_grouped(a, offsets, w_gate, w_up, w_down):
     return out
 
 
-def combine(y_perm, slot_pos, topk_w, y_shared=None, d_model=None):
+def combine(y_perm, slot_pos, topk_w, y_shared=None, d_model=None, null_src=None):
     """y_t = E_shared(x_t) + sum_k w_tk E_{i_k}(x_t), summed in slot order
     ([Review] core formula of the token-choice layer with a shared expert); a
-    null slot adds E_null = 0."""
+    null slot adds E_null = 0, or with ``null_src`` w_tk times its row t ([T, d],
+    copy experts) or the one vector ([d], constant experts)."""
     T, K = slot_pos.shape
     d = y_perm.shape[1] if d_model is None else d_model
     y = np.zeros((T, d), dtype=f64) if y_shared is None else np.array(y_shared, dtype=f64)
+    src = None if null_src is None else np.asarray(null_src, dtype=f64)
     for k in range(K):
         p = slot_pos[:, k]
         m = p >= 0
         y[m] += topk_w[m, k][:, None] * np.asarray(y_perm, f64)[p[m]]
+        if src is not None:
+            n = ~m
+            y[n] += topk_w[n, k][:, None] * (src[n] if src.ndim == 2 else src[None, :])
     return y
 
 
@@ -225,14 +262,14 @@ def layer_forward(wl, logits=None, K=None, M=None):
     if logits is None:
         logits = router_logits(x, wl.values("w_router"), wl.null_bias, wl.null_bias_tok)
     logits = np.asarray(logits, dtype=f64)
-    topk, w, n_real = route(logits, N, M, K)
+    topk, w, n_real = route(logits, N, M, K, cfg.null_kind)
     counts, offsets, perm_token, slot_pos = permute(topk, N)
     xp = x[perm_token]
     yp = expert_ffn_grouped(xp, offsets, wl.w_gate, wl.w_up, wl.w_down)
     ys = None
     if cfg.d_ff_shared:
         ys = swiglu_ffn(x, wl.ws_gate, wl.ws_up, wl.ws_down)
-    y = combine(yp, slot_pos, w, ys, d_model=cfg.d_model)
+    y = combine(yp, slot_pos, w, ys, d_model=cfg.d_model, null_src=null_source(wl))
     aux = aux_stats(logits, topk, N, M, K)
     return dict(logits=logits, topk_idx=topk, topk_w=w, n_real=n_real, counts=counts,
                 offsets=offsets, perm_token=perm_token, slot_pos=slot_pos, x_perm=xp,
@@ -259,7 +296,7 @@ def layer_dense(wl, logits=None, K=None, M=None, tokens=None):
         logits = router_logits(xs, wl.values("w_router"), wl.null_bias, btok)
     else:
         logits = np.asarray(logits, dtype=f64)[rows]
-    topk, w, _ = route(logits, N, M, K)
+    topk, w, _ = route(logits, N, M, K, cfg.null_kind)
     G = np.zeros((len(rows), N), dtype=f64)
     for k in range(K):
         real = topk[:, k] < N
@@ -267,6 +304,10 @@ def layer_dense(wl, logits=None, K=None, M=None, tokens=None):
     y = np.zeros((len(rows), cfg.d_model), dtype=f64)
     if cfg.d_ff_shared:
         y += swiglu_ffn(xs, wl.ws_gate, wl.ws_up, wl.ws_down)
+    src = null_source(wl, rows)
+    if src is not None:
+        g_null = (w * (topk >= N)).sum(axis=1)  # total weight of the null slots
+        y += g_null[:, None] * (src if src.ndim == 2 else src[None, :])
     for e in range(N):
         used = G[:, e] != 0
         if used.any():

@@ -133,3 +133,73 @@ def test_stored_calibration_reproduces_targets():
             vT = int(cfg.vision_frac * cfg.T)
             assert abs((1 - r[:vT].mean() / cfg.top_k) - 0.70) <= 0.01
             assert abs((1 - r[vT:].mean() / cfg.top_k) - 0.30) <= 0.01
+
+
+# ---------------------------------------------------------------- copy / constant null slots
+def _all_null(kind):
+    """Every slot null: a large null bias with M >= K."""
+    wl = generate(_small_cfg(null_kind=kind, n_null=6, top_k=3))
+    wl.null_bias = 1.0e4
+    return wl
+
+
+def test_copy_all_null_gives_token_plus_shared():
+    """All K slots null with copy experts: K equal weights 1/K, so y = x + E_shared(x)."""
+    wl = _all_null("copy")
+    out = O.layer_forward(wl)
+    assert (out["n_real"] == 0).all()
+    np.testing.assert_allclose(out["topk_w"], 1.0 / 3.0, rtol=1e-15)
+    x = wl.values("x")
+    ref = x + O.swiglu_ffn(x, wl.ws_gate, wl.ws_up, wl.ws_down)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_constant_all_null_gives_vector_plus_shared():
+    wl = _all_null("constant")
+    out = O.layer_forward(wl)
+    x = wl.values("x")
+    ref = wl.values("null_value")[None, :] + O.swiglu_ffn(x, wl.ws_gate, wl.ws_up, wl.ws_down)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_zero_kind_all_null_gives_shared_only():
+    wl = _all_null("zero")
+    out = O.layer_forward(wl)
+    assert (out["topk_w"] == 0).all()
+    x = wl.values("x")
+    np.testing.assert_allclose(out["y"], O.swiglu_ffn(x, wl.ws_gate, wl.ws_up, wl.ws_down), rtol=1e-13)
+
+
+def test_copy_equal_logits_is_one_minus_rho_x_plus_rho_mean():
+    """All logits equal (router weights 0, null bias 0), M < K: the null logit wins
+    every tie, so each token takes r = K - M reals (experts 0..r-1 by the index
+    order) and M null copies, all with weight 1/K. Copy experts then give
+    y = (1 - rho) x + rho * mean_{e < r} E_e(x) + E_shared(x) with rho = r / K,
+    the table's (1 - rho) x + rho y_dense, exactly."""
+    K, M = 4, 1
+    wl = generate(_small_cfg(null_kind="copy", n_null=M, top_k=K, n_experts=6))
+    wl.w_router = np.zeros_like(wl.w_router)
+    wl.null_bias = 0.0
+    out = O.layer_forward(wl)
+    r = K - M
+    assert (out["n_real"] == r).all()
+    np.testing.assert_allclose(out["topk_w"], 1.0 / K, rtol=1e-15)
+    x = wl.values("x")
+    rho = r / K
+    dense = sum(O.swiglu_ffn(x, wl.w_gate[e], wl.w_up[e], wl.w_down[e]) for e in range(r)) / r
+    ref = (1 - rho) * x + rho * dense + O.swiglu_ffn(x, wl.ws_gate, wl.ws_up, wl.ws_down)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    # the dense form agrees
+    yd, _, _ = O.layer_dense(wl)
+    np.testing.assert_allclose(yd, out["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_chosen_weights_are_pool_softmax_over_the_chosen():
+    """Copy-variant weights: softmax over the K chosen pool entries (null slots at
+    the null logit), checked on a hand-made row."""
+    s = np.array([[2.0, 0.5, 1.0, 1.5]])          # N = 3 reals, null logit 1.5
+    topk, n_real = O.select(s, 3, 2, 3)           # reals 2.0 (e0) beat null; then null, null
+    assert n_real[0] == 1 and list(topk[0]) == [0, 3, 4]
+    w = O.chosen_weights(s, topk, 3)[0]
+    e = np.exp(np.array([2.0, 1.5, 1.5]) - 2.0)
+    np.testing.assert_allclose(w, e / e.sum(), rtol=1e-15)

@@ -36,6 +36,7 @@ class Config:
     vision_frac: float = 0.0
     seed: int = 0
     note: str = ""
+    null_kind: str = "zero"  # output of a null slot: "zero", "copy" (the token) or "constant" (a vector)
 
     @property
     def rho_nominal(self) -> float:

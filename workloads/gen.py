@@ -19,7 +19,7 @@ from .configs import Config
 
 _TID = {"x": 1, "w_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
         "ws_gate": 6, "ws_up": 7, "ws_down": 8,
-        "vision_basis": 9, "vision_z": 10, "vision_noise": 11}
+        "vision_basis": 9, "vision_z": 10, "vision_noise": 11, "null_value": 12}
 
 BIAS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "null_bias.json")
 
@@ -91,6 +91,7 @@ class Workload:
     ws_gate: Optional[np.ndarray] = None  # [d_ffs, d]
     ws_up: Optional[np.ndarray] = None
     ws_down: Optional[np.ndarray] = None  # [d, d_ffs]
+    null_value: Optional[np.ndarray] = None  # [d] the constant expert's vector (null_kind "constant")
 
     def values(self, name: str) -> Optional[np.ndarray]:
         """float64 copy of the exact stored values of one tensor."""
@@ -141,4 +142,6 @@ def generate(cfg: Config, experts: bool = True, bias: bool = True, T: Optional[i
             wl.ws_gate = _normal(cfg.seed, "ws_gate", (fs, d), s, dt)
             wl.ws_up = _normal(cfg.seed, "ws_up", (fs, d), s, dt)
             wl.ws_down = _normal(cfg.seed, "ws_down", (d, fs), s, dt)
+    if cfg.null_kind == "constant":
+        wl.null_value = _normal(cfg.seed, "null_value", (cfg.d_model,), 1.0, dt)
     return wl
