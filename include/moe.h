@@ -62,6 +62,14 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* What a null slot outputs (paper review section 3 compares null and copy
+ * experts; the MoE++ page lists zero, copy and constant zero-compute experts).
+ * MOE_NULL_ZERO: 0, and the weights are renormalised over the chosen reals.
+ * MOE_NULL_COPY: the token x. MOE_NULL_CONSTANT: a vector v [d_model].
+ * For copy and constant the weights are a softmax over all K chosen pool
+ * entries, null slots taking the effective null logit. */
+typedef enum { MOE_NULL_ZERO = 0, MOE_NULL_COPY = 1, MOE_NULL_CONSTANT = 2 } moe_null_kind;
+
 typedef struct {
   int64_t T;           /* tokens */
   int32_t d_model;
@@ -71,6 +79,7 @@ typedef struct {
   int32_t d_ff;        /* routed expert hidden size */
   int32_t d_ff_shared; /* shared expert hidden size, 0 = no shared expert */
   int32_t dtype;       /* moe_dtype */
+  int32_t null_kind;   /* moe_null_kind */
 } moe_dims;
 
 /* Which workspace size moe_workspace_bytes() returns. */
@@ -88,7 +97,9 @@ typedef void* moe_stream; /* hipStream_t */
  *   topk_idx[t, 0..r-1] = the r largest real logits, by (value desc, index asc)
  *   topk_idx[t, r..K-1] = null copies N, N+1, ... (lowest copy ids first)
  *   topk_w = softmax over the chosen real logits (computed in float64 from the
- *            float32 logits, rounded once); 0 on null slots.
+ *            float32 logits, rounded once); 0 on null slots. With null_kind
+ *            MOE_NULL_COPY or MOE_NULL_CONSTANT: softmax over all K chosen
+ *            entries, null slots at the effective null logit.
  *   n_real[t] = r.
  * x: [T][d_model] dtype; w_router: [N+1][d_model] float32.
  * logits_in: optional [T][N+1] float32 whose column N is already the effective
@@ -173,14 +184,18 @@ moe_status moe_grouped_gemm(const moe_dims* dims, int32_t op, int32_t n_groups, 
 
 /*
  * moe_combine -- y_t = y_shared_t + sum_k topk_w[t,k] * y_perm[slot_pos[t,k]]
- * (paper review section 3, core formula; a null slot contributes E_null = 0).
- * Summed in slot order in float32 with one rounding to dtype; no atomics, so
- * the result is bitwise reproducible. Slots with slot_pos outside
- * [0, T*min(K,N)) are skipped. y_shared [T][d] float32, may be NULL (no shared
- * expert). y_perm: [T*min(K,N)][d] float32; y: [T][d] dtype.
+ * (paper review section 3, core formula). A null slot (slot_pos = -1) adds
+ * nothing with null_kind MOE_NULL_ZERO, topk_w[t,k] * null_src[t] with
+ * MOE_NULL_COPY (null_src = x, [T][d] dtype) and topk_w[t,k] * null_src with
+ * MOE_NULL_CONSTANT (null_src = v, [d] dtype); null_src is required for those
+ * two and ignored otherwise. Summed in slot order in float32 with one rounding
+ * to dtype; no atomics, so the result is bitwise reproducible. Other slots with
+ * slot_pos outside [0, T*min(K,N)) are skipped. y_shared [T][d] float32, may be
+ * NULL (no shared expert). y_perm: [T*min(K,N)][d] float32; y: [T][d] dtype.
  */
 moe_status moe_combine(const moe_dims* dims, const void* y_perm, const int32_t* slot_pos,
-                       const float* topk_w, const void* y_shared, void* y, moe_stream stream);
+                       const float* topk_w, const void* y_shared, const void* null_src, void* y,
+                       moe_stream stream);
 
 /*
  * moe_aux_stats -- load-balance and z-loss statistics over the N+M pool
@@ -212,6 +227,8 @@ typedef struct {
   const void* ws_gate;         /* [d_ff_shared][d_model] or NULL when d_ff_shared = 0 */
   const void* ws_up;           /* [d_ff_shared][d_model] */
   const void* ws_down;         /* [d_model][d_ff_shared] */
+  const void* null_value;      /* [d_model] dtype, the constant expert's vector
+                                  (null_kind MOE_NULL_CONSTANT), else unused */
 } moe_layer_params;
 
 /* Optional device outputs of moe_layer_forward; any member may be NULL. */

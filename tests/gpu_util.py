@@ -66,9 +66,9 @@ def empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda")
 
 
-def route_from_logits(logits_f32, N, M, K):
+def route_from_logits(logits_f32, N, M, K, null_kind=0):
     T = logits_f32.shape[0]
-    dims = tcr.make_dims(T, 64, N, M, K, 64, 0, tcr.MOE_F32)
+    dims = tcr.make_dims(T, 64, N, M, K, 64, 0, tcr.MOE_F32, null_kind)
     topk = empty((T, K), torch.int32)
     w = empty((T, K), torch.float32)
     nr = empty((T,), torch.int32)

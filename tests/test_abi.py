@@ -52,6 +52,7 @@ def test_workspace_sizes_cover_the_worst_case():
 BAD_DIMS = [
     dict(T=-1), dict(n_experts=0), dict(n_null=-1), dict(top_k=0), dict(top_k=17, n_null=8),
     dict(n_null=0, top_k=9), dict(d_model=12), dict(d_ff=4), dict(d_ff_shared=-8), dict(dtype=7),
+    dict(null_kind=3), dict(null_kind=-1),
 ]
 UNSUPPORTED_DIMS = [dict(n_experts=256, top_k=2), dict(top_k=33, n_null=64), dict(n_null=5000),
                     dict(T=1 << 30, top_k=2)]
@@ -74,7 +75,7 @@ def test_invalid_dims_rejected(lib, kw):
 @pytest.mark.parametrize("kw", UNSUPPORTED_DIMS)
 def test_unsupported_dims_rejected(lib, kw):
     d = _dims(**kw)
-    st = lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None)
+    st = lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None)
     assert st == MOE_ERR_UNSUPPORTED
 
 
@@ -87,8 +88,8 @@ def test_null_and_misaligned_pointers(lib):
     assert lib.moe_route(b, None, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
     assert lib.moe_permute(b, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
     assert lib.moe_permute(b, FAKE, MIS, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == MOE_ERR_ALIGN
-    assert lib.moe_combine(b, FAKE, FAKE, FAKE, MIS, FAKE, None) == MOE_ERR_ALIGN
-    assert lib.moe_combine(b, None, FAKE, FAKE, None, FAKE, None) == MOE_ERR_ARG
+    assert lib.moe_combine(b, FAKE, FAKE, FAKE, MIS, None, FAKE, None) == MOE_ERR_ALIGN
+    assert lib.moe_combine(b, None, FAKE, FAKE, None, None, FAKE, None) == MOE_ERR_ARG
     assert lib.moe_aux_stats(b, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, None) == MOE_ERR_ARG
     assert lib.moe_expert_ffn(b, 0, 64, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_ARG
     assert lib.moe_expert_ffn(b, 2, 64, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_ARG
@@ -96,6 +97,13 @@ def test_null_and_misaligned_pointers(lib):
     p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, None, None, None, None)
     assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
     assert lib.moe_layer_forward(b, None, FAKE, None, FAKE, big, None) == MOE_ERR_ARG
+    # copy / constant null slots: combine needs the null source, the layer the vector
+    dc = _dims(null_kind=tcr.MOE_NULL_COPY)
+    assert lib.moe_combine(ctypes.byref(dc), FAKE, FAKE, FAKE, None, None, FAKE, None) == MOE_ERR_ARG
+    assert lib.moe_combine(ctypes.byref(dc), FAKE, FAKE, FAKE, None, MIS, FAKE, None) == MOE_ERR_ALIGN
+    dk = _dims(null_kind=tcr.MOE_NULL_CONSTANT)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None, None)
+    assert lib.moe_layer_forward(ctypes.byref(dk), ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
     ds = _dims(d_ff_shared=64)
     p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
     assert lib.moe_layer_forward(ctypes.byref(ds), ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
@@ -124,7 +132,7 @@ def test_empty_inputs_are_noops(lib):
     b = ctypes.byref(d)
     big = 1 << 34
     assert lib.moe_route(b, FAKE, FAKE, 0.0, None, None, None, FAKE, FAKE, None, FAKE, big, None) == MOE_OK
-    assert lib.moe_combine(b, FAKE, FAKE, FAKE, None, FAKE, None) == MOE_OK
+    assert lib.moe_combine(b, FAKE, FAKE, FAKE, None, None, FAKE, None) == MOE_OK
     assert lib.moe_permute(b, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == MOE_OK
     p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
     assert lib.moe_layer_forward(b, ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_OK

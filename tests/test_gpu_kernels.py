@@ -37,6 +37,22 @@ def test_route_from_logits_bit_exact_on_ties(N, M, K):
     say(f"  weights: {int((w != ow.astype(np.float32)).sum())} of {w.size} differ from the float32-rounded oracle")
 
 
+@pytest.mark.parametrize("N,M,K", [(8, 8, 2), (8, 3, 8), (64, 192, 8), (100, 28, 16), (64, 0, 2)])
+def test_route_weights_over_all_chosen(N, M, K):
+    """Copy / constant null slots: the weights are a softmax over all K chosen pool
+    entries (null slots at the null logit); the selection is unchanged."""
+    say(f"route weights over all K N={N} M={M} K={K}")
+    rng = np.random.default_rng(N + 7 * M + K)
+    s = (rng.standard_normal((3001, N + 1)) * 2).astype(np.float32)
+    s[5, :] = 0.0
+    topk, w, nr = route_from_logits(s, N, M, K, tcr.MOE_NULL_COPY)
+    ot, ow, onr = O.route(s.astype(np.float64), N, M, K, "copy")
+    np.testing.assert_array_equal(topk, ot)
+    np.testing.assert_array_equal(nr, onr)
+    np.testing.assert_allclose(w, ow, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+
+
 @pytest.mark.parametrize("name", list(CONFIGS))
 def test_route_from_config_logits_bit_exact(name):
     cfg = CONFIGS[name]
@@ -247,6 +263,33 @@ def test_combine(T, K, d, shared):
     got = vals(to_host(y))
     assert_rows_close(got, ref, TOL_BF16, "combine")
     # float32 accumulation + one bf16 rounding: within one bf16 half-ulp plus accumulation noise
+    assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+
+
+@pytest.mark.parametrize("kind", ["copy", "constant"])
+def test_combine_null_sources(kind):
+    """Null slots add w x (copy) or w v (constant), in slot order with the reals."""
+    say(f"combine with {kind} null slots")
+    rng = np.random.default_rng(11)
+    T, K, d, N, M = 700, 4, 512, 64, 64
+    s = rng.standard_normal((T, N + 1))
+    s[:, N] += 0.8
+    topk, w, _ = O.route(s, N, M, K, kind)
+    _, off, _, slot = O.permute(topk, N)
+    assert (slot < 0).any() and (slot >= 0).any()
+    yp = rng.standard_normal((T * K, d)).astype(np.float32)
+    ys = rng.standard_normal((T, d)).astype(np.float32)
+    src = bf16_round(rng.standard_normal((T, d) if kind == "copy" else (d,)).astype(np.float32))
+    w32 = w.astype(np.float32)
+    dims = tcr.make_dims(T, d, N, M, K, 64, 64, tcr.MOE_BF16, tcr.NULL_KINDS[kind])
+    y = empty((T, d), torch.bfloat16)
+    tcr.moe_combine(dims, to_device(yp), to_device(slot), to_device(w32), to_device(ys), y,
+                    null_src=to_device(src))
+    torch.cuda.synchronize()
+    ref = O.combine(yp.astype(np.float64), slot, w32.astype(np.float64), ys.astype(np.float64),
+                    d_model=d, null_src=vals(src))
+    got = vals(to_host(y))
+    assert_rows_close(got, ref, TOL_BF16, f"combine {kind}")
     assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
 
 

@@ -44,7 +44,7 @@ def check_routing(wl, out, rows=None, stats=True):
     cfg = wl.cfg
     N, M, K = cfg.n_experts, cfg.n_null, cfg.top_k
     gl = out["logits"]
-    ot, ow, on = O.route(gl.astype(np.float64), N, M, K)
+    ot, ow, on = O.route(gl.astype(np.float64), N, M, K, cfg.null_kind)
     np.testing.assert_array_equal(out["topk_idx"], ot)
     np.testing.assert_array_equal(out["n_real"], on)
     np.testing.assert_allclose(out["topk_w"], ow, rtol=1e-6, atol=0)
@@ -84,7 +84,7 @@ def check_full(wl, stats=True):
     ref = O.layer_forward(wl, logits=gl.astype(np.float64))
     assert_rows_close(out["y"], ref["y"], tol(wl.cfg), f"y {wl.cfg.name}")
     nul = out["n_real"] == 0
-    if nul.any() and not wl.cfg.d_ff_shared:
+    if nul.any() and not wl.cfg.d_ff_shared and wl.cfg.null_kind == "zero":
         assert (vals(out["y"])[nul] == 0).all()
     return out
 
@@ -193,6 +193,19 @@ def test_one_expert_takes_every_slot():
 def test_tiny_token_counts(T):
     say(f"T = {T}")
     check_full(sub_workload(generate(_small()), np.arange(T)))
+
+
+@pytest.mark.parametrize("kind", ["copy", "constant"])
+def test_copy_and_constant_null_slots(kind):
+    """Copy / constant zero-compute experts: full compare on a small shape and on
+    1500 tokens of the rho = 0.5 Qwen3-0.6B shape (about half the slots null)."""
+    say(f"layer with {kind} null slots")
+    out = check_full(generate(_small(null_kind=kind)))
+    assert (out["n_real"] < 4).any()
+    from dataclasses import replace
+    cfg = replace(CONFIGS["qwen3_0p6b_rho0p5"], null_kind=kind)
+    out = check_full(sub_workload(generate(cfg), np.arange(1500)))
+    assert (out["topk_w"][out["topk_idx"] >= cfg.n_experts] > 0).any()
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])

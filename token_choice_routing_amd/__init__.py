@@ -22,6 +22,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(6)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_NULL_ZERO, MOE_NULL_COPY, MOE_NULL_CONSTANT = 0, 1, 2
+NULL_KINDS = {"zero": MOE_NULL_ZERO, "copy": MOE_NULL_COPY, "constant": MOE_NULL_CONSTANT}
 MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_AUX = range(4)
 MOE_GEMM_GATE_UP, MOE_GEMM_DOWN = 0, 1
 
@@ -35,14 +37,14 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("n_null", ctypes.c_int32), ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32), ("null_kind", ctypes.c_int32)]
 
 
 class LayerParams(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("w_router", ctypes.c_void_p), ("null_bias", ctypes.c_float),
                 ("null_bias_tok", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("ws_gate", ctypes.c_void_p),
-                ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p)]
+                ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p), ("null_value", ctypes.c_void_p)]
 
 
 class AuxOut(ctypes.Structure):
@@ -67,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_permute": [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
         "moe_expert_ffn": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
                            _P, ctypes.c_size_t, _P],
-        "moe_combine": [D, _P, _P, _P, _P, _P, _P],
+        "moe_combine": [D, _P, _P, _P, _P, _P, _P, _P],
         "moe_grouped_gemm": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                              ctypes.c_int64, _P, _P, _P, _P, _P, _P],
         "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -136,14 +138,16 @@ def version() -> int:
     return load_library().moe_version()
 
 
-def make_dims(T, d_model, n_experts, n_null, top_k, d_ff, d_ff_shared=0, dtype=MOE_BF16) -> Dims:
+def make_dims(T, d_model, n_experts, n_null, top_k, d_ff, d_ff_shared=0, dtype=MOE_BF16,
+              null_kind=MOE_NULL_ZERO) -> Dims:
     return Dims(int(T), int(d_model), int(n_experts), int(n_null), int(top_k), int(d_ff),
-                int(d_ff_shared), int(dtype))
+                int(d_ff_shared), int(dtype), int(null_kind))
 
 
 def dims_from_config(cfg, T=None) -> Dims:
     return make_dims(cfg.T if T is None else T, cfg.d_model, cfg.n_experts, cfg.n_null, cfg.top_k,
-                     cfg.d_ff, cfg.d_ff_shared, MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+                     cfg.d_ff, cfg.d_ff_shared, MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
+                     NULL_KINDS[cfg.null_kind])
 
 
 def workspace_bytes(dims: Dims, which: int = MOE_WS_LAYER) -> int:
@@ -185,9 +189,11 @@ def moe_grouped_gemm(dims, op, n_groups, n_out, k_dim, rows, a, offsets, b0, b1,
                                             _ptr(b1), _ptr(out), _stream(stream)), "moe_grouped_gemm")
 
 
-def moe_combine(dims, y_perm, slot_pos, topk_w, y_shared, y, stream=None):
+def moe_combine(dims, y_perm, slot_pos, topk_w, y_shared, y, stream=None, null_src=None):
+    """null_src: the rows a null slot adds (x for copy experts, v for constant)."""
     _check(load_library().moe_combine(ctypes.byref(dims), _ptr(y_perm), _ptr(slot_pos),
-                                       _ptr(topk_w), _ptr(y_shared), _ptr(y), _stream(stream)),
+                                       _ptr(topk_w), _ptr(y_shared), _ptr(null_src), _ptr(y),
+                                       _stream(stream)),
            "moe_combine")
 
 

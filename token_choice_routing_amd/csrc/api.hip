@@ -23,6 +23,7 @@ moe_status check_dims(const moe_dims* d) {
   if (d->d_model < 8 || d->d_model % 8 || d->d_ff < 8 || d->d_ff % 8) return MOE_ERR_ARG;
   if (d->d_ff_shared < 0 || d->d_ff_shared % 8) return MOE_ERR_ARG;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_ARG;
+  if (d->null_kind < MOE_NULL_ZERO || d->null_kind > MOE_NULL_CONSTANT) return MOE_ERR_ARG;
   if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK ||
       (int64_t)d->n_experts + d->n_null > MOE_MAX_POOL)
     return MOE_ERR_UNSUPPORTED;
@@ -162,7 +163,7 @@ moe_status moe_route(const moe_dims* d, const void* x, const float* w_router, fl
   (void)hipGetLastError();
   RouteArgs a{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, false, x, w_router,
               null_bias, null_bias_tok, logits_in, logits_out, topk_idx, topk_w, n_real,
-              ws, nullptr, nullptr, nullptr};
+              ws, nullptr, nullptr, nullptr, d->null_kind};
   HIP_TRY(launch_route(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -241,18 +242,24 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
   return MOE_OK;
 }
 
+// Per-token stride (elements) of the rows a null slot adds: x for copy experts,
+// the one vector v for constant experts.
+inline int64_t null_stride(const moe_dims* d) { return d->null_kind == MOE_NULL_COPY ? d->d_model : 0; }
+
 moe_status moe_combine(const moe_dims* d, const void* y_perm, const int32_t* slot_pos,
-                       const float* topk_w, const void* y_shared, void* y, moe_stream stream) {
+                       const float* topk_w, const void* y_shared, const void* null_src, void* y,
+                       moe_stream stream) {
   MOE_TRY(check_dims(d));
   MOE_TRY(need(y_perm));
   MOE_TRY(need(slot_pos));
   MOE_TRY(need(topk_w));
   MOE_TRY(maybe(y_shared));
+  if (d->null_kind != MOE_NULL_ZERO) MOE_TRY(need(null_src));
   MOE_TRY(need(y));
   if (d->T == 0) return MOE_OK;
   (void)hipGetLastError();
   CombineArgs c{d->dtype == MOE_BF16, d->T, d->top_k, d->d_model, max_rows(d), y_perm, slot_pos,
-                topk_w, y_shared, y};
+                topk_w, y_shared, d->null_kind != MOE_NULL_ZERO ? null_src : nullptr, null_stride(d), y};
   HIP_TRY(launch_combine(c, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
@@ -293,6 +300,7 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
     MOE_TRY(need(p->ws_up));
     MOE_TRY(need(p->ws_down));
   }
+  if (d->null_kind == MOE_NULL_CONSTANT) MOE_TRY(need(p->null_value));
   MOE_TRY(need(y));
   moe_aux_out ao{};
   if (aux) ao = *aux;
@@ -332,7 +340,7 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   // 1. scores, selection, weights; per-chunk expert histogram; statistics sums
   RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
                p->null_bias, p->null_bias_tok, nullptr, logits, topk_idx, topk_w, n_real,
-               at(L.route), permute_ws, rhist, tstats};
+               at(L.route), permute_ws, rhist, tstats, d->null_kind};
   HIP_TRY(launch_route(ra, s));
 
   // 2. counting sort (histograms already written) + statistics finalisation
@@ -365,8 +373,11 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   HIP_TRY(launch_gemm_pair(bf16, 1, r2, s2, cus, s, 2));
 
   // 5. weighted combine in slot order, one rounding
+  const void* nsrc = d->null_kind == MOE_NULL_COPY       ? p->x
+                     : d->null_kind == MOE_NULL_CONSTANT ? p->null_value
+                                                         : nullptr;
   CombineArgs ca{bf16, d->T, d->top_k, d->d_model, R, at(L.yp), slot_pos, topk_w,
-                 d->d_ff_shared ? at(L.ys) : nullptr, y};
+                 d->d_ff_shared ? at(L.ys) : nullptr, nsrc, null_stride(d), y};
   HIP_TRY(launch_combine(ca, s));
   return MOE_OK;
 }

@@ -2,8 +2,9 @@
 //
 // Paper review "Improving MoE Compute Efficiency by Composing Weight and Data
 // Sparsity", section 3, core formula of the token-choice layer with a shared
-// expert: y = E_shared(x) + sum_k g_k E_{i_k}(x). A null slot contributes
-// E_null(x) = 0 and is skipped (slot_pos = -1).
+// expert: y = E_shared(x) + sum_k g_k E_{i_k}(x). A null slot (slot_pos = -1)
+// contributes E_null(x) = 0, or with copy / constant zero-compute experts g_k x
+// or g_k v (its row of null_src, in the same slot order).
 //
 // One wavefront per token row: the K (position, weight) pairs are loaded once
 // by lanes 0..K-1 and broadcast with shuffles; each lane owns 8-element
@@ -56,6 +57,7 @@ template <typename ET, int VPL>  // VPL: 8-element vectors per lane per pass
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y_perm, const int32_t* __restrict__ slot_pos,
                const float* __restrict__ topk_w, const float* __restrict__ y_shared,
+               const ET* __restrict__ null_src, int64_t null_stride,
                ET* __restrict__ y, int64_t T, int K, int d, int64_t max_rows) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / kWave;
@@ -67,7 +69,8 @@ combine_kernel(const float* __restrict__ y_perm, const int32_t* __restrict__ slo
     if (lane < K) {
       my_p = slot_pos[t * K + lane];
       my_w = topk_w[t * K + lane];
-      if (my_p < 0 || my_p >= max_rows) my_p = -1;
+      // -1: a null slot; -2: nothing to add (a slot past capacity, or no null source)
+      if (my_p == -1 ? !null_src : (my_p < 0 || my_p >= max_rows)) my_p = -2;
     }
     for (int v0 = 0; v0 < vpr; v0 += kWave * VPL) {
       float acc[VPL][8];
@@ -84,13 +87,14 @@ combine_kernel(const float* __restrict__ y_perm, const int32_t* __restrict__ slo
       for (int k = 0; k < K; ++k) {
         const int p = __shfl(my_p, k, kWave);
         const float w = __shfl(my_w, k, kWave);
-        if (p < 0) continue;
+        if (p == -2) continue;
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
           const int v = v0 + u * kWave + lane;
           if (v < vpr) {
             float r[8];
-            Vec8<float>::load(y_perm + (int64_t)p * d + v * 8, r);
+            if (p >= 0) Vec8<float>::load(y_perm + (int64_t)p * d + v * 8, r);
+            else Vec8<ET>::load(null_src + t * null_stride + v * 8, r);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[u][j] = fmaf(w, r[j], acc[u][j]);
           }
@@ -114,13 +118,16 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.bf16) {
     if (vpr >= 4 * kWave)
       combine_kernel<bf16_t, 4><<<(unsigned)blocks, 256, 0, stream>>>(
-          yp, a.slot_pos, a.topk_w, ys, static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
+          yp, a.slot_pos, a.topk_w, ys, static_cast<const bf16_t*>(a.null_src), a.null_stride,
+          static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
     else
       combine_kernel<bf16_t, 2><<<(unsigned)blocks, 256, 0, stream>>>(
-          yp, a.slot_pos, a.topk_w, ys, static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
+          yp, a.slot_pos, a.topk_w, ys, static_cast<const bf16_t*>(a.null_src), a.null_stride,
+          static_cast<bf16_t*>(a.y), a.T, a.K, a.d, a.max_rows);
   } else {
     combine_kernel<float, 1><<<(unsigned)blocks, 256, 0, stream>>>(
-        yp, a.slot_pos, a.topk_w, ys, static_cast<float*>(a.y), a.T, a.K, a.d, a.max_rows);
+        yp, a.slot_pos, a.topk_w, ys, static_cast<const float*>(a.null_src), a.null_stride,
+        static_cast<float*>(a.y), a.T, a.K, a.d, a.max_rows);
   }
   return hipGetLastError();
 }

@@ -29,6 +29,7 @@ struct RouteArgs {
   int32_t* chunk_hist; // fused: [tiles][N] real slots per expert and 64-token tile
   int32_t* rhist;      // fused: [tiles][K + 1] tokens per number of chosen reals r
   double* tstats;      // fused: [tiles][N + 3] sums of p_t,j (j <= N), lse_t^2 and r_t
+  int null_kind;       // moe_null_kind: 0 weights over the chosen reals, else over all K slots
 };
 int route_tokens_per_block();
 size_t route_ws_bytes(int64_t T, int N, int d);
@@ -120,6 +121,8 @@ struct CombineArgs {
   const int32_t* slot_pos;
   const float* topk_w;
   const void* y_shared;
+  const void* null_src;    // rows a null slot adds (dtype), or NULL
+  int64_t null_stride;     // elements between the rows of consecutive tokens (0: one row)
   void* y;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -84,6 +84,7 @@ struct RouteKernelArgs {
   int KS;                  // bf16 scoring: K splits (partials path)
   int partials;            // bf16 scoring: 1 = write partial logits for route_select_kernel
   float* lpart;            // bf16 scoring, partials path: [KS][T][N + 1] partial logits
+  int null_kind;           // 0: weights over the chosen reals; else over all K slots
 };
 
 // fp64 LDS scratch of the fused epilogue: block sums [N + 3], per-token lse^2 and r
@@ -206,7 +207,7 @@ __device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld,
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) tk[i] = lk[i];
     tk[32] = ((uint64_t)__float_as_uint(mp) << 32) | __float_as_uint(vmax);
-    tk[33] = (uint64_t)r;
+    tk[33] = ((uint64_t)__float_as_uint(snull) << 32) | (uint32_t)r;
   }
   if (FUSED) {
     // pool softmax [reals, null x M] numerators written over the logits row
@@ -240,14 +241,19 @@ __device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld,
     }
     return;
   }
-  const int rr = (int)tt[33];
+  const int rr = (int)(uint32_t)tt[33];
+  const float sn = __uint_as_float((uint32_t)(tt[33] >> 32));
   const float vm = __uint_as_float((uint32_t)tt[32]), pm = __uint_as_float((uint32_t)(tt[32] >> 32));
-  // weights: softmax over the chosen reals in fp64, summed in rank order
+  // weights in fp64, summed in rank order: a softmax over the chosen reals (null
+  // slots 0), or for copy / constant null slots over all K chosen entries, the
+  // null slots at the null logit (shifted by the pool maximum)
+  const bool all_k = a.null_kind != 0;
   double e[KMAX];
   double tot = 0.0;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
-    e[i] = i < rr ? exp((double)from_ordered_bits((uint32_t)(tt[i] >> 32)) - (double)vm) : 0.0;
+    const double v = i < rr ? (double)from_ordered_bits((uint32_t)(tt[i] >> 32)) : (double)sn;
+    e[i] = (i < rr || (all_k && i < K)) ? exp(v - (double)(all_k ? pm : vm)) : 0.0;
     tot += e[i];
   }
   const int64_t tg = t0 + t;
@@ -258,7 +264,7 @@ __device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld,
     if (i < K) {
       const int id = i < rr ? (int)(0xffffffffu - (uint32_t)tt[i]) : N + (i - rr);
       idx_row[i] = id;
-      w_row[i] = i < rr ? (float)(e[i] / tot) : 0.0f;
+      w_row[i] = (i < rr || all_k) ? (float)(e[i] / tot) : 0.0f;
       if (FUSED && i < rr) atomicAdd(&L.cnt[id], 1);
     }
   }
@@ -783,7 +789,8 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
                     r.w_router ? r.w_router + (int64_t)r.N * r.d : nullptr, r.null_bias,
                     r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, r.logits_out,
                     r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.rhist, r.tstats,
-                    pl.ks, pl.partials ? 1 : 0, mfma ? static_cast<float*>(r.ws) : nullptr};
+                    pl.ks, pl.partials ? 1 : 0, mfma ? static_cast<float*>(r.ws) : nullptr,
+                    r.null_kind};
   const size_t lds = route_lds_bytes(r, mfma && !pl.partials);
   const size_t lds_score = route_etw(r.N) == 1 ? RouteTile<1>::lds : RouteTile<2>::lds;
   const size_t lds_select = route_lds_bytes(r, false);

@@ -27,7 +27,7 @@ def to_host(t):
 
 
 class MoeLayer:
-    WEIGHTS = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    WEIGHTS = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "null_value")
 
     def __init__(self, workload, device="cuda", T=None, weights_from=None):
         """weights_from: another MoeLayer whose device weights are reused (same arrays)."""
@@ -68,7 +68,7 @@ class MoeLayer:
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
         self.params = LayerParams(p(self.x), p(self.w_router), self.null_bias, p(self.null_bias_tok),
                                   p(self.w_gate), p(self.w_up), p(self.w_down), p(self.ws_gate),
-                                  p(self.ws_up), p(self.ws_down))
+                                  p(self.ws_up), p(self.ws_down), p(self.null_value))
         self.aux_full = AuxOut(p(self.logits), p(self.topk_idx), p(self.topk_w), p(self.n_real),
                                p(self.offsets), p(self.counts), p(self.f), p(self.P), p(self.scalars))
 
