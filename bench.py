@@ -309,7 +309,9 @@ def cpu_baseline(budget_s=12.0):
 
 def sweep(torch, tcr, steps, warmup):
     """Other workloads, timed only: the rho sweep at the Qwen3-1.7B shape, the
-    matched-FLOPs pair at T=8192, and the modality-skewed mix."""
+    matched-FLOPs pair at T=8192, the modality-skewed mix, and the rho = 0.5
+    Qwen3-0.6B shape with copy and with constant null slots (the zero-compute
+    variants that add w x or w v in the combine)."""
     import copy
     from token_choice_routing_amd.layer import MoeLayer
     from workloads import CONFIGS, MATCHED_PAIR, SWEEP, generate
@@ -343,6 +345,17 @@ def sweep(torch, tcr, steps, warmup):
         l1 = l1 or layer
         out.append(measure(torch, layer, steps, warmup))
         log(f"  {name}: {out[-1]}")
+    from dataclasses import replace
+    for kind in ("zero", "copy", "constant"):
+        cfg = replace(CONFIGS["qwen3_0p6b_rho0p5"], null_kind=kind, name=f"qwen3_0p6b_rho0p5_{kind}")
+        wl = generate(cfg, experts=False, bias=False)
+        wl.w_gate, wl.w_up, wl.w_down = c1.w_gate, c1.w_up, c1.w_down
+        wl.ws_gate, wl.ws_up, wl.ws_down = c1.ws_gate, c1.ws_up, c1.ws_down
+        wl.null_bias, wl.null_bias_tok = null_bias_for(CONFIGS["qwen3_0p6b_rho0p5"])
+        layer = MoeLayer(wl)
+        out.append(measure(torch, layer, steps, warmup))
+        log(f"  {cfg.name}: {out[-1]}")
+        del layer
     return out
 
 
