@@ -109,9 +109,10 @@ typedef void* moe_stream; /* hipStream_t */
  * null_bias_tok: optional [T] float32 per-token null bias.
  * topk_idx [T][K] int32, topk_w [T][K] float32 required; n_real [T] optional.
  * ws: MOE_WS_ROUTE bytes (float32 partial logits, up to 4 planes of [T][N+1],
- *   written when the d_model sum is split over workgroups: few 64-token tiles or
- *   N > 64; at least 256 bytes); may be NULL when logits_in is given or dtype is
- *   MOE_F32. Calls that share a workspace must not overlap.
+ *   16 when the batch is one 64-token tile, written when the d_model sum is split
+ *   over workgroups: few 64-token tiles or N > 64; at least 256 bytes); may be
+ *   NULL when logits_in is given or dtype is MOE_F32. Calls that share a
+ *   workspace must not overlap.
  */
 moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
                      float null_bias, const float* null_bias_tok, const float* logits_in,
