@@ -160,6 +160,8 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void
  * Rows outside the segments are not written.
  * bf16: MFMA with float32 accumulation, h stored as bf16 (the input type of
  * the down projection's MFMA); float32: float FMA throughout.
+ * bf16 limit: (d_ff + 1) * d_model * 2 bytes (one group's weight matrix plus a
+ * row) must fit in 4 GB, else MOE_ERR_UNSUPPORTED.
  * ws: moe_expert_ffn_workspace_bytes() bytes (holds h).
  */
 moe_status moe_expert_ffn(const moe_dims* dims, int32_t n_groups, int32_t d_ff, int64_t max_rows,
@@ -177,6 +179,8 @@ size_t moe_expert_ffn_workspace_bytes(const moe_dims* dims, int32_t d_ff, int64_
  *   op = MOE_GEMM_DOWN:    out[p] = b0[e] a_p                        out float32, [rows][n_out]
  *                          a: [rows][k_dim] dtype; b0: [n_groups][n_out][k_dim]; b1 unused
  * n_out and k_dim multiples of 8. No workspace.
+ * bf16 limit: (n_out + 1) * k_dim * 2 bytes must fit in 4 GB, else
+ * MOE_ERR_UNSUPPORTED.
  */
 enum { MOE_GEMM_GATE_UP = 0, MOE_GEMM_DOWN = 1 };
 moe_status moe_grouped_gemm(const moe_dims* dims, int32_t op, int32_t n_groups, int32_t n_out,
@@ -252,6 +256,9 @@ typedef struct {
  * aux may be NULL; the statistics kernels run only when aux requests
  * counts, f, P or scalars. ws: moe_workspace_bytes(dims, MOE_WS_LAYER) bytes,
  * sized for the worst case of T*min(K,N) real slots.
+ * bf16 limit: (T + 1), (d_ff + 1) and (d_ff_shared + 1) rows of d_model bf16
+ * each fit in 4 GB (x is gathered through 32-bit offsets), else
+ * MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_layer_forward(const moe_dims* dims, const moe_layer_params* params, void* y,
                              const moe_aux_out* aux, void* ws, size_t ws_bytes,

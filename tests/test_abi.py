@@ -109,6 +109,20 @@ def test_null_and_misaligned_pointers(lib):
     assert lib.moe_layer_forward(ctypes.byref(ds), ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_ARG
 
 
+def test_bf16_operands_past_4g_unsupported(lib):
+    """bf16 GEMM operands are read at 32-bit byte offsets that may run one row past
+    the end: a group's weight matrix and the gathered activation matrix, plus a row,
+    must fit in 4 GB; larger ones are refused before anything is launched."""
+    d = make_dims(T=16, d_model=32768, n_experts=4, n_null=0, top_k=2, d_ff=65536, dtype=MOE_BF16)
+    b = ctypes.byref(d)
+    big = 1 << 40
+    assert lib.moe_grouped_gemm(b, 0, 1, 65536, 32768, 10, FAKE, None, FAKE, FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn(b, 1, 65536, 10, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == MOE_ERR_UNSUPPORTED
+    d2 = make_dims(T=70000, d_model=32768, n_experts=4, n_null=0, top_k=2, d_ff=64, dtype=MOE_BF16)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_layer_forward(ctypes.byref(d2), ctypes.byref(p), FAKE, None, FAKE, big, None) == MOE_ERR_UNSUPPORTED
+
+
 def test_short_workspace(lib):
     d = _dims()
     b = ctypes.byref(d)

@@ -15,6 +15,11 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// bf16 GEMM operands are addressed with 32-bit byte offsets that may run one row
+// past the end: one group's weight matrix and a gathered activation matrix, plus a
+// row, must each fit in 4 GB.
+inline bool fits_4g(int64_t rows, int64_t cols) { return (rows + 1) * cols * 2 <= 0xFFFFFFFFll; }
+
 moe_status check_dims(const moe_dims* d) {
   if (!d) return MOE_ERR_ARG;
   if (d->T < 0 || d->n_experts < 1 || d->n_null < 0 || d->top_k < 1) return MOE_ERR_ARG;
@@ -200,6 +205,7 @@ moe_status moe_expert_ffn(const moe_dims* d, int32_t n_groups, int32_t d_ff, int
     return MOE_ERR_ARG;
   if (!offsets && n_groups != 1) return MOE_ERR_ARG;
   if (rows * (int64_t)std::max(d->d_model, d_ff) >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_BF16 && !fits_4g(d_ff, d->d_model)) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(need(a));
   MOE_TRY(maybe(offsets));
   MOE_TRY(need(w_gate));
@@ -226,6 +232,7 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
       k_dim % 8 || rows < 0)
     return MOE_ERR_ARG;
   if (!offsets && n_groups != 1) return MOE_ERR_ARG;
+  if (d->dtype == MOE_BF16 && !fits_4g(n_out, k_dim)) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(need(a));
   MOE_TRY(maybe(offsets));
   MOE_TRY(need(b0));
@@ -289,6 +296,9 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
                              moe_stream stream) {
   MOE_TRY(check_dims(d));
   if (!p) return MOE_ERR_ARG;
+  if (d->dtype == MOE_BF16 && (!fits_4g(d->T, d->d_model) || !fits_4g(d->d_ff, d->d_model) ||
+                               !fits_4g(d->d_ff_shared, d->d_model)))
+    return MOE_ERR_UNSUPPORTED;
   MOE_TRY(need(p->x));
   MOE_TRY(need(p->w_router));
   MOE_TRY(maybe(p->null_bias_tok));

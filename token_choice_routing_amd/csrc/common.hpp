@@ -103,12 +103,36 @@ __device__ __forceinline__ void load_lds16(const bf16_t* g, bf16_t* l) {
 #endif
 }
 
+// Raw buffer resource over [base, base + bytes) (stride 0, 32-bit data format
+// word as for every CDNA raw buffer access). Reads at offsets past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer -> LDS load (buffer_load_dwordx4 ... lds), same LDS placement as
+// load_lds16. Unlike the global form, the compiler's wait-count tracking does not
+// count it as an LDS-side (lgkm) event, so LDS reads after it keep exact waits.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, bf16_t* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(l),
+                                           16, voffset, 0, 0, 0);
+#else
+  (void)r;
+  (void)voffset;
+  (void)l;
+#endif
+}
+
 // LDS-only workgroup barrier for tiles written by global->LDS loads: each wavefront
 // first retires its own LDS reads; the caller has already waited (vmcnt) for the
 // loads that filled the stage about to be read. The asm statement is also a
 // compiler memory barrier, so no LDS access moves across it.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // The same wait again through the builtin, which the compiler's counter tracking
+  // sees (it does not read the asm): the LDS reads after the barrier then get exact
+  // lgkmcnt waits instead of lgkmcnt(0).
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

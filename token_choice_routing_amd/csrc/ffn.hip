@@ -18,13 +18,17 @@
 //    wavefronts of 64 x 64). For the gate/up pass the BN weight rows are BN/2 gate
 //    + BN/2 up rows of the same output columns, so a lane holds gate and up values
 //    of the same (row, column) and applies SwiGLU in registers; h is written once.
-//  * K tiles stream through S LDS stages filled by global->LDS loads
-//    (global_load_lds_dwordx4): no staging registers, S-1 tiles in flight while
-//    one is multiplied, and the wait before each barrier counts only this
-//    wavefront's loads of the tile about to be read. LDS rows are 128 bytes with
-//    16-byte chunks XOR-swizzled by (row mod 8), so the 32 rows a fragment read
-//    touches fall in distinct banks; the swizzle is applied on the global side
-//    of each load.
+//  * K tiles stream through S LDS stages filled by buffer->LDS loads
+//    (buffer_load_dwordx4 ... lds): no staging registers, S-1 tiles in flight
+//    while one is multiplied, and the wait before each barrier counts only this
+//    wavefront's loads issued after the tile about to be read. The loads of the
+//    next tile are spread between the MFMA steps: the CU's address unit takes one
+//    1 KB load at a time, so issuing them all after the barrier stalled every
+//    wavefront. LDS rows are 128 bytes with 16-byte chunks XOR-swizzled by
+//    (row / 2) mod 8, so the 16 rows one pass of a fragment read touches fall in
+//    distinct banks of the 64; the swizzle is applied on the global side of each
+//    load. A stage's fragment reads are all issued before its MFMAs, each MFMA
+//    step waiting only for its own reads.
 //  * Persistent grid. Each workgroup builds the tile table from the device
 //    offsets (no host round trip for R), and tiles are ordered
 //    (expert, column tile, row tile) and cut into 8 contiguous ranges, one per
@@ -32,10 +36,11 @@
 //    tiles that share one expert's weight panel run on the same L2.
 //  * When a range's last round has fewer tiles than the range has workgroups,
 //    those tiles are split by output columns into 2 or 4 sub-tiles, so every
-//    workgroup streams about the same weight bytes. Load instructions whose rows
-//    are all past the segment or outside the sub-tile are not issued. Each
-//    workgroup issues its next item's first stages before it stores the current
-//    item's outputs.
+//    workgroup streams about the same weight bytes. Rows past the segment or
+//    outside the sub-tile are read one row past their buffer's end (zero, no
+//    memory traffic). Each workgroup fetches the next item's row indices while it
+//    multiplies the current item, and issues the next item's first stages before
+//    it stores the current item's outputs.
 #include <algorithm>
 #include <type_traits>
 
@@ -48,14 +53,35 @@ constexpr int kMaxGroups = 320;   // routed groups (<= 256) + the dense shared-e
 
 enum { kSwiGLU = 0, kPlain = 1 };
 
-// Element offset of (row, 16-byte chunk) in a [rows][BK] bf16 LDS tile. 128-byte
-// rows (BK = 64) XOR the chunk with row % 8; 64-byte rows (BK = 32) with
-// (row / 4) % 4. Either way the 16-byte reads of 16 consecutive rows at one
-// logical chunk land on 16 distinct bank quads.
+// Element offset of (row, 16-byte chunk) in a [rows][BK] bf16 LDS tile. The LDS
+// has 64 four-byte banks, and a 16-byte read serves 16 lanes per pass, here 16
+// consecutive rows at one logical chunk. 128-byte rows (BK = 64) XOR the chunk with
+// (row / 2) % 8: an even and an odd row cover the two 128-byte halves of the banks,
+// and the 8 even (8 odd) rows take 8 distinct chunks. 64-byte rows (BK = 32) XOR
+// with (row / 4) % 4 for the same reason. (XOR with row % 8 leaves two-way
+// conflicts: measured 120 against 181 bytes per clock per CU.)
 template <int BK>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  if constexpr (BK == 64) return row * 64 + ((chunk ^ (row & 7)) << 3);
+  if constexpr (BK == 64) return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
   else return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+// Scheduling pins for one multiplied K tile after its LDS reads: for each of the KS
+// MFMA steps, the tile loads issued there (part ks of J, none when NJ is 0), then the
+// step's NM MFMAs.
+constexpr int loads_in_part(int nj, int ks_count, int ks) {
+  int c = 0;
+  for (int j = 0; j < nj; ++j) c += j * ks_count / nj == ks;
+  return c;
+}
+template <int NJ, int KS, int NM, int KSI = 0>
+__device__ __forceinline__ void sched_steps() {
+  if constexpr (KSI < KS) {
+    constexpr int nl = loads_in_part(NJ, KS, KSI);
+    if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x010, nl, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    sched_steps<NJ, KS, NM, KSI + 1>();
+  }
 }
 
 struct TileTable {
@@ -129,14 +155,16 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 //
 // Tile BM rows x BN weight rows x BK K on WM x WN wavefronts; each wavefront owns
 // (BM/WM) x (BN/WN) outputs as 32x32 MFMA blocks. K tiles stream through S LDS
-// stages filled by global->LDS loads (global_load_lds_dwordx4): no staging
-// registers, S-1 stages in flight while one is multiplied. One wavefront load
-// instruction fills 1 KB of LDS: 8 rows of 128 bytes (BK = 64) or 16 rows of 64
-// bytes (BK = 32), lane l writing physical chunk l % CPR of row l / CPR; it
-// fetches the logical chunk that lds_off() places there, which realises the XOR
-// swizzle that keeps the MFMA fragment reads free of bank conflicts.
+// stages filled by buffer->LDS loads: no staging registers, S-1 stages in flight
+// while one is multiplied. One wavefront load instruction fills 1 KB of LDS: 8 rows
+// of 128 bytes (BK = 64) or 16 rows of 64 bytes (BK = 32), lane l writing physical
+// chunk l % CPR of row l / CPR; it fetches the logical chunk that lds_off() places
+// there, which realises the XOR swizzle that keeps the MFMA fragment reads free of
+// bank conflicts. (The buffer form, not global_load_lds: the compiler counts the
+// global form as a possible LDS-side event and then waits for every LDS read at
+// once.)
 template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S, int BK>
-__global__ void __launch_bounds__(64 * WM * WN)
+__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   static_assert(BK == 32 || BK == 64, "K tile of 64- or 128-byte rows");
   constexpr int NW = WM * WN;
@@ -150,7 +178,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   constexpr int STAGE = (BM + BN) * BK;              // elements per stage
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows must split over the wavefronts");
   static_assert(MODE != kSwiGLU || FN % 2 == 0, "gate/up tiles come in pairs");
-  static_assert(S >= 2 && S <= 5 && J * (S - 2) < 64, "stages in flight must fit the vmcnt counter");
+  static_assert(S >= 2 && S <= 6 && J * (S - 2) + JA < 64, "loads in flight must fit the vmcnt counter");
   __shared__ TileTable tt;
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // [S][BM + BN][BK]
   build_tile_table(tt, p0, p1, OC, BM);
@@ -164,8 +192,11 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   // this lane's load: row RPI (wave + NW j) + lane / CPR of the stage, physical chunk
   // lane % CPR, so logical chunk lc (the swizzle of lds_off, which depends only on
   // the row's offset within the instruction's RPI rows)
+  // (the instruction's first row is RPI (wave + NW j): a multiple of 16 for BK = 32,
+  // and for BK = 64 a multiple of 8 whose half-row parity is that of wave, NW being even)
+  static_assert(BK == 32 || NW % 2 == 0, "the load swizzle assumes an even wavefront count");
   const int lrow = lane / CPR;
-  const int lc = (lane % CPR) ^ (BK == 64 ? lrow : (lrow >> 2) & 3);
+  const int lc = (lane % CPR) ^ (BK == 64 ? (((wave & 1) << 2) | (lrow >> 1)) : (lrow >> 2) & 3);
 
   // XCD-contiguous tile ranges. When a range's last round would leave workgroups
   // idle, its tiles are split by output columns into 2 or 4 sub-tiles, so that every
@@ -180,12 +211,18 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   const int split = rem == 0 ? 1 : (WN >= 4 && 4 * rem <= Bx) ? 4 : (WN >= 2 && 2 * rem <= Bx) ? 2 : 1;
   const int items = full + rem * split;
 
-  // One work item: where its operands come from and where its outputs go.
+  // One work item: where its operands come from and where its outputs go. The
+  // operands are read through buffer resources (the activation matrix; this group's
+  // gate or up weight matrix) at 32-bit byte offsets, one row start per load. Rows
+  // that feed nothing stored (past the segment, outside a sub-tile's columns) point
+  // one row past the resource's end, where reads return zero without a memory access,
+  // so every wavefront issues the same J loads per K tile.
   struct Tile {
     bool second, wact;
-    int ge, Kdim, nk, m0, rows_valid, col0, jn;
-    unsigned lmask;
-    const bf16_t* src[J];
+    int ge, Kdim, nk, m0, rows_valid, col0;
+    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+    uint32_t a_end, b_end;  // one past each resource (reads there return zero)
+    uint32_t off[J];
   };
   // Locates work item it (group, column tile, row tile, sub-tile columns), decides
   // which load instructions fetch something used (A rows before rows_valid, weight
@@ -193,7 +230,11 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   // each stage of the item holds jn of this wavefront's loads) and sets each load's
   // row source, always a valid row: rows past the segment and columns past n_out
   // only feed outputs that are never stored.
-  auto setup = [&](int it, Tile& t) {
+  struct Where {
+    bool second;
+    int ge, Kdim, nk, m0, rows_valid, col0, ocp;
+  };
+  auto locate = [&](int it, Where& w) {
     int L = r_begin + it, part = 0, parts = 1;
     if (it >= full) {
       L = r_begin + full + (it - full) / split;
@@ -206,83 +247,125 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
       if (tt.prefix[mid] <= L) lo = mid; else hi = mid;
     }
     const int e = lo;
-    t.second = e >= G0;
-    const GemmProblem pr = t.second ? p1 : p0;
-    t.ge = t.second ? e - G0 : e;
-    const int Nout = pr.n_out;
-    t.Kdim = pr.k_dim;
-    t.nk = (t.Kdim + BK - 1) / BK;
+    w.second = e >= G0;
+    const GemmProblem pr = w.second ? p1 : p0;
+    w.ge = w.second ? e - G0 : e;
+    w.Kdim = pr.k_dim;
+    w.nk = (w.Kdim + BK - 1) / BK;
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
     const int ntile = local / mt, mtile = local - ntile * mt;
-    t.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
-    t.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - t.m0));
-    const int ocp = OC / parts;  // output columns of this item
-    t.col0 = __builtin_amdgcn_readfirstlane(ntile * OC + part * ocp);
-    // wavefronts whose rows or columns all fall outside skip the MFMAs and the stores
-    t.wact = __builtin_amdgcn_readfirstlane(wn < WN / parts && wm * TM < t.rows_valid);
-    unsigned lmask = 0;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int r0 = RPI * (wave + NW * j);
-      const bool use = j < JA ? r0 < t.rows_valid : (MODE == kSwiGLU ? (r0 - BM) % OC : r0 - BM) < ocp;
-      lmask |= (unsigned)use << j;
-    }
-    t.lmask = __builtin_amdgcn_readfirstlane(lmask);
-    t.jn = __builtin_popcount(t.lmask);
+    w.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
+    w.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - w.m0));
+    w.ocp = OC / parts;  // output columns of this item
+    w.col0 = __builtin_amdgcn_readfirstlane(ntile * OC + part * w.ocp);
+  };
+  // First half of an item's set-up: where it is and the row indices of its A loads
+  // (global loads of a_rows for a gathered problem). Issued one item ahead, so their
+  // latency passes during the current item's K loop.
+  struct Pre {
+    Where w;
     int64_t arow[JA > 0 ? JA : 1];
+  };
+  auto fetch = [&](int it, Pre& q) {
+    locate(it, q.w);
+    const GemmProblem pr = q.w.second ? p1 : p0;
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int r = RPI * (wave + NW * j) + lrow;
-      arow[j] = t.m0 + (r < t.rows_valid ? r : 0);
+      q.arow[j] = q.w.m0 + (r < q.w.rows_valid ? r : 0);
     }
     if (pr.a_rows) {
-      int32_t sr[JA > 0 ? JA : 1];
 #pragma unroll
-      for (int j = 0; j < JA; ++j) sr[j] = pr.a_rows[arow[j]];
-#pragma unroll
-      for (int j = 0; j < JA; ++j) arow[j] = min<int64_t>(max<int64_t>(sr[j], 0), pr.a_nrows - 1);
+      for (int j = 0; j < JA; ++j) q.arow[j] = pr.a_rows[q.arow[j]];
     }
+  };
+  // a_rows loads fetch() leaves in flight (wave-uniform)
+  auto fetch_loads = [&](const Pre& q) { return (q.w.second ? p1 : p0).a_rows ? JA : 0; };
+  auto setup = [&](const Pre& q, Tile& t) {
+    const Where& w = q.w;
+    t.second = w.second;
+    t.ge = w.ge;
+    t.Kdim = w.Kdim;
+    t.nk = w.nk;
+    t.m0 = w.m0;
+    t.rows_valid = w.rows_valid;
+    t.col0 = w.col0;
+    const int ocp = w.ocp, parts = OC / ocp;
+    const GemmProblem pr = t.second ? p1 : p0;
+    const int Nout = pr.n_out;
+    // wavefronts whose rows or columns all fall outside skip the MFMAs and the stores
+    t.wact = __builtin_amdgcn_readfirstlane(wn < WN / parts && wm * TM < t.rows_valid);
+    int64_t arow[JA > 0 ? JA : 1];
 #pragma unroll
-    for (int j = 0; j < JA; ++j) t.src[j] = pr.a + arow[j] * t.Kdim;
+    for (int j = 0; j < JA; ++j)
+      arow[j] = pr.a_rows ? min<int64_t>(max<int64_t>(q.arow[j], 0), pr.a_nrows - 1) : q.arow[j];
+    const uint32_t row_bytes = (uint32_t)t.Kdim * 2;
+    const int64_t wofs = (int64_t)t.ge * Nout * t.Kdim;
+    // gathered rows address the whole activation matrix ((rows + 1) x row bytes at
+    // most 4 GB, checked on the host); a contiguous segment's resource covers just
+    // the item's valid rows
+    const int64_t abase = pr.a_rows ? 0 : t.m0;
+    const uint32_t a_end = (uint32_t)((pr.a_rows ? pr.a_nrows : t.rows_valid) * row_bytes);
+    const uint32_t b_end = (uint32_t)Nout * row_bytes;
+    t.a_end = a_end;
+    t.b_end = b_end;
+    t.ra = buffer_rsrc(pr.a + abase * t.Kdim, a_end);
+    t.rb0 = buffer_rsrc(pr.b0 + wofs, b_end);
+    t.rb1 = buffer_rsrc(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs, b_end);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow;
+      t.off[j] = r < t.rows_valid ? (uint32_t)(arow[j] - abase) * row_bytes : a_end;
+    }
 #pragma unroll
     for (int j = JA; j < J; ++j) {
       const int r = RPI * (wave + NW * j) + lrow - BM;
-      int n;
-      const bf16_t* base;
-      if (MODE == kSwiGLU) {
-        n = t.col0 + (r % OC);
-        base = r < OC ? pr.b0 : pr.b1;
-      } else {
-        n = t.col0 + r;
-        base = pr.b0;
-      }
-      t.src[j] = base + ((int64_t)t.ge * Nout + (n < Nout ? n : 0)) * t.Kdim;
+      const int c = MODE == kSwiGLU ? r % OC : r;  // output column within the tile
+      const int n = t.col0 + c;
+      t.off[j] = c < ocp && n < Nout ? (uint32_t)n * row_bytes : b_end;
     }
   };
-  // K tile kt of item t into stage st. Chunks past k_dim (last tile only) read
-  // column 0; their fragments are zeroed before the MFMAs.
-  auto issue = [&](const Tile& t, int kt, int st) {
+  // K tile kt of item t into stage st; with q >= 0 only the loads of part q of
+  // BK / 16 (spread over the MFMA steps of the tile being multiplied). Chunks past
+  // k_dim (last tile only) read column 0; they are zeroed in LDS before the MFMAs
+  // read the stage. Past the item's last K tile every load reads past its resource's
+  // end (zero, no memory access) into a stage that nothing reads before it is
+  // refilled: the K loop body stays one straight instruction sequence.
+  auto issue = [&](const Tile& t, int kt, int st, int q) {
+    const bool past = kt >= t.nk;
     const int k = kt * BK + lc * 8;
-    const int kc = k < t.Kdim ? k : 0;
+    const uint32_t kb = (uint32_t)(k < t.Kdim ? k : 0) * 2;
     bf16_t* stage = smem + st * STAGE;
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (t.lmask >> j & 1) load_lds16(t.src[j] + kc, stage + RPI * (wave + NW * j) * BK);
+    for (int j = 0; j < J; ++j) {
+      if (q >= 0 && j * (BK / 16) / J != q) continue;
+      // which resource: A rows, then gate (or plain) weight rows, then up rows
+      const bool up = MODE == kSwiGLU && j >= JA && RPI * (wave + NW * j) - BM >= OC;
+      const uint32_t end = j < JA ? t.a_end : t.b_end;
+      buffer_load_lds16(j < JA ? t.ra : up ? t.rb1 : t.rb0, past ? end : t.off[j] + kb,
+                        stage + RPI * (wave + NW * j) * BK);
+    }
   };
   // the first S-1 K tiles of an item, into stages 0 .. S-2
   auto prologue = [&](const Tile& t) {
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (s < t.nk) issue(t, s, s);
+      if (s < t.nk) issue(t, s, s, -1);
   };
 
   Tile cur;
+  Pre pre;
   if (slot < items) {
-    setup(slot, cur);
+    fetch(slot, pre);
+    setup(pre, cur);
     prologue(cur);
   }
   for (int it = slot; it < items; it += Bx) {
+    // the next item's row indices, behind this item's first S-1 K tiles
+    const bool more = it + Bx < items;
+    if (more) fetch(it + Bx, pre);
+    const int na = more ? fetch_loads(pre) : 0;
     f32x16_t acc[FN][FM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
@@ -291,10 +374,13 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
 
     // One K tile from stage st in four 16-wide steps; the fragments of step ks+1
     // are read while step ks multiplies.
-    auto compute = [&](auto tail, int st, int kvalid) {
+    // With ISS, K tile nt's loads are issued between the MFMA steps (part ks before
+    // step ks's MFMAs): the CU's address unit takes each 1 KB load in turn, so loads
+    // issued by every wavefront at once after the barrier would hold up all MFMAs.
+    auto compute = [&](auto iss, int st, int nt) {
+      constexpr bool ISS = decltype(iss)::value;
       const bf16_t* As = smem + st * STAGE;
       const bf16_t* Bs = As + BM * BK;
-      bf16x8_t wf[2][FN], af[2][FM];
       auto frags = [&](int ks, bf16x8_t* w, bf16x8_t* a) {
         const int ch = ks * 2 + half;
 #pragma unroll
@@ -309,47 +395,69 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
         for (int g = 0; g < FM; ++g)
           a[g] = *reinterpret_cast<const bf16x8_t*>(&As[lds_off<BK>(wm * TM + g * 32 + l32, ch)]);
-        if constexpr (decltype(tail)::value) {  // last K tile: zero the chunks past k_dim
-          const bool z = ch * 8 >= kvalid;
-#pragma unroll
-          for (int f = 0; f < FN; ++f) w[f] = z ? bf16x8_t{} : w[f];
-#pragma unroll
-          for (int g = 0; g < FM; ++g) a[g] = z ? bf16x8_t{} : a[g];
-        }
       };
-      // double-buffered fragments only while they are few (register pressure)
-      constexpr bool kDouble = FN + FM <= 6;
-      frags(0, wf[0], af[0]);
+      constexpr int KS = BK / 16;
+      if constexpr ((FN + FM) * KS * 4 <= 64) {
+        // All of the stage's fragment reads are issued first (64 VGPRs at most), so
+        // each 16-wide step's MFMAs wait only for their own reads (LDS reads return
+        // in order) while the later ones are still in flight.
+        bf16x8_t wa[KS][FN], aa[KS][FM];
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int cur_buf = kDouble ? (ks & 1) : 0;
-        if (kDouble && ks + 1 < BK / 16) frags(ks + 1, wf[cur_buf ^ 1], af[cur_buf ^ 1]);
-        if (!kDouble && ks > 0) frags(ks, wf[0], af[0]);
+        for (int ks = 0; ks < KS; ++ks) frags(ks, wa[ks], aa[ks]);
 #pragma unroll
-        for (int f = 0; f < FN; ++f)
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (ISS) issue(cur, nt, nt % S, ks);
 #pragma unroll
-          for (int g = 0; g < FM; ++g)
-            acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur_buf][f], af[cur_buf][g], acc[f][g], 0, 0, 0);
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int g = 0; g < FM; ++g)
+              acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks][f], aa[ks][g], acc[f][g], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, (FN + FM) * KS, 0);  // LDS reads
+        sched_steps<ISS ? J : 0, KS, FN * FM>();  // then per step: its loads, its MFMAs
+      } else {
+        // larger wavefront tiles: fragments of step ks + 1 are read while step ks multiplies
+        bf16x8_t wf[2][FN], af[2][FM];
+        frags(0, wf[0], af[0]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int cb = ks & 1;
+          if (ks + 1 < KS) frags(ks + 1, wf[cb ^ 1], af[cb ^ 1]);
+          if constexpr (ISS) issue(cur, nt, nt % S, ks);
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int g = 0; g < FM; ++g)
+              acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][f], af[cb][g], acc[f][g], 0, 0, 0);
+        }
       }
     };
 
     // Stage kt % S holds K tile kt (the item's first S-1 tiles were issued before
-    // it started). Before reading a stage a wavefront waits until at most the loads
-    // of the later tiles already issued are outstanding; on the first tile it waits
-    // for everything, because the previous item's output stores may retire out of
-    // order with the loads.
+    // it started, then the next item's row-index loads). Before reading a stage a
+    // wavefront waits until at most the loads issued after that tile's are
+    // outstanding. Loads complete in issue order among themselves, so this is exact
+    // for the loads; stores in flight (the previous item's outputs) only hold the
+    // count up, never let it pass early.
     for (int kt = 0; kt < cur.nk; ++kt) {
       const int ahead = min(S - 2, cur.nk - 1 - kt);  // tiles issued after kt
-      if (kt == 0 || ahead <= 0) wait_vmcnt<0>();
-      else wait_vmcnt_upto<J * (S - 2)>(cur.jn * ahead);
+      if (ahead <= 0) wait_vmcnt<0>();
+      else wait_vmcnt_upto<J * (S - 2) + JA>(J * ahead + (kt < S - 1 ? na : 0));
       stage_barrier();
-      if (kt + S - 1 < cur.nk) issue(cur, kt + S - 1, (kt + S - 1) % S);
+      const int nt = kt + S - 1;  // K tile whose loads this step issues
       const int kvalid = cur.Kdim - kt * BK;
-      if (!cur.wact) continue;
-      if (kvalid < BK)
-        compute(std::true_type{}, kt % S, kvalid);
-      else
-        compute(std::false_type{}, kt % S, kvalid);
+      if (kvalid < BK) {  // ragged last K tile: zero its chunks past k_dim (k_dim % 8 == 0)
+        bf16_t* stg = smem + (kt % S) * STAGE;
+        const int c0 = kvalid / 8, nc = CPR - c0;
+        for (int i = tid; i < (BM + BN) * nc; i += 64 * NW)
+          *reinterpret_cast<u32x4_t*>(&stg[lds_off<BK>(i / nc, c0 + i % nc)]) = u32x4_t{0, 0, 0, 0};
+        stage_barrier();
+      }
+      if (!cur.wact) {
+        issue(cur, nt, nt % S, -1);
+        continue;
+      }
+      compute(std::true_type{}, kt % S, nt);
     }
 
     // Every wavefront is done with the stages: issue the next item's first tiles,
@@ -357,8 +465,8 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     const bool second = cur.second, wact = cur.wact;
     const int m0 = cur.m0, rows_valid = cur.rows_valid, col0 = cur.col0;
     stage_barrier();
-    if (it + Bx < items) {
-      setup(it + Bx, cur);
+    if (more) {
+      setup(pre, cur);
       prologue(cur);
     }
     if (!wact) continue;
@@ -607,6 +715,10 @@ static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& 
     case 5: launch_variant<MODE, ROLE, 128, 384, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
     case 6: launch_variant<MODE, ROLE, 128, 384, 2, 2, 4, 32>(q0, q1, num_cus, stream); break;
     case 7: launch_variant<MODE, ROLE, 128, 256, 2, 4, 5, 32>(q0, q1, num_cus, stream); break;
+    case 8: launch_variant<MODE, ROLE, 256, 256, 2, 2, 4, 32>(q0, q1, num_cus, stream); break;
+    case 9: launch_variant<MODE, ROLE, 256, 256, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
+    case 10: launch_variant<MODE, ROLE, 128, 256, 2, 4, 6, 32>(q0, q1, num_cus, stream); break;
+    case 11: launch_variant<MODE, ROLE, 128, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
 #endif
     default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
   }
@@ -635,10 +747,18 @@ static void launch_skinny(const GemmProblem& q0, const GemmProblem& q1, int num_
   skinny_gemm_kernel<MODE, ROLE><<<grid, 256, 0, stream>>>(q0, q1);
 }
 
+bool gemm_operands_fit(const GemmProblem& p) {
+  if (p.groups == 0 || p.max_rows <= 0) return true;
+  const int64_t row_bytes = (int64_t)p.k_dim * 2;
+  return (int64_t)(p.n_out + 1) * row_bytes <= 0xFFFFFFFFll &&
+         (!p.a_rows || (p.a_nrows + 1) * row_bytes <= 0xFFFFFFFFll);
+}
+
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
                             int num_cus, hipStream_t stream, int role) {
   const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
   if (!any0 && !any1) return hipSuccess;
+  if (bf16 && (!gemm_operands_fit(p0) || !gemm_operands_fit(p1))) return hipErrorInvalidValue;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
     if (std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows) {

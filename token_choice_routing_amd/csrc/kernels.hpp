@@ -111,6 +111,11 @@ struct GemmProblem {
 // segment, 2 the layer's fused launch.
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
                             int num_cus, hipStream_t stream, int role);
+// bf16 operands are read through buffer resources with 32-bit byte offsets that may
+// point one row past the end: one group's weight matrix, and a gathered activation
+// matrix (a_rows), each plus one row, must fit in 4 GB. False means the launch is
+// refused.
+bool gemm_operands_fit(const GemmProblem& p);
 
 struct CombineArgs {
   bool bf16;
