@@ -83,7 +83,7 @@ typedef struct {
 } moe_dims;
 
 /* Which workspace size moe_workspace_bytes() returns. */
-enum { MOE_WS_LAYER = 0, MOE_WS_ROUTE = 1, MOE_WS_PERMUTE = 2, MOE_WS_AUX = 3 };
+enum { MOE_WS_LAYER = 0, MOE_WS_ROUTE = 1, MOE_WS_PERMUTE = 2, MOE_WS_AUX = 3, MOE_WS_BACKWARD = 4 };
 
 typedef void* moe_stream; /* hipStream_t */
 
@@ -264,7 +264,42 @@ moe_status moe_layer_forward(const moe_dims* dims, const moe_layer_params* param
                              const moe_aux_out* aux, void* ws, size_t ws_bytes,
                              moe_stream stream);
 
-/* Workspace bytes for MOE_WS_LAYER / ROUTE / PERMUTE / AUX; 0 on invalid dims. */
+/* Gradients written by moe_layer_backward (float32, device, 16-byte aligned). */
+typedef struct {
+  float* dx;        /* [T][d_model] */
+  float* dw_router; /* [N+1][d_model]; row N (the null logit's row) is 0 when n_null = 0 */
+  float* dw_gate;   /* [N][d_ff][d_model] */
+  float* dw_up;     /* [N][d_ff][d_model] */
+  float* dw_down;   /* [N][d_model][d_ff] */
+  float* dws_gate;  /* [d_ff_shared][d_model]; required when d_ff_shared > 0 */
+  float* dws_up;    /* [d_ff_shared][d_model] */
+  float* dws_down;  /* [d_model][d_ff_shared] */
+} moe_layer_grads;
+
+/*
+ * moe_layer_backward -- gradients of the training objective
+ *   L = <dy, y> + alpha * L_bal + beta * L_z
+ * with y the output of moe_layer_forward on the same inputs, dy [T][d_model] dtype
+ * the upstream gradient, and L_bal, L_z the statistics of moe_aux_stats (paper
+ * review section 3: load-balance loss and z-loss are added to the task loss; the
+ * pages train with alpha = 2e-2, beta = 1e-3). The routing decision is held fixed
+ * (top-K is piecewise constant): gradients reach the router through the
+ * renormalised weights of the chosen reals and through the pool softmax of L_bal
+ * and L_z (the null logit's M copies summed into row N). Expert gradients follow
+ * the SwiGLU chain rule per segment; the shared expert's when present.
+ * The routing, permutation and expert pre-activations are recomputed from x
+ * (nothing is kept from the forward call). All enqueued on `stream`, no host
+ * synchronisation; deterministic.
+ * bf16 and MOE_NULL_ZERO only (MOE_ERR_UNSUPPORTED otherwise); 32-bit offset
+ * limits as for moe_layer_forward, on the transposed activations too.
+ * ws: moe_workspace_bytes(dims, MOE_WS_BACKWARD) bytes.
+ */
+moe_status moe_layer_backward(const moe_dims* dims, const moe_layer_params* params, const void* dy,
+                              float alpha, float beta, const moe_layer_grads* grads, void* ws,
+                              size_t ws_bytes, moe_stream stream);
+
+/* Workspace bytes for MOE_WS_LAYER / ROUTE / PERMUTE / AUX / BACKWARD (bf16 only);
+ * 0 on invalid dims. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t which);
 
 /* Static, NUL-terminated description of a status code. */

@@ -1,0 +1,120 @@
+"""GPU parity of moe_layer_backward against the float64 backward oracle.
+
+The oracle routes with the GPU's float32 logits (the routing decision is held fixed
+by both sides), so every gradient is compared element by element:
+  * dx per token row, max |err| <= 2e-2 RMS(row) (the layer-output rule, TOL_BF16);
+  * every weight gradient per expert matrix and the router gradient:
+    RMS(err) <= TOL_RMS * RMS(ref) and max |err| <= TOL_MAX * RMS(ref); an expert
+    that receives no token gets exactly zero; the router's null row exactly zero
+    when M = 0.
+Tolerances: the GPU rounds dY = g dy, h and [dg | du] to bf16 (the inputs of its
+MFMA contractions) and accumulates in float32. A bf16 rounding (8 significant bits)
+moves a value by at most 2^-8 relative, RMS 2^-8 / sqrt(3) = 0.23%; a gradient term
+carries one or two of them, so the RMS error of a summed gradient is 0.2-0.3% of its
+RMS (measured 0.15-0.32%): TOL_RMS = 1e-2 leaves a factor 3 and still fails any
+systematic error (a lost term, a wrong scale or index). The largest single error is
+a weaker statistic: a weight-gradient entry is a sum of products of two heavy-tailed
+values, and for an expert with a handful of tokens it does not average at all, so one
+term's rounding sets it (measured up to 5.6% of the RMS, for an expert with 3 rows):
+TOL_MAX = 1e-1 bounds it."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_backward as B
+from token_choice_routing_amd.layer import MoeLayer, to_device, to_host
+from workloads import bf16_round, generate
+from workloads.configs import Config
+from tests.gpu_util import TOL_BF16, assert_rows_close, say, vals
+
+pytestmark = pytest.mark.gpu
+
+TOL_RMS = 1e-2
+TOL_MAX = 1e-1
+
+CASES = {
+    # M >= K with a shared expert; d_ff a multiple of 32, not of 64
+    "nullpool_shared": dict(T=200, d_model=128, n_experts=8, n_null=8, top_k=4, d_ff=96, d_ff_shared=64),
+    # plain top-K (M = 0), no shared expert, K tails (72 = 64 + 8)
+    "topk_m0": dict(T=150, d_model=64, n_experts=6, n_null=0, top_k=2, d_ff=72, d_ff_shared=0),
+    # more tokens: several row tiles per expert, wgrad K over several 64-wide tiles
+    "wide": dict(T=1024, d_model=256, n_experts=16, n_null=16, top_k=4, d_ff=192, d_ff_shared=128),
+    # 0 < M < K and an expert count that leaves some experts empty
+    "few_nulls": dict(T=40, d_model=64, n_experts=32, n_null=2, top_k=4, d_ff=64, d_ff_shared=32),
+}
+
+
+def _run(case, alpha, beta, seed=0):
+    cfg = Config(name=f"bwd_{case}", dtype="bf16", w_std=None, seed=seed, **CASES[case])
+    wl = generate(cfg)
+    say(f"  backward {case} T={cfg.T} d={cfg.d_model} N={cfg.n_experts} M={cfg.n_null} K={cfg.top_k} "
+        f"alpha={alpha} beta={beta}")
+    layer = MoeLayer(wl)
+    layer.forward()
+    out = layer.results()
+    rng = np.random.default_rng(seed + 7)
+    dy_bits = bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+    dy = to_device(dy_bits)
+    g = layer.backward(dy, alpha, beta)
+    torch.cuda.synchronize()
+    got = {k: (to_host(v) if v is not None else None) for k, v in g.items()}
+    ref = B.layer_backward(wl, vals(dy_bits), alpha, beta, logits=out["logits"].astype(np.float64))
+    return cfg, layer, dy, got, ref
+
+
+def _ratios(got, ref):
+    """(RMS(err), max|err|) relative to RMS(ref)."""
+    err = np.asarray(got, np.float64) - ref
+    scale = max(float(np.sqrt((ref * ref).mean())), 1e-300)
+    return float(np.sqrt((err * err).mean())) / scale, float(np.abs(err).max()) / scale
+
+
+def _check_matrix(got, ref, what):
+    r_rms, r_max = _ratios(got, ref)
+    assert r_rms <= TOL_RMS and r_max <= TOL_MAX, f"{what}: RMS ratio {r_rms:.3e}, max ratio {r_max:.3e}"
+    return r_rms, r_max
+
+
+def _check(cfg, got, ref):
+    N = cfg.n_experts
+    assert_rows_close(got["dx"], ref["dx"], TOL_BF16, "dx")
+    r = _check_matrix(got["dw_router"], ref["dw_router"], "dw_router")
+    say(f"  dw_router: RMS(err)/RMS = {r[0]:.3e}, max|err|/RMS = {r[1]:.3e}")
+    if cfg.n_null == 0:
+        assert (got["dw_router"][N] == 0).all()
+    counts = np.diff(ref["fwd"]["offsets"])
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        worst = (0.0, 0.0)
+        for e in range(N):
+            if counts[e] == 0:
+                assert (got[name][e] == 0).all(), f"{name}[{e}]: expert without tokens"
+                continue
+            r = _check_matrix(got[name][e], ref[name][e], f"{name}[{e}]")
+            worst = (max(worst[0], r[0]), max(worst[1], r[1]))
+        say(f"  {name}: worst per-expert RMS(err)/RMS = {worst[0]:.3e}, max|err|/RMS = {worst[1]:.3e} "
+            f"over {int((counts > 0).sum())} experts")
+    if cfg.d_ff_shared:
+        for name in ("dws_gate", "dws_up", "dws_down"):
+            r = _check_matrix(got[name], ref[name], name)
+            say(f"  {name}: RMS(err)/RMS = {r[0]:.3e}, max|err|/RMS = {r[1]:.3e}")
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_matches_oracle(case):
+    cfg, _, _, got, ref = _run(case, 2e-2, 1e-3)
+    _check(cfg, got, ref)
+
+
+def test_backward_strong_aux_terms():
+    """Large loss weights make the router gradient dominated by L_bal and L_z."""
+    cfg, _, _, got, ref = _run("nullpool_shared", 3.0, 0.5, seed=3)
+    _check(cfg, got, ref)
+
+
+def test_backward_deterministic():
+    cfg, layer, dy, got, _ = _run("wide", 2e-2, 1e-3, seed=5)
+    g2 = layer.backward(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    for k, v in g2.items():
+        if v is not None:
+            np.testing.assert_array_equal(to_host(v), got[k], err_msg=k)

@@ -24,7 +24,7 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_
 MOE_F32, MOE_BF16 = 0, 1
 MOE_NULL_ZERO, MOE_NULL_COPY, MOE_NULL_CONSTANT = 0, 1, 2
 NULL_KINDS = {"zero": MOE_NULL_ZERO, "copy": MOE_NULL_COPY, "constant": MOE_NULL_CONSTANT}
-MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_AUX = range(4)
+MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_AUX, MOE_WS_BACKWARD = range(5)
 MOE_GEMM_GATE_UP, MOE_GEMM_DOWN = 0, 1
 
 
@@ -52,6 +52,11 @@ class AuxOut(ctypes.Structure):
                 ("logits", "topk_idx", "topk_w", "n_real", "offsets", "counts", "f", "P", "scalars")]
 
 
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down")]
+
+
 _lib = None
 _P = ctypes.c_void_p
 
@@ -75,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
         "moe_layer_forward": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P,
                               ctypes.c_size_t, _P],
+        "moe_layer_backward": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_float, ctypes.c_float,
+                               ctypes.POINTER(LayerGrads), _P, ctypes.c_size_t, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -209,6 +216,14 @@ def moe_layer_forward(dims, params: LayerParams, y, aux: AuxOut = None, ws=None,
     _check(load_library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(params), _ptr(y),
                                              ctypes.byref(aux) if aux is not None else None, wp, wb,
                                              _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_backward(dims, params: LayerParams, dy, alpha: float, beta: float, grads: LayerGrads,
+                       ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _check(load_library().moe_layer_backward(ctypes.byref(dims), ctypes.byref(params), _ptr(dy),
+                                              float(alpha), float(beta), ctypes.byref(grads), wp, wb,
+                                              _stream(stream)), "moe_layer_backward")
 
 
 from .layer import MoeLayer  # noqa: E402,F401

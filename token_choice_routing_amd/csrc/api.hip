@@ -108,6 +108,67 @@ LayerWs layer_ws(const moe_dims* d) {
   return w;
 }
 
+// Backward workspace: the forward's routing state (recomputed), the expert
+// pre-activations and gradients of the routed slots, bf16 transposed weights, and the
+// activations transposed per segment for the weight gradients (segments padded to 8
+// columns: Rp = R + 8 N columns at most).
+struct BwdWs {
+  LayerWs fwd;
+  size_t f, g, u, h, yp, dyp, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
+  size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, total;
+  int64_t Rp, Tp;
+};
+
+BwdWs bwd_ws(const moe_dims* d) {
+  BwdWs w{};
+  w.fwd = layer_ws(d);
+  const int64_t T = d->T, R = max_rows(d), dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
+  const int N = d->n_experts, M = d->n_null;
+  w.Rp = R + 8 * (int64_t)N;
+  w.Tp = (T + 7) & ~int64_t(7);
+  size_t o = w.fwd.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.f = take((size_t)(N + M) * 4);
+  w.g = take((size_t)R * F * 4);
+  w.u = take((size_t)R * F * 4);
+  w.h = take((size_t)R * F * 2);
+  w.yp = take((size_t)R * dm * 4);
+  w.dyp = take((size_t)R * dm * 2);
+  w.dw = take((size_t)T * d->top_k * 4);
+  w.ds = take((size_t)T * (N + 1) * 4);
+  w.wdT = take((size_t)N * F * dm * 2);
+  w.wguT = take((size_t)N * dm * 2 * F * 2);
+  w.dh = take((size_t)R * F * 4);
+  w.dgu = take((size_t)R * 2 * F * 2);
+  w.dxp = take((size_t)R * dm * 4);
+  w.kofs = take((size_t)(N + 1) * 4);
+  w.xpT = take((size_t)dm * w.Rp * 2);
+  w.dypT = take((size_t)dm * w.Rp * 2);
+  w.hT = take((size_t)F * w.Rp * 2);
+  w.dguT = take((size_t)2 * F * w.Rp * 2);
+  w.rpart = take(router_wgrad_ws_bytes(T, N + 1, (int)dm));
+  if (Fs) {
+    w.gs = take((size_t)T * Fs * 4);
+    w.us = take((size_t)T * Fs * 4);
+    w.hs = take((size_t)T * Fs * 2);
+    w.dhs = take((size_t)T * Fs * 4);
+    w.dgus = take((size_t)T * 2 * Fs * 2);
+    w.dxs = take((size_t)T * dm * 4);
+    w.wsdT = take((size_t)Fs * dm * 2);
+    w.wsguT = take((size_t)dm * 2 * Fs * 2);
+    w.xT = take((size_t)dm * w.Tp * 2);
+    w.dyT = take((size_t)dm * w.Tp * 2);
+    w.hsT = take((size_t)Fs * w.Tp * 2);
+    w.dgusT = take((size_t)2 * Fs * w.Tp * 2);
+  }
+  w.total = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,6 +195,7 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t which) {
       return d->dtype == MOE_BF16 ? route_ws_bytes(d->T, d->n_experts, d->d_model) : 0;
     case MOE_WS_PERMUTE: return permute_ws_bytes(d->T, d->n_experts);
     case MOE_WS_AUX: return aux_ws_bytes(d->n_experts, d->n_null);
+    case MOE_WS_BACKWARD: return d->dtype == MOE_BF16 ? bwd_ws(d).total : 0;
   }
   return 0;
 }
@@ -389,6 +451,163 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   CombineArgs ca{bf16, d->T, d->top_k, d->d_model, R, at(L.yp), slot_pos, topk_w,
                  d->d_ff_shared ? at(L.ys) : nullptr, nsrc, null_stride(d), y};
   HIP_TRY(launch_combine(ca, s));
+  return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,
+                              float beta, const moe_layer_grads* gr, void* ws, size_t ws_bytes,
+                              moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (!p || !gr) return MOE_ERR_ARG;
+  if (d->dtype != MOE_BF16 || d->null_kind != MOE_NULL_ZERO) return MOE_ERR_UNSUPPORTED;
+  const BwdWs W = bwd_ws(d);
+  const int64_t T = d->T, dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
+  // bf16 operands at 32-bit byte offsets (transposed activations: rows of Rp columns)
+  if (!fits_4g(T, dm) || !fits_4g(2 * F, dm) || !fits_4g(2 * std::max<int64_t>(F, Fs), W.Rp) ||
+      !fits_4g(dm, W.Rp) || !fits_4g(Fs, W.Tp) || !fits_4g(dm, 2 * F) || !fits_4g(dm, W.Tp))
+    return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(need(p->x));
+  MOE_TRY(need(p->w_router));
+  MOE_TRY(maybe(p->null_bias_tok));
+  MOE_TRY(need(p->w_gate));
+  MOE_TRY(need(p->w_up));
+  MOE_TRY(need(p->w_down));
+  if (Fs) {
+    MOE_TRY(need(p->ws_gate));
+    MOE_TRY(need(p->ws_up));
+    MOE_TRY(need(p->ws_down));
+    MOE_TRY(need(gr->dws_gate));
+    MOE_TRY(need(gr->dws_up));
+    MOE_TRY(need(gr->dws_down));
+  }
+  MOE_TRY(need(dy));
+  MOE_TRY(need(gr->dx));
+  MOE_TRY(need(gr->dw_router));
+  MOE_TRY(need(gr->dw_gate));
+  MOE_TRY(need(gr->dw_up));
+  MOE_TRY(need(gr->dw_down));
+  if (!ws || ws_bytes < W.total) return MOE_ERR_WORKSPACE;
+  MOE_TRY(need(ws));
+  if (T == 0) return MOE_OK;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  auto fp = [&](size_t off) { return static_cast<float*>(at(off)); };
+  auto ip = [&](size_t off) { return static_cast<int32_t*>(at(off)); };
+  const LayerWs& L = W.fwd;
+  float* logits = fp(L.logits);
+  int32_t* topk_idx = ip(L.topk_idx);
+  float* topk_w = fp(L.topk_w);
+  int32_t* offsets = ip(L.offsets);
+  int32_t* perm_token = ip(L.perm_token);
+  int32_t* slot_pos = ip(L.slot_pos);
+  int32_t* permute_ws = ip(L.permute);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t R = max_rows(d);
+  const int N = d->n_experts, M = d->n_null, K = d->top_k;
+  const int cus = cu_count();
+  const uint16_t* x16 = static_cast<const uint16_t*>(p->x);
+  auto bf = [&](size_t off) { return static_cast<const uint16_t*>(at(off)); };
+  (void)hipGetLastError();
+
+  // 1-2. the forward's routing, permutation and pool counts f, recomputed
+  RouteArgs ra{T, d->d_model, N, M, K, true, true, p->x, p->w_router, p->null_bias, p->null_bias_tok,
+               nullptr, logits, topk_idx, topk_w, ip(L.n_real), at(L.route), permute_ws, ip(L.rhist),
+               static_cast<double*>(at(L.tstats)), d->null_kind};
+  HIP_TRY(launch_route(ra, s));
+  AuxTiles af{static_cast<double*>(at(L.tstats)), ip(L.rhist), fp(W.f), nullptr, nullptr, nullptr};
+  PermuteArgs pa{T, K, N, M, d->d_model, 2, topk_idx, nullptr, ip(L.counts), offsets, perm_token, slot_pos,
+                 nullptr, permute_ws, true, &af};
+  HIP_TRY(launch_permute(pa, s));
+
+  // 3. expert pre-activations g = x W_g^T, u = x W_u^T (float32) and h = silu(g) u
+  GemmProblem g1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate), nullptr,
+                 (int)F, (int)dm, at(W.g)};
+  GemmProblem u1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_up), nullptr,
+                 (int)F, (int)dm, at(W.u)};
+  HIP_TRY(launch_gemm_pair(true, 1, g1, u1, cus, s, 3));
+  HIP_TRY(launch_swiglu_h(fp(W.g), fp(W.u), offsets, N, R, (int)F, at(W.h), s));
+  if (Fs) {
+    GemmProblem gs{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_gate), nullptr, (int)Fs,
+                   (int)dm, at(W.gs)};
+    GemmProblem us{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_up), nullptr, (int)Fs,
+                   (int)dm, at(W.us)};
+    HIP_TRY(launch_gemm_pair(true, 1, gs, us, cus, s, 3));
+    HIP_TRY(launch_swiglu_h(fp(W.gs), fp(W.us), nullptr, 1, T, (int)Fs, at(W.hs), s));
+  }
+  // 4. expert outputs Y = h W_d^T (float32), for the weight gradients dg = <dy, Y>
+  GemmProblem y2{bf(W.h), nullptr, R, offsets, N, R, static_cast<const uint16_t*>(p->w_down), nullptr, (int)dm,
+                 (int)F, at(W.yp)};
+  HIP_TRY(launch_gemm_pair(true, 1, y2, GemmProblem{}, cus, s, 3));
+
+  // 5. combine backward (dY = g dy per real slot, dg) and router backward (ds)
+  HIP_TRY(launch_combine_bwd(dy, fp(W.yp), slot_pos, topk_w, T, K, (int)dm, R, at(W.dyp), fp(W.dw), s));
+  HIP_TRY(launch_router_bwd(logits, topk_idx, topk_w, fp(W.dw), fp(W.f), T, N, M, K, alpha, beta, fp(W.ds), s));
+
+  // 6. transposed bf16 weights: W_d^T [N][F][d]; [W_g ; W_u]^T [N][d][2F]
+  HIP_TRY(launch_transpose(p->w_down, N, dm, F, at(W.wdT), dm, 0, F * dm, s));
+  HIP_TRY(launch_transpose(p->w_gate, N, F, dm, at(W.wguT), 2 * F, 0, dm * 2 * F, s));
+  HIP_TRY(launch_transpose(p->w_up, N, F, dm, at(W.wguT), 2 * F, F, dm * 2 * F, s));
+  if (Fs) {
+    HIP_TRY(launch_transpose(p->ws_down, 1, dm, Fs, at(W.wsdT), dm, 0, 0, s));
+    HIP_TRY(launch_transpose(p->ws_gate, 1, Fs, dm, at(W.wsguT), 2 * Fs, 0, 0, s));
+    HIP_TRY(launch_transpose(p->ws_up, 1, Fs, dm, at(W.wsguT), 2 * Fs, Fs, 0, s));
+  }
+
+  // 7. dh = dY W_d (routed) and dy W_sd (shared), then the SwiGLU backward
+  GemmProblem h3{bf(W.dyp), nullptr, R, offsets, N, R, bf(W.wdT), nullptr, (int)F, (int)dm, at(W.dh)};
+  GemmProblem hs3{};
+  if (Fs)
+    hs3 = GemmProblem{static_cast<const uint16_t*>(dy), nullptr, T, nullptr, 1, T, bf(W.wsdT), nullptr, (int)Fs,
+                      (int)dm, at(W.dhs)};
+  HIP_TRY(launch_gemm_pair(true, 1, h3, hs3, cus, s, 3));
+  HIP_TRY(launch_swiglu_bwd(fp(W.g), fp(W.u), fp(W.dh), offsets, N, R, (int)F, at(W.dgu), s));
+  if (Fs) HIP_TRY(launch_swiglu_bwd(fp(W.gs), fp(W.us), fp(W.dhs), nullptr, 1, T, (int)Fs, at(W.dgus), s));
+
+  // 8. da = [dg | du] [W_g ; W_u]: routed rows and shared rows (float32)
+  GemmProblem a4{bf(W.dgu), nullptr, R, offsets, N, R, bf(W.wguT), nullptr, (int)dm, (int)(2 * F), at(W.dxp)};
+  GemmProblem as4{};
+  if (Fs)
+    as4 = GemmProblem{bf(W.dgus), nullptr, T, nullptr, 1, T, bf(W.wsguT), nullptr, (int)dm, (int)(2 * Fs),
+                      at(W.dxs)};
+  HIP_TRY(launch_gemm_pair(true, 1, a4, as4, cus, s, 3));
+
+  // 9. dx = sum over the token's slots of da + shared da + ds W_r; dW_r = ds^T x
+  HIP_TRY(launch_scatter_dx(fp(W.dxp), slot_pos, K, R, Fs ? fp(W.dxs) : nullptr, fp(W.ds), p->w_router, N + 1,
+                            (int)dm, T, gr->dx, s));
+  HIP_TRY(launch_router_wgrad(fp(W.ds), p->x, T, N + 1, (int)dm, fp(W.rpart), gr->dw_router, s));
+
+  // 10. weight gradients: activations transposed per segment, K = the segment's rows
+  int32_t* kofs = ip(W.kofs);
+  HIP_TRY(launch_pad_offsets(offsets, N, R, kofs, s));
+  HIP_TRY(launch_transpose_segments(p->x, perm_token, T, offsets, kofs, N, R, dm, at(W.xpT), W.Rp, s));
+  HIP_TRY(launch_transpose_segments(at(W.dyp), nullptr, R, offsets, kofs, N, R, dm, at(W.dypT), W.Rp, s));
+  HIP_TRY(launch_transpose_segments(at(W.h), nullptr, R, offsets, kofs, N, R, F, at(W.hT), W.Rp, s));
+  HIP_TRY(launch_transpose_segments(at(W.dgu), nullptr, R, offsets, kofs, N, R, 2 * F, at(W.dguT), W.Rp, s));
+  // dW_d[e] = dY_e^T h_e: rows d of dY^T, columns F of h^T
+  GemmProblem wd{bf(W.dypT), nullptr, dm, nullptr, N, N * dm, bf(W.hT), nullptr, (int)F, (int)W.Rp, gr->dw_down,
+                 kofs, W.Rp, W.Rp, (int)dm};
+  GemmProblem wsd{};
+  if (Fs) {
+    HIP_TRY(launch_transpose_segments(p->x, nullptr, T, nullptr, nullptr, 1, T, dm, at(W.xT), W.Tp, s));
+    HIP_TRY(launch_transpose_segments(dy, nullptr, T, nullptr, nullptr, 1, T, dm, at(W.dyT), W.Tp, s));
+    HIP_TRY(launch_transpose_segments(at(W.hs), nullptr, T, nullptr, nullptr, 1, T, Fs, at(W.hsT), W.Tp, s));
+    HIP_TRY(launch_transpose_segments(at(W.dgus), nullptr, T, nullptr, nullptr, 1, T, 2 * Fs, at(W.dgusT), W.Tp, s));
+    wsd = GemmProblem{bf(W.dyT), nullptr, dm, nullptr, 1, dm, bf(W.hsT), nullptr, (int)Fs, (int)W.Tp, gr->dws_down};
+  }
+  HIP_TRY(launch_gemm_pair(true, 1, wd, wsd, cus, s, 3));
+  // dW_g[e] = dg_e^T x_e, dW_u[e] = du_e^T x_e (rows F and F..2F of [dg | du]^T)
+  GemmProblem wg{bf(W.dguT), nullptr, F, nullptr, N, N * F, bf(W.xpT), nullptr, (int)dm, (int)W.Rp, gr->dw_gate,
+                 kofs, W.Rp, W.Rp, (int)F};
+  GemmProblem wu{bf(W.dguT) + F * W.Rp, nullptr, F, nullptr, N, N * F, bf(W.xpT), nullptr, (int)dm, (int)W.Rp,
+                 gr->dw_up, kofs, W.Rp, W.Rp, (int)F};
+  HIP_TRY(launch_gemm_pair(true, 1, wg, wu, cus, s, 3));
+  if (Fs) {
+    GemmProblem wsg{bf(W.dgusT), nullptr, Fs, nullptr, 1, Fs, bf(W.xT), nullptr, (int)dm, (int)W.Tp, gr->dws_gate};
+    GemmProblem wsu{bf(W.dgusT) + Fs * W.Tp, nullptr, Fs, nullptr, 1, Fs, bf(W.xT), nullptr, (int)dm, (int)W.Tp,
+                    gr->dws_up};
+    HIP_TRY(launch_gemm_pair(true, 1, wsg, wsu, cus, s, 3));
+  }
   return MOE_OK;
 }
 

@@ -1,0 +1,388 @@
+// Backward pass of the null-expert MoE layer (bf16, null experts that output zero).
+//
+// Role: the gradients that training the layer needs ([Review] section 3 trains the
+// layer with the load-balance and z-loss terms added to the task loss; [Primer]
+// sections 4.2 and 4.3). The objective is L = <dy, y> + alpha L_bal + beta L_z for an
+// upstream gradient dy, the routing decision held fixed (top-K is piecewise constant).
+// The backward recomputes what the forward produced (routing, permutation, expert
+// pre-activations) instead of keeping it, then:
+//
+//   combine      dY_p = g dy_t (bf16) and dg = <dy_t, Y_p> per real slot
+//   router       ds = renormalised-softmax backward of dg + the pool-softmax terms of
+//                L_bal and L_z; dW_r = ds^T x, and dx gets ds W_r
+//   experts      dh = dY W_d, (dg, du) = SwiGLU backward, da = [dg | du] [W_g ; W_u],
+//                dW_d = dY^T h, dW_g = dg^T a, dW_u = du^T a
+//
+// Every contraction of the experts runs on the MFMA grouped GEMM of the forward: the
+// data gradients on the weights transposed per expert (bf16 copies made here), the
+// weight gradients on the activations transposed per segment (segments padded to 8
+// columns, so every group's K range starts 16-byte aligned), with K the segment's
+// rows. This file holds the data-movement and element-wise kernels around them.
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTile = 64;
+
+// out[b][c][r] = in[b][r][c] (bf16 bits) for an [R][C] matrix per batch b; out rows have
+// stride ldo and start at column offset c_out of a wider output row. 64 x 64 tiles
+// through LDS, 256 threads: coalesced on C when reading, on R when writing.
+__global__ void __launch_bounds__(256)
+transpose_kernel(const bf16_t* __restrict__ in, int64_t R, int64_t C, int64_t in_batch,
+                 bf16_t* __restrict__ out, int64_t ldo, int64_t c_out, int64_t out_batch) {
+  __shared__ bf16_t t[kTile][kTile + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
+  const bf16_t* src = in + (int64_t)blockIdx.z * in_batch;
+  bf16_t* dst = out + (int64_t)blockIdx.z * out_batch;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    t[i][tx] = r < R && c < C ? src[r * C + c] : bf16_t(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) dst[c * ldo + c_out + r] = t[tx][i];
+  }
+}
+
+// Segment starts padded to multiples of 8: kofs[e] = sum_{i<e} round_up(len_i, 8),
+// kofs[G] the total. One wavefront; segments read from offsets exactly as the GEMM
+// clamps them.
+__global__ void __launch_bounds__(64) pad_offsets_kernel(const int32_t* __restrict__ offsets, int G,
+                                                         int64_t rows, int32_t* __restrict__ kofs) {
+  if (threadIdx.x != 0) return;
+  int run = 0;
+  for (int e = 0; e < G; ++e) {
+    int64_t a = offsets[e], b = offsets[e + 1];
+    a = min<int64_t>(max<int64_t>(a, 0), rows);
+    b = min<int64_t>(max<int64_t>(b, a), rows);
+    kofs[e] = run;
+    run += (int)((b - a + 7) & ~int64_t(7));
+  }
+  kofs[G] = run;
+}
+
+// dst[c][q] for padded positions q of the segments: row p = offsets[e] + (q - kofs[e])
+// of src (read through src_rows[p] when given) while q - kofs[e] < len_e, else 0.
+// offsets == NULL means one segment [0, rows) padded to ld. Columns c < C; dst rows
+// have stride ld (>= kofs[G]); positions at or past kofs[G] are not written.
+__global__ void __launch_bounds__(256)
+transpose_segments_kernel(const bf16_t* __restrict__ src, const int32_t* __restrict__ src_rows,
+                          int64_t src_nrows, const int32_t* __restrict__ offsets,
+                          const int32_t* __restrict__ kofs, int G, int64_t rows, int64_t C,
+                          bf16_t* __restrict__ dst, int64_t ld) {
+  __shared__ bf16_t t[kTile][kTile + 2];
+  __shared__ int64_t srow[kTile];
+  const int64_t q0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
+  const int64_t total = offsets ? kofs[G] : (rows + 7) & ~int64_t(7);
+  if (q0 >= total) return;
+  if (threadIdx.x < kTile) {
+    const int64_t q = q0 + threadIdx.x;
+    int64_t p = -1;
+    if (q < total) {
+      if (offsets) {
+        int lo = 0, hi = G;  // kofs[lo] <= q < kofs[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (kofs[mid] <= q) lo = mid; else hi = mid;
+        }
+        int64_t a = offsets[lo], b = offsets[lo + 1];
+        a = min<int64_t>(max<int64_t>(a, 0), rows);
+        b = min<int64_t>(max<int64_t>(b, a), rows);
+        const int64_t local = q - kofs[lo];
+        if (local < b - a) p = a + local;
+      } else if (q < rows) {
+        p = q;
+      }
+      if (p >= 0 && src_rows) p = min<int64_t>(max<int64_t>(src_rows[p], 0), src_nrows - 1);
+    }
+    srow[threadIdx.x] = p;
+  }
+  __syncthreads();
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) {
+    const int64_t p = srow[i], c = c0 + tx;
+    t[i][tx] = p >= 0 && c < C ? src[p * C + c] : bf16_t(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int64_t c = c0 + i, q = q0 + tx;
+    if (c < C && q < total) dst[c * ld + q] = t[tx][i];
+  }
+}
+
+// Rows below the real-row count (offsets[G], or rows when offsets is NULL).
+__device__ __forceinline__ int64_t live_rows(const int32_t* offsets, int G, int64_t rows) {
+  return offsets ? min<int64_t>(max<int64_t>(offsets[G], 0), rows) : rows;
+}
+
+// h = silu(g) * u, rounded to bf16 (the forward's expert activation, recomputed).
+__global__ void __launch_bounds__(256)
+swiglu_h_kernel(const float* __restrict__ g, const float* __restrict__ u, const int32_t* offsets, int G,
+                int64_t rows, int F, bf16_t* __restrict__ h) {
+  const int64_t n = live_rows(offsets, G, rows) * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    h[i] = f32_to_bf16(silu(g[i]) * u[i]);
+}
+
+// SwiGLU backward: dgu[p][j] = dh u silu'(g), dgu[p][F + j] = dh silu(g), bf16, with
+// silu'(z) = sigma(z) (1 + z (1 - sigma(z))).
+__global__ void __launch_bounds__(256)
+swiglu_bwd_kernel(const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ dh,
+                  const int32_t* offsets, int G, int64_t rows, int F, bf16_t* __restrict__ dgu) {
+  const int64_t n = live_rows(offsets, G, rows) * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = i / F, j = i - p * F;
+    const float z = g[i], sg = 1.0f / (1.0f + __expf(-z));
+    const float d = dh[i];
+    dgu[p * 2 * F + j] = f32_to_bf16(d * u[i] * (sg * (1.0f + z * (1.0f - sg))));
+    dgu[p * 2 * F + F + j] = f32_to_bf16(d * z * sg);
+  }
+}
+
+// Combine backward, one wavefront per token: for each real slot k (slot_pos >= 0)
+// dy_perm[p] = topk_w dy_t (bf16) and dw[t][k] = <dy_t, y_perm[p]> (float32, lanes
+// add in a fixed order).
+__global__ void __launch_bounds__(256)
+combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y_perm,
+                   const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w, int64_t T,
+                   int K, int d, int64_t R, bf16_t* __restrict__ dy_perm, float* __restrict__ dw) {
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const bf16_t* dyt = dy + t * d;
+  for (int k = 0; k < K; ++k) {
+    const int32_t p = slot_pos[t * K + k];
+    if (p < 0 || p >= R) {
+      if (lane == 0) dw[t * K + k] = 0.0f;
+      continue;
+    }
+    const float w = topk_w[t * K + k];
+    const float* yp = y_perm + (int64_t)p * d;
+    bf16_t* o = dy_perm + (int64_t)p * d;
+    float acc = 0.0f;
+    for (int c = lane; c < d; c += kWave) {
+      const float v = bf16_to_f32(dyt[c]);
+      o[c] = f32_to_bf16(w * v);
+      acc += v * yp[c];
+    }
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kWave);
+    if (lane == 0) dw[t * K + k] = acc;
+  }
+}
+
+// Router backward, one wavefront per token, in float64: ds[t][j] for the N real logits
+// and the null logit (column N) from
+//   the renormalised weights: ds_j += g_j (dg_j - sum_i g_i dg_i) over the chosen reals;
+//   L_bal:  ds_c += alpha (N / T) p_c (f_c - sum_i f_i p_i) over the N + M pool;
+//   L_z:    ds_c += beta (2 / T) lse p_c;
+// the M null copies share one logit, so the null column gets their sum (none if M = 0).
+__global__ void __launch_bounds__(256)
+router_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+                  const float* __restrict__ topk_w, const float* __restrict__ dw,
+                  const float* __restrict__ f, int64_t T, int N, int M, int K, float alpha, float beta,
+                  float* __restrict__ ds) {
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const float* s = logits + t * (N + 1);
+  const double sn = s[N];
+  // pool max and partition function
+  double mx = M > 0 ? sn : -INFINITY;
+  for (int j = lane; j < N; j += kWave) mx = fmax(mx, (double)s[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, kWave));
+  double z = 0.0, fz = 0.0;  // sum e^{v - m}, sum f e^{v - m}
+  for (int j = lane; j < N; j += kWave) {
+    const double e = exp((double)s[j] - mx);
+    z += e;
+    fz += (double)f[j] * e;
+  }
+  double fnull = 0.0;  // sum of f over the null copies
+  for (int c = lane; c < M; c += kWave) fnull += (double)f[N + c];
+  z = wave_sum_double(z);
+  fz = wave_sum_double(fz);
+  fnull = wave_sum_double(fnull);
+  const double en = M > 0 ? exp(sn - mx) : 0.0;
+  z += M * en;
+  fz += fnull * en;
+  const double lse = mx + log(z), fbar = fz / z;
+  const double ka = (double)alpha * N / (double)T, kb = (double)beta * 2.0 / (double)T;
+  // weight term: sum over the chosen reals of g dg
+  double gdg = 0.0;
+  for (int k = 0; k < K; ++k)
+    if (topk_idx[t * K + k] < N) gdg += (double)topk_w[t * K + k] * dw[t * K + k];
+  float* o = ds + t * (N + 1);
+  for (int j = lane; j < N; j += kWave) {
+    const double p = exp((double)s[j] - mx) / z;
+    double v = ka * p * ((double)f[j] - fbar) + kb * lse * p;
+    for (int k = 0; k < K; ++k)
+      if (topk_idx[t * K + k] == j) v += (double)topk_w[t * K + k] * ((double)dw[t * K + k] - gdg);
+    o[j] = (float)v;
+  }
+  if (lane == 0) {
+    const double pn = en / z;
+    o[N] = M > 0 ? (float)(ka * pn * (fnull - M * fbar) + kb * lse * M * pn) : 0.0f;
+  }
+}
+
+// dW_r partial sums: part[c][j][col] = sum over tokens t of chunk c of ds[t][j] x[t][col]
+// (float32); 8 router rows x 256 columns per workgroup, one column per thread.
+constexpr int kRouterRows = 8;
+__global__ void __launch_bounds__(256)
+router_wgrad_partial_kernel(const float* __restrict__ ds, const bf16_t* __restrict__ x, int64_t T, int N1,
+                            int d, int64_t chunk, float* __restrict__ part) {
+  const int j0 = blockIdx.y * kRouterRows, col = blockIdx.x * 256 + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.z * chunk, t1 = min<int64_t>(T, t0 + chunk);
+  float acc[kRouterRows] = {};
+  __shared__ float sds[64][kRouterRows];
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * kRouterRows; i += 256) {
+      const int64_t t = tb + i / kRouterRows;
+      const int j = j0 + i % kRouterRows;
+      sds[i / kRouterRows][i % kRouterRows] = t < t1 && j < N1 ? ds[t * N1 + j] : 0.0f;
+    }
+    __syncthreads();
+    if (col < d) {
+      const int n = (int)min<int64_t>(64, t1 - tb);
+      for (int i = 0; i < n; ++i) {
+        const float xv = bf16_to_f32(x[(tb + i) * d + col]);
+#pragma unroll
+        for (int r = 0; r < kRouterRows; ++r) acc[r] += sds[i][r] * xv;
+      }
+    }
+  }
+  if (col < d)
+#pragma unroll
+    for (int r = 0; r < kRouterRows; ++r)
+      if (j0 + r < N1) part[((int64_t)blockIdx.z * N1 + j0 + r) * d + col] = acc[r];
+}
+
+// dW_r = sum of the chunk partials in chunk order (deterministic).
+__global__ void __launch_bounds__(256)
+router_wgrad_reduce_kernel(const float* __restrict__ part, int chunks, int64_t n, float* __restrict__ dw) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int c = 0; c < chunks; ++c) s += part[c * n + i];
+    dw[i] = s;
+  }
+}
+
+// dx[t] = sum over real slots of dx_perm[p] (slot order) + dx_shared[t] + ds[t] W_r,
+// one workgroup per token, float32.
+__global__ void __launch_bounds__(256)
+scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_pos, int K, int64_t R,
+                  const float* __restrict__ dx_shared, const float* __restrict__ ds,
+                  const float* __restrict__ w_router, int N1, int d, float* __restrict__ dx) {
+  const int64_t t = blockIdx.x;
+  __shared__ float sds[320];
+  __shared__ int32_t sp[64];
+  for (int j = threadIdx.x; j < N1; j += 256) sds[j] = ds[t * N1 + j];
+  for (int k = threadIdx.x; k < K; k += 256) sp[k] = slot_pos[t * K + k];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = dx_shared ? dx_shared[t * d + c] : 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const int32_t p = sp[k];
+      if (p >= 0 && p < R) v += dx_perm[(int64_t)p * d + c];
+    }
+    float r = 0.0f;
+    for (int j = 0; j < N1; ++j) r += sds[j] * w_router[(int64_t)j * d + c];
+    dx[t * d + c] = v + r;
+  }
+}
+
+unsigned grid_for(int64_t n, int per = 256) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + per - 1) / per, 8192));
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const void* in, int64_t batches, int64_t R, int64_t C, void* out, int64_t ldo,
+                            int64_t c_out, int64_t out_batch, hipStream_t s) {
+  if (batches <= 0 || R <= 0 || C <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + kTile - 1) / kTile), (unsigned)((R + kTile - 1) / kTile), (unsigned)batches);
+  transpose_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(in), R, C, R * C,
+                                        static_cast<bf16_t*>(out), ldo, c_out, out_batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int G, int64_t rows, int32_t* kofs, hipStream_t s) {
+  pad_offsets_kernel<<<1, 64, 0, s>>>(offsets, G, rows, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_segments(const void* src, const int32_t* src_rows, int64_t src_nrows,
+                                     const int32_t* offsets, const int32_t* kofs, int G, int64_t rows,
+                                     int64_t C, void* dst, int64_t ld, hipStream_t s) {
+  if (rows <= 0 || C <= 0 || ld <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + kTile - 1) / kTile), (unsigned)((ld + kTile - 1) / kTile));
+  transpose_segments_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), src_rows, src_nrows,
+                                                 offsets, kofs, G, rows, C, static_cast<bf16_t*>(dst), ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offsets, int G, int64_t rows, int F,
+                           void* h, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_h_kernel<<<grid_for(rows * F), 256, 0, s>>>(g, u, offsets, G, rows, F, static_cast<bf16_t*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
+                             int64_t rows, int F, void* dgu, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_bwd_kernel<<<grid_for(rows * F), 256, 0, s>>>(g, u, dh, offsets, G, rows, F, static_cast<bf16_t*>(dgu));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dy, const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                              int64_t T, int K, int d, int64_t R, void* dy_perm, float* dw, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  combine_bwd_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(static_cast<const bf16_t*>(dy), y_perm, slot_pos,
+                                                            topk_w, T, K, d, R, static_cast<bf16_t*>(dy_perm), dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* dw,
+                             const float* f, int64_t T, int N, int M, int K, float alpha, float beta, float* ds,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  router_bwd_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, topk_idx, topk_w, dw, f, T, N, M, K, alpha,
+                                                           beta, ds);
+  return hipGetLastError();
+}
+
+size_t router_wgrad_ws_bytes(int64_t T, int N1, int d) {
+  const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(32, (T + 511) / 512));
+  return (size_t)chunks * N1 * d * sizeof(float);
+}
+
+hipError_t launch_router_wgrad(const float* ds, const void* x, int64_t T, int N1, int d, float* part, float* dw,
+                               hipStream_t s) {
+  const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(32, (T + 511) / 512));
+  const int64_t chunk = (T + chunks - 1) / chunks;
+  const dim3 grid((unsigned)((d + 255) / 256), (unsigned)((N1 + kRouterRows - 1) / kRouterRows), (unsigned)chunks);
+  router_wgrad_partial_kernel<<<grid, 256, 0, s>>>(ds, static_cast<const bf16_t*>(x), T, N1, d, chunk, part);
+  const int64_t n = (int64_t)N1 * d;
+  router_wgrad_reduce_kernel<<<grid_for(n), 256, 0, s>>>(part, (int)chunks, n, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_dx(const float* dx_perm, const int32_t* slot_pos, int K, int64_t R, const float* dx_shared,
+                             const float* ds, const float* w_router, int N1, int d, int64_t T, float* dx,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  scatter_dx_kernel<<<(unsigned)T, 256, 0, s>>>(dx_perm, slot_pos, K, R, dx_shared, ds, w_router, N1, d, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -90,6 +90,8 @@ struct TileTable {
   int mt[kMaxGroups + 1];
   int nt[kMaxGroups + 1];
   int prefix[kMaxGroups + 1];
+  int kofs[kMaxGroups + 1];  // K range of each group (k_offsets problems; else 0, k_dim)
+  int klen[kMaxGroups + 1];
 };
 
 // Table of (group, column tile, row tile) over problem 0's groups followed by
@@ -106,11 +108,20 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int e = lane * kPer + q;
-      int s = 0, l = 0, nt = 0;
+      int s = 0, l = 0, nt = 0, ko = 0, kl = 0;
       if (e < G) {
         const GemmProblem& pr = e < G0 ? p0 : p1;
         const int ge = e < G0 ? e : e - G0;
-        if (pr.offsets) {
+        kl = pr.k_dim;
+        if (pr.k_offsets) {
+          ko = pr.k_offsets[ge];
+          kl = max(0, pr.k_offsets[ge + 1] - ko);
+        }
+        if (pr.rows_per_group > 0) {
+          const int64_t a = min<int64_t>((int64_t)ge * pr.rows_per_group, pr.max_rows);
+          s = (int)a;
+          l = (int)(min<int64_t>(a + pr.rows_per_group, pr.max_rows) - a);
+        } else if (pr.offsets) {
           int64_t a = pr.offsets[ge], b = pr.offsets[ge + 1];
           a = min<int64_t>(max<int64_t>(a, 0), pr.max_rows);
           b = min<int64_t>(max<int64_t>(b, a), pr.max_rows);
@@ -127,6 +138,8 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
         tt.len[e] = l;
         tt.mt[e] = m;
         tt.nt[e] = nt;
+        tt.kofs[e] = ko;
+        tt.klen[e] = kl;
       }
       cnt[q] = m * nt;
       local += cnt[q];
@@ -151,7 +164,8 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 
 // MODE kSwiGLU writes h as bf16 (the next MFMA's input); kPlain writes float32.
 // ROLE only names the launch in profiles (the code is identical): 0 standalone
-// grouped, 1 standalone single segment, 2 the layer's routed + shared launch.
+// grouped, 1 standalone single segment, 2 the layer's routed + shared launch, 3 the
+// layer backward's launches.
 //
 // Tile BM rows x BN weight rows x BK K on WM x WN wavefronts; each wavefront owns
 // (BM/WM) x (BN/WN) outputs as 32x32 MFMA blocks. K tiles stream through S LDS
@@ -232,7 +246,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   // only feed outputs that are never stored.
   struct Where {
     bool second;
-    int ge, Kdim, nk, m0, rows_valid, col0, ocp;
+    int ge, Kdim, kofs, nk, m0, rows_valid, col0, ocp;
   };
   auto locate = [&](int it, Where& w) {
     int L = r_begin + it, part = 0, parts = 1;
@@ -250,7 +264,8 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     w.second = e >= G0;
     const GemmProblem pr = w.second ? p1 : p0;
     w.ge = w.second ? e - G0 : e;
-    w.Kdim = pr.k_dim;
+    w.Kdim = tt.klen[e];
+    w.kofs = tt.kofs[e];
     w.nk = (w.Kdim + BK - 1) / BK;
     const int local = L - tt.prefix[e];
     const int mt = tt.mt[e];
@@ -300,30 +315,33 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
     for (int j = 0; j < JA; ++j)
       arow[j] = pr.a_rows ? min<int64_t>(max<int64_t>(q.arow[j], 0), pr.a_nrows - 1) : q.arow[j];
-    const uint32_t row_bytes = (uint32_t)t.Kdim * 2;
-    const int64_t wofs = (int64_t)t.ge * Nout * t.Kdim;
+    const int64_t lda = pr.lda ? pr.lda : pr.k_dim, ldb = pr.ldb ? pr.ldb : pr.k_dim;
+    const uint32_t a_rb = (uint32_t)lda * 2, b_rb = (uint32_t)ldb * 2;  // row strides, bytes
+    // b0/b1: this group's matrix, or for k_offsets problems the one shared matrix,
+    // entered at the group's first K column
+    const int64_t wofs = pr.k_offsets ? (int64_t)w.kofs : (int64_t)t.ge * Nout * ldb;
     // gathered rows address the whole activation matrix ((rows + 1) x row bytes at
     // most 4 GB, checked on the host); a contiguous segment's resource covers just
-    // the item's valid rows
-    const int64_t abase = pr.a_rows ? 0 : t.m0;
-    const uint32_t a_end = (uint32_t)((pr.a_rows ? pr.a_nrows : t.rows_valid) * row_bytes);
-    const uint32_t b_end = (uint32_t)Nout * row_bytes;
+    // the item's valid rows (for rows_per_group problems rows of the shared a)
+    const int64_t abase = pr.a_rows ? 0 : t.m0 - (pr.rows_per_group ? (int64_t)t.ge * pr.rows_per_group : 0);
+    const uint32_t a_end = (uint32_t)((pr.a_rows ? pr.a_nrows : t.rows_valid) * a_rb);
+    const uint32_t b_end = (uint32_t)Nout * b_rb;
     t.a_end = a_end;
     t.b_end = b_end;
-    t.ra = buffer_rsrc(pr.a + abase * t.Kdim, a_end);
+    t.ra = buffer_rsrc(pr.a + abase * lda + w.kofs, a_end);
     t.rb0 = buffer_rsrc(pr.b0 + wofs, b_end);
     t.rb1 = buffer_rsrc(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs, b_end);
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int r = RPI * (wave + NW * j) + lrow;
-      t.off[j] = r < t.rows_valid ? (uint32_t)(arow[j] - abase) * row_bytes : a_end;
+      t.off[j] = r >= t.rows_valid ? a_end : pr.a_rows ? (uint32_t)arow[j] * a_rb : (uint32_t)r * a_rb;
     }
 #pragma unroll
     for (int j = JA; j < J; ++j) {
       const int r = RPI * (wave + NW * j) + lrow - BM;
       const int c = MODE == kSwiGLU ? r % OC : r;  // output column within the tile
       const int n = t.col0 + c;
-      t.off[j] = c < ocp && n < Nout ? (uint32_t)n * row_bytes : b_end;
+      t.off[j] = c < ocp && n < Nout ? (uint32_t)n * b_rb : b_end;
     }
   };
   // K tile kt of item t into stage st; with q >= 0 only the loads of part q of
@@ -719,6 +737,8 @@ static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& 
     case 9: launch_variant<MODE, ROLE, 256, 256, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
     case 10: launch_variant<MODE, ROLE, 128, 256, 2, 4, 6, 32>(q0, q1, num_cus, stream); break;
     case 11: launch_variant<MODE, ROLE, 128, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
+    case 12: launch_variant<MODE, ROLE, 256, 256, 2, 4, 2, 64>(q0, q1, num_cus, stream); break;
+    case 13: launch_variant<MODE, ROLE, 256, 256, 4, 2, 2, 64>(q0, q1, num_cus, stream); break;
 #endif
     default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
   }
@@ -749,9 +769,10 @@ static void launch_skinny(const GemmProblem& q0, const GemmProblem& q1, int num_
 
 bool gemm_operands_fit(const GemmProblem& p) {
   if (p.groups == 0 || p.max_rows <= 0) return true;
-  const int64_t row_bytes = (int64_t)p.k_dim * 2;
-  return (int64_t)(p.n_out + 1) * row_bytes <= 0xFFFFFFFFll &&
-         (!p.a_rows || (p.a_nrows + 1) * row_bytes <= 0xFFFFFFFFll);
+  const int64_t a_rb = (p.lda ? p.lda : p.k_dim) * 2, b_rb = (p.ldb ? p.ldb : p.k_dim) * 2;
+  return (int64_t)(p.n_out + 1) * b_rb <= 0xFFFFFFFFll &&
+         (!p.a_rows || (p.a_nrows + 1) * a_rb <= 0xFFFFFFFFll) &&
+         (!p.rows_per_group || (int64_t)(p.rows_per_group + 1) * a_rb <= 0xFFFFFFFFll);
 }
 
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
@@ -761,10 +782,13 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   if (bf16 && (!gemm_operands_fit(p0) || !gemm_operands_fit(p1))) return hipErrorInvalidValue;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
-    if (std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows) {
+    auto plain_form = [](const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; };
+    if (plain_form(q0) && plain_form(q1) &&
+        std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows) {
 #define MOE_SKINNY_DISPATCH(M_)                                            \
   do {                                                                     \
-    if (role == 2) launch_skinny<M_, 2>(q0, q1, num_cus, stream);          \
+    if (role == 3) launch_skinny<M_, 3>(q0, q1, num_cus, stream);          \
+    else if (role == 2) launch_skinny<M_, 2>(q0, q1, num_cus, stream);     \
     else if (role == 1) launch_skinny<M_, 1>(q0, q1, num_cus, stream);     \
     else launch_skinny<M_, 0>(q0, q1, num_cus, stream);                    \
   } while (0)
@@ -776,7 +800,8 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     const int variant = MOE_GEMM_VARIANT;
 #define MOE_GEMM_DISPATCH(M_)                                                  \
   do {                                                                         \
-    if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream);      \
+    if (role == 3) launch_shape<M_, 3>(variant, q0, q1, num_cus, stream);      \
+    else if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream); \
     else if (role == 1) launch_shape<M_, 1>(variant, q0, q1, num_cus, stream); \
     else launch_shape<M_, 0>(variant, q0, q1, num_cus, stream);                \
   } while (0)

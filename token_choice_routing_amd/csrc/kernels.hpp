@@ -105,10 +105,17 @@ struct GemmProblem {
   const uint16_t* b1;       // gate/up: the up weights
   int n_out, k_dim;
   void* out;                // [max_rows][n_out]: bf16 h (op 0) or float32 (op 1)
+  // Weight-gradient form (bf16 op 1 only; all zero otherwise):
+  const int32_t* k_offsets;  // [groups+1] device or NULL: group e reduces over the K
+                             // columns [k_offsets[e], k_offsets[e+1]) (multiples of 8) of A
+                             // and of b0, which is then one [n_out][ldb] matrix for all groups
+  int64_t lda, ldb;          // row strides of a and b0/b1 in elements (0 = k_dim)
+  int rows_per_group;        // > 0: group e owns output rows [e*rpg, (e+1)*rpg) and reads
+                             // rows [0, rpg) of a (offsets unused)
 };
 // op 0: out = silu(a b0^T) * (a b1^T); op 1: out = a b0^T. Both problems in one launch.
 // role names the launch in profiles: 0 standalone grouped, 1 standalone single
-// segment, 2 the layer's fused launch.
+// segment, 2 the layer's fused launch, 3 the layer backward.
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
                             int num_cus, hipStream_t stream, int role);
 // bf16 operands are read through buffer resources with 32-bit byte offsets that may
@@ -116,6 +123,33 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
 // matrix (a_rows), each plus one row, must fit in 4 GB. False means the launch is
 // refused.
 bool gemm_operands_fit(const GemmProblem& p);
+
+// Backward-pass helpers (backward.hip); all enqueue on `s`, bf16 tensors as bits.
+// out[b][c][c_out + r] (row stride ldo, batch stride out_batch) = in[b][r][c], in [b][R][C].
+hipError_t launch_transpose(const void* in, int64_t batches, int64_t R, int64_t C, void* out, int64_t ldo,
+                            int64_t c_out, int64_t out_batch, hipStream_t s);
+// kofs[e] = segment starts padded to multiples of 8 (segments as the GEMM clamps them).
+hipError_t launch_pad_offsets(const int32_t* offsets, int G, int64_t rows, int32_t* kofs, hipStream_t s);
+// dst [C][ld]: each segment's rows (read through src_rows when given) as columns from
+// kofs[e], zero up to the next padded start; offsets NULL = one segment of `rows`.
+hipError_t launch_transpose_segments(const void* src, const int32_t* src_rows, int64_t src_nrows,
+                                     const int32_t* offsets, const int32_t* kofs, int G, int64_t rows,
+                                     int64_t C, void* dst, int64_t ld, hipStream_t s);
+hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offsets, int G, int64_t rows, int F,
+                           void* h, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
+                             int64_t rows, int F, void* dgu, hipStream_t s);
+hipError_t launch_combine_bwd(const void* dy, const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                              int64_t T, int K, int d, int64_t R, void* dy_perm, float* dw, hipStream_t s);
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* dw,
+                             const float* f, int64_t T, int N, int M, int K, float alpha, float beta, float* ds,
+                             hipStream_t s);
+size_t router_wgrad_ws_bytes(int64_t T, int N1, int d);
+hipError_t launch_router_wgrad(const float* ds, const void* x, int64_t T, int N1, int d, float* part, float* dw,
+                               hipStream_t s);
+hipError_t launch_scatter_dx(const float* dx_perm, const int32_t* slot_pos, int K, int64_t R, const float* dx_shared,
+                             const float* ds, const float* w_router, int N1, int d, int64_t T, float* dx,
+                             hipStream_t s);
 
 struct CombineArgs {
   bool bf16;

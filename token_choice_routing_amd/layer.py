@@ -1,11 +1,11 @@
 """Device-side holder for one layer call: uploads a workload's tensors once,
-owns the workspace and output buffers, and calls ``moe_layer_forward``.
-Marshalling only; the layer itself runs in the HIP library."""
+owns the workspace and output buffers, and calls ``moe_layer_forward`` (and
+``moe_layer_backward``). Marshalling only; the layer itself runs in the HIP library."""
 import numpy as np
 import torch
 
-from . import (AuxOut, LayerParams, MOE_BF16, MOE_WS_LAYER, dims_from_config, moe_layer_forward,
-               workspace_bytes)
+from . import (AuxOut, LayerGrads, LayerParams, MOE_BF16, MOE_WS_BACKWARD, MOE_WS_LAYER, dims_from_config,
+               moe_layer_backward, moe_layer_forward, workspace_bytes)
 
 
 def to_device(a, device="cuda"):
@@ -76,6 +76,26 @@ class MoeLayer:
         moe_layer_forward(self.dims, self.params, self.y, self.aux_full if aux else None, self.ws,
                           stream=stream)
         return self.y
+
+    GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down")
+
+    def backward(self, dy, alpha=0.0, beta=0.0, stream=None):
+        """Gradients of <dy, y> + alpha L_bal + beta L_z (float32 device tensors,
+        allocated on the first call and reused)."""
+        if getattr(self, "grads", None) is None:
+            cfg, dev, f32 = self.cfg, self.x.device, torch.float32
+            N, d, F, Fs = cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+            shapes = dict(dx=(self.T, d), dw_router=(N + 1, d), dw_gate=(N, F, d), dw_up=(N, F, d),
+                          dw_down=(N, d, F), dws_gate=(Fs, d), dws_up=(Fs, d), dws_down=(d, Fs))
+            self.grads = {k: torch.empty(v, dtype=f32, device=dev) if (Fs or not k.startswith("dws")) else None
+                          for k, v in shapes.items()}
+            p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+            self.grads_struct = LayerGrads(*(p(self.grads[k]) for k in self.GRADS))
+            self.ws_bwd = torch.empty((max(workspace_bytes(self.dims, MOE_WS_BACKWARD), 256),),
+                                      dtype=torch.uint8, device=dev)
+        moe_layer_backward(self.dims, self.params, dy, alpha, beta, self.grads_struct, self.ws_bwd,
+                           stream=stream)
+        return self.grads
 
     def results(self):
         """Host copies of every output (synchronises)."""
