@@ -143,3 +143,63 @@ def layer_loss(wl, dy, alpha=0.0, beta=0.0):
     fwd = O.layer_forward(wl)
     a = fwd["aux"]
     return float((np.asarray(dy, f64) * fwd["y"]).sum() + alpha * a["L_bal"] + beta * a["L_z"])
+
+
+def sampled_backward(wl, dy, alpha, beta, logits, tokens, experts):
+    """The same gradients restricted to what some outputs depend on, at any size: the
+    dx rows of ``tokens`` (their router term, their slots' expert terms and their
+    shared-expert term) and the weight gradients of ``experts`` (their segments'
+    rows). Routing, permutation and the pool statistics f, p, lse come from the whole
+    batch; the expert chains run only on the rows needed. Returns dict(dx [tokens],
+    ds [tokens], dw_gate / dw_up / dw_down {expert: matrix})."""
+    cfg = wl.cfg
+    if cfg.null_kind != "zero":
+        raise NotImplementedError("backward covers null experts that output zero")
+    N, M, K = cfg.n_experts, cfg.n_null, cfg.top_k
+    logits = np.asarray(logits, f64)
+    x = wl.values("x")
+    wr = wl.values("w_router")
+    T = x.shape[0]
+    dy = np.asarray(dy, f64)
+    topk, w, _ = O.route(logits, N, M, K)
+    counts, offsets, perm, slot_pos = O.permute(topk, N)
+    aux = O.aux_stats(logits, topk, N, M, K)
+    v = O._pool(logits, N, M)
+    tokens = np.asarray(tokens)
+    out = dict(dw_gate={}, dw_up={}, dw_down={})
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows = perm[lo:hi]
+        ks = np.array([int(np.nonzero(slot_pos[t] == p)[0][0]) for t, p in zip(rows, range(lo, hi))],
+                      dtype=np.int64).reshape(-1)
+        dY = w[rows, ks][:, None] * dy[rows] if hi > lo else np.zeros((0, x.shape[1]))
+        b = _swiglu_backward(x[rows], wl.w_gate[e], wl.w_up[e], wl.w_down[e], dY)
+        out["dw_gate"][e], out["dw_up"][e], out["dw_down"][e] = b["dw_gate"], b["dw_up"], b["dw_down"]
+    ds = np.zeros((len(tokens), N + 1), f64)
+    dx = np.zeros((len(tokens), x.shape[1]), f64)
+    mx = v[tokens].max(axis=1, keepdims=True)
+    ex = np.exp(v[tokens] - mx)
+    p = ex / ex.sum(axis=1, keepdims=True)
+    lse = aux["lse"][tokens]
+    f = aux["f"]
+    fbar = p @ f
+    dv = alpha * (N / T) * p * (f[None, :] - fbar[:, None]) + beta * (2.0 / T) * lse[:, None] * p
+    ds[:, :N] = dv[:, :N]
+    if M:
+        ds[:, N] = dv[:, N:].sum(axis=1)
+    for i, t in enumerate(tokens):
+        real = [k for k in range(K) if topk[t, k] < N]
+        dg = {}
+        for k in real:
+            e = topk[t, k]
+            a = x[t:t + 1]
+            dg[k] = float((dy[t] * O.swiglu_ffn(a, wl.w_gate[e], wl.w_up[e], wl.w_down[e])[0]).sum())
+            dx[i] += _swiglu_backward(a, wl.w_gate[e], wl.w_up[e], wl.w_down[e], w[t, k] * dy[t:t + 1])["da"][0]
+        gdg = sum(w[t, k] * dg[k] for k in real)
+        for k in real:
+            ds[i, topk[t, k]] += w[t, k] * (dg[k] - gdg)
+        if cfg.d_ff_shared:
+            dx[i] += _swiglu_backward(x[t:t + 1], wl.ws_gate, wl.ws_up, wl.ws_down, dy[t:t + 1])["da"][0]
+    dx += ds @ wr
+    out.update(dx=dx, ds=ds)
+    return out

@@ -118,3 +118,36 @@ def test_backward_deterministic():
     for k, v in g2.items():
         if v is not None:
             np.testing.assert_array_equal(to_host(v), got[k], err_msg=k)
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_rho1", "qwen3_1p7b_rho0p25"])
+def test_backward_full_size_sampled(name):
+    """Benchmark shapes at full size: dx of sampled tokens and the weight gradients of
+    sampled experts (the first, a middle and the last expert that received rows)
+    against the sampled oracle, routed with the GPU's logits; the router gradient
+    and the shared expert's through the RMS criterion on sampled rows of dW."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[name]
+    say(f"  backward full size {name}")
+    wl = generate(cfg)
+    layer = MoeLayer(wl)
+    layer.forward()
+    out = layer.results()
+    rng = np.random.default_rng(11)
+    dy_bits = bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+    alpha, beta = 2e-2, 1e-3
+    g = layer.backward(to_device(dy_bits), alpha, beta)
+    torch.cuda.synchronize()
+    counts = np.diff(out["offsets"])
+    nonempty = np.nonzero(counts)[0]
+    experts = sorted({int(nonempty[0]), int(nonempty[len(nonempty) // 2]), int(nonempty[-1])})
+    tokens = np.sort(rng.choice(cfg.T, size=24, replace=False))
+    ref = B.sampled_backward(wl, vals(dy_bits), alpha, beta, out["logits"].astype(np.float64), tokens, experts)
+    assert_rows_close(to_host(g["dx"])[tokens], ref["dx"], TOL_BF16, f"dx sampled {name}")
+    for nm in ("dw_gate", "dw_up", "dw_down"):
+        full = to_host(g[nm])
+        for e in experts:
+            r = _check_matrix(full[e], ref[nm][e], f"{nm}[{e}]")
+            say(f"  {nm}[{e}] ({counts[e]} rows): RMS(err)/RMS = {r[0]:.3e}, max|err|/RMS = {r[1]:.3e}")
+        for e in np.nonzero(counts == 0)[0]:
+            assert (full[e] == 0).all()

@@ -154,3 +154,20 @@ def test_expert_gradients_equal_dense_per_expert_autodiff_free_form():
             h = O.silu(wl.w_gate[e] @ x[t]) * (wl.w_up[e] @ x[t])
             ref[e] += np.outer(fwd["topk_w"][t, k] * dy[t], h)
     np.testing.assert_allclose(g["dw_down"], ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed,M,K", [(3, 5, 3), (11, 0, 2), (5, 2, 4)])
+def test_sampled_backward_equals_full(seed, M, K):
+    """The sampled form (used at full sizes) returns exactly the full oracle's rows
+    and expert matrices."""
+    wl, dy = _layer(seed, T=30, M=M, K=K)
+    g = B.layer_backward(wl, dy, 0.4, 0.3)
+    s = O.router_logits(wl.values("x"), wl.values("w_router"), wl.null_bias, wl.null_bias_tok)
+    tokens = [0, 7, 29, 13]
+    experts = [0, 2, 4]
+    sb = B.sampled_backward(wl, dy, 0.4, 0.3, s, tokens, experts)
+    np.testing.assert_allclose(sb["dx"], g["dx"][tokens], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sb["ds"], g["ds"][tokens], rtol=1e-12, atol=1e-14)
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        for e in experts:
+            np.testing.assert_allclose(sb[name][e], g[name][e], rtol=1e-12, atol=1e-12)
