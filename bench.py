@@ -409,6 +409,43 @@ def decode_sweep(torch, base, main_layer, steps):
     return out
 
 
+def backward_bench(torch, layers, steps, warmup):
+    """moe_layer_backward (gradients of <dy, y> + 2e-2 L_bal + 1e-3 L_z, routing and
+    expert pre-activations recomputed from x) on each layer, timed with events on the
+    current stream. TFLOP/s are counted on the gradient contractions of the real
+    slots and the shared expert (2 x the forward's: data and weight gradients,
+    12 d d_ff per row); the recomputation (the forward's gate/up and down for routed
+    rows, gate/up for the shared expert) is reported as executed FLOPs beside them."""
+    out = []
+    for layer in layers:
+        cfg = layer.cfg
+        g = torch.Generator(device="cuda").manual_seed(0)
+        dy = torch.randn((layer.T, cfg.d_model), generator=g, device="cuda").to(torch.bfloat16)
+        for _ in range(warmup):
+            layer.backward(dy, 2e-2, 1e-3)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(steps):
+            layer.backward(dy, 2e-2, 1e-3)
+        b.record(s)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        fwd_ms, _ = time_layer(torch, layer, steps, 2)  # also fills the holder's offsets
+        R = int(layer.offsets[-1].item())
+        d, F, Fs, T = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, layer.T
+        useful = 12.0 * d * F * R + 12.0 * d * Fs * T
+        executed = useful + 6.0 * d * F * R + 4.0 * d * Fs * T
+        out.append({"workload": cfg.name, "T": T, "real_slots": R, "ms": round(ms, 4),
+                    "forward_ms": round(fwd_ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
+                    "grad_tflops": round(useful / ms / 1e9, 2),
+                    "grad_mfma_frac": round(useful / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                    "executed_tflops": round(executed / ms / 1e9, 2)})
+        log(f"  backward {cfg.name}: {out[-1]}")
+    return out
+
+
 def measure(torch, layer, steps, warmup):
     ms, _ = time_layer(torch, layer, steps, warmup)
     cfg = layer.cfg
@@ -490,6 +527,11 @@ def main():
         line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
         log("bench: decode regime")
         line["decode"] = decode_sweep(torch, wl, layer, max(5, args.steps // 2))
+        log("bench: backward")
+        big = MoeLayer(generate(CONFIGS["qwen3_1p7b_rho0p25"]))
+        line["backward"] = backward_bench(torch, [layer, big], max(5, args.steps // 2), 2)
+        del big
+        torch.cuda.empty_cache()
         log("bench: measured peaks")
         line["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu:

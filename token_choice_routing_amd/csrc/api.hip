@@ -115,9 +115,15 @@ LayerWs layer_ws(const moe_dims* d) {
 struct BwdWs {
   LayerWs fwd;
   size_t f, g, u, h, yp, dyp, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
-  size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, total;
+  size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, kofs_s, part_sd, part_sg, part_su, total;
   int64_t Rp, Tp;
+  int S;  // K chunks of the shared expert's weight gradients (its K is all T tokens)
 };
+
+// The shared expert's weight gradients reduce over all T tokens: split into chunks of
+// about 1024 tokens (groups of one GEMM launch, summed in order afterwards), so they
+// spread over the chip like the routed experts' segments.
+inline int shared_splits(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>(32, (T + 1023) / 1024)); }
 
 BwdWs bwd_ws(const moe_dims* d) {
   BwdWs w{};
@@ -164,6 +170,11 @@ BwdWs bwd_ws(const moe_dims* d) {
     w.dyT = take((size_t)dm * w.Tp * 2);
     w.hsT = take((size_t)Fs * w.Tp * 2);
     w.dgusT = take((size_t)2 * Fs * w.Tp * 2);
+    w.S = shared_splits(T);
+    w.kofs_s = take((size_t)(w.S + 1) * 4);
+    w.part_sd = take((size_t)w.S * dm * Fs * 4);
+    w.part_sg = take((size_t)w.S * Fs * dm * 4);
+    w.part_su = take((size_t)w.S * Fs * dm * 4);
   }
   w.total = o;
   return w;
@@ -588,14 +599,20 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
   GemmProblem wd{bf(W.dypT), nullptr, dm, nullptr, N, N * dm, bf(W.hT), nullptr, (int)F, (int)W.Rp, gr->dw_down,
                  kofs, W.Rp, W.Rp, (int)dm};
   GemmProblem wsd{};
+  const int S = W.S;
+  int32_t* kofs_s = Fs ? ip(W.kofs_s) : nullptr;
   if (Fs) {
     HIP_TRY(launch_transpose_segments(p->x, nullptr, T, nullptr, nullptr, 1, T, dm, at(W.xT), W.Tp, s));
     HIP_TRY(launch_transpose_segments(dy, nullptr, T, nullptr, nullptr, 1, T, dm, at(W.dyT), W.Tp, s));
     HIP_TRY(launch_transpose_segments(at(W.hs), nullptr, T, nullptr, nullptr, 1, T, Fs, at(W.hsT), W.Tp, s));
     HIP_TRY(launch_transpose_segments(at(W.dgus), nullptr, T, nullptr, nullptr, 1, T, 2 * Fs, at(W.dgusT), W.Tp, s));
-    wsd = GemmProblem{bf(W.dyT), nullptr, dm, nullptr, 1, dm, bf(W.hsT), nullptr, (int)Fs, (int)W.Tp, gr->dws_down};
+    HIP_TRY(launch_split_offsets(T, S, kofs_s, s));
+    // partial dW_sd per token chunk (groups = chunks, each [d][Fs])
+    wsd = GemmProblem{bf(W.dyT), nullptr, dm, nullptr, S, S * dm, bf(W.hsT), nullptr, (int)Fs, (int)W.Tp,
+                      at(W.part_sd), kofs_s, W.Tp, W.Tp, (int)dm};
   }
   HIP_TRY(launch_gemm_pair(true, 1, wd, wsd, cus, s, 3));
+  if (Fs) HIP_TRY(launch_sum_partials(fp(W.part_sd), S, dm * Fs, gr->dws_down, s));
   // dW_g[e] = dg_e^T x_e, dW_u[e] = du_e^T x_e (rows F and F..2F of [dg | du]^T)
   GemmProblem wg{bf(W.dguT), nullptr, F, nullptr, N, N * F, bf(W.xpT), nullptr, (int)dm, (int)W.Rp, gr->dw_gate,
                  kofs, W.Rp, W.Rp, (int)F};
@@ -603,10 +620,13 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
                  gr->dw_up, kofs, W.Rp, W.Rp, (int)F};
   HIP_TRY(launch_gemm_pair(true, 1, wg, wu, cus, s, 3));
   if (Fs) {
-    GemmProblem wsg{bf(W.dgusT), nullptr, Fs, nullptr, 1, Fs, bf(W.xT), nullptr, (int)dm, (int)W.Tp, gr->dws_gate};
-    GemmProblem wsu{bf(W.dgusT) + Fs * W.Tp, nullptr, Fs, nullptr, 1, Fs, bf(W.xT), nullptr, (int)dm, (int)W.Tp,
-                    gr->dws_up};
+    GemmProblem wsg{bf(W.dgusT), nullptr, Fs, nullptr, S, S * Fs, bf(W.xT), nullptr, (int)dm, (int)W.Tp,
+                    at(W.part_sg), kofs_s, W.Tp, W.Tp, (int)Fs};
+    GemmProblem wsu{bf(W.dgusT) + Fs * W.Tp, nullptr, Fs, nullptr, S, S * Fs, bf(W.xT), nullptr, (int)dm,
+                    (int)W.Tp, at(W.part_su), kofs_s, W.Tp, W.Tp, (int)Fs};
     HIP_TRY(launch_gemm_pair(true, 1, wsg, wsu, cus, s, 3));
+    HIP_TRY(launch_sum_partials(fp(W.part_sg), S, Fs * dm, gr->dws_gate, s));
+    HIP_TRY(launch_sum_partials(fp(W.part_su), S, Fs * dm, gr->dws_up, s));
   }
   return MOE_OK;
 }

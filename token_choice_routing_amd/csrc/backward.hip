@@ -29,25 +29,53 @@ namespace {
 
 constexpr int kTile = 64;
 
-// out[b][c][r] = in[b][r][c] (bf16 bits) for an [R][C] matrix per batch b; out rows have
-// stride ldo and start at column offset c_out of a wider output row. 64 x 64 tiles
-// through LDS, 256 threads: coalesced on C when reading, on R when writing.
+// 64 x 64 bf16 tile through LDS: rows of 66 elements (33 four-byte words), so the
+// 8 consecutive rows one lane reads at a column fall in distinct banks.
+struct TTile {
+  bf16_t v[kTile][kTile + 2];
+};
+
+// Thread i of 256 moves 16 bytes: row i / 8 (and row 32 + i / 8) of the tile, 8
+// elements from column 8 (i % 8). All widths here are multiples of 8 elements, so
+// every global access is one aligned 16-byte load or store; edge tiles are masked
+// per 8-element chunk.
+__device__ __forceinline__ void tile_to_lds(TTile& t, int r, int c8, const bf16_t* src_row, bool valid) {
+  u32x4_t v = valid ? *reinterpret_cast<const u32x4_t*>(src_row) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    t.v[r][c8 + 2 * e] = (bf16_t)(v[e] & 0xFFFF);
+    t.v[r][c8 + 2 * e + 1] = (bf16_t)(v[e] >> 16);
+  }
+}
+
+// Column c of the tile, rows r8 .. r8 + 7, as one 16-byte word.
+__device__ __forceinline__ u32x4_t tile_column(const TTile& t, int c, int r8) {
+  u32x4_t v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    v[e] = (uint32_t)t.v[r8 + 2 * e][c] | ((uint32_t)t.v[r8 + 2 * e + 1][c] << 16);
+  return v;
+}
+
+// out[b][c][c_out + r] = in[b][r][c] (bf16 bits) for an [R][C] matrix per batch b;
+// out rows have stride ldo. R, C, ldo and c_out multiples of 8.
 __global__ void __launch_bounds__(256)
 transpose_kernel(const bf16_t* __restrict__ in, int64_t R, int64_t C, int64_t in_batch,
                  bf16_t* __restrict__ out, int64_t ldo, int64_t c_out, int64_t out_batch) {
-  __shared__ bf16_t t[kTile][kTile + 2];
+  __shared__ TTile t;
   const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
   const bf16_t* src = in + (int64_t)blockIdx.z * in_batch;
   bf16_t* dst = out + (int64_t)blockIdx.z * out_batch;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < kTile; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    t[i][tx] = r < R && c < C ? src[r * C + c] : bf16_t(0);
+  const int i = threadIdx.x, c8 = (i & 7) * 8;
+  for (int r = i >> 3; r < kTile; r += 32) {
+    const bool ok = r0 + r < R && c0 + c8 < C;
+    tile_to_lds(t, r, c8, src + (ok ? (r0 + r) * C + c0 + c8 : 0), ok);
   }
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) dst[c * ldo + c_out + r] = t[tx][i];
+  for (int c = i >> 3; c < kTile; c += 32) {
+    const int64_t r = r0 + c8;  // this thread's 8 output elements: rows r .. r + 7
+    if (c0 + c < C && r < R)
+      *reinterpret_cast<u32x4_t*>(dst + (c0 + c) * ldo + c_out + r) = tile_column(t, c, c8);
   }
 }
 
@@ -77,7 +105,7 @@ transpose_segments_kernel(const bf16_t* __restrict__ src, const int32_t* __restr
                           int64_t src_nrows, const int32_t* __restrict__ offsets,
                           const int32_t* __restrict__ kofs, int G, int64_t rows, int64_t C,
                           bf16_t* __restrict__ dst, int64_t ld) {
-  __shared__ bf16_t t[kTile][kTile + 2];
+  __shared__ TTile t;
   __shared__ int64_t srow[kTile];
   const int64_t q0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
   const int64_t total = offsets ? kofs[G] : (rows + 7) & ~int64_t(7);
@@ -105,15 +133,17 @@ transpose_segments_kernel(const bf16_t* __restrict__ src, const int32_t* __restr
     srow[threadIdx.x] = p;
   }
   __syncthreads();
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < kTile; i += 4) {
-    const int64_t p = srow[i], c = c0 + tx;
-    t[i][tx] = p >= 0 && c < C ? src[p * C + c] : bf16_t(0);
+  const int i = threadIdx.x, c8 = (i & 7) * 8;
+  for (int r = i >> 3; r < kTile; r += 32) {
+    const int64_t p = srow[r];
+    const bool ok = p >= 0 && c0 + c8 < C;
+    tile_to_lds(t, r, c8, src + (ok ? p * C + c0 + c8 : 0), ok);
   }
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) {
-    const int64_t c = c0 + i, q = q0 + tx;
-    if (c < C && q < total) dst[c * ld + q] = t[tx][i];
+  for (int c = i >> 3; c < kTile; c += 32) {
+    const int64_t q = q0 + c8;  // positions q .. q + 7 (total is a multiple of 8)
+    if (c0 + c < C && q < total)
+      *reinterpret_cast<u32x4_t*>(dst + (c0 + c) * ld + q) = tile_column(t, c, c8);
   }
 }
 
@@ -146,36 +176,44 @@ swiglu_bwd_kernel(const float* __restrict__ g, const float* __restrict__ u, cons
   }
 }
 
-// Combine backward, one wavefront per token: for each real slot k (slot_pos >= 0)
+// Combine backward, one wavefront per (token, slot): for a real slot (slot_pos >= 0)
 // dy_perm[p] = topk_w dy_t (bf16) and dw[t][k] = <dy_t, y_perm[p]> (float32, lanes
-// add in a fixed order).
+// add in a fixed order); 8 elements per lane and step (d is a multiple of 8).
 __global__ void __launch_bounds__(256)
 combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y_perm,
                    const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w, int64_t T,
                    int K, int d, int64_t R, bf16_t* __restrict__ dy_perm, float* __restrict__ dw) {
-  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t ts = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  if (t >= T) return;
-  const bf16_t* dyt = dy + t * d;
-  for (int k = 0; k < K; ++k) {
-    const int32_t p = slot_pos[t * K + k];
-    if (p < 0 || p >= R) {
-      if (lane == 0) dw[t * K + k] = 0.0f;
-      continue;
-    }
-    const float w = topk_w[t * K + k];
-    const float* yp = y_perm + (int64_t)p * d;
-    bf16_t* o = dy_perm + (int64_t)p * d;
-    float acc = 0.0f;
-    for (int c = lane; c < d; c += kWave) {
-      const float v = bf16_to_f32(dyt[c]);
-      o[c] = f32_to_bf16(w * v);
-      acc += v * yp[c];
-    }
-#pragma unroll
-    for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kWave);
-    if (lane == 0) dw[t * K + k] = acc;
+  if (ts >= T * K) return;
+  const int64_t t = ts / K;
+  const int32_t p = slot_pos[ts];
+  if (p < 0 || p >= R) {
+    if (lane == 0) dw[ts] = 0.0f;
+    return;
   }
+  const float w = topk_w[ts];
+  const bf16_t* dyt = dy + t * d;
+  const float* yp = y_perm + (int64_t)p * d;
+  bf16_t* o = dy_perm + (int64_t)p * d;
+  float acc = 0.0f;
+  for (int c = lane * 8; c < d; c += kWave * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(dyt + c);
+    const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(yp + c);
+    const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(yp + c + 4);
+    u32x4_t ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_to_f32((bf16_t)(v[e] & 0xFFFF)), hi = bf16_to_f32((bf16_t)(v[e] >> 16));
+      const float ya = e < 2 ? y0[2 * e] : y1[2 * e - 4], yb = e < 2 ? y0[2 * e + 1] : y1[2 * e - 3];
+      acc += lo * ya + hi * yb;
+      ov[e] = pack_bf16x2(w * lo, w * hi);
+    }
+    *reinterpret_cast<u32x4_t*>(o + c) = ov;
+  }
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kWave);
+  if (lane == 0) dw[ts] = acc;
 }
 
 // Router backward, one wavefront per token, in float64: ds[t][j] for the N real logits
@@ -234,14 +272,15 @@ router_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ 
 }
 
 // dW_r partial sums: part[c][j][col] = sum over tokens t of chunk c of ds[t][j] x[t][col]
-// (float32); 8 router rows x 256 columns per workgroup, one column per thread.
-constexpr int kRouterRows = 8;
+// (float32); 16 router rows x 512 columns per workgroup, two adjacent columns per
+// thread (one 4-byte load of x per token).
+constexpr int kRouterRows = 16;
 __global__ void __launch_bounds__(256)
 router_wgrad_partial_kernel(const float* __restrict__ ds, const bf16_t* __restrict__ x, int64_t T, int N1,
                             int d, int64_t chunk, float* __restrict__ part) {
-  const int j0 = blockIdx.y * kRouterRows, col = blockIdx.x * 256 + threadIdx.x;
+  const int j0 = blockIdx.y * kRouterRows, col = (blockIdx.x * 256 + threadIdx.x) * 2;
   const int64_t t0 = (int64_t)blockIdx.z * chunk, t1 = min<int64_t>(T, t0 + chunk);
-  float acc[kRouterRows] = {};
+  float a0[kRouterRows] = {}, a1[kRouterRows] = {};
   __shared__ float sds[64][kRouterRows];
   for (int64_t tb = t0; tb < t1; tb += 64) {
     __syncthreads();
@@ -254,16 +293,24 @@ router_wgrad_partial_kernel(const float* __restrict__ ds, const bf16_t* __restri
     if (col < d) {
       const int n = (int)min<int64_t>(64, t1 - tb);
       for (int i = 0; i < n; ++i) {
-        const float xv = bf16_to_f32(x[(tb + i) * d + col]);
+        const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + (tb + i) * d + col);
+        const float x0 = bf16_to_f32((bf16_t)(xv & 0xFFFF)), x1 = bf16_to_f32((bf16_t)(xv >> 16));
 #pragma unroll
-        for (int r = 0; r < kRouterRows; ++r) acc[r] += sds[i][r] * xv;
+        for (int r = 0; r < kRouterRows; ++r) {
+          a0[r] += sds[i][r] * x0;
+          a1[r] += sds[i][r] * x1;
+        }
       }
     }
   }
   if (col < d)
 #pragma unroll
     for (int r = 0; r < kRouterRows; ++r)
-      if (j0 + r < N1) part[((int64_t)blockIdx.z * N1 + j0 + r) * d + col] = acc[r];
+      if (j0 + r < N1) {
+        float* o = part + ((int64_t)blockIdx.z * N1 + j0 + r) * d + col;
+        o[0] = a0[r];
+        o[1] = a1[r];
+      }
 }
 
 // dW_r = sum of the chunk partials in chunk order (deterministic).
@@ -277,26 +324,64 @@ router_wgrad_reduce_kernel(const float* __restrict__ part, int chunks, int64_t n
 }
 
 // dx[t] = sum over real slots of dx_perm[p] (slot order) + dx_shared[t] + ds[t] W_r,
-// one workgroup per token, float32.
+// float32. A workgroup takes 16 tokens x 256 columns, one column per thread: each
+// router row element is read once per 16 tokens, the tokens' ds from LDS.
+constexpr int kScatterTok = 16;
 __global__ void __launch_bounds__(256)
 scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_pos, int K, int64_t R,
                   const float* __restrict__ dx_shared, const float* __restrict__ ds,
-                  const float* __restrict__ w_router, int N1, int d, float* __restrict__ dx) {
-  const int64_t t = blockIdx.x;
-  __shared__ float sds[320];
-  __shared__ int32_t sp[64];
-  for (int j = threadIdx.x; j < N1; j += 256) sds[j] = ds[t * N1 + j];
-  for (int k = threadIdx.x; k < K; k += 256) sp[k] = slot_pos[t * K + k];
+                  const float* __restrict__ w_router, int N1, int d, int64_t T, float* __restrict__ dx) {
+  const int64_t t0 = (int64_t)blockIdx.x * kScatterTok;
+  const int nt = (int)min<int64_t>(kScatterTok, T - t0);
+  __shared__ float sds[kScatterTok][260];
+  __shared__ int32_t sp[kScatterTok][MOE_MAX_TOPK];
+  for (int i = threadIdx.x; i < kScatterTok * N1; i += 256) {
+    const int tt = i / N1, j = i - tt * N1;
+    sds[tt][j] = tt < nt ? ds[(t0 + tt) * N1 + j] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kScatterTok * K; i += 256) {
+    const int tt = i / K, k = i - tt * K;
+    sp[tt][k] = tt < nt ? slot_pos[(t0 + tt) * K + k] : -1;
+  }
   __syncthreads();
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float v = dx_shared ? dx_shared[t * d + c] : 0.0f;
-    for (int k = 0; k < K; ++k) {
-      const int32_t p = sp[k];
-      if (p >= 0 && p < R) v += dx_perm[(int64_t)p * d + c];
+  for (int c = blockIdx.y * 256 + threadIdx.x; c < d; c += gridDim.y * 256) {
+    float acc[kScatterTok];
+#pragma unroll
+    for (int tt = 0; tt < kScatterTok; ++tt) acc[tt] = 0.0f;
+    for (int j = 0; j < N1; ++j) {
+      const float w = w_router[(int64_t)j * d + c];
+#pragma unroll
+      for (int tt = 0; tt < kScatterTok; ++tt) acc[tt] += sds[tt][j] * w;
     }
-    float r = 0.0f;
-    for (int j = 0; j < N1; ++j) r += sds[j] * w_router[(int64_t)j * d + c];
-    dx[t * d + c] = v + r;
+#pragma unroll
+    for (int tt = 0; tt < kScatterTok; ++tt) {
+      if (tt >= nt) break;
+      const int64_t t = t0 + tt;
+      float v = dx_shared ? dx_shared[t * d + c] : 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int32_t p = sp[tt][k];
+        if (p >= 0 && p < R) v += dx_perm[(int64_t)p * d + c];
+      }
+      dx[t * d + c] = v + acc[tt];
+    }
+  }
+}
+
+// Uniform K chunks for a split weight gradient: kofs[s] = min(s * chunk, rows) with
+// chunk a multiple of 8, kofs[S] = rows rounded up to 8 (the padded column count).
+__global__ void __launch_bounds__(64) split_offsets_kernel(int64_t rows, int S, int32_t* __restrict__ kofs) {
+  const int64_t padded = (rows + 7) & ~int64_t(7);
+  const int64_t chunk = ((padded + S - 1) / S + 7) & ~int64_t(7);
+  for (int s = threadIdx.x; s <= S; s += 64) kofs[s] = (int32_t)min<int64_t>((int64_t)s * chunk, padded);
+}
+
+// out[i] = sum over the S partial matrices in order (deterministic).
+__global__ void __launch_bounds__(256)
+sum_partials_kernel(const float* __restrict__ part, int S, int64_t n, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float v = 0.0f;
+    for (int s = 0; s < S; ++s) v += part[s * n + i];
+    out[i] = v;
   }
 }
 
@@ -347,7 +432,7 @@ hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, co
 hipError_t launch_combine_bwd(const void* dy, const float* y_perm, const int32_t* slot_pos, const float* topk_w,
                               int64_t T, int K, int d, int64_t R, void* dy_perm, float* dw, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  combine_bwd_kernel<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(static_cast<const bf16_t*>(dy), y_perm, slot_pos,
+  combine_bwd_kernel<<<(unsigned)((T * K + 3) / 4), 256, 0, s>>>(static_cast<const bf16_t*>(dy), y_perm, slot_pos,
                                                             topk_w, T, K, d, R, static_cast<bf16_t*>(dy_perm), dw);
   return hipGetLastError();
 }
@@ -361,16 +446,18 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
   return hipGetLastError();
 }
 
+// Token chunks of the router weight gradient: 64 tokens each, at most 256 chunks.
+static int64_t router_chunks(int64_t T) { return std::max<int64_t>(1, std::min<int64_t>(256, (T + 63) / 64)); }
+
 size_t router_wgrad_ws_bytes(int64_t T, int N1, int d) {
-  const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(32, (T + 511) / 512));
-  return (size_t)chunks * N1 * d * sizeof(float);
+  return (size_t)router_chunks(T) * N1 * d * sizeof(float);
 }
 
 hipError_t launch_router_wgrad(const float* ds, const void* x, int64_t T, int N1, int d, float* part, float* dw,
                                hipStream_t s) {
-  const int64_t chunks = std::max<int64_t>(1, std::min<int64_t>(32, (T + 511) / 512));
+  const int64_t chunks = router_chunks(T);
   const int64_t chunk = (T + chunks - 1) / chunks;
-  const dim3 grid((unsigned)((d + 255) / 256), (unsigned)((N1 + kRouterRows - 1) / kRouterRows), (unsigned)chunks);
+  const dim3 grid((unsigned)((d + 511) / 512), (unsigned)((N1 + kRouterRows - 1) / kRouterRows), (unsigned)chunks);
   router_wgrad_partial_kernel<<<grid, 256, 0, s>>>(ds, static_cast<const bf16_t*>(x), T, N1, d, chunk, part);
   const int64_t n = (int64_t)N1 * d;
   router_wgrad_reduce_kernel<<<grid_for(n), 256, 0, s>>>(part, (int)chunks, n, dw);
@@ -381,7 +468,20 @@ hipError_t launch_scatter_dx(const float* dx_perm, const int32_t* slot_pos, int 
                              const float* ds, const float* w_router, int N1, int d, int64_t T, float* dx,
                              hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  scatter_dx_kernel<<<(unsigned)T, 256, 0, s>>>(dx_perm, slot_pos, K, R, dx_shared, ds, w_router, N1, d, dx);
+  const dim3 grid((unsigned)((T + kScatterTok - 1) / kScatterTok), (unsigned)((d + 255) / 256));
+  scatter_dx_kernel<<<grid, 256, 0, s>>>(
+      dx_perm, slot_pos, K, R, dx_shared, ds, w_router, N1, d, T, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_offsets(int64_t rows, int S, int32_t* kofs, hipStream_t s) {
+  split_offsets_kernel<<<1, 64, 0, s>>>(rows, S, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const float* part, int S, int64_t n, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  sum_partials_kernel<<<grid_for(n), 256, 0, s>>>(part, S, n, out);
   return hipGetLastError();
 }
 

@@ -150,6 +150,10 @@ hipError_t launch_router_wgrad(const float* ds, const void* x, int64_t T, int N1
 hipError_t launch_scatter_dx(const float* dx_perm, const int32_t* slot_pos, int K, int64_t R, const float* dx_shared,
                              const float* ds, const float* w_router, int N1, int d, int64_t T, float* dx,
                              hipStream_t s);
+// kofs[0..S]: S uniform K chunks (multiples of 8) of `rows` rows, for a split weight gradient.
+hipError_t launch_split_offsets(int64_t rows, int S, int32_t* kofs, hipStream_t s);
+// out = sum over s < S of part[s] (n floats each), in order.
+hipError_t launch_sum_partials(const float* part, int S, int64_t n, float* out, hipStream_t s);
 
 struct CombineArgs {
   bool bf16;
