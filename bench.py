@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true", help="skip the rho sweep and other workloads")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="time the backward pass even with --no-sweep (it runs with the sweep anyway)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--copy-ref", action="store_true",
@@ -527,11 +529,13 @@ def main():
         line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
         log("bench: decode regime")
         line["decode"] = decode_sweep(torch, wl, layer, max(5, args.steps // 2))
+    if not args.no_sweep or args.with_backward:
         log("bench: backward")
         big = MoeLayer(generate(CONFIGS["qwen3_1p7b_rho0p25"]))
         line["backward"] = backward_bench(torch, [layer, big], max(5, args.steps // 2), 2)
         del big
         torch.cuda.empty_cache()
+    if not args.no_sweep:
         log("bench: measured peaks")
         line["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu:
