@@ -22,7 +22,9 @@ def is_flush(name):
 
 
 def short(name):
-    return name.split("(")[0]
+    """Kernel name without its argument list (and without the anonymous namespace,
+    whose parentheses would otherwise end the name)."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0]
 
 
 def dispatches(db):
