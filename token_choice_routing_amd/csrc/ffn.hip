@@ -31,9 +31,10 @@
 //    step waiting only for its own reads.
 //  * Persistent grid. Each workgroup builds the tile table from the device
 //    offsets (no host round trip for R), and tiles are ordered
-//    (expert, column tile, row tile) and cut into 8 contiguous ranges, one per
-//    XCD (workgroups are dispatched round-robin over the 8 XCDs), so the row
-//    tiles that share one expert's weight panel run on the same L2.
+//    (expert, column tile, row tile); each problem's list is cut into 8 contiguous
+//    ranges, one per XCD (workgroups are dispatched round-robin over the 8 XCDs),
+//    so the row tiles that share one expert's weight panel run on the same L2 and
+//    the shared expert's tiles are spread over all XCDs.
 //  * When a range's last round has fewer tiles than the range has workgroups,
 //    those tiles are split by output columns into 2 or 4 sub-tiles, so every
 //    workgroup streams about the same weight bytes. Rows past the segment or
@@ -162,6 +163,12 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
   __syncthreads();
 }
 
+// Workgroups of a tile shape that fit one CU's 160 KB of LDS (stages + tile table);
+// the register budget per wavefront follows from it.
+constexpr int gemm_groups_per_cu(int bm, int bn, int s, int bk) {
+  return (int)((160 * 1024) / ((size_t)s * (bm + bn) * bk * 2 + sizeof(TileTable)));
+}
+
 // MODE kSwiGLU writes h as bf16 (the next MFMA's input); kPlain writes float32.
 // ROLE only names the launch in profiles (the code is identical): 0 standalone
 // grouped, 1 standalone single segment, 2 the layer's routed + shared launch, 3 the
@@ -178,7 +185,9 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
 // global form as a possible LDS-side event and then waits for every LDS read at
 // once.)
 template <int MODE, int ROLE, int BM, int BN, int WM, int WN, int S, int BK>
-__global__ void __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+__global__ void __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4 * gemm_groups_per_cu(BM, BN, S, BK),
+                                   WM * WN / 4 * gemm_groups_per_cu(BM, BN, S, BK))))
 grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   static_assert(BK == 32 || BK == 64, "K tile of 64- or 128-byte rows");
   constexpr int NW = WM * WN;
@@ -212,15 +221,19 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
   const int lrow = lane / CPR;
   const int lc = (lane % CPR) ^ (BK == 64 ? (((wave & 1) << 2) | (lrow >> 1)) : (lrow >> 2) & 3);
 
-  // XCD-contiguous tile ranges. When a range's last round would leave workgroups
-  // idle, its tiles are split by output columns into 2 or 4 sub-tiles, so that every
-  // workgroup of the range streams about the same number of weight bytes.
+  // XCD-contiguous tile ranges: each XCD takes an eighth of problem 1's tiles
+  // followed by an eighth of problem 0's, so a second problem (the dense shared
+  // expert, whose tiles are long MFMA chains) is spread over every XCD instead of
+  // filling the last ones. When a range's last round would leave workgroups idle,
+  // its tiles (problem 0's last) are split by output columns into 2 or 4 sub-tiles,
+  // so that every workgroup of the range streams about the same number of weight bytes.
   const int P = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int Bx = P >> 3;
-  const int Sx = (total + 7) / 8;
-  const int r_begin = xcd * Sx, r_end = min(total, r_begin + Sx);
-  const int nx = max(0, r_end - r_begin);
+  const int T0 = tt.prefix[G0], T1 = total - T0;
+  const int b0 = (int)((int64_t)xcd * T0 / 8), n0 = (int)((int64_t)(xcd + 1) * T0 / 8) - b0;
+  const int b1 = T0 + (int)((int64_t)xcd * T1 / 8), n1 = T0 + (int)((int64_t)(xcd + 1) * T1 / 8) - b1;
+  const int nx = n0 + n1;
   const int full = nx / Bx * Bx, rem = nx - full;
   const int split = rem == 0 ? 1 : (WN >= 4 && 4 * rem <= Bx) ? 4 : (WN >= 2 && 2 * rem <= Bx) ? 2 : 1;
   const int items = full + rem * split;
@@ -249,12 +262,13 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     int ge, Kdim, kofs, nk, m0, rows_valid, col0, ocp;
   };
   auto locate = [&](int it, Where& w) {
-    int L = r_begin + it, part = 0, parts = 1;
+    int i = it, part = 0, parts = 1;
     if (it >= full) {
-      L = r_begin + full + (it - full) / split;
+      i = full + (it - full) / split;
       part = (it - full) % split;
       parts = split;
     }
+    const int L = i < n1 ? b1 + i : b0 + (i - n1);
     int lo = 0, hi = G;  // prefix[lo] <= L < prefix[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -739,6 +753,8 @@ static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& 
     case 11: launch_variant<MODE, ROLE, 128, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
     case 12: launch_variant<MODE, ROLE, 256, 256, 2, 4, 2, 64>(q0, q1, num_cus, stream); break;
     case 13: launch_variant<MODE, ROLE, 256, 256, 4, 2, 2, 64>(q0, q1, num_cus, stream); break;
+    case 14: launch_variant<MODE, ROLE, 128, 128, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
+    case 15: launch_variant<MODE, ROLE, 128, 128, 2, 2, 3, 32>(q0, q1, num_cus, stream); break;
 #endif
     default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
   }
