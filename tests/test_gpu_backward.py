@@ -151,3 +151,54 @@ def test_backward_full_size_sampled(name):
             say(f"  {nm}[{e}] ({counts[e]} rows): RMS(err)/RMS = {r[0]:.3e}, max|err|/RMS = {r[1]:.3e}")
         for e in np.nonzero(counts == 0)[0]:
             assert (full[e] == 0).all()
+
+
+def _run_wl(wl, alpha, beta, seed=0):
+    """_run for a workload prepared by the caller."""
+    cfg = wl.cfg
+    say(f"  backward {cfg.name} T={cfg.T} N={cfg.n_experts} M={cfg.n_null} K={cfg.top_k} alpha={alpha} beta={beta}")
+    layer = MoeLayer(wl)
+    layer.forward()
+    out = layer.results()
+    rng = np.random.default_rng(seed + 7)
+    dy_bits = bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+    g = layer.backward(to_device(dy_bits), alpha, beta)
+    torch.cuda.synchronize()
+    got = {k: (to_host(v) if v is not None else None) for k, v in g.items()}
+    ref = B.layer_backward(wl, vals(dy_bits), alpha, beta, logits=out["logits"].astype(np.float64))
+    return got, ref
+
+
+@pytest.mark.parametrize("shared", [64, 0])
+def test_backward_every_token_null(shared):
+    """A large per-token null bias sends every slot to a null copy (no routed rows):
+    every expert gradient is exactly zero, and dx and the router gradient hold only
+    the auxiliary-loss and shared-expert terms."""
+    cfg = Config(name="bwd_all_null", dtype="bf16", w_std=None, seed=2,
+                 **dict(CASES["nullpool_shared"], d_ff_shared=shared))
+    wl = generate(cfg)
+    wl.null_bias_tok = np.full(cfg.T, 1e3, dtype=np.float32)
+    got, ref = _run_wl(wl, 2e-2, 1e-3)
+    assert ref["fwd"]["offsets"][-1] == 0
+    _check(cfg, got, ref)
+
+
+@pytest.mark.parametrize("T", [1, 3, 65])
+def test_backward_tiny_token_counts(T):
+    """One token, a few tokens and one token past a 64-token tile."""
+    cfg = Config(name=f"bwd_t{T}", dtype="bf16", w_std=None, seed=T, **dict(CASES["nullpool_shared"], T=T))
+    got, ref = _run_wl(generate(cfg), 2e-2, 1e-3)
+    _check(cfg, got, ref)
+
+
+def test_backward_one_expert_takes_every_slot():
+    """K = 1 and one expert wins every token: a single 700-row segment (a ragged last
+    K tile of the weight gradient) and every other expert empty."""
+    cfg = Config(name="bwd_one_expert", dtype="bf16", w_std=None, seed=4,
+                 **dict(CASES["topk_m0"], T=700, top_k=1))
+    wl = generate(cfg)
+    wl.x[:, 0] = 0x3F80          # bf16 1.0 in column 0 of every token
+    wl.w_router[3, 0] = 100.0    # expert 3 wins every token
+    got, ref = _run_wl(wl, 2e-2, 1e-3)
+    assert (ref["fwd"]["topk_idx"][:, 0] == 3).all()
+    _check(cfg, got, ref)

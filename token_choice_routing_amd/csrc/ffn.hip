@@ -755,6 +755,8 @@ static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& 
     case 13: launch_variant<MODE, ROLE, 256, 256, 4, 2, 2, 64>(q0, q1, num_cus, stream); break;
     case 14: launch_variant<MODE, ROLE, 128, 128, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
     case 15: launch_variant<MODE, ROLE, 128, 128, 2, 2, 3, 32>(q0, q1, num_cus, stream); break;
+    case 16: launch_variant<MODE, ROLE, 256, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
+    case 17: launch_variant<MODE, ROLE, 256, 256, 2, 4, 3, 32>(q0, q1, num_cus, stream); break;
 #endif
     default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
   }
