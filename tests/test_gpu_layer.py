@@ -223,3 +223,51 @@ def test_expert_counts_across_router_tilings(N, M, K, T):
     tile covers every expert (N <= 32)."""
     say(f"layer with N={N} M={M} K={K} T={T}")
     check_full(generate(_small(n_experts=N, n_null=M, top_k=K, T=T)))
+
+
+def test_layer_forward_and_backward_replay_in_a_hip_graph():
+    """The layer forward and backward enqueue only kernels on the caller's stream (no
+    allocation, copy, fill or host synchronisation), so both can be captured in a
+    HIP graph: every replay, with eager calls and synchronisations in between, gives
+    the eager results bit for bit."""
+    from workloads.configs import Config
+    say("forward + backward captured in a HIP graph")
+    cfg = Config(name="graph", T=300, d_model=128, n_experts=8, n_null=8, top_k=4, d_ff=96,
+                 d_ff_shared=64, dtype="bf16", w_std=None, seed=9)
+    layer = MoeLayer(generate(cfg))
+    rng = np.random.default_rng(1)
+    dy = to_device(bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32)))
+    layer.forward()
+    grads = layer.backward(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    ref_y = layer.y.clone()
+    ref_g = {k: v.clone() for k, v in grads.items() if v is not None}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on a side stream, as capture requires
+        layer.forward(stream=side)
+        layer.backward(dy, 2e-2, 1e-3, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        layer.forward(stream=cs)
+        layer.backward(dy, 2e-2, 1e-3, stream=cs)
+    torch.cuda.synchronize()
+    for i in range(3):
+        layer.y.zero_()
+        for v in grads.values():
+            if v is not None:
+                v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, ref_y), f"replay {i}: y"
+        for k, v in ref_g.items():
+            assert torch.equal(grads[k], v), f"replay {i}: {k}"
+        layer.forward()                 # eager work between replays
+        layer.backward(dy, 2e-2, 1e-3)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, ref_y)
+    del graph
