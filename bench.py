@@ -416,8 +416,8 @@ def backward_bench(torch, layers, steps, warmup):
     expert pre-activations recomputed from x) on each layer, timed with events on the
     current stream. TFLOP/s are counted on the gradient contractions of the real
     slots and the shared expert (2 x the forward's: data and weight gradients,
-    12 d d_ff per row); the recomputation (the forward's gate/up and down for routed
-    rows, gate/up for the shared expert) is reported as executed FLOPs beside them."""
+    12 d d_ff per row); the recomputation (the forward's gate/up for routed rows and
+    for the shared expert) is reported as executed FLOPs beside them."""
     out = []
     for layer in layers:
         cfg = layer.cfg
@@ -438,7 +438,7 @@ def backward_bench(torch, layers, steps, warmup):
         R = int(layer.offsets[-1].item())
         d, F, Fs, T = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, layer.T
         useful = 12.0 * d * F * R + 12.0 * d * Fs * T
-        executed = useful + 6.0 * d * F * R + 4.0 * d * Fs * T
+        executed = useful + 4.0 * d * F * R + 4.0 * d * Fs * T
         out.append({"workload": cfg.name, "T": T, "real_slots": R, "ms": round(ms, 4),
                     "forward_ms": round(fwd_ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
                     "grad_tflops": round(useful / ms / 1e9, 2),

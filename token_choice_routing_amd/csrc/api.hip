@@ -114,7 +114,7 @@ LayerWs layer_ws(const moe_dims* d) {
 // columns: Rp = R + 8 N columns at most).
 struct BwdWs {
   LayerWs fwd;
-  size_t f, g, u, h, yp, dyp, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
+  size_t f, g, u, h, dyp, wperm, rslot, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
   size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, kofs_s, part_sd, part_sg, part_su, total;
   int64_t Rp, Tp;
   int S;  // K chunks of the shared expert's weight gradients (its K is all T tokens)
@@ -142,8 +142,9 @@ BwdWs bwd_ws(const moe_dims* d) {
   w.g = take((size_t)R * F * 4);
   w.u = take((size_t)R * F * 4);
   w.h = take((size_t)R * F * 2);
-  w.yp = take((size_t)R * dm * 4);
   w.dyp = take((size_t)R * dm * 2);
+  w.wperm = take((size_t)R * 4);
+  w.rslot = take((size_t)R * 4);
   w.dw = take((size_t)T * d->top_k * 4);
   w.ds = take((size_t)T * (N + 1) * 4);
   w.wdT = take((size_t)N * F * dm * 2);
@@ -546,16 +547,11 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     HIP_TRY(launch_gemm_pair(true, 1, gs, us, cus, s, 3));
     HIP_TRY(launch_swiglu_h(fp(W.gs), fp(W.us), nullptr, 1, T, (int)Fs, at(W.hs), s));
   }
-  // 4. expert outputs Y = h W_d^T (float32), for the weight gradients dg = <dy, Y>
-  GemmProblem y2{bf(W.h), nullptr, R, offsets, N, R, static_cast<const uint16_t*>(p->w_down), nullptr, (int)dm,
-                 (int)F, at(W.yp)};
-  HIP_TRY(launch_gemm_pair(true, 1, y2, GemmProblem{}, cus, s, 3));
+  // 4. per real slot: its expert row's dY = g dy (bf16, for dW_down), g and slot index
+  HIP_TRY(launch_slot_rows(dy, slot_pos, topk_w, T, K, (int)dm, R, at(W.dyp), fp(W.wperm), ip(W.rslot), fp(W.dw),
+                           s));
 
-  // 5. combine backward (dY = g dy per real slot, dg) and router backward (ds)
-  HIP_TRY(launch_combine_bwd(dy, fp(W.yp), slot_pos, topk_w, T, K, (int)dm, R, at(W.dyp), fp(W.dw), s));
-  HIP_TRY(launch_router_bwd(logits, topk_idx, topk_w, fp(W.dw), fp(W.f), T, N, M, K, alpha, beta, fp(W.ds), s));
-
-  // 6. transposed bf16 weights: W_d^T [N][F][d]; [W_g ; W_u]^T [N][d][2F]
+  // 5. transposed bf16 weights: W_d^T [N][F][d]; [W_g ; W_u]^T [N][d][2F]
   HIP_TRY(launch_transpose(p->w_down, N, dm, F, at(W.wdT), dm, 0, F * dm, s));
   HIP_TRY(launch_transpose(p->w_gate, N, F, dm, at(W.wguT), 2 * F, 0, dm * 2 * F, s));
   HIP_TRY(launch_transpose(p->w_up, N, F, dm, at(W.wguT), 2 * F, F, dm * 2 * F, s));
@@ -565,17 +561,23 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     HIP_TRY(launch_transpose(p->ws_up, 1, Fs, dm, at(W.wsguT), 2 * Fs, Fs, 0, s));
   }
 
-  // 7. dh = dY W_d (routed) and dy W_sd (shared), then the SwiGLU backward
-  GemmProblem h3{bf(W.dyp), nullptr, R, offsets, N, R, bf(W.wdT), nullptr, (int)F, (int)dm, at(W.dh)};
+  // 6. U = dy W_d on the routed rows (dy read through perm_token) and dh_s = dy W_sd;
+  // then per routed row dg = <U, h> (the slot's weight gradient, so the expert output
+  // Y is never recomputed) and the SwiGLU backward of dh = g U; the shared expert's
+  // SwiGLU backward; then the router backward (ds), which needs every dg
+  GemmProblem h3{static_cast<const uint16_t*>(dy), perm_token, T, offsets, N, R, bf(W.wdT), nullptr, (int)F,
+                 (int)dm, at(W.dh)};
   GemmProblem hs3{};
   if (Fs)
     hs3 = GemmProblem{static_cast<const uint16_t*>(dy), nullptr, T, nullptr, 1, T, bf(W.wsdT), nullptr, (int)Fs,
                       (int)dm, at(W.dhs)};
   HIP_TRY(launch_gemm_pair(true, 1, h3, hs3, cus, s, 3));
-  HIP_TRY(launch_swiglu_bwd(fp(W.g), fp(W.u), fp(W.dh), offsets, N, R, (int)F, at(W.dgu), s));
+  HIP_TRY(launch_swiglu_bwd_routed(fp(W.g), fp(W.u), fp(W.dh), at(W.h), fp(W.wperm), ip(W.rslot), offsets, N, R,
+                                    (int)F, at(W.dgu), fp(W.dw), s));
   if (Fs) HIP_TRY(launch_swiglu_bwd(fp(W.gs), fp(W.us), fp(W.dhs), nullptr, 1, T, (int)Fs, at(W.dgus), s));
+  HIP_TRY(launch_router_bwd(logits, topk_idx, topk_w, fp(W.dw), fp(W.f), T, N, M, K, alpha, beta, fp(W.ds), s));
 
-  // 8. da = [dg | du] [W_g ; W_u]: routed rows and shared rows (float32)
+  // 7. da = [dg | du] [W_g ; W_u]: routed rows and shared rows (float32)
   GemmProblem a4{bf(W.dgu), nullptr, R, offsets, N, R, bf(W.wguT), nullptr, (int)dm, (int)(2 * F), at(W.dxp)};
   GemmProblem as4{};
   if (Fs)
@@ -583,12 +585,12 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
                       at(W.dxs)};
   HIP_TRY(launch_gemm_pair(true, 1, a4, as4, cus, s, 3));
 
-  // 9. dx = sum over the token's slots of da + shared da + ds W_r; dW_r = ds^T x
+  // 8. dx = sum over the token's slots of da + shared da + ds W_r; dW_r = ds^T x
   HIP_TRY(launch_scatter_dx(fp(W.dxp), slot_pos, K, R, Fs ? fp(W.dxs) : nullptr, fp(W.ds), p->w_router, N + 1,
                             (int)dm, T, gr->dx, s));
   HIP_TRY(launch_router_wgrad(fp(W.ds), p->x, T, N + 1, (int)dm, fp(W.rpart), gr->dw_router, s));
 
-  // 10. weight gradients: activations transposed per segment, K = the segment's rows
+  // 9. weight gradients: activations transposed per segment, K = the segment's rows
   int32_t* kofs = ip(W.kofs);
   HIP_TRY(launch_pad_offsets(offsets, N, R, kofs, s));
   HIP_TRY(launch_transpose_segments(p->x, perm_token, T, offsets, kofs, N, R, dm, at(W.xpT), W.Rp, s));

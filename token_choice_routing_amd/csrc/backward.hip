@@ -176,13 +176,16 @@ swiglu_bwd_kernel(const float* __restrict__ g, const float* __restrict__ u, cons
   }
 }
 
-// Combine backward, one wavefront per (token, slot): for a real slot (slot_pos >= 0)
-// dy_perm[p] = topk_w dy_t (bf16) and dw[t][k] = <dy_t, y_perm[p]> (float32, lanes
-// add in a fixed order); 8 elements per lane and step (d is a multiple of 8).
+// Slots to expert-ordered rows, one wavefront per (token, slot): for a real slot
+// (slot_pos >= 0) row p gets dy_perm[p] = topk_w dy_t (bf16, the output gradient of
+// the expert row, for dW_down), w_perm[p] = topk_w and row_slot[p] = the slot's flat
+// index; a null slot's weight gradient dw[t][k] is 0 (nothing flows through it). 8
+// elements per lane and step (d is a multiple of 8).
 __global__ void __launch_bounds__(256)
-combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y_perm,
-                   const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w, int64_t T,
-                   int K, int d, int64_t R, bf16_t* __restrict__ dy_perm, float* __restrict__ dw) {
+slot_rows_kernel(const bf16_t* __restrict__ dy, const int32_t* __restrict__ slot_pos,
+                 const float* __restrict__ topk_w, int64_t T, int K, int d, int64_t R,
+                 bf16_t* __restrict__ dy_perm, float* __restrict__ w_perm, int32_t* __restrict__ row_slot,
+                 float* __restrict__ dw) {
   const int64_t ts = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (ts >= T * K) return;
@@ -193,27 +196,61 @@ combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y_pe
     return;
   }
   const float w = topk_w[ts];
+  if (lane == 0) {
+    w_perm[p] = w;
+    row_slot[p] = (int32_t)ts;
+  }
   const bf16_t* dyt = dy + t * d;
-  const float* yp = y_perm + (int64_t)p * d;
   bf16_t* o = dy_perm + (int64_t)p * d;
-  float acc = 0.0f;
   for (int c = lane * 8; c < d; c += kWave * 8) {
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(dyt + c);
-    const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(yp + c);
-    const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(yp + c + 4);
     u32x4_t ov;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf16_to_f32((bf16_t)(v[e] & 0xFFFF)), hi = bf16_to_f32((bf16_t)(v[e] >> 16));
-      const float ya = e < 2 ? y0[2 * e] : y1[2 * e - 4], yb = e < 2 ? y0[2 * e + 1] : y1[2 * e - 3];
-      acc += lo * ya + hi * yb;
-      ov[e] = pack_bf16x2(w * lo, w * hi);
-    }
+    for (int e = 0; e < 4; ++e)
+      ov[e] = pack_bf16x2(w * bf16_to_f32((bf16_t)(v[e] & 0xFFFF)), w * bf16_to_f32((bf16_t)(v[e] >> 16)));
     *reinterpret_cast<u32x4_t*>(o + c) = ov;
+  }
+}
+
+// SwiGLU and combine backward of the routed rows, one wavefront per row p, from
+// U_p = dy_t W_d (the unweighted output gradient pulled back through W_d; the GEMM
+// reads dy_t through perm_token): the slot's weight gradient is
+//   dg_tk = <dy_t, Y_p> = <dy_t, h_p W_d^T> = <U_p, h_p>
+// (so Y_p is never recomputed), written to dw[row_slot[p]] (float32, lanes add in a
+// fixed order), and with dh = topk_w U_p the SwiGLU backward as in swiglu_bwd_kernel.
+// 4 elements per lane and step (F is a multiple of 8).
+__global__ void __launch_bounds__(256)
+swiglu_bwd_routed_kernel(const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ U,
+                         const bf16_t* __restrict__ h, const float* __restrict__ w_perm,
+                         const int32_t* __restrict__ row_slot, const int32_t* offsets, int G, int64_t rows,
+                         int F, bf16_t* __restrict__ dgu, float* __restrict__ dw) {
+  const int64_t p = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (p >= live_rows(offsets, G, rows)) return;
+  const float w = w_perm[p];
+  const int64_t o = p * F;
+  float acc = 0.0f;
+  for (int j = lane * 4; j < F; j += kWave * 4) {
+    const f32x4_t uu = *reinterpret_cast<const f32x4_t*>(U + o + j);
+    const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(g + o + j);
+    const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(u + o + j);
+    const u32x2_t hh = *reinterpret_cast<const u32x2_t*>(h + o + j);
+    float dg[4], du[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t hw = hh[e >> 1];
+      acc += uu[e] * bf16_to_f32((bf16_t)(e & 1 ? hw >> 16 : hw & 0xFFFF));
+      const float z = gg[e], sg = 1.0f / (1.0f + __expf(-z)), d = w * uu[e];
+      dg[e] = d * vv[e] * (sg * (1.0f + z * (1.0f - sg)));
+      du[e] = d * z * sg;
+    }
+    bf16_t* row = dgu + p * 2 * F;
+    *reinterpret_cast<u32x2_t*>(row + j) = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+    *reinterpret_cast<u32x2_t*>(row + F + j) = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
   }
 #pragma unroll
   for (int o2 = 32; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kWave);
-  if (lane == 0) dw[ts] = acc;
+  if (lane == 0) dw[row_slot[p]] = acc;
 }
 
 // Router backward, one wavefront per token, in float64: ds[t][j] for the N real logits
@@ -429,11 +466,22 @@ hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, co
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(const void* dy, const float* y_perm, const int32_t* slot_pos, const float* topk_w,
-                              int64_t T, int K, int d, int64_t R, void* dy_perm, float* dw, hipStream_t s) {
+hipError_t launch_slot_rows(const void* dy, const int32_t* slot_pos, const float* topk_w, int64_t T, int K,
+                            int d, int64_t R, void* dy_perm, float* w_perm, int32_t* row_slot, float* dw,
+                            hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  combine_bwd_kernel<<<(unsigned)((T * K + 3) / 4), 256, 0, s>>>(static_cast<const bf16_t*>(dy), y_perm, slot_pos,
-                                                            topk_w, T, K, d, R, static_cast<bf16_t*>(dy_perm), dw);
+  slot_rows_kernel<<<(unsigned)((T * K + 3) / 4), 256, 0, s>>>(static_cast<const bf16_t*>(dy), slot_pos, topk_w,
+                                                                T, K, d, R, static_cast<bf16_t*>(dy_perm), w_perm,
+                                                                row_slot, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_routed(const float* g, const float* u, const float* U, const void* h,
+                                    const float* w_perm, const int32_t* row_slot, const int32_t* offsets, int G,
+                                    int64_t rows, int F, void* dgu, float* dw, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  swiglu_bwd_routed_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+      g, u, U, static_cast<const bf16_t*>(h), w_perm, row_slot, offsets, G, rows, F, static_cast<bf16_t*>(dgu), dw);
   return hipGetLastError();
 }
 

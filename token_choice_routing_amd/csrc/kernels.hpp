@@ -139,8 +139,16 @@ hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offset
                            void* h, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
                              int64_t rows, int F, void* dgu, hipStream_t s);
-hipError_t launch_combine_bwd(const void* dy, const float* y_perm, const int32_t* slot_pos, const float* topk_w,
-                              int64_t T, int K, int d, int64_t R, void* dy_perm, float* dw, hipStream_t s);
+// Real slot (t, k) at row p: dy_perm[p] = topk_w dy_t (bf16), w_perm[p] = topk_w,
+// row_slot[p] = t K + k; null slots: dw[t][k] = 0.
+hipError_t launch_slot_rows(const void* dy, const int32_t* slot_pos, const float* topk_w, int64_t T, int K,
+                            int d, int64_t R, void* dy_perm, float* w_perm, int32_t* row_slot, float* dw,
+                            hipStream_t s);
+// Routed rows from U = dy W_d: dw[row_slot[p]] = <U_p, h_p>, and the SwiGLU backward
+// of dh = w_perm U into dgu (as launch_swiglu_bwd).
+hipError_t launch_swiglu_bwd_routed(const float* g, const float* u, const float* U, const void* h,
+                                    const float* w_perm, const int32_t* row_slot, const int32_t* offsets, int G,
+                                    int64_t rows, int F, void* dgu, float* dw, hipStream_t s);
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* dw,
                              const float* f, int64_t T, int N, int M, int K, float alpha, float beta, float* ds,
                              hipStream_t s);
