@@ -495,15 +495,21 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const
 }
 
 // Token chunks of the router weight gradient: 64 tokens each, at most 256 chunks.
-static int64_t router_chunks(int64_t T) { return std::max<int64_t>(1, std::min<int64_t>(256, (T + 63) / 64)); }
+// Token chunks of the router weight gradient: 64 tokens each, but no more than keep
+// the grid near 1024 workgroups, so the float32 partials (chunks x (N+1) x d) stay
+// small next to x.
+static int64_t router_chunks(int64_t T, int N1, int d) {
+  const int64_t tiles = (int64_t)((d + 511) / 512) * ((N1 + kRouterRows - 1) / kRouterRows);
+  return std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(1, 1024 / tiles), (T + 63) / 64));
+}
 
 size_t router_wgrad_ws_bytes(int64_t T, int N1, int d) {
-  return (size_t)router_chunks(T) * N1 * d * sizeof(float);
+  return (size_t)router_chunks(T, N1, d) * N1 * d * sizeof(float);
 }
 
 hipError_t launch_router_wgrad(const float* ds, const void* x, int64_t T, int N1, int d, float* part, float* dw,
                                hipStream_t s) {
-  const int64_t chunks = router_chunks(T);
+  const int64_t chunks = router_chunks(T, N1, d);
   const int64_t chunk = (T + chunks - 1) / chunks;
   const dim3 grid((unsigned)((d + 511) / 512), (unsigned)((N1 + kRouterRows - 1) / kRouterRows), (unsigned)chunks);
   router_wgrad_partial_kernel<<<grid, 256, 0, s>>>(ds, static_cast<const bf16_t*>(x), T, N1, d, chunk, part);
