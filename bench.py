@@ -39,6 +39,9 @@ def parse():
                     help="time the backward pass even with --no-sweep (it runs with the sweep anyway)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_0p6b_rho1",
+                    help="configuration of the timed layer and kernel table (the headline by default; "
+                         "another one for profiling runs)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run three 256 MiB device copies: the reference that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters (token_choice_routing_amd.traffic)")
@@ -474,7 +477,10 @@ def main():
 
     tcr.load_library()
     torch.cuda.set_device(0)
-    cfg = CONFIGS["qwen3_0p6b_rho1"]
+    if args.workload not in CONFIGS:
+        print(f"unknown workload {args.workload}; one of {sorted(CONFIGS)}", file=sys.stderr)
+        sys.exit(2)
+    cfg = CONFIGS[args.workload]
     log(f"bench: generating {cfg.name}")
     wl = generate(cfg)
     layer = MoeLayer(wl)
