@@ -154,3 +154,40 @@ def test_empty_inputs_are_noops(lib):
     assert lib.moe_expert_ffn(ctypes.byref(d1), 3, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                               None) == MOE_OK
     assert tcr.workspace_bytes(_dims(dtype=MOE_F32), MOE_WS_ROUTE) == 0
+
+
+def test_backward_argument_checks(lib):
+    """moe_layer_backward refuses what it does not cover and bad pointers or
+    workspaces with the documented status, before anything is launched; T = 0 is a
+    no-op."""
+    big = 1 << 40
+    grads = tcr.LayerGrads(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+
+    def call(d, params=p, dy=FAKE, g=grads, ws=FAKE, nbytes=big):
+        return lib.moe_layer_backward(ctypes.byref(d), ctypes.byref(params) if params else None, dy,
+                                      ctypes.c_float(0.02), ctypes.c_float(0.001),
+                                      ctypes.byref(g) if g else None, ws, ctypes.c_size_t(nbytes), None)
+
+    d = _dims()
+    assert call(_dims(dtype=MOE_F32)) == MOE_ERR_UNSUPPORTED
+    assert call(_dims(null_kind=tcr.MOE_NULL_COPY)) == MOE_ERR_UNSUPPORTED
+    assert call(d, params=None) == MOE_ERR_ARG
+    assert call(d, g=None) == MOE_ERR_ARG
+    assert call(d, dy=None) == MOE_ERR_ARG
+    assert call(d, dy=MIS) == MOE_ERR_ALIGN
+    assert call(d, g=tcr.LayerGrads(FAKE, FAKE, FAKE, None, FAKE, None, None, None)) == MOE_ERR_ARG
+    assert call(d, g=tcr.LayerGrads(FAKE, FAKE, FAKE, FAKE, MIS, None, None, None)) == MOE_ERR_ALIGN
+    # a shared expert needs its weights and its three gradients
+    ds = _dims(d_ff_shared=64)
+    assert call(ds) == MOE_ERR_ARG
+    ps = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ds, params=ps) == MOE_ERR_ARG
+    need = tcr.workspace_bytes(d, tcr.MOE_WS_BACKWARD)
+    assert need > tcr.workspace_bytes(d, MOE_WS_LAYER)
+    assert call(d, nbytes=need - 1) == MOE_ERR_WORKSPACE
+    assert call(d, ws=None, nbytes=need) == MOE_ERR_WORKSPACE
+    # bf16 operands past the 32-bit offsets (transposed activations included)
+    assert call(make_dims(T=70000, d_model=32768, n_experts=4, n_null=0, top_k=2, d_ff=64,
+                          dtype=MOE_BF16)) == MOE_ERR_UNSUPPORTED
+    assert call(_dims(T=0)) == MOE_OK
