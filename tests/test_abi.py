@@ -191,3 +191,11 @@ def test_backward_argument_checks(lib):
     assert call(make_dims(T=70000, d_model=32768, n_experts=4, n_null=0, top_k=2, d_ff=64,
                           dtype=MOE_BF16)) == MOE_ERR_UNSUPPORTED
     assert call(_dims(T=0)) == MOE_OK
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding passes device addresses only: a host tensor or a strided view would be
+    read as a dense device array, so it is refused before the call."""
+    import torch
+    with pytest.raises(ValueError):
+        tcr._ptr(torch.zeros(4))

@@ -107,10 +107,17 @@ def header_functions(path: str = HEADER):
 
 
 def _ptr(t):
+    """Device address of a tensor argument (an int is taken as an address as is).
+    The library reads every array as a dense row-major block in device memory, so a
+    host tensor or a strided view is refused here rather than read wrongly there."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if t.device.type != "cuda":
+        raise ValueError(f"expected a device tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor (the library reads dense row-major arrays)")
     return t.data_ptr()
 
 
