@@ -26,7 +26,8 @@
  *     reduction dimension contiguous: w_gate, w_up [N][d_ff][d_model];
  *     w_down [N][d_model][d_ff]; the router [N+1][d_model], row N = null.
  *   - Ownership: the caller allocates and frees all memory. The library never
- *     allocates, frees or synchronises; it keeps no state between calls
+ *     allocates, frees or synchronises (moe_validate_inputs, a checking call,
+ *     synchronises); it keeps no state between calls
  *     except a per-device cache of the compute-unit count. Calls on distinct
  *     buffers may run concurrently.
  *   - Execution: every kernel is enqueued on `stream` (a hipStream_t; NULL is
@@ -57,7 +58,8 @@ typedef enum {
   MOE_ERR_ALIGN = 2,       /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   MOE_ERR_UNSUPPORTED = 4, /* valid but outside this build's limits */
-  MOE_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+  MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
+  MOE_ERR_NONFINITE = 6    /* moe_validate_inputs found a NaN or an infinity */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -297,6 +299,20 @@ typedef struct {
 moe_status moe_layer_backward(const moe_dims* dims, const moe_layer_params* params, const void* dy,
                               float alpha, float beta, const moe_layer_grads* grads, void* ws,
                               size_t ws_bytes, moe_stream stream);
+
+/*
+ * moe_validate_inputs -- optional check of the layer's inputs, not part of the
+ * forward: NaN or +-inf anywhere in x, the router, the expert and shared-expert
+ * weights or the constant vector, and NaN in null_bias / null_bias_tok (an
+ * infinite null bias is a valid input: it sends every slot of a token to the
+ * null copies, or none). The layer's outputs are undefined for such inputs; the
+ * pages fix nothing for them. Same dims and params as moe_layer_forward (and the
+ * same pointer checks). Unlike every other entry point this one synchronises
+ * `stream`, to read one count back. ws: at least 16 bytes of device memory.
+ * Returns MOE_ERR_NONFINITE if anything is found, MOE_OK otherwise.
+ */
+moe_status moe_validate_inputs(const moe_dims* dims, const moe_layer_params* params, void* ws,
+                               size_t ws_bytes, moe_stream stream);
 
 /* Workspace bytes for MOE_WS_LAYER / ROUTE / PERMUTE / AUX / BACKWARD (bf16 only);
  * 0 on invalid dims. */

@@ -199,3 +199,19 @@ def test_binding_refuses_host_and_strided_tensors():
     import torch
     with pytest.raises(ValueError):
         tcr._ptr(torch.zeros(4))
+
+
+def test_validate_inputs_argument_checks(lib):
+    """moe_validate_inputs checks pointers and workspace like the forward, and a NaN
+    host-side null bias is reported before anything is launched."""
+    d = _dims()
+    b = ctypes.byref(d)
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_validate_inputs(b, None, FAKE, 256, None) == MOE_ERR_ARG
+    assert lib.moe_validate_inputs(b, ctypes.byref(tcr.LayerParams(None, FAKE, 0.0, None, FAKE, FAKE, FAKE,
+                                                                   None, None, None)), FAKE, 256, None) == MOE_ERR_ARG
+    assert lib.moe_validate_inputs(b, ctypes.byref(p), FAKE, 8, None) == MOE_ERR_WORKSPACE
+    assert lib.moe_validate_inputs(b, ctypes.byref(p), MIS, 256, None) == MOE_ERR_ALIGN
+    pn = tcr.LayerParams(FAKE, FAKE, float("nan"), None, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.moe_validate_inputs(b, ctypes.byref(pn), FAKE, 256, None) == tcr.MOE_ERR_NONFINITE
+    assert lib.moe_status_str(tcr.MOE_ERR_NONFINITE).decode().startswith("non-finite")

@@ -271,3 +271,33 @@ def test_layer_forward_and_backward_replay_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(layer.y, ref_y)
     del graph
+
+
+def test_validate_inputs_finds_nan_and_inf():
+    """moe_validate_inputs: a clean layer passes; a NaN in x, an infinity in an expert
+    weight or in the router, or a NaN null bias is found; an infinite per-token null
+    bias (a valid input: all slots of that token null) passes."""
+    say("moe_validate_inputs")
+    cfg = Config(name="validate", T=200, d_model=128, n_experts=8, n_null=8, top_k=4, d_ff=96,
+                 d_ff_shared=64, dtype="bf16", w_std=None, seed=3)
+    wl = generate(cfg)
+    wl.null_bias_tok = np.zeros(cfg.T, dtype=np.float32)
+    layer = MoeLayer(wl)
+    assert layer.validate()
+
+    def planted(t, index, value):
+        old = t.view(-1)[index].clone()
+        t.view(-1)[index] = value
+        ok = layer.validate()
+        t.view(-1)[index] = old
+        assert layer.validate()
+        return ok
+
+    nan16, inf16 = torch.tensor(0x7FC0, dtype=torch.int16), torch.tensor(0x7F80, dtype=torch.int16)
+    assert not planted(layer.x.view(torch.int16), 1234, nan16)
+    assert not planted(layer.w_up.view(torch.int16), layer.w_up.numel() - 1, inf16)
+    assert not planted(layer.ws_down.view(torch.int16), 7, inf16)
+    assert not planted(layer.w_router, 5, float("inf"))
+    assert not planted(layer.null_bias_tok, 17, float("nan"))
+    assert planted(layer.null_bias_tok, 17, float("inf"))
+    assert planted(layer.null_bias_tok, 18, float("-inf"))

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
-MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(6)
+MOE_OK, MOE_ERR_ARG, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_NONFINITE = range(7)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_NULL_ZERO, MOE_NULL_COPY, MOE_NULL_CONSTANT = 0, 1, 2
 NULL_KINDS = {"zero": MOE_NULL_ZERO, "copy": MOE_NULL_COPY, "constant": MOE_NULL_CONSTANT}
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.c_size_t, _P],
         "moe_layer_backward": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(LayerGrads), _P, ctypes.c_size_t, _P],
+        "moe_validate_inputs": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_size_t, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -231,6 +232,18 @@ def moe_layer_backward(dims, params: LayerParams, dy, alpha: float, beta: float,
     _check(load_library().moe_layer_backward(ctypes.byref(dims), ctypes.byref(params), _ptr(dy),
                                               float(alpha), float(beta), ctypes.byref(grads), wp, wb,
                                               _stream(stream)), "moe_layer_backward")
+
+
+def moe_validate_inputs(dims, params: LayerParams, ws, stream=None) -> bool:
+    """True when the layer's inputs hold no NaN or infinity (null biases may be
+    infinite), False when they do; synchronises the stream. ws: >= 16 device bytes."""
+    wp, wb = _ws(ws)
+    status = load_library().moe_validate_inputs(ctypes.byref(dims), ctypes.byref(params), wp, wb,
+                                                _stream(stream))
+    if status == MOE_ERR_NONFINITE:
+        return False
+    _check(status, "moe_validate_inputs")
+    return True
 
 
 from .layer import MoeLayer  # noqa: E402,F401

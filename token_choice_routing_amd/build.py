@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "aux.hip", "backward.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "aux.hip", "backward.hip", "validate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

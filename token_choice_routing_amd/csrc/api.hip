@@ -2,6 +2,7 @@
 // launches for the null-expert token-choice MoE layer forward. The entry points
 // and their contracts are documented in include/moe.h.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 
 #include "common.hpp"
@@ -193,6 +194,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_UNSUPPORTED: return "dimensions outside this build's limits";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_NONFINITE: return "non-finite input (NaN or infinity)";
   }
   return "unknown status";
 }
@@ -464,6 +466,49 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
                  d->d_ff_shared ? at(L.ys) : nullptr, nsrc, null_stride(d), y};
   HIP_TRY(launch_combine(ca, s));
   return MOE_OK;
+}
+
+moe_status moe_validate_inputs(const moe_dims* d, const moe_layer_params* p, void* ws, size_t ws_bytes,
+                               moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (!p) return MOE_ERR_ARG;
+  MOE_TRY(need(p->x));
+  MOE_TRY(need(p->w_router));
+  MOE_TRY(maybe(p->null_bias_tok));
+  MOE_TRY(need(p->w_gate));
+  MOE_TRY(need(p->w_up));
+  MOE_TRY(need(p->w_down));
+  if (d->d_ff_shared) {
+    MOE_TRY(need(p->ws_gate));
+    MOE_TRY(need(p->ws_up));
+    MOE_TRY(need(p->ws_down));
+  }
+  if (d->null_kind == MOE_NULL_CONSTANT) MOE_TRY(need(p->null_value));
+  if (!ws || ws_bytes < 16) return MOE_ERR_WORKSPACE;
+  MOE_TRY(need(ws));
+  if (std::isnan(p->null_bias)) return MOE_ERR_NONFINITE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = d->dtype == MOE_BF16;
+  const int64_t T = d->T, dm = d->d_model, N = d->n_experts, F = d->d_ff, Fs = d->d_ff_shared;
+  int32_t* count = static_cast<int32_t*>(ws);
+  (void)hipGetLastError();
+  HIP_TRY(launch_zero_count(count, s));
+  HIP_TRY(launch_count_nonfinite(p->x, T * dm, bf16, false, count, s));
+  HIP_TRY(launch_count_nonfinite(p->w_router, (N + 1) * dm, false, false, count, s));
+  HIP_TRY(launch_count_nonfinite(p->null_bias_tok, T, false, true, count, s));
+  HIP_TRY(launch_count_nonfinite(p->w_gate, N * F * dm, bf16, false, count, s));
+  HIP_TRY(launch_count_nonfinite(p->w_up, N * F * dm, bf16, false, count, s));
+  HIP_TRY(launch_count_nonfinite(p->w_down, N * dm * F, bf16, false, count, s));
+  if (Fs) {
+    HIP_TRY(launch_count_nonfinite(p->ws_gate, Fs * dm, bf16, false, count, s));
+    HIP_TRY(launch_count_nonfinite(p->ws_up, Fs * dm, bf16, false, count, s));
+    HIP_TRY(launch_count_nonfinite(p->ws_down, dm * Fs, bf16, false, count, s));
+  }
+  if (d->null_kind == MOE_NULL_CONSTANT) HIP_TRY(launch_count_nonfinite(p->null_value, dm, bf16, false, count, s));
+  int32_t host = 0;
+  HIP_TRY(hipMemcpyAsync(&host, count, sizeof(host), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return host ? MOE_ERR_NONFINITE : MOE_OK;
 }
 
 moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,

@@ -124,6 +124,12 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
 // refused.
 bool gemm_operands_fit(const GemmProblem& p);
 
+// Input check (validate.hip): count[0] = 0; count[0] += non-finite elements of data
+// (bf16 or float32; nan_only: NaN alone, infinities allowed).
+hipError_t launch_zero_count(int32_t* count, hipStream_t s);
+hipError_t launch_count_nonfinite(const void* data, int64_t n, bool bf16, bool nan_only, int32_t* count,
+                                  hipStream_t s);
+
 // Backward-pass helpers (backward.hip); all enqueue on `s`, bf16 tensors as bits.
 // out[b][c][c_out + r] (row stride ldo, batch stride out_batch) = in[b][r][c], in [b][R][C].
 hipError_t launch_transpose(const void* in, int64_t batches, int64_t R, int64_t C, void* out, int64_t ldo,

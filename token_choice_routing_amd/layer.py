@@ -97,6 +97,12 @@ class MoeLayer:
                            stream=stream)
         return self.grads
 
+    def validate(self):
+        """True when x, the router, the expert weights and the null biases are free of
+        NaN (and, except for the null biases, of infinities); synchronises."""
+        from . import moe_validate_inputs
+        return moe_validate_inputs(self.dims, self.params, self.ws)
+
     def results(self):
         """Host copies of every output (synchronises)."""
         torch.cuda.synchronize()
