@@ -456,11 +456,22 @@ def measure(torch, layer, steps, warmup):
     cfg = layer.cfg
     R = int(layer.offsets[-1].item())
     fl = layer_flops(cfg, R, layer.T)
-    return {"workload": cfg.name, "T": layer.T, "K": cfg.top_k, "M": cfg.n_null,
-            "rho_nominal": round(cfg.rho_nominal, 4), "rho_realised": round(R / (layer.T * cfg.top_k), 4),
-            "real_slots": R, "ms": round(ms, 4), "tokens_per_s": round(layer.T / ms * 1e3, 1),
-            "real_expert_tflops": round(fl / ms / 1e9, 2),
-            "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    seg = layer.offsets.diff().double()
+    out = {"workload": cfg.name, "T": layer.T, "K": cfg.top_k, "M": cfg.n_null,
+           "rho_nominal": round(cfg.rho_nominal, 4), "rho_realised": round(R / (layer.T * cfg.top_k), 4),
+           "real_slots": R, "ms": round(ms, 4), "tokens_per_s": round(layer.T / ms * 1e3, 1),
+           "real_expert_tflops": round(fl / ms / 1e9, 2),
+           "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           # expert segment lengths (rows per expert): the grouped GEMM's load balance
+           "segments": {"min": int(seg.min().item()), "max": int(seg.max().item()),
+                        "cv": round(float((seg.std(unbiased=False) / seg.mean().clamp(min=1e-9)).item()), 3)}}
+    if cfg.x_kind == "modality":
+        # compute intensity r / K per class (the first round(vision_frac T) tokens are vision)
+        vT = int(round(cfg.vision_frac * layer.T))
+        r = layer.n_real.double()
+        out["intensity"] = {"vision": round(float(r[:vT].mean().item()) / cfg.top_k, 4),
+                            "text": round(float(r[vT:].mean().item()) / cfg.top_k, 4)}
+    return out
 
 
 def main():
