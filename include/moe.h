@@ -57,7 +57,7 @@ typedef enum {
   MOE_ERR_ARG = 1,         /* bad dimension or NULL required pointer */
   MOE_ERR_ALIGN = 2,       /* a device pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  MOE_ERR_UNSUPPORTED = 4, /* valid but outside this build's limits */
+  MOE_ERR_UNSUPPORTED = 4, /* valid but outside this library's limits */
   MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
   MOE_ERR_NONFINITE = 6    /* moe_validate_inputs found a NaN or an infinity */
 } moe_status;

@@ -192,7 +192,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_ARG: return "invalid argument (dimension or NULL pointer)";
     case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
-    case MOE_ERR_UNSUPPORTED: return "dimensions outside this build's limits";
+    case MOE_ERR_UNSUPPORTED: return "dimensions outside this library's limits";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_NONFINITE: return "non-finite input (NaN or infinity)";
   }
