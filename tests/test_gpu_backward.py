@@ -202,3 +202,11 @@ def test_backward_one_expert_takes_every_slot():
     got, ref = _run_wl(wl, 2e-2, 1e-3)
     assert (ref["fwd"]["topk_idx"][:, 0] == 3).all()
     _check(cfg, got, ref)
+
+
+def test_backward_at_the_size_limits():
+    """N = 255, M = 3841 (the largest pool), K = 32, with a shared expert."""
+    cfg = Config(name="bwd_limits", T=150, d_model=64, n_experts=255, n_null=3841, top_k=32, d_ff=64,
+                 d_ff_shared=32, dtype="bf16", w_std=None, seed=12)
+    got, ref = _run_wl(generate(cfg), 2e-2, 1e-3)
+    _check(cfg, got, ref)

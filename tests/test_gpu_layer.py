@@ -301,3 +301,14 @@ def test_validate_inputs_finds_nan_and_inf():
     assert not planted(layer.null_bias_tok, 17, float("nan"))
     assert planted(layer.null_bias_tok, 17, float("inf"))
     assert planted(layer.null_bias_tok, 18, float("-inf"))
+
+
+def test_layer_at_the_size_limits():
+    """The largest pool the library takes: N = 255 experts (MOE_MAX_EXPERTS), M = 3841
+    null copies (N + M = MOE_MAX_POOL) and K = 32 (MOE_MAX_TOPK), with a shared
+    expert: routing, permutation over 255 segments, 256 GEMM groups and a 32-slot
+    combine against the oracle."""
+    say("layer at N = 255, M = 3841, K = 32")
+    cfg = Config(name="limits", T=150, d_model=64, n_experts=255, n_null=3841, top_k=32, d_ff=64,
+                 d_ff_shared=32, dtype="bf16", w_std=None, seed=12)
+    check_full(generate(cfg))

@@ -50,7 +50,11 @@
 
 namespace moe {
 
-constexpr int kMaxGroups = 320;   // routed groups (<= 256) + the dense shared-expert problem
+// Groups of one launch's two problems together: the backward pairs two grouped
+// problems of up to MOE_MAX_EXPERTS (255) groups each (gate and up), or 255 routed
+// groups and up to 32 chunks of the shared expert. The tile table lives in LDS next
+// to the stages (7 x 513 ints, 14 KB).
+constexpr int kMaxGroups = 512;
 
 enum { kSwiGLU = 0, kPlain = 1 };
 
@@ -798,6 +802,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
   if (!any0 && !any1) return hipSuccess;
   if (bf16 && (!gemm_operands_fit(p0) || !gemm_operands_fit(p1))) return hipErrorInvalidValue;
+  if ((any0 ? p0.groups : 0) + (any1 ? p1.groups : 0) > kMaxGroups) return hipErrorInvalidValue;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
     auto plain_form = [](const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; };
