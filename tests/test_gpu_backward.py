@@ -41,6 +41,9 @@ CASES = {
     "wide": dict(T=1024, d_model=256, n_experts=16, n_null=16, top_k=4, d_ff=192, d_ff_shared=128),
     # 0 < M < K and an expert count that leaves some experts empty
     "few_nulls": dict(T=40, d_model=64, n_experts=32, n_null=2, top_k=4, d_ff=64, d_ff_shared=32),
+    # d_model, d_ff and d_ff_shared multiples of 8 but not of 64 or 32: ragged K tiles
+    # in every contraction and ragged 64 x 64 tiles in every transpose
+    "ragged_dims": dict(T=333, d_model=200, n_experts=12, n_null=4, top_k=3, d_ff=104, d_ff_shared=40),
 }
 
 
