@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the rho sweep and other workloads")
     ap.add_argument("--with-backward", action="store_true",
                     help="time the backward pass even with --no-sweep (it runs with the sweep anyway)")
+    ap.add_argument("--with-decode", action="store_true",
+                    help="time the decode regime even with --no-sweep (it runs with the sweep anyway)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_0p6b_rho1",
@@ -544,6 +546,7 @@ def main():
     if not args.no_sweep:
         log("bench: rho sweep and other workloads")
         line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
+    if not args.no_sweep or args.with_decode:
         log("bench: decode regime")
         line["decode"] = decode_sweep(torch, wl, layer, max(5, args.steps // 2))
     if not args.no_sweep or args.with_backward:
