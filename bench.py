@@ -488,11 +488,11 @@ def main():
     from token_choice_routing_amd.layer import MoeLayer
     from workloads import CONFIGS, generate
 
-    tcr.load_library()
-    torch.cuda.set_device(0)
     if args.workload not in CONFIGS:
         print(f"unknown workload {args.workload}; one of {sorted(CONFIGS)}", file=sys.stderr)
         sys.exit(2)
+    tcr.load_library()
+    torch.cuda.set_device(0)
     cfg = CONFIGS[args.workload]
     log(f"bench: generating {cfg.name}")
     wl = generate(cfg)
