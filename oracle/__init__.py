@@ -29,6 +29,6 @@ fixtures under ``tests/golden/``, invariants).
 """
 from .moe_oracle import (  # noqa: F401
     router_logits, select, renorm_weights, route, permute, silu, swiglu_ffn,
-    expert_ffn_grouped, combine, aux_stats, layer_forward, layer_dense,
+    expert_ffn_grouped, combine, pool_softmax, aux_stats, layer_forward, layer_dense,
     decisive_gap,
 )

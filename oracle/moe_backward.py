@@ -20,6 +20,11 @@ derivative; the counts f_i are constants for the same reason):
   L_z          = mean_t lse_t^2;   d/dv_tc = (2/T) lse_t p_tc
                the M null copies all read the null logit, so its gradient is the
                sum over the copies (and 0 when M = 0: the null row is not used)
+  null at +inf a token whose null logit is +inf (infinite per-token bias) has the
+               limit pool softmax (1/M per null copy, reals 0) and lse = +inf, so
+               L_z = +inf and its z-loss gradient has no finite value: it is taken
+               as 0. Its balance term is 0 as well (p is constant in every finite
+               logit), so the token's logit gradient is the weight term alone.
   router       s = x W_r^T (+ constant null biases): dW_r = ds^T x, dx += ds W_r
   expert e     g = a W_g^T, u = a W_u^T, h = silu(g) u, Y = h W_d^T:
                dh = dY W_d, dW_d = dY^T h, dg = dh u silu'(g), du = dh silu(g),
@@ -95,15 +100,12 @@ def layer_backward(wl, dy, alpha=0.0, beta=0.0, logits=None):
 
     # auxiliary losses over the pool
     aux = fwd["aux"]
-    v = O._pool(fwd["logits"], N, M)
-    mx = v.max(axis=1, keepdims=True)
-    ex = np.exp(v - mx)
-    p = ex / ex.sum(axis=1, keepdims=True)
-    lse = aux["lse"]
+    p, lse = O.pool_softmax(fwd["logits"], N, M)
     f = aux["f"]
     if T:
         fbar = p @ f
-        dv = alpha * (N / T) * p * (f[None, :] - fbar[:, None]) + beta * (2.0 / T) * lse[:, None] * p
+        zt = np.where(np.isfinite(lse), lse, 0.0)   # z-loss term of a null at +inf: 0
+        dv = alpha * (N / T) * p * (f[None, :] - fbar[:, None]) + beta * (2.0 / T) * zt[:, None] * p
         ds[:, :N] += dv[:, :N]
         if M:
             ds[:, N] += dv[:, N:].sum(axis=1)
@@ -164,7 +166,6 @@ def sampled_backward(wl, dy, alpha, beta, logits, tokens, experts):
     topk, w, _ = O.route(logits, N, M, K)
     counts, offsets, perm, slot_pos = O.permute(topk, N)
     aux = O.aux_stats(logits, topk, N, M, K)
-    v = O._pool(logits, N, M)
     tokens = np.asarray(tokens)
     out = dict(dw_gate={}, dw_up={}, dw_down={})
     for e in experts:
@@ -177,13 +178,11 @@ def sampled_backward(wl, dy, alpha, beta, logits, tokens, experts):
         out["dw_gate"][e], out["dw_up"][e], out["dw_down"][e] = b["dw_gate"], b["dw_up"], b["dw_down"]
     ds = np.zeros((len(tokens), N + 1), f64)
     dx = np.zeros((len(tokens), x.shape[1]), f64)
-    mx = v[tokens].max(axis=1, keepdims=True)
-    ex = np.exp(v[tokens] - mx)
-    p = ex / ex.sum(axis=1, keepdims=True)
-    lse = aux["lse"][tokens]
+    p, lse = O.pool_softmax(logits[tokens], N, M)
     f = aux["f"]
     fbar = p @ f
-    dv = alpha * (N / T) * p * (f[None, :] - fbar[:, None]) + beta * (2.0 / T) * lse[:, None] * p
+    zt = np.where(np.isfinite(lse), lse, 0.0)   # z-loss term of a null at +inf: 0
+    dv = alpha * (N / T) * p * (f[None, :] - fbar[:, None]) + beta * (2.0 / T) * zt[:, None] * p
     ds[:, :N] = dv[:, :N]
     if M:
         ds[:, N] = dv[:, N:].sum(axis=1)

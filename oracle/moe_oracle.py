@@ -223,6 +223,26 @@ def combine(y_perm, slot_pos, topk_w, y_shared=None, d_model=None, null_src=None
 
 
 # ---------------------------------------------------------------- statistics
+def pool_softmax(logits, N, M):
+    """Pool softmax p_t over [s_1..s_N, s_null x M] and lse_t = log sum_i e^{v_t,i},
+    max-shifted ([Review] load-balance loss and z-loss). A null logit of +inf (an
+    infinite per-token null bias, M > 0) takes the limit of a growing null logit:
+    each null copy 1/M, every real 0, and lse_t = +inf. Returns (p [T, N+M], lse [T])."""
+    v = _pool(logits, N, M)
+    T, P = v.shape
+    inf_null = np.zeros(T, dtype=bool) if M == 0 else np.isposinf(v[:, N])
+    if inf_null.any():
+        # the limit: the null copies at 0 and the reals at -inf after the shift
+        limit = np.where(np.arange(P) >= N, 0.0, -np.inf)
+        v = np.where(inf_null[:, None], limit[None, :], v)
+    m = v.max(axis=1, keepdims=True) if P else np.zeros((T, 1))
+    ex = np.exp(v - m)
+    z = ex.sum(axis=1, keepdims=True)
+    p = ex / z
+    lse = np.where(inf_null, np.inf, (m + np.log(z))[:, 0])
+    return p, lse
+
+
 def aux_stats(logits, topk_idx, N, M, K):
     """Load-balance and z-loss statistics over the N+M pool.
       p_t = softmax of the pool [s_1..s_N, s_null x M]      ([Review] load-balance loss)
@@ -230,14 +250,11 @@ def aux_stats(logits, topk_idx, N, M, K):
       L_bal = N * sum_{i<N+M} f_i P_i                          ([Review] load-balance loss)
       L_z = mean_t (log sum_{i<N+M} exp v_t,i)^2              ([Review] z-loss; [Primer] 4.3)
     plus mean_r = mean number of chosen reals per token ([Review] expected
-    active experts; r/K is the compute intensity of [Summary] Figure 4)."""
-    v = _pool(logits, N, M)
-    T, P = v.shape
-    m = v.max(axis=1, keepdims=True)
-    ex = np.exp(v - m)
-    z = ex.sum(axis=1, keepdims=True)
-    p = ex / z
-    lse = (m + np.log(z))[:, 0]
+    active experts; r/K is the compute intensity of [Summary] Figure 4).
+    A token whose null logit is +inf contributes the limit of ``pool_softmax``
+    (1/M per null copy) to P and lse = +inf, so L_z = +inf."""
+    p, lse = pool_softmax(logits, N, M)
+    T, P = p.shape
     Pm = p.mean(axis=0) if T else np.zeros(P)
     flat = topk_idx.reshape(-1)
     counts = np.bincount(flat[(flat >= 0) & (flat < P)], minlength=P).astype(np.int64)

@@ -73,3 +73,51 @@ def test_m0_reduction_to_plain_aux():
     p = np.exp(s[:, :N]) / np.exp(s[:, :N]).sum(axis=1, keepdims=True)
     np.testing.assert_allclose(a["P"], p.mean(axis=0), rtol=1e-13)
     assert abs(a["L_z"] - np.mean(np.log(np.exp(s[:, :N]).sum(axis=1)) ** 2)) < 1e-12
+
+
+def test_infinite_null_bias_closed_forms():
+    """Every token's null logit at +inf (an infinite per-token bias): the pool softmax
+    is its limit, 1/M per null copy and 0 per real; with M >= K the K slots are null
+    copies N .. N+K-1, so L_bal = N K / M; every lse is +inf, so L_z = +inf."""
+    rng = np.random.default_rng(12)
+    for N, M, K, T in ((8, 8, 2, 40), (64, 192, 8, 16), (6, 3, 3, 9)):
+        s = rng.standard_normal((T, N + 1))
+        s[:, N] = np.inf
+        topk, w, n_real = O.route(s, N, M, K)
+        a = O.aux_stats(s, topk, N, M, K)
+        assert (n_real == 0).all() and (w == 0).all()
+        assert (a["P"][:N] == 0).all()
+        np.testing.assert_allclose(a["P"][N:], 1.0 / M, rtol=1e-14)
+        f = np.zeros(N + M)
+        f[N:N + K] = 1.0
+        np.testing.assert_array_equal(a["f"], f)
+        assert abs(a["L_bal"] - N * K / M) < 1e-12
+        assert a["L_z"] == np.inf and (a["lse"] == np.inf).all()
+        assert a["mean_r"] == 0.0
+
+
+def test_infinite_null_bias_is_the_large_bias_limit():
+    """Some tokens' null logit at +inf: P, f, counts and L_bal equal those of a null
+    logit of 1e4 (where exp(s - 1e4) already underflows to 0 in float64, so the finite
+    path computes the limit itself), the other tokens' lse are unchanged, and only
+    the L_z of the infinite tokens differs (+inf instead of 1e4 + log M)."""
+    rng = np.random.default_rng(13)
+    for N, M, K in ((16, 16, 4), (8, 2, 4)):          # 0 < M < K forces K - M reals
+        T = 60
+        s = rng.standard_normal((T, N + 1))
+        inf_rows = np.arange(T) % 7 == 3
+        s_inf, s_big = s.copy(), s.copy()
+        s_inf[inf_rows, N] = np.inf
+        s_big[inf_rows, N] = 1e4
+        t_inf, w_inf, r_inf = O.route(s_inf, N, M, K)
+        t_big, w_big, r_big = O.route(s_big, N, M, K)
+        np.testing.assert_array_equal(t_inf, t_big)
+        np.testing.assert_array_equal(w_inf, w_big)
+        assert (r_inf[inf_rows] == max(0, K - M)).all()
+        a, b = O.aux_stats(s_inf, t_inf, N, M, K), O.aux_stats(s_big, t_big, N, M, K)
+        for key in ("P", "f", "counts"):
+            np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+        assert a["L_bal"] == b["L_bal"]
+        np.testing.assert_array_equal(a["lse"][~inf_rows], b["lse"][~inf_rows])
+        np.testing.assert_allclose(b["lse"][inf_rows], 1e4 + np.log(M), rtol=1e-15)
+        assert a["L_z"] == np.inf and np.isfinite(b["L_z"])

@@ -171,3 +171,31 @@ def test_sampled_backward_equals_full(seed, M, K):
     for name in ("dw_gate", "dw_up", "dw_down"):
         for e in experts:
             np.testing.assert_allclose(sb[name][e], g[name][e], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("M,K", [(5, 3), (2, 4)])
+def test_infinite_null_bias_token_gradient(M, K):
+    """Tokens whose null logit is +inf: their logit gradient is the weight term alone
+    (the z-loss term has no finite value and is taken as 0, and the balance term of a
+    saturated pool softmax is 0). Against a null bias of 1e4, where the pool softmax
+    already is the limit in float64: with beta = 0 every gradient is the same; with
+    beta > 0 the infinite tokens' rows equal the beta = 0 ones, every other row is
+    unchanged, and the router gradient stays finite."""
+    T = 24
+    inf_tok = np.zeros(T)
+    inf_tok[::5] = np.inf
+    big_tok = np.where(np.isinf(inf_tok), 1e4, 0.0)
+    wl_inf, dy = _layer(21, T=T, M=M, K=K, tok_bias=inf_tok)
+    wl_big, _ = _layer(21, T=T, M=M, K=K, tok_bias=big_tok)
+    rows = np.isinf(inf_tok)
+    g_inf0 = B.layer_backward(wl_inf, dy, 0.4, 0.0)
+    g_big0 = B.layer_backward(wl_big, dy, 0.4, 0.0)
+    for k in ("dx", "dw_router", "ds", "dw_gate", "dw_up", "dw_down"):
+        np.testing.assert_allclose(g_inf0[k], g_big0[k], rtol=1e-13, atol=1e-14, err_msg=k)
+    g_inf = B.layer_backward(wl_inf, dy, 0.4, 0.3)
+    g_big = B.layer_backward(wl_big, dy, 0.4, 0.3)
+    assert np.isfinite(g_inf["dw_router"]).all() and np.isfinite(g_inf["dx"]).all()
+    np.testing.assert_allclose(g_inf["ds"][rows], g_big0["ds"][rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(g_inf["ds"][~rows], g_big["ds"][~rows], rtol=1e-13, atol=1e-14)
+    if K <= M:   # no real slot: the whole row is zero (up to the rounding of f - fbar)
+        assert np.abs(g_inf["ds"][rows]).max() <= 1e-15
