@@ -126,12 +126,18 @@ def renorm_weights(logits, topk_idx, N):
 
 def chosen_weights(logits, topk_idx, N):
     """Weights of the copy / constant variants: a softmax over all K chosen pool
-    entries, null slots taking the effective null logit (column N), max-shifted."""
+    entries, null slots taking the effective null logit (column N), max-shifted.
+    An entry equal to the maximum has numerator 1, which for a null logit at +inf
+    is the limit (every chosen null copy equally, the reals 0)."""
     s = np.asarray(logits, dtype=f64)
     T, K = topk_idx.shape
+    if not K:
+        return np.zeros((T, 0))
     vals = np.where(topk_idx < N, np.take_along_axis(s, np.minimum(topk_idx, N), axis=1), s[:, N:N + 1])
-    e = np.exp(vals - vals.max(axis=1, keepdims=True)) if K else vals
-    return e / e.sum(axis=1, keepdims=True) if K else e
+    mx = vals.max(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        e = np.where(vals == mx, 1.0, np.exp(vals - mx))
+    return e / e.sum(axis=1, keepdims=True)
 
 
 def route(logits, N, M, K, null_kind="zero"):

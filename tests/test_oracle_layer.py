@@ -154,6 +154,24 @@ def test_copy_all_null_gives_token_plus_shared():
     np.testing.assert_allclose(out["y"], ref, rtol=1e-13, atol=1e-13)
 
 
+def test_copy_infinite_null_bias_is_the_large_bias_limit():
+    """A null logit at +inf with copy experts: the weights are the limit of a large
+    finite null bias (every chosen null copy equally, the reals 0), so with M >= K
+    y = x + E_shared(x) exactly as with the 1e4 bias; with 0 < M < K the K - M forced
+    reals get weight 0 and the M null copies 1/M each."""
+    for M, K in ((6, 3), (2, 4)):
+        wl = generate(_small_cfg(null_kind="copy", n_null=M, top_k=K))
+        wl.null_bias = 1.0e4
+        big = O.layer_forward(wl)
+        wl.null_bias = np.inf
+        inf = O.layer_forward(wl)
+        np.testing.assert_array_equal(inf["topk_idx"], big["topk_idx"])
+        np.testing.assert_array_equal(inf["topk_w"], big["topk_w"])
+        np.testing.assert_array_equal(inf["y"], big["y"])
+        w = np.where(inf["topk_idx"] >= wl.cfg.n_experts, 1.0 / min(M, K), 0.0)
+        np.testing.assert_allclose(inf["topk_w"], w, rtol=1e-15)
+
+
 def test_constant_all_null_gives_vector_plus_shared():
     wl = _all_null("constant")
     out = O.layer_forward(wl)
