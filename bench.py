@@ -5,16 +5,18 @@
 
 A step is one moe_layer_forward call (route, permute, gather, grouped SwiGLU
 GEMMs, shared expert, combine, statistics) over one batch of synthetic tokens
-already resident in HBM. The headline workload is the Qwen3-0.6B-shaped layer
-(T=2048, d_model=1024, N=64 experts of d_ff=768, shared expert d_ff=768, K=2,
-M=0). Real-expert FLOPs count only the slots routed to real experts
-(6 d d_ff per slot) plus the shared expert (6 d d_ff_shared per token).
+already resident in HBM. The headline workload is the Qwen3-1.7B-shaped layer at
+rho = 0.25 (T=16384, d_model=2048, N=64 experts of d_ff=1536, shared expert
+d_ff=1536, K=8, M=192, null bias calibrated to 2 real experts per token), the
+shape the rho sweep runs at. Real-expert FLOPs count only the slots routed to real
+experts (6 d d_ff per slot); the shared expert's FLOPs (6 d d_ff_shared per
+token) are reported beside them.
 
 Besides the JSON line's required fields it reports, per kernel, the average
 launch time measured with HIP events on the launch stream and the algorithmic
-bytes / FLOPs per launch; the rho sweep at the Qwen3-1.7B shape and the other
-workloads (timed only); and the CPU oracle's throughput on a bounded sample.
-Prints exactly one JSON line on stdout.
+bytes / FLOPs per launch; the rho sweep and the other workloads (timed only);
+the decode regime; the backward pass; and the CPU oracle's throughput on a
+bounded sample. Prints exactly one JSON line on stdout.
 """
 import argparse
 import json
@@ -41,7 +43,7 @@ def parse():
                     help="time the decode regime even with --no-sweep (it runs with the sweep anyway)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_0p6b_rho1",
+    ap.add_argument("--workload", default="qwen3_1p7b_rho0p25",
                     help="configuration of the timed layer and kernel table (the headline by default; "
                          "another one for profiling runs)")
     ap.add_argument("--copy-ref", action="store_true",
@@ -152,8 +154,13 @@ class Flush:
         self.torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def layer_flops(cfg, R, T):
-    return 6.0 * cfg.d_model * cfg.d_ff * R + 6.0 * cfg.d_model * cfg.d_ff_shared * T
+def routed_flops(cfg, R):
+    """Real-expert FLOPs of the routed slots: 6 d d_ff per real slot (gate, up, down)."""
+    return 6.0 * cfg.d_model * cfg.d_ff * R
+
+
+def shared_flops(cfg, T):
+    return 6.0 * cfg.d_model * cfg.d_ff_shared * T
 
 
 def time_layer(torch, layer, steps, warmup):
@@ -203,6 +210,10 @@ def kernel_table(torch, tcr, layer, iters):
     def permute_gather():
         tcr.moe_permute(dims, topk, layer.x, counts, offsets, perm, slot, xp, ws_p)
 
+    def gate_up_layer():
+        tcr.moe_expert_gate_up(dims, layer.x, perm, offsets, layer.w_gate, layer.w_up, layer.ws_gate,
+                               layer.ws_up, h, hs if fs else None)
+
     def gemm1():
         tcr.moe_grouped_gemm(dims, tcr.MOE_GEMM_GATE_UP, N, f, d, Rmax, xp, offsets, layer.w_gate,
                              layer.w_up, h)
@@ -250,6 +261,9 @@ def kernel_table(torch, tcr, layer, iters):
     t_pg = tm.run(permute_gather, iters)
     add("gather", max(t_pg - t_perm, 1e-3), 2 * R * d * 2 + 4 * R)
     # GEMMs: "us" after a last-level-cache flush (the roofline figure), "us_warm" back to back
+    add("gate_up_layer", tm.run_cold(gate_up_layer, iters, flush),
+        T * d * 2 + active * 2 * f * d * 2 + R * f * 2 + (2 * fs * d * 2 + T * fs * 2 if fs else 0),
+        4.0 * R * d * f + 4.0 * T * d * fs, us_warm=tm.run(gate_up_layer, iters))
     add("gemm_gate_up", tm.run_cold(gemm1, iters, flush), R * d * 2 + active * 2 * f * d * 2 + R * f * 2,
         4.0 * R * d * f, us_warm=tm.run(gemm1, iters))
     add("gemm_down", tm.run_cold(gemm2, iters, flush), R * f * 2 + active * d * f * 2 + R * d * 4,
@@ -289,20 +303,27 @@ def traffic_from_profiles(kernel, workload):
         return None
 
 
-def cpu_baseline(budget_s=12.0):
-    """The CPU oracle as it stands, on the first 512 tokens of the headline
-    workload, repeated until about budget_s seconds of CPU work."""
-    import numpy as np  # noqa: F401
+def cpu_baseline(wl_full, budget_s=15.0, Ts=512):
+    """The CPU oracle as it stands, on the first Ts tokens of the headline workload
+    (same weights, same per-token biases), repeated until about budget_s seconds of
+    CPU work. NumPy's BLAS runs on its default thread pool; the threads it used,
+    the host cores this process may run on and the BLAS library are reported."""
+    import copy
+    import numpy as np
     from oracle import moe_oracle as O
-    from workloads import CONFIGS, generate
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            threads = max(int(i.get("num_threads", 1)) for i in pools)
+            blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools}))
     except Exception:  # noqa: BLE001
-        threads = 1
-    cfg = CONFIGS["qwen3_0p6b_rho1"]
-    Ts = 512
-    wl = generate(cfg, T=Ts)
+        pass
+    wl = copy.copy(wl_full)
+    wl.x = np.ascontiguousarray(wl_full.x[:Ts])
+    if wl_full.null_bias_tok is not None:
+        wl.null_bias_tok = np.ascontiguousarray(wl_full.null_bias_tok[:Ts])
     O.layer_forward(wl)            # warm caches
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
@@ -310,11 +331,13 @@ def cpu_baseline(budget_s=12.0):
         n += 1
     el = time.perf_counter() - t0
     return {"value": round(n * Ts / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {Ts} tokens of the headline workload (same weights), float64 NumPy oracle, "
-                      f"{n} full layer forwards in {el:.1f} s"}
+            "host_cores_available": len(os.sched_getaffinity(0)), "blas": blas,
+            "sample": f"first {Ts} tokens of the headline workload {wl_full.cfg.name} (same weights and "
+                      f"null bias), float64 NumPy oracle (whole layer: router, selection, sort, "
+                      f"expert FFNs, combine, statistics), {n} layer forwards in {el:.1f} s"}
 
 
-def sweep(torch, tcr, steps, warmup):
+def sweep(torch, tcr, steps, warmup, base=None):
     """Other workloads, timed only: the rho sweep at the Qwen3-1.7B shape, the
     matched-FLOPs pair at T=8192, the modality-skewed mix, and the rho = 0.5
     Qwen3-0.6B shape with copy and with constant null slots (the zero-compute
@@ -324,7 +347,7 @@ def sweep(torch, tcr, steps, warmup):
     from workloads import CONFIGS, MATCHED_PAIR, SWEEP, generate
     from workloads.gen import null_bias_for
     out = []
-    base = generate(CONFIGS["qwen3_1p7b_rho0p25"])
+    base = base if base is not None else generate(CONFIGS["qwen3_1p7b_rho0p25"])
     base_layer = None
     names = list(SWEEP) + ["modality_skew_rho0p5"]
     for name in names:
@@ -367,8 +390,9 @@ def sweep(torch, tcr, steps, warmup):
 
 
 def measured_peaks(torch):
-    """This GPU's attainable rates: a 1 GiB device copy (bytes read + written) and a
-    large bf16 GEMM through torch (hipBLASLt)."""
+    """This GPU's attainable rates: a 1 GiB device copy (bytes read + written), a
+    large bf16 GEMM through torch (hipBLASLt), and hipBLASLt on one dense GEMM with
+    the FLOPs of the headline layer's routed gate/up (32768 x 3072 x 2048)."""
     tm = Timer(torch)
     n = 1 << 30
     a = torch.ones((n,), dtype=torch.uint8, device="cuda")
@@ -380,10 +404,18 @@ def measured_peaks(torch):
     y = torch.randn((m, m), device="cuda").to(torch.bfloat16).contiguous()
     us_g = tm.run(lambda: torch.matmul(x, y), 10)
     del x, y
+    a = torch.randn((32768, 2048), device="cuda").to(torch.bfloat16)
+    b = torch.randn((3072, 2048), device="cuda").to(torch.bfloat16)
+    bt = b.t()
+    us_s = tm.run(lambda: torch.matmul(a, bt), 10)
+    del a, b, bt
     torch.cuda.empty_cache()
     return {"copy_GB_s": round(2 * n / us_c / 1e3, 1), "copy": "1 GiB device-to-device copy, read + write",
             "bf16_gemm_TFLOP_s": round(2.0 * m ** 3 / us_g / 1e6, 1),
             "gemm": "8192 x 8192 x 8192 bf16 torch.matmul (hipBLASLt)",
+            "bf16_gemm_gate_up_shape_TFLOP_s": round(2.0 * 32768 * 3072 * 2048 / us_s / 1e6, 1),
+            "gemm_gate_up_shape": "32768 x 2048 times 2048 x 3072 bf16 torch.matmul (hipBLASLt), one dense "
+                                  "GEMM with the routed gate/up FLOPs of the headline layer",
             "datasheet": {"hbm_GB_s": HBM_PEAK_GBS, "bf16_TFLOP_s": BF16_PEAK_TFLOPS}}
 
 
@@ -457,13 +489,16 @@ def measure(torch, layer, steps, warmup):
     ms, _ = time_layer(torch, layer, steps, warmup)
     cfg = layer.cfg
     R = int(layer.offsets[-1].item())
-    fl = layer_flops(cfg, R, layer.T)
+    fl = routed_flops(cfg, R)
+    fs = shared_flops(cfg, layer.T)
     seg = layer.offsets.diff().double()
     out = {"workload": cfg.name, "T": layer.T, "K": cfg.top_k, "M": cfg.n_null,
            "rho_nominal": round(cfg.rho_nominal, 4), "rho_realised": round(R / (layer.T * cfg.top_k), 4),
            "real_slots": R, "ms": round(ms, 4), "tokens_per_s": round(layer.T / ms * 1e3, 1),
            "real_expert_tflops": round(fl / ms / 1e9, 2),
-           "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "real_expert_mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "executed_tflops": round((fl + fs) / ms / 1e9, 2),
+           "executed_mfma_frac": round((fl + fs) / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
            # expert segment lengths (rows per expert): the grouped GEMM's load balance
            "segments": {"min": int(seg.min().item()), "max": int(seg.max().item()),
                         "cv": round(float((seg.std(unbiased=False) / seg.mean().clamp(min=1e-9)).item()), 3)}}
@@ -502,7 +537,7 @@ def main():
     R = int(layer.offsets[-1].item())
     T = layer.T
     tok_s = T / ms * 1e3
-    fl = layer_flops(cfg, R, T)
+    fl, fs = routed_flops(cfg, R), shared_flops(cfg, T)
     log(f"bench: {ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (wall), R={R}")
     if args.copy_ref:
         src = torch.ones((COPY_REF_BYTES,), dtype=torch.uint8, device="cuda")
@@ -513,11 +548,14 @@ def main():
         del src, dst
     log("bench: per-kernel timing")
     kernels, _ = kernel_table(torch, tcr, layer, args.kernel_iters)
-    dom = "gemm_gate_up"
+    dom = "gate_up_layer"
     rl = roofline(kernels[dom])
-    rl["kernel"] = ("grouped_gemm_bf16_kernel<0, 0>: routed gate/up + SwiGLU, standalone launch on "
-                    "the layer's permuted rows, caches flushed by a 512 MB read before each timed launch")
-    rl["traffic"] = traffic_from_profiles("gemm_gate_up", cfg.name)
+    rl["kernel"] = ("grouped_gemm_bf16_kernel<0, 2>: the layer's gate/up + SwiGLU launch (routed rows of x "
+                    "read through perm_token, and the shared expert) through moe_expert_gate_up, caches "
+                    "flushed by a 512 MB read before each timed launch")
+    rl["flops_per_launch"] = kernels[dom]["flops"]
+    rl["us_per_launch"] = kernels[dom]["us"]
+    rl["traffic"] = traffic_from_profiles(dom, cfg.name)
     line = {
         "metric": "MoE-layer tokens/s + real-expert TFLOP/s (% bf16 MFMA peak) vs rho",
         "value": round(tok_s, 1),
@@ -539,20 +577,30 @@ def main():
         "real_slots": R,
         "real_expert_tflops": round(fl / ms / 1e9, 2),
         "real_expert_mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "shared_expert_tflops": round(fs / ms / 1e9, 2),
+        "executed_tflops": round((fl + fs) / ms / 1e9, 2),
+        "executed_mfma_frac": round((fl + fs) / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "flop_counting": "real_expert_tflops: 6 d d_ff per real slot (routed experts only); "
+                         "executed adds the shared expert's 6 d d_ff_shared per token",
         "wall_ms_per_step": round(wall_ms, 4),
         "roofline": rl,
         "kernels": kernels,
     }
+    c3 = "qwen3_1p7b_rho0p25"
     if not args.no_sweep:
         log("bench: rho sweep and other workloads")
-        line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3)
+        line["workloads"] = sweep(torch, tcr, max(5, args.steps // 2), 3, base=wl if cfg.name == c3 else None)
+    small = small_layer = None
+    if not args.no_sweep or args.with_decode or args.with_backward:
+        small = generate(CONFIGS["qwen3_0p6b_rho1"])
+        small_layer = MoeLayer(small)
     if not args.no_sweep or args.with_decode:
-        log("bench: decode regime")
-        line["decode"] = decode_sweep(torch, wl, layer, max(5, args.steps // 2))
+        log("bench: decode regime (Qwen3-0.6B shape)")
+        line["decode"] = decode_sweep(torch, small, small_layer, max(5, args.steps // 2))
     if not args.no_sweep or args.with_backward:
         log("bench: backward")
-        big = MoeLayer(generate(CONFIGS["qwen3_1p7b_rho0p25"]))
-        line["backward"] = backward_bench(torch, [layer, big], max(5, args.steps // 2), 2)
+        big = layer if cfg.name == c3 else MoeLayer(generate(CONFIGS[c3]))
+        line["backward"] = backward_bench(torch, [small_layer, big], max(5, args.steps // 2), 2)
         del big
         torch.cuda.empty_cache()
     if not args.no_sweep:
@@ -560,7 +608,7 @@ def main():
         line["measured_peaks"] = measured_peaks(torch)
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
 
 

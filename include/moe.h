@@ -33,6 +33,10 @@
  *   - Execution: every kernel is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream). MOE_OK means validated and enqueued. A launch
  *     failure returns MOE_ERR_HIP. Nothing is launched when validation fails.
+ *     A HIP error already pending on the calling thread when an entry point is
+ *     called (hipPeekAtLastError, left by earlier work) is not cleared: the call
+ *     returns MOE_ERR_HIP before launching anything and the error stays for its
+ *     owner to read.
  *   - Validation: N >= 1, M >= 0, 1 <= K <= N + M, K <= N when M = 0,
  *     N <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK, N + M <= MOE_MAX_POOL,
  *     0 <= T and T * K < 2^31, d_model and d_ff multiples of 8. T = 0 is a no-op.
@@ -190,6 +194,26 @@ moe_status moe_grouped_gemm(const moe_dims* dims, int32_t op, int32_t n_groups, 
                             const void* b0, const void* b1, void* out, moe_stream stream);
 
 /*
+ * moe_expert_gate_up -- the layer's gate/up launch on its own (the grouped GEMM
+ * of the paper review's "implementation" paragraph over the truncated slot list,
+ * with the shared expert of the core formula in the same launch):
+ *   h[p]  = silu(W_gate[e] x_{perm_token[p]}) * (W_up[e] x_{perm_token[p]})
+ *           for p in [offsets[e], offsets[e+1]), the rows of expert e
+ *   hs[t] = silu(Ws_gate x_t) * (Ws_up x_t) for every token (d_ff_shared > 0)
+ * x: [T][d_model] dtype; perm_token [T*min(K,N)] and offsets [N+1] as written by
+ * moe_permute (device; read on the device only, segments clamped as in
+ * moe_expert_ffn, perm_token entries clamped to [0, T)); w_gate, w_up as in the
+ * layer; ws_gate, ws_up: [d_ff_shared][d_model] (ignored when d_ff_shared = 0).
+ * h: [T*min(K,N)][d_ff] and hs: [T][d_ff_shared] in the layer's intermediate
+ * type (bf16 dtype: bf16; float32 dtype: float32). No workspace. bf16 limits as
+ * for moe_layer_forward.
+ */
+moe_status moe_expert_gate_up(const moe_dims* dims, const void* x, const int32_t* perm_token,
+                              const int32_t* offsets, const void* w_gate, const void* w_up,
+                              const void* ws_gate, const void* ws_up, void* h, void* hs,
+                              moe_stream stream);
+
+/*
  * moe_combine -- y_t = y_shared_t + sum_k topk_w[t,k] * y_perm[slot_pos[t,k]]
  * (paper review section 3, core formula). A null slot (slot_pos = -1) adds
  * nothing with null_kind MOE_NULL_ZERO, topk_w[t,k] * null_src[t] with
@@ -212,8 +236,10 @@ moe_status moe_combine(const moe_dims* dims, const void* y_perm, const int32_t* 
  *   scalars[0] = L_bal = N * sum_{i < N+M} f[i] P[i]
  *   scalars[1] = L_z   = mean_t (log sum_i exp v_t,i)^2
  *   scalars[2] = mean_t n_real[t]  (mean number of chosen real experts)
- * With M = 0 the pool is the N reals (column N ignored). Reductions run in
- * float64 in a fixed order (bitwise reproducible), rounded once to float32.
+ * With M = 0 the pool is the N reals (column N ignored). A null logit of +inf
+ * (an infinite per-token null bias) takes the limit: 1/M per null copy, 0 per
+ * real, lse = +inf, so L_z = +inf. Reductions run in float64 in a fixed order
+ * (bitwise reproducible), rounded once to float32.
  * logits: [T][N+1] float32 (column N effective); topk_idx: [T][K] int32.
  * f, P: [N+M] float32; counts: [N+M] int32 or NULL; scalars: [3] float32.
  * ws: MOE_WS_AUX bytes.

@@ -201,6 +201,17 @@ def test_binding_refuses_host_and_strided_tensors():
         tcr._ptr(torch.zeros(4))
 
 
+def test_binding_refuses_host_workspace():
+    """A workspace tensor in host memory is refused by the binding like any other
+    host tensor (its address would otherwise reach device kernels)."""
+    import torch
+    with pytest.raises(ValueError):
+        tcr._ws(torch.zeros(256, dtype=torch.uint8))
+    d = _dims()
+    with pytest.raises(ValueError):
+        tcr.moe_aux_stats(d, FAKE, FAKE, FAKE, FAKE, None, FAKE, torch.zeros(4096, dtype=torch.uint8))
+
+
 def test_validate_inputs_argument_checks(lib):
     """moe_validate_inputs checks pointers and workspace like the forward, and a NaN
     host-side null bias is reported before anything is launched."""

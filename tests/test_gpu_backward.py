@@ -186,6 +186,25 @@ def test_backward_every_token_null(shared):
     _check(cfg, got, ref)
 
 
+@pytest.mark.parametrize("case", ["nullpool_shared", "few_nulls"])
+def test_backward_infinite_null_bias(case):
+    """Tokens whose per-token null bias is +inf (a valid input: with M >= K every slot
+    null, with 0 < M < K the K - M forced reals): their lse is +inf, the z-loss term of
+    their logit gradient is taken as 0 and the balance term is 0 by itself, so the
+    router gradient stays finite and matches the oracle's limit."""
+    cfg = Config(name=f"bwd_inf_{case}", dtype="bf16", w_std=None, seed=6, **CASES[case])
+    wl = generate(cfg)
+    btok = np.zeros(cfg.T, dtype=np.float32)
+    btok[::4] = np.inf
+    wl.null_bias_tok = btok
+    got, ref = _run_wl(wl, 2e-2, 1e-3)
+    assert np.isinf(ref["fwd"]["aux"]["L_z"])
+    for k, v in got.items():
+        if v is not None:
+            assert np.isfinite(v).all(), k
+    _check(cfg, got, ref)
+
+
 @pytest.mark.parametrize("T", [1, 3, 65])
 def test_backward_tiny_token_counts(T):
     """One token, a few tokens and one token past a 64-token tile."""

@@ -295,9 +295,22 @@ def test_combine_null_sources(kind):
 
 @pytest.mark.parametrize("N,M,K,T", [(64, 192, 8, 5000), (8, 8, 2, 128), (64, 0, 2, 2048), (255, 1000, 32, 300)])
 def test_aux_stats(N, M, K, T):
-    say(f"aux_stats N={N} M={M} K={K} T={T}")
+    check_aux_stats(N, M, K, T, inf_every=0)
+
+
+@pytest.mark.parametrize("N,M,K,T,inf_every", [(64, 192, 8, 3000, 7), (16, 2, 4, 500, 3), (8, 8, 2, 64, 1)])
+def test_aux_stats_infinite_null_logit(N, M, K, T, inf_every):
+    """Tokens whose null logit is +inf (an infinite per-token null bias): P takes the
+    limit (1/M per null copy, reals 0), f and L_bal stay finite and L_z = +inf."""
+    check_aux_stats(N, M, K, T, inf_every)
+
+
+def check_aux_stats(N, M, K, T, inf_every):
+    say(f"aux_stats N={N} M={M} K={K} T={T} null at +inf every {inf_every}")
     rng = np.random.default_rng(N + M + K + T)
     s = (rng.standard_normal((T, N + 1)) * 1.5).astype(np.float32)
+    if inf_every:
+        s[::inf_every, N] = np.inf
     topk, _, _ = O.route(s.astype(np.float64), N, M, K)
     dims = tcr.make_dims(T, 64, N, M, K, 64, 0, tcr.MOE_BF16)
     P = N + M
@@ -311,4 +324,7 @@ def test_aux_stats(N, M, K, T):
     np.testing.assert_allclose(to_host(P_), a["P"], rtol=1e-4, atol=1e-12)
     g = to_host(sc)
     for i, key in enumerate(("L_bal", "L_z", "mean_r")):
-        assert abs(g[i] - a[key]) <= 1e-4 * abs(a[key]) + 1e-12, (key, g[i], a[key])
+        if np.isinf(a[key]):
+            assert g[i] == a[key], (key, g[i], a[key])
+        else:
+            assert abs(g[i] - a[key]) <= 1e-4 * abs(a[key]) + 1e-12, (key, g[i], a[key])

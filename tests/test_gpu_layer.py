@@ -70,7 +70,10 @@ def check_routing(wl, out, rows=None, stats=True):
     np.testing.assert_allclose(out["P"], a["P"], rtol=1e-4, atol=1e-12)
     np.testing.assert_allclose(out["f"], a["f"], rtol=1e-6)
     for i, key in enumerate(("L_bal", "L_z", "mean_r")):
-        assert abs(out["scalars"][i] - a[key]) <= 1e-4 * abs(a[key]) + 1e-12, key
+        if np.isinf(a[key]):   # L_z with a null logit at +inf
+            assert out["scalars"][i] == a[key], key
+        else:
+            assert abs(out["scalars"][i] - a[key]) <= 1e-4 * abs(a[key]) + 1e-12, key
     return gl
 
 
@@ -166,7 +169,8 @@ def test_null_routed_tokens_give_shared_output(shared):
         np.testing.assert_array_equal(out["y"][nul], bf16_round(to_host(ys)[nul]))
     else:
         assert (vals(out["y"])[nul] == 0).all()
-    check_routing(wl, out, stats=False)
+    check_routing(wl, out)
+    assert out["scalars"][1] == np.inf
 
 
 @pytest.mark.parametrize("shared", [64, 0])
@@ -178,6 +182,8 @@ def test_every_token_null(shared):
     assert out["offsets"][-1] == 0
     if not shared:
         assert (vals(out["y"]) == 0).all()
+    check_routing(wl, out)
+    assert out["scalars"][1] == np.inf and np.isfinite(out["scalars"][0])
 
 
 def test_one_expert_takes_every_slot():

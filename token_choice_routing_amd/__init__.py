@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_expert_ffn": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
                            _P, ctypes.c_size_t, _P],
         "moe_combine": [D, _P, _P, _P, _P, _P, _P, _P],
+        "moe_expert_gate_up": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "moe_grouped_gemm": [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                              ctypes.c_int64, _P, _P, _P, _P, _P, _P],
         "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -138,11 +139,13 @@ def _check(status, where):
 
 
 def _ws(ws):
+    """(device address, bytes) of a workspace tensor, checked like every other
+    tensor argument (device memory, contiguous); a tuple is taken as given."""
     if ws is None:
         return None, 0
     if isinstance(ws, tuple):
         return ws
-    return ws.data_ptr(), ws.numel() * ws.element_size()
+    return _ptr(ws), ws.numel() * ws.element_size()
 
 
 def status_str(status: int) -> str:
@@ -202,6 +205,12 @@ def moe_grouped_gemm(dims, op, n_groups, n_out, k_dim, rows, a, offsets, b0, b1,
     _check(load_library().moe_grouped_gemm(ctypes.byref(dims), int(op), int(n_groups), int(n_out),
                                             int(k_dim), int(rows), _ptr(a), _ptr(offsets), _ptr(b0),
                                             _ptr(b1), _ptr(out), _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_expert_gate_up(dims, x, perm_token, offsets, w_gate, w_up, ws_gate, ws_up, h, hs, stream=None):
+    _check(load_library().moe_expert_gate_up(ctypes.byref(dims), _ptr(x), _ptr(perm_token), _ptr(offsets),
+                                              _ptr(w_gate), _ptr(w_up), _ptr(ws_gate), _ptr(ws_up), _ptr(h),
+                                              _ptr(hs), _stream(stream)), "moe_expert_gate_up")
 
 
 def moe_combine(dims, y_perm, slot_pos, topk_w, y_shared, y, stream=None, null_src=None):

@@ -53,6 +53,11 @@ moe_status maybe(const void* p) { return (!p || aligned16(p)) ? MOE_OK : MOE_ERR
     if (s_ != MOE_OK) return s_;       \
   } while (0)
 
+// A HIP error left pending on this thread by earlier work (hipPeekAtLastError) is
+// reported before anything is launched and left in place for its owner to read:
+// the status after a launch then names this call's own launches only.
+inline moe_status no_pending_error() { return hipPeekAtLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
 #define HIP_TRY(expr)                              \
   do {                                             \
     if ((expr) != hipSuccess) return MOE_ERR_HIP;  \
@@ -241,7 +246,7 @@ moe_status moe_route(const moe_dims* d, const void* x, const float* w_router, fl
     }
   }
   if (d->T == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   RouteArgs a{d->T, d->d_model, d->n_experts, d->n_null, d->top_k, bf16, false, x, w_router,
               null_bias, null_bias_tok, logits_in, logits_out, topk_idx, topk_w, n_real,
               ws, nullptr, nullptr, nullptr, d->null_kind};
@@ -264,7 +269,7 @@ moe_status moe_permute(const moe_dims* d, const int32_t* topk_idx, const void* x
   if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   MOE_TRY(maybe(ws));
   if (d->T == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   PermuteArgs a{d->T, d->top_k, d->n_experts, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx,
                 x, counts, offsets, perm_token, slot_pos, x_perm, static_cast<int32_t*>(ws),
                 false, nullptr};
@@ -292,7 +297,7 @@ moe_status moe_expert_ffn(const moe_dims* d, int32_t n_groups, int32_t d_ff, int
   if (need_ws && (!ws || ws_bytes < need_ws)) return MOE_ERR_WORKSPACE;
   MOE_TRY(maybe(ws));
   if (rows == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   FfnArgs f{d->dtype == MOE_BF16, n_groups, d->d_model, d_ff, rows, a, offsets, w_gate, w_up,
             w_down, ws, out, cu_count()};
   HIP_TRY(launch_expert_ffn(f, static_cast<hipStream_t>(stream)));
@@ -315,7 +320,7 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
   if (op == MOE_GEMM_GATE_UP) MOE_TRY(need(b1));
   MOE_TRY(need(out));
   if (rows == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   GemmProblem g{static_cast<const uint16_t*>(a), nullptr, rows, offsets, n_groups, rows,
                 static_cast<const uint16_t*>(b0),
                 op == MOE_GEMM_GATE_UP ? static_cast<const uint16_t*>(b1) : nullptr, n_out, k_dim,
@@ -325,9 +330,51 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
   return MOE_OK;
 }
 
+// The layer's gate/up + SwiGLU launch: routed rows of x read through perm_token and,
+// with a shared expert, every token through the shared expert, as one launch.
+static hipError_t launch_layer_gate_up(const moe_dims* d, const void* x, const int32_t* perm_token,
+                                       const int32_t* offsets, const void* w_gate, const void* w_up,
+                                       const void* ws_gate, const void* ws_up, void* h, void* hs,
+                                       hipStream_t s) {
+  const uint16_t* x16 = static_cast<const uint16_t*>(x);
+  GemmProblem r1{x16, perm_token, d->T, offsets, d->n_experts, max_rows(d), static_cast<const uint16_t*>(w_gate),
+                 static_cast<const uint16_t*>(w_up), d->d_ff, d->d_model, h};
+  GemmProblem s1{};
+  if (d->d_ff_shared)
+    s1 = GemmProblem{x16, nullptr, d->T, nullptr, 1, d->T, static_cast<const uint16_t*>(ws_gate),
+                     static_cast<const uint16_t*>(ws_up), d->d_ff_shared, d->d_model, hs};
+  return launch_gemm_pair(d->dtype == MOE_BF16, 0, r1, s1, cu_count(), s, 2);
+}
+
 // Per-token stride (elements) of the rows a null slot adds: x for copy experts,
 // the one vector v for constant experts.
 inline int64_t null_stride(const moe_dims* d) { return d->null_kind == MOE_NULL_COPY ? d->d_model : 0; }
+
+moe_status moe_expert_gate_up(const moe_dims* d, const void* x, const int32_t* perm_token,
+                              const int32_t* offsets, const void* w_gate, const void* w_up,
+                              const void* ws_gate, const void* ws_up, void* h, void* hs,
+                              moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (d->dtype == MOE_BF16 && (!fits_4g(d->T, d->d_model) || !fits_4g(d->d_ff, d->d_model) ||
+                               !fits_4g(d->d_ff_shared, d->d_model)))
+    return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(need(x));
+  MOE_TRY(need(perm_token));
+  MOE_TRY(need(offsets));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(h));
+  if (d->d_ff_shared) {
+    MOE_TRY(need(ws_gate));
+    MOE_TRY(need(ws_up));
+    MOE_TRY(need(hs));
+  }
+  if (d->T == 0) return MOE_OK;
+  MOE_TRY(no_pending_error());
+  HIP_TRY(launch_layer_gate_up(d, x, perm_token, offsets, w_gate, w_up, ws_gate, ws_up, h, hs,
+                               static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
 
 moe_status moe_combine(const moe_dims* d, const void* y_perm, const int32_t* slot_pos,
                        const float* topk_w, const void* y_shared, const void* null_src, void* y,
@@ -340,7 +387,7 @@ moe_status moe_combine(const moe_dims* d, const void* y_perm, const int32_t* slo
   if (d->null_kind != MOE_NULL_ZERO) MOE_TRY(need(null_src));
   MOE_TRY(need(y));
   if (d->T == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   CombineArgs c{d->dtype == MOE_BF16, d->T, d->top_k, d->d_model, max_rows(d), y_perm, slot_pos,
                 topk_w, y_shared, d->null_kind != MOE_NULL_ZERO ? null_src : nullptr, null_stride(d), y};
   HIP_TRY(launch_combine(c, static_cast<hipStream_t>(stream)));
@@ -361,7 +408,7 @@ moe_status moe_aux_stats(const moe_dims* d, const float* logits, const int32_t* 
   if (!ws || ws_bytes < need_ws) return MOE_ERR_WORKSPACE;
   MOE_TRY(maybe(ws));
   if (d->T == 0) return MOE_OK;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   AuxArgs a{d->T, d->n_experts, d->n_null, d->top_k, logits, topk_idx, f, P, counts, scalars, ws};
   HIP_TRY(launch_aux(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
@@ -421,7 +468,7 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   const bool bf16 = d->dtype == MOE_BF16;
   const int64_t R = max_rows(d);
   const int N = d->n_experts;
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
 
   // 1. scores, selection, weights; per-chunk expert histogram; statistics sums
   RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
@@ -439,14 +486,8 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   // 3. gate/up + SwiGLU: routed experts read x through perm_token (the gather), and the
   //    shared expert runs in the same launch
   const int cus = cu_count();
-  const uint16_t* x16 = static_cast<const uint16_t*>(p->x);
-  GemmProblem r1{x16, perm_token, d->T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate),
-                 static_cast<const uint16_t*>(p->w_up), d->d_ff, d->d_model, at(L.h)};
-  GemmProblem s1{};
-  if (d->d_ff_shared)
-    s1 = GemmProblem{x16, nullptr, d->T, nullptr, 1, d->T, static_cast<const uint16_t*>(p->ws_gate),
-                     static_cast<const uint16_t*>(p->ws_up), d->d_ff_shared, d->d_model, at(L.hs)};
-  HIP_TRY(launch_gemm_pair(bf16, 0, r1, s1, cus, s, 2));
+  HIP_TRY(launch_layer_gate_up(d, p->x, perm_token, offsets, p->w_gate, p->w_up, p->ws_gate, p->ws_up,
+                               at(L.h), at(L.hs), s));
 
   // 4. down projection, routed and shared, float32 outputs
   GemmProblem r2{static_cast<const uint16_t*>(at(L.h)), nullptr, R, offsets, N, R,
@@ -491,7 +532,7 @@ moe_status moe_validate_inputs(const moe_dims* d, const moe_layer_params* p, voi
   const bool bf16 = d->dtype == MOE_BF16;
   const int64_t T = d->T, dm = d->d_model, N = d->n_experts, F = d->d_ff, Fs = d->d_ff_shared;
   int32_t* count = static_cast<int32_t*>(ws);
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
   HIP_TRY(launch_zero_count(count, s));
   HIP_TRY(launch_count_nonfinite(p->x, T * dm, bf16, false, count, s));
   HIP_TRY(launch_count_nonfinite(p->w_router, (N + 1) * dm, false, false, count, s));
@@ -565,7 +606,7 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
   const int cus = cu_count();
   const uint16_t* x16 = static_cast<const uint16_t*>(p->x);
   auto bf = [&](size_t off) { return static_cast<const uint16_t*>(at(off)); };
-  (void)hipGetLastError();
+  MOE_TRY(no_pending_error());
 
   // 1-2. the forward's routing, permutation and pool counts f, recomputed
   RouteArgs ra{T, d->d_model, N, M, K, true, true, p->x, p->w_router, p->null_bias, p->null_bias_tok,

@@ -29,8 +29,11 @@ constexpr int kAuxThreads = 256;
 static int aux_tokens_per_block(int64_t T) { return T <= 4096 ? 16 : 32; }
 constexpr int kQa = (MOE_MAX_EXPERTS + kWave - 1) / kWave;
 
+// Accumulators: [N + 4] uint64 (probability sums of the N reals and the null, lse^2,
+// n_real, tokens whose lse is +inf), then the slot counts [N + M] int32.
+constexpr int kAuxAcc = 4;
 size_t aux_ws_bytes(int N, int M) {
-  return (size_t)(N + 3) * sizeof(uint64_t) + (size_t)(N + M) * sizeof(int32_t);
+  return (size_t)(N + kAuxAcc) * sizeof(uint64_t) + (size_t)(N + M) * sizeof(int32_t);
 }
 
 __global__ void aux_clear_kernel(uint64_t* __restrict__ acc, int nacc, int32_t* __restrict__ cnt,
@@ -45,7 +48,7 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
                    int32_t* __restrict__ cnt) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int nw = kAuxThreads / kWave;
-  const int rd = N + 3, P = N + M;
+  const int rd = N + kAuxAcc, P = N + M;
   double* wacc = reinterpret_cast<double*>(smem_raw);          // [nw][N+3]
   int* cnt_lds = reinterpret_cast<int*>(wacc + nw * rd);       // [N+M]
   for (int i = threadIdx.x; i < P; i += blockDim.x) cnt_lds[i] = 0;
@@ -56,7 +59,7 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
 #pragma unroll
   for (int q = 0; q < kQa; ++q) psum[q] = 0.0;
   double pnull = 0.0, lz = 0.0;
-  int nreal = 0;
+  int nreal = 0, ninf = 0;
   for (int64_t t = tb + wave; t < te; t += nw) {
     const float* s = logits + t * (N + 1);
     float v[kQa];
@@ -77,7 +80,8 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
       ex[q] = (lane + q * kWave < N) ? expf(v[q] - m) : 0.0f;
       part += (double)ex[q];
     }
-    const float en = M > 0 ? expf(sn - m) : 0.0f;
+    // a null logit at +inf is the pool maximum: numerator 1 (the limit), reals 0
+    const float en = M > 0 ? (sn == m ? 1.0f : expf(sn - m)) : 0.0f;
     const double z = wave_sum_double(part) + (double)M * (double)en;
     const double iz = 1.0 / z;
 #pragma unroll
@@ -85,7 +89,9 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
     if (lane == 0) {
       pnull += (double)en * iz;
       const double lse = (double)m + log(z);
-      lz += lse * lse;
+      // +inf (null logit at +inf) is counted apart: the sums are fixed point
+      if (isinf(lse)) ++ninf;
+      else lz += lse * lse;
     }
     if (lane < K) {
       const int id = topk_idx[t * K + lane];
@@ -101,12 +107,13 @@ aux_partial_kernel(const float* __restrict__ logits, const int32_t* __restrict__
     wacc[wave * rd + N] = pnull;
     wacc[wave * rd + N + 1] = lz;
     wacc[wave * rd + N + 2] = (double)nreal;
+    wacc[wave * rd + N + 3] = (double)ninf;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < rd; i += blockDim.x) {
     double s = 0.0;
     for (int w = 0; w < nw; ++w) s += wacc[w * rd + i];
-    const double scale = (i == N + 1) ? kAuxZScale : (i == N + 2 ? 1.0 : kAuxPScale);
+    const double scale = (i == N + 1) ? kAuxZScale : (i >= N + 2 ? 1.0 : kAuxPScale);
     const uint64_t q = (uint64_t)(s * scale + 0.5);
     if (q) atomicAdd(reinterpret_cast<unsigned long long*>(&acc[i]), (unsigned long long)q);
   }
@@ -123,12 +130,12 @@ aux_final_kernel(AuxFinal a, int64_t T, int N, int M) {
 hipError_t launch_aux(const AuxArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
   uint64_t* acc = static_cast<uint64_t*>(a.ws);
-  int32_t* cnt = reinterpret_cast<int32_t*>(acc + (a.N + 3));
+  int32_t* cnt = reinterpret_cast<int32_t*>(acc + (a.N + kAuxAcc));
   const int P = a.N + a.M;
-  aux_clear_kernel<<<1, 256, 0, stream>>>(acc, a.N + 3, cnt, P);
+  aux_clear_kernel<<<1, 256, 0, stream>>>(acc, a.N + kAuxAcc, cnt, P);
   const int bt = aux_tokens_per_block(a.T);
   const unsigned nb = (unsigned)((a.T + bt - 1) / bt);
-  const size_t lds1 = (size_t)(kAuxThreads / kWave) * (a.N + 3) * sizeof(double) + (size_t)P * sizeof(int);
+  const size_t lds1 = (size_t)(kAuxThreads / kWave) * (a.N + kAuxAcc) * sizeof(double) + (size_t)P * sizeof(int);
   aux_partial_kernel<<<nb, kAuxThreads, lds1, stream>>>(a.logits, a.topk_idx, a.T, a.N, a.M, a.K, bt,
                                                         acc, cnt);
   AuxFinal f{acc, cnt, a.f, a.P, a.counts, a.scalars};

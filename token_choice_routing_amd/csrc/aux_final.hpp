@@ -32,7 +32,7 @@ __device__ inline void aux_finalize(const AuxFinal& a, int64_t T, int N, int M, 
     s = wave_sum_double(s);
     if (threadIdx.x == 0 && a.scalars) {
       a.scalars[0] = (float)((double)N * s);
-      a.scalars[1] = (float)((double)a.acc[N + 1] / kAuxZScale * invT);
+      a.scalars[1] = a.acc[N + 3] ? INFINITY : (float)((double)a.acc[N + 1] / kAuxZScale * invT);
       a.scalars[2] = (float)((double)a.acc[N + 2] * invT);
     }
   }

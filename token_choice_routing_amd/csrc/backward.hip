@@ -285,11 +285,14 @@ router_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ 
   z = wave_sum_double(z);
   fz = wave_sum_double(fz);
   fnull = wave_sum_double(fnull);
-  const double en = M > 0 ? exp(sn - mx) : 0.0;
+  // a null logit at +inf is the pool maximum: numerator 1 (the limit), reals 0
+  const double en = M > 0 ? (sn == mx ? 1.0 : exp(sn - mx)) : 0.0;
   z += M * en;
   fz += fnull * en;
   const double lse = mx + log(z), fbar = fz / z;
-  const double ka = (double)alpha * N / (double)T, kb = (double)beta * 2.0 / (double)T;
+  // the z-loss term of a token whose lse is +inf (null logit at +inf) has no finite
+  // value and is taken as 0; its balance term is 0 by itself (p is saturated)
+  const double ka = (double)alpha * N / (double)T, kb = isinf(lse) ? 0.0 : (double)beta * 2.0 / (double)T;
   // weight term: sum over the chosen reals of g dg
   double gdg = 0.0;
   for (int k = 0; k < K; ++k)
@@ -297,14 +300,14 @@ router_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ 
   float* o = ds + t * (N + 1);
   for (int j = lane; j < N; j += kWave) {
     const double p = exp((double)s[j] - mx) / z;
-    double v = ka * p * ((double)f[j] - fbar) + kb * lse * p;
+    double v = ka * p * ((double)f[j] - fbar) + (kb ? kb * lse * p : 0.0);
     for (int k = 0; k < K; ++k)
       if (topk_idx[t * K + k] == j) v += (double)topk_w[t * K + k] * ((double)dw[t * K + k] - gdg);
     o[j] = (float)v;
   }
   if (lane == 0) {
     const double pn = en / z;
-    o[N] = M > 0 ? (float)(ka * pn * (fnull - M * fbar) + kb * lse * M * pn) : 0.0f;
+    o[N] = M > 0 ? (float)(ka * pn * (fnull - M * fbar) + (kb ? kb * lse * M * pn : 0.0)) : 0.0f;
   }
 }
 

@@ -7,6 +7,8 @@ namespace moe {
 
 typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -28,6 +30,27 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Two float32 values as IEEE half, round to nearest even (beyond +-65504: infinity).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight bf16 values as IEEE half: exact for every bf16 value of magnitude in
+// [2^-17, 65504] (bf16's 8 significant bits fit half's 11, and half subnormals
+// reach down to 2^-24 in steps of 2^-24); smaller magnitudes are truncated toward
+// zero to a multiple of 2^-24. Each bf16 pair is widened to float32 by a shift or a
+// mask and packed by one v_cvt_pkrtz_f16_f32.
+__device__ __forceinline__ f16x8_t bf16x8_to_f16x8(bf16x8_t v) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(u[i] << 16),
+                                                                  __uint_as_float(u[i] & 0xffff0000u)));
+  return __builtin_bit_cast(f16x8_t, o);
 }
 
 // Element access for the two storage types.

@@ -690,11 +690,8 @@ grouped_gemm_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__
   }
 }
 
-// Tile shape (BM x BN, wavefronts, stages, K tile): 128 x 256 on eight wavefronts,
-// three stages of 64-wide K tiles. It measured fastest at both ends of the
-// rows-per-expert range (64 and 512) among 128 x 128, 64 x 256, 128 x 384 (two
-// stages, or four of 32-wide K tiles) and 128 x 256 with five 32-wide stages;
-// those are compiled only for tuning builds (-DMOE_GEMM_VARIANT=k).
+// Tile shape: 128 rows x 256 weight rows on eight wavefronts (2 x 4, 64 x 64 each),
+// three stages of 64-wide K tiles.
 struct GemmShape {
   int bm, bn, threads;
   size_t lds;
@@ -703,10 +700,6 @@ template <int BM, int BN, int WM, int WN, int S, int BK>
 constexpr GemmShape shape_of() {
   return GemmShape{BM, BN, 64 * WM * WN, (size_t)S * (BM + BN) * BK * sizeof(bf16_t)};
 }
-
-#ifndef MOE_GEMM_VARIANT
-#define MOE_GEMM_VARIANT 0
-#endif
 
 static unsigned gemm_grid(const GemmProblem& p0, const GemmProblem& p1, int bm, int oc,
                           int num_cus, int per_cu) {
@@ -741,29 +734,8 @@ static void launch_variant(const GemmProblem& q0, const GemmProblem& q1, int num
 }
 
 template <int MODE, int ROLE>
-static void launch_shape(int variant, const GemmProblem& q0, const GemmProblem& q1, int num_cus,
-                         hipStream_t stream) {
-  switch (variant) {
-#if MOE_GEMM_VARIANT
-    case 1: launch_variant<MODE, ROLE, 128, 128, 2, 2, 4, 64>(q0, q1, num_cus, stream); break;
-    case 2: launch_variant<MODE, ROLE, 128, 256, 2, 2, 3, 64>(q0, q1, num_cus, stream); break;
-    case 3: launch_variant<MODE, ROLE, 64, 256, 1, 4, 3, 64>(q0, q1, num_cus, stream); break;
-    case 5: launch_variant<MODE, ROLE, 128, 384, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
-    case 6: launch_variant<MODE, ROLE, 128, 384, 2, 2, 4, 32>(q0, q1, num_cus, stream); break;
-    case 7: launch_variant<MODE, ROLE, 128, 256, 2, 4, 5, 32>(q0, q1, num_cus, stream); break;
-    case 8: launch_variant<MODE, ROLE, 256, 256, 2, 2, 4, 32>(q0, q1, num_cus, stream); break;
-    case 9: launch_variant<MODE, ROLE, 256, 256, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
-    case 10: launch_variant<MODE, ROLE, 128, 256, 2, 4, 6, 32>(q0, q1, num_cus, stream); break;
-    case 11: launch_variant<MODE, ROLE, 128, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
-    case 12: launch_variant<MODE, ROLE, 256, 256, 2, 4, 2, 64>(q0, q1, num_cus, stream); break;
-    case 13: launch_variant<MODE, ROLE, 256, 256, 4, 2, 2, 64>(q0, q1, num_cus, stream); break;
-    case 14: launch_variant<MODE, ROLE, 128, 128, 2, 2, 2, 64>(q0, q1, num_cus, stream); break;
-    case 15: launch_variant<MODE, ROLE, 128, 128, 2, 2, 3, 32>(q0, q1, num_cus, stream); break;
-    case 16: launch_variant<MODE, ROLE, 256, 256, 2, 4, 4, 32>(q0, q1, num_cus, stream); break;
-    case 17: launch_variant<MODE, ROLE, 256, 256, 2, 4, 3, 32>(q0, q1, num_cus, stream); break;
-#endif
-    default: launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream); break;
-  }
+static void launch_shape(const GemmProblem& q0, const GemmProblem& q1, int num_cus, hipStream_t stream) {
+  launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream);
 }
 
 // Groups of at most this many rows take the skinny kernel (measured at the
@@ -820,13 +792,12 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
 #undef MOE_SKINNY_DISPATCH
       return hipGetLastError();
     }
-    const int variant = MOE_GEMM_VARIANT;
-#define MOE_GEMM_DISPATCH(M_)                                                  \
-  do {                                                                         \
-    if (role == 3) launch_shape<M_, 3>(variant, q0, q1, num_cus, stream);      \
-    else if (role == 2) launch_shape<M_, 2>(variant, q0, q1, num_cus, stream); \
-    else if (role == 1) launch_shape<M_, 1>(variant, q0, q1, num_cus, stream); \
-    else launch_shape<M_, 0>(variant, q0, q1, num_cus, stream);                \
+#define MOE_GEMM_DISPATCH(M_)                                         \
+  do {                                                                \
+    if (role == 3) launch_shape<M_, 3>(q0, q1, num_cus, stream);      \
+    else if (role == 2) launch_shape<M_, 2>(q0, q1, num_cus, stream); \
+    else if (role == 1) launch_shape<M_, 1>(q0, q1, num_cus, stream); \
+    else launch_shape<M_, 0>(q0, q1, num_cus, stream);                \
   } while (0)
     if (op == 0) MOE_GEMM_DISPATCH(kSwiGLU);
     else MOE_GEMM_DISPATCH(kPlain);

@@ -37,7 +37,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 // Statistics accumulated in fixed point by the standalone statistics kernels.
 struct AuxFinal {
-  const uint64_t* acc;   // [N + 3]
+  const uint64_t* acc;   // [N + 4]: P sums (N reals, null), lse^2, n_real, tokens with lse = +inf
   const int32_t* cnt;    // [N + M]
   float* f;
   float* P;

@@ -223,7 +223,9 @@ __device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld,
     zq += dpp_xchg_f64<1>(zq);
     if constexpr (LPT >= 8) zq += dpp_xchg_f64<2>(zq);
     if constexpr (LPT == 16) zq += dpp_xchg_f64<3>(zq);
-    const float en = M > 0 ? expf(snull - mp) : 0.0f;
+    // a null logit at +inf is the pool maximum itself: its numerator is 1 (the limit;
+    // exp(inf - inf) would be NaN), every real one 0, z = M and lse = +inf
+    const float en = M > 0 ? (snull == mp ? 1.0f : expf(snull - mp)) : 0.0f;
     if (q == 0) {
       tk[34] = (uint64_t)__double_as_longlong(zq + (double)M * (double)en);
       if (live) s[N] = en;
@@ -253,7 +255,8 @@ __device__ void select_tokens(const RouteKernelArgs& a, const EpiLds& L, int ld,
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
     const double v = i < rr ? (double)from_ordered_bits((uint32_t)(tt[i] >> 32)) : (double)sn;
-    e[i] = (i < rr || (all_k && i < K)) ? exp(v - (double)(all_k ? pm : vm)) : 0.0;
+    const double sh = (double)(all_k ? pm : vm);  // at v == sh the numerator is 1, also at +inf
+    e[i] = (i < rr || (all_k && i < K)) ? (v == sh ? 1.0 : exp(v - sh)) : 0.0;
     tot += e[i];
   }
   const int64_t tg = t0 + t;
