@@ -292,6 +292,25 @@ moe_status moe_layer_forward(const moe_dims* dims, const moe_layer_params* param
                              const moe_aux_out* aux, void* ws, size_t ws_bytes,
                              moe_stream stream);
 
+/*
+ * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): same arguments and results, but no workspace argument. The
+ * workspace is a static device array of MOE_NOALLOC_MAX_WS_BYTES bytes that the
+ * library holds on every GPU it runs on until the process ends (its address is
+ * looked up once per device, on the first call with that device current). Layers
+ * whose moe_workspace_bytes(dims, MOE_WS_LAYER) exceeds that size return
+ * MOE_ERR_UNSUPPORTED with nothing launched. The calling thread's current device
+ * (hipGetDevice) must be the one `stream` belongs to. Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and give undefined results; calls ordered on one stream are safe. The
+ * forward writes every workspace byte it reads, so nothing needs clearing between
+ * calls. Calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define MOE_NOALLOC_MAX_WS_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_dims* dims, const moe_layer_params* params, void* y,
+                                     const moe_aux_out* aux, moe_stream stream);
+
 /* Gradients written by moe_layer_backward (float32, device, 16-byte aligned). */
 typedef struct {
   float* dx;        /* [T][d_model] */

@@ -226,3 +226,15 @@ def test_validate_inputs_argument_checks(lib):
     pn = tcr.LayerParams(FAKE, FAKE, float("nan"), None, FAKE, FAKE, FAKE, None, None, None)
     assert lib.moe_validate_inputs(b, ctypes.byref(pn), FAKE, 256, None) == tcr.MOE_ERR_NONFINITE
     assert lib.moe_status_str(tcr.MOE_ERR_NONFINITE).decode().startswith("non-finite")
+
+
+def test_noalloc_entry_checks(lib):
+    """moe_layer_forward_noalloc: bad dims, a NULL params struct, and a layer whose
+    workspace exceeds the static array are refused before anything touches a GPU."""
+    d = _dims()
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(_dims(top_k=0)), None, FAKE, None, None) == MOE_ERR_ARG
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(d), None, FAKE, None, None) == MOE_ERR_ARG
+    big = tcr.dims_from_config(CONFIGS["qwen3_1p7b_rho0p25"])
+    assert tcr.workspace_bytes(big, MOE_WS_LAYER) > tcr.MOE_NOALLOC_MAX_WS_BYTES
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(big), ctypes.byref(p), FAKE, None, None) == MOE_ERR_UNSUPPORTED

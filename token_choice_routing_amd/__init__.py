@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_aux_stats": [D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
         "moe_layer_forward": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P,
                               ctypes.c_size_t, _P],
+        "moe_layer_forward_noalloc": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P],
         "moe_layer_backward": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(LayerGrads), _P, ctypes.c_size_t, _P],
         "moe_validate_inputs": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_size_t, _P],
@@ -233,6 +234,16 @@ def moe_layer_forward(dims, params: LayerParams, y, aux: AuxOut = None, ws=None,
     _check(load_library().moe_layer_forward(ctypes.byref(dims), ctypes.byref(params), _ptr(y),
                                              ctypes.byref(aux) if aux is not None else None, wp, wb,
                                              _stream(stream)), "moe_layer_forward")
+
+
+MOE_NOALLOC_MAX_WS_BYTES = 64 << 20
+
+
+def moe_layer_forward_noalloc(dims, params: LayerParams, y, aux: AuxOut = None, stream=None):
+    """moe_layer_forward with the library's static per-device workspace (no allocation)."""
+    _check(load_library().moe_layer_forward_noalloc(ctypes.byref(dims), ctypes.byref(params), _ptr(y),
+                                                     ctypes.byref(aux) if aux is not None else None,
+                                                     _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_layer_backward(dims, params: LayerParams, dy, alpha: float, beta: float, grads: LayerGrads,

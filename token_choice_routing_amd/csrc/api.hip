@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -185,6 +186,34 @@ BwdWs bwd_ws(const moe_dims* d) {
   }
   w.total = o;
   return w;
+}
+
+}  // namespace
+
+// Workspace of moe_layer_forward_noalloc: one static array per device, held until the
+// process ends. Host code never uses this name as an address (on the host it is a
+// stand-in symbol); the device address comes from hipGetSymbolAddress, once per
+// device, and only that address reaches kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_MAX_WS_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on first use).
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -507,6 +536,17 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
                  d->d_ff_shared ? at(L.ys) : nullptr, nsrc, null_stride(d), y};
   HIP_TRY(launch_combine(ca, s));
   return MOE_OK;
+}
+
+moe_status moe_layer_forward_noalloc(const moe_dims* d, const moe_layer_params* p, void* y,
+                                     const moe_aux_out* aux, moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (!p) return MOE_ERR_ARG;
+  if (layer_ws(d).total > MOE_NOALLOC_MAX_WS_BYTES) return MOE_ERR_UNSUPPORTED;
+  if (d->T == 0) return moe_layer_forward(d, p, y, aux, nullptr, 0, stream);
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
+  return moe_layer_forward(d, p, y, aux, ws, MOE_NOALLOC_MAX_WS_BYTES, stream);
 }
 
 moe_status moe_validate_inputs(const moe_dims* d, const moe_layer_params* p, void* ws, size_t ws_bytes,
