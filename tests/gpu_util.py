@@ -38,6 +38,42 @@ def assert_close_rms(got, ref, tol, what=""):
     assert err <= tol * scale, f"{what}: max abs error {err} > {tol} * RMS {scale}"
 
 
+def output_floor(ref, bf16):
+    """max |round(ref) - ref| / RMS(ref): the least whole-tensor error ratio any output in
+    the layer's storage type can have (ref rounded once to bf16, or to float32)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0
+    if bf16:
+        from workloads import bf16_round
+        r = bf16_bits_to_f32(bf16_round(ref.astype(np.float32))).astype(np.float64)
+    else:
+        r = ref.astype(np.float32).astype(np.float64)
+    return float(np.abs(r - ref).max()) / max(rms(ref), 1e-300)
+
+
+def assert_layer_close(got, ref, tol, bf16, what=""):
+    """Layer-output tolerance: max |got - ref| <= tol * RMS(ref) over the whole tensor,
+    the stated rule, wherever the rule is reachable with room to spare: the exact output
+    rounded once to the output type (output_floor) stays below 0.9 tol. Where it does not
+    (the modality-skewed workload: vision rows ~17x larger than text rows, floor 3.9%;
+    copy null slots, whose copied tokens dominate the largest outputs), no output in that
+    type meets the whole-tensor rule, and each token row is held to tol * RMS(row)
+    instead. The floors of the benchmark workloads are computed on the CPU in
+    tests/test_tolerance_floor.py. Both ratios are printed."""
+    fl = output_floor(ref, bf16)
+    if fl >= 0.9 * tol:
+        say(f"  {what}: output floor {fl:.3e} >= 0.9 tol: per-row rule")
+        assert_rows_close(got, ref, tol, what)
+        return
+    assert_close_rms(got, ref, tol, what)
+    g, r = vals(got), np.asarray(ref, dtype=np.float64)
+    if r.size:
+        rr = np.sqrt((r * r).mean(axis=1))
+        ratio = np.abs(g - r).max(axis=1) / np.where(rr > 0, rr, 1.0)
+        say(f"  {what}: output floor {fl:.3e}; per-row max|err|/RMS(row) = {ratio.max():.3e}")
+
+
 def assert_rows_close(got, ref, tol, what=""):
     """Layer-output tolerance, one token row at a time: max_j |got - ref| <= tol * RMS_j(ref)
     for every row; a row whose reference is exactly zero must be exactly zero. The

@@ -354,7 +354,7 @@ moe_status moe_grouped_gemm(const moe_dims* d, int32_t op, int32_t n_groups, int
                 static_cast<const uint16_t*>(b0),
                 op == MOE_GEMM_GATE_UP ? static_cast<const uint16_t*>(b1) : nullptr, n_out, k_dim,
                 out};
-  HIP_TRY(launch_gemm_pair(d->dtype == MOE_BF16, op, g, GemmProblem{}, cu_count(),
+  HIP_TRY(launch_gemm_pair(d->dtype == MOE_BF16, op == MOE_GEMM_DOWN ? 2 : 0, g, GemmProblem{}, cu_count(),
                            static_cast<hipStream_t>(stream), offsets ? 0 : 1));
   return MOE_OK;
 }
@@ -526,7 +526,7 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
     s2 = GemmProblem{static_cast<const uint16_t*>(at(L.hs)), nullptr, d->T, nullptr, 1, d->T,
                      static_cast<const uint16_t*>(p->ws_down), nullptr, d->d_model,
                      d->d_ff_shared, at(L.ys)};
-  HIP_TRY(launch_gemm_pair(bf16, 1, r2, s2, cus, s, 2));
+  HIP_TRY(launch_gemm_pair(bf16, 2, r2, s2, cus, s, 2));
 
   // 5. weighted combine in slot order, one rounding
   const void* nsrc = d->null_kind == MOE_NULL_COPY       ? p->x

@@ -132,6 +132,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// v unchanged, but opaque to the optimiser: values computed from the result cannot
+// be computed earlier than this point (keeps them out of long loops' live ranges).
+__device__ __forceinline__ int opaque_v(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// A pointer the caller knows to be the same in every lane, as the compiler's
+// uniform (scalar) value: buffer resources built from it stay in SGPRs.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // 16-byte buffer -> LDS load (buffer_load_dwordx4 ... lds), same LDS placement as
 // load_lds16. Unlike the global form, the compiler's wait-count tracking does not
 // count it as an LDS-side (lgkm) event, so LDS reads after it keep exact waits.

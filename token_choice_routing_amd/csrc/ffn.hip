@@ -56,7 +56,22 @@ namespace moe {
 // to the stages (7 x 513 ints, 14 KB).
 constexpr int kMaxGroups = 512;
 
-enum { kSwiGLU = 0, kPlain = 1 };
+// kSwiGLU: h = silu(a b0^T) * (a b1^T), a and both weights bf16, h stored as IEEE half.
+// kPlain:  out = a b0^T, a and b0 bf16, float32 out.
+// kDown16: out = h b0^T with h IEEE half (the layer's intermediate) and b0 bf16, each
+//          weight fragment widened to half in registers (exact for |w| >= 2^-17) so the
+//          MFMA runs in half precision; float32 out.
+enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2 };
+
+// One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
+// fragment a (bf16 bits, or half bits for kDown16).
+template <int MODE>
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t w, bf16x8_t a, f32x16_t c) {
+  if constexpr (MODE == kDown16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bf16x8_to_f16x8(w), __builtin_bit_cast(f16x8_t, a), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, c, 0, 0, 0);
+}
 
 // Element offset of (row, 16-byte chunk) in a [rows][BK] bf16 LDS tile. The LDS
 // has 64 four-byte banks, and a 16-byte read serves 16 lanes per pass, here 16
@@ -115,7 +130,7 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
       const int e = lane * kPer + q;
       int s = 0, l = 0, nt = 0, ko = 0, kl = 0;
       if (e < G) {
-        const GemmProblem& pr = e < G0 ? p0 : p1;
+        const GemmProblem pr = e < G0 ? p0 : p1;
         const int ge = e < G0 ? e : e - G0;
         kl = pr.k_dim;
         if (pr.k_offsets) {
@@ -447,7 +462,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
           for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int g = 0; g < FM; ++g)
-              acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[ks][f], aa[ks][g], acc[f][g], 0, 0, 0);
+              acc[f][g] = mfma32<MODE>(wa[ks][f], aa[ks][g], acc[f][g]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, (FN + FM) * KS, 0);  // LDS reads
         sched_steps<ISS ? J : 0, KS, FN * FM>();  // then per step: its loads, its MFMAs
@@ -464,7 +479,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
           for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int g = 0; g < FM; ++g)
-              acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][f], af[cb][g], acc[f][g], 0, 0, 0);
+              acc[f][g] = mfma32<MODE>(wf[cb][f], af[cb][g], acc[f][g]);
         }
       }
     };
@@ -526,7 +541,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
               for (int j = 0; j < 4; ++j)
                 h[j] = silu(acc[f][g][4 * q + j]) * acc[f + FN / 2][g][4 * q + j];
               *reinterpret_cast<u32x2_t*>(crow + col) =
-                  u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+                  u32x2_t{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])};
             }
           }
       } else {
@@ -542,6 +557,347 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
                   f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
             }
           }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large tiles for MFMA-bound shapes: 256 activation rows x 256 weight rows x 32 K
+// per tile, eight wavefronts in two groups of four that take turns ("ping-pong"):
+// while one group's wavefronts run their MFMAs from registers, the other group's
+// read their next fragments from LDS and issue global->LDS loads, and a workgroup
+// barrier swaps the roles. With one wavefront of each group on every SIMD, the
+// SIMD's matrix pipe always has a wavefront whose operands are in registers, and
+// the LDS reads and the barrier waits of one group hide behind the other group's
+// MFMAs instead of stalling all eight wavefronts at once.
+//
+// Per K tile a wavefront multiplies 128 activation rows by 64 weight rows (4 x 2
+// blocks of v_mfma_f32_32x32x16, 16 MFMAs; 128 float32 accumulators): LDS reads of
+// 0.75 KB per MFMA, and 64 KB of global->LDS loads feed 2^25 multiply-adds, 1.5x
+// fewer bytes per FLOP than the 128 x 256 tile. Four LDS stages (128 KB) keep three
+// K tiles in flight. Which wavefronts share a SIMD is read from the hardware (HW_ID)
+// at kernel start; the group and the output block of each wavefront follow from it
+// (if the placement is not two wavefronts per SIMD, wavefront w takes role w, which
+// only costs speed).
+//
+// Phases, separated by barriers, for an item of nk K tiles (MEM(k): read tile k's
+// fragments into registers; COMP(k): its 16 MFMAs):
+//   group 0:        MEM(0) | COMP(0) | MEM(1) | COMP(1) | ... | COMP(nk-1) |
+//   group 1:  ----- | MEM(0) | COMP(0) | MEM(1) | ...        | MEM(nk-1) | COMP(nk-1)
+// Tile k's loads are issued in phase 2(k - 3) (group 0 in its MEM, group 1 before its
+// MFMAs) into the stage tile k - 4 used, which every wavefront has read by then; each
+// wavefront waits for its own loads of tile k before the barrier that opens phase 2k.
+constexpr int kPpBM = 256, kPpBN = 256, kPpBK = 32, kPpS = 4, kPpNW = 8;
+constexpr size_t kPpLds = (size_t)kPpS * (kPpBM + kPpBN) * kPpBK * sizeof(bf16_t);  // 128 KB
+
+// SIMD of the calling wavefront within its CU (HW_ID bits 5:4).
+__device__ __forceinline__ int wave_simd() {
+  return (int)__builtin_amdgcn_s_getreg(4 | (4 << 6) | ((2 - 1) << 11));
+}
+
+// Workgroup barrier that nothing is scheduled across (LDS reads retired first).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  stage_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE, int ROLE>
+__global__ void __launch_bounds__(64 * kPpNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
+  constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, S = kPpS, NW = kPpNW;
+  constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int FM = 4, FN = 2;                      // 32-row blocks per wavefront: activations, weights
+  constexpr int CPR = BK / 8, RPI = kWave / CPR;     // 16-byte chunks per row; rows per load instruction
+  constexpr int J = (BM + BN) / (RPI * NW);          // load instructions per stage per wavefront (4)
+  constexpr int JA = BM / (RPI * NW);                // of which fill activation rows (2)
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(S == 4 && J == 4 && JA == 2, "the phase schedule below is written for this shape");
+  __shared__ TileTable tt;
+  __shared__ int simd_count[4];
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];  // [S][BM + BN][BK]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  if (tid < 4) simd_count[tid] = 0;
+  build_tile_table(tt, p0, p1, OC, BM);  // ends with a workgroup barrier
+  const int simd = __builtin_amdgcn_readfirstlane(wave_simd()) & 3;
+  int ord = 0;
+  if (lane == 0) ord = atomicAdd(&simd_count[simd], 1);
+  ord = __builtin_amdgcn_readfirstlane(__shfl(ord, 0, kWave));
+  __syncthreads();
+  // (read back through readfirstlane: the LDS values are the same in every lane, and the
+  // compiler must know the role is wave-uniform or every branch on it becomes divergent)
+  const int paired = __builtin_amdgcn_readfirstlane(
+      simd_count[0] == 2 && simd_count[1] == 2 && simd_count[2] == 2 && simd_count[3] == 2);
+  const int role = __builtin_amdgcn_readfirstlane(paired ? (ord & 1) * 4 + simd : wave);
+  const int grp = role >> 2, wm = role & 1, wn = role >> 1;  // wn: weight quarter (group 0: 0, 1)
+  const int G0 = p0.groups, G = p0.groups + p1.groups;
+  const int total = tt.prefix[kMaxGroups];
+  const int half = lane >> 5, l32 = lane & 31;
+  // this lane's loads: row RPI (wave + NW j) + lrow of the stage, physical chunk lane % CPR,
+  // logical chunk lc (the swizzle of lds_off<32>; each instruction's first row is a
+  // multiple of 16)
+  const int lrow = lane / CPR;
+  const uint32_t lk = (uint32_t)(((lane % CPR) ^ ((lrow >> 2) & 3)) * 8);  // K column of the lane's chunk
+
+  // XCD-contiguous tile ranges with the last round split by output columns, as in
+  // the 128 x 256 kernel (here into halves or quarters of the four weight quarters).
+  const int P = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int Bx = P >> 3;
+  const int T0 = tt.prefix[G0], T1 = total - T0;
+  const int b0 = (int)((int64_t)xcd * T0 / 8), n0 = (int)((int64_t)(xcd + 1) * T0 / 8) - b0;
+  const int b1 = T0 + (int)((int64_t)xcd * T1 / 8), n1 = T0 + (int)((int64_t)(xcd + 1) * T1 / 8) - b1;
+  const int nx = n0 + n1;
+  const int full = nx / Bx * Bx, rem = nx - full;
+  const int split = rem == 0 ? 1 : (4 * rem <= Bx) ? 4 : (2 * rem <= Bx) ? 2 : 1;
+  const int items = full + rem * split;
+
+  // One work item, every field wave-uniform.
+  struct Where {
+    int second, ge, Kdim, kofs, nk, m0, rows_valid, col0, parts;
+  };
+  auto locate = [&](int it, Where& w) {
+    int i = it, part = 0, parts = 1;
+    if (it >= full) {
+      i = full + (it - full) / split;
+      part = (it - full) % split;
+      parts = split;
+    }
+    const int L = i < n1 ? b1 + i : b0 + (i - n1);
+    int lo = 0, hi = G;  // prefix[lo] <= L < prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tt.prefix[mid] <= L) lo = mid; else hi = mid;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    w.second = e >= G0;
+    w.ge = w.second ? e - G0 : e;
+    w.Kdim = __builtin_amdgcn_readfirstlane(tt.klen[e]);
+    w.kofs = __builtin_amdgcn_readfirstlane(tt.kofs[e]);
+    w.nk = (w.Kdim + BK - 1) / BK;
+    const int local = L - __builtin_amdgcn_readfirstlane(tt.prefix[e]);
+    const int mt = __builtin_amdgcn_readfirstlane(tt.mt[e]);
+    const int ntile = local / mt, mtile = local - ntile * mt;
+    w.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
+    w.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - w.m0));
+    w.parts = parts;
+    w.col0 = ntile * OC + part * (OC / parts);
+  };
+  // Row indices of this lane's activation loads for item w: gathered problems read
+  // them from a_rows (global loads left in flight).
+  auto fetch_rows = [&](const Where& w, int (&arow)[JA]) {
+    const GemmProblem pr = w.second ? p1 : p0;
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow;
+      arow[j] = w.m0 + (r < w.rows_valid ? r : 0);
+    }
+    if (pr.a_rows) {
+#pragma unroll
+      for (int j = 0; j < JA; ++j) arow[j] = pr.a_rows[arow[j]];
+    }
+  };
+  // Operand resources and this lane's row offsets for item w. Rows past the segment
+  // and weight rows outside the item's output columns point one row past their
+  // resource's end: their loads read zero without touching memory.
+  struct Tile {
+    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+    uint32_t a_end, b_end;
+    uint32_t off[J];
+  };
+  auto setup = [&](const Where& w, const int (&arow)[JA], Tile& t) {
+    const GemmProblem pr = w.second ? p1 : p0;
+    const int Nout = pr.n_out, ocp = OC / w.parts;
+    const int64_t lda = pr.lda ? pr.lda : pr.k_dim, ldb = pr.ldb ? pr.ldb : pr.k_dim;
+    const uint32_t a_rb = (uint32_t)lda * 2, b_rb = (uint32_t)ldb * 2;
+    const int64_t wofs = pr.k_offsets ? (int64_t)w.kofs : (int64_t)w.ge * Nout * ldb;
+    const int64_t abase = pr.a_rows ? 0 : w.m0 - (pr.rows_per_group ? (int64_t)w.ge * pr.rows_per_group : 0);
+    t.a_end = __builtin_amdgcn_readfirstlane((uint32_t)((pr.a_rows ? pr.a_nrows : w.rows_valid) * a_rb));
+    t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)Nout * b_rb);
+    t.ra = buffer_rsrc(uniform_ptr(pr.a + abase * lda + w.kofs), t.a_end);
+    t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + wofs), t.b_end);
+    t.rb1 = buffer_rsrc(uniform_ptr(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs), t.b_end);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow;
+      const int64_t row = pr.a_rows ? min<int64_t>(max<int64_t>(arow[j], 0), pr.a_nrows - 1) : r;
+      t.off[j] = (r >= w.rows_valid ? t.a_end : (uint32_t)row * a_rb) + lk * 2;
+    }
+#pragma unroll
+    for (int j = JA; j < J; ++j) {
+      const int r = RPI * (wave + NW * j) + lrow - BM;
+      const int c = MODE == kSwiGLU ? r % OC : r;
+      const int n = w.col0 + c;
+      t.off[j] = (c < ocp && n < Nout ? (uint32_t)n * b_rb : t.b_end) + lk * 2;
+    }
+  };
+  // This wavefront's J loads of K tile kt into stage st. Chunks past the K range,
+  // and every chunk of a tile past the item's last, read past their resource's end
+  // (zero, no memory access), so no LDS fix-up is needed and every wavefront issues J
+  // loads per tile slot, which keeps the wait counts constant. (A tile past the end
+  // lands in a stage that nothing reads before this wavefront's own later loads
+  // refill it.)
+  auto issue = [&](const Tile& t, const Where& w, int kt, int st) {
+    const uint32_t kb = (uint32_t)kt * (BK * 2);
+    const bool in = kt < w.nk && (int)(kt * BK + lk) < w.Kdim;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const bool up = MODE == kSwiGLU && j >= JA && RPI * (wave + NW * j) - BM >= OC;
+      const uint32_t end = j < JA ? t.a_end : t.b_end;
+      buffer_load_lds16(j < JA ? t.ra : up ? t.rb1 : t.rb0, in ? t.off[j] + kb : end,
+                        smem + st * STAGE + RPI * (wave + NW * j) * BK);
+    }
+  };
+  // Stages rotate across items: K tile kt of an item lives in stage (sb + kt) % S,
+  // where sb advances by the item's tile count, so the next item's first tiles never
+  // land in the stage of the current item's last tile, which group 1 still reads
+  // after the last barrier.
+  auto prologue = [&](const Tile& t, const Where& w, int sb) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue(t, w, s, (sb + s) & (S - 1));
+  };
+
+  // Fragment addresses: one per-lane byte offset per 16-wide K step for the first
+  // activation block and the first weight block; the other blocks of the same K step
+  // are whole 32-row strides further on (the swizzle term (row / 4) % 4 repeats every
+  // 32 rows), so they fold into the LDS reads' immediate offsets.
+  uint32_t a_lane[2], b_lane[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    a_lane[ks] = (uint32_t)lds_off<BK>(wm * (BM / 2) + l32, ks * 2 + half) * 2;
+    b_lane[ks] = (uint32_t)(BM * BK + lds_off<BK>((MODE == kSwiGLU ? wn * 32 : wn * 64) + l32, ks * 2 + half)) * 2;
+  }
+  constexpr uint32_t kRow32 = 32 * BK * 2;                                   // bytes between 32-row blocks
+  constexpr uint32_t kWStep = MODE == kSwiGLU ? (BN / 2) * BK * 2 : kRow32;  // gate -> up, or block -> block
+  typedef bf16x8_t Frags[2][FN + FM];  // per 16-wide K step: FN weight fragments, then FM activation ones
+  auto read_frags = [&](int st, Frags& fr) {
+    const char* base = reinterpret_cast<const char*>(smem) + st * (STAGE * 2);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) fr[ks][f] = *reinterpret_cast<const bf16x8_t*>(base + b_lane[ks] + f * kWStep);
+#pragma unroll
+      for (int g = 0; g < FM; ++g)
+        fr[ks][FN + g] = *reinterpret_cast<const bf16x8_t*>(base + a_lane[ks] + g * kRow32);
+    }
+  };
+
+  if (slot >= items) return;
+  Where cur, nxt;
+  Tile tl;
+  int rows[JA];
+  int sb = 0;
+  locate(slot, cur);
+  fetch_rows(cur, rows);
+  setup(cur, rows, tl);
+  prologue(tl, cur, sb);
+  // The next item's row indices are loaded right behind the current item's first
+  // tiles; the K loop's waits (at most 2J of this wavefront's loads outstanding)
+  // cover them by the third tile, long before the next set-up reads them.
+  const bool has_next0 = slot + Bx < items;
+  if (has_next0) {
+    locate(slot + Bx, nxt);
+    fetch_rows(nxt, rows);
+  }
+  for (int it = slot; it < items; it += Bx) {
+    const bool more = it + Bx < items;
+    const int nk = cur.nk;
+    const bool wact = __builtin_amdgcn_readfirstlane(wn < 4 / cur.parts && wm * (BM / 2) < cur.rows_valid);
+    f32x16_t acc[FN][FM];
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int g = 0; g < FM; ++g) acc[f][g] = f32x16_t{};
+    auto compute = [&](const Frags& fr) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int g = 0; g < FM; ++g) acc[f][g] = mfma32<MODE>(fr[ks][f], fr[ks][FN + g], acc[f][g]);
+    };
+    // Before the barrier that opens tile kt's first read: this wavefront's loads of
+    // tile kt have landed. Loads complete in issue order, and at most the loads of
+    // tiles kt + 1 and kt + 2 (and the next item's row indices, before tile 3's) were
+    // issued after them: wait until at most 2J are outstanding (stores only hold the
+    // count up).
+    auto wait_tile = [&]() { wait_vmcnt<2 * J>(); };
+    auto st_of = [&](int kt) { return (sb + kt) & (S - 1); };
+    // MEM(k): issue tile k + 3's loads (into the stage of tile k - 1, which both groups
+    // have read by then), then read all of tile k's fragments into registers; COMP(k):
+    // tile k's 32 MFMAs from registers only. Loads are issued only in MEM phases, so the
+    // computing group never waits on the address unit.
+    Frags fr;
+    wait_tile();
+    phase_barrier();
+    if (grp == 0) {
+      for (int kt = 0; kt < nk; ++kt) {
+        issue(tl, cur, kt + S - 1, st_of(kt + S - 1));  // MEM(kt)
+        if (wact) read_frags(st_of(kt), fr);
+        phase_barrier();
+        if (wact) compute(fr);                           // COMP(kt)
+        wait_tile();                                     // tile kt + 1
+        phase_barrier();
+      }
+    } else {
+      phase_barrier();                                   // phase 0
+      for (int kt = 0; kt < nk; ++kt) {
+        issue(tl, cur, kt + S - 1, st_of(kt + S - 1));  // MEM(kt)
+        if (wact) read_frags(st_of(kt), fr);
+        wait_tile();                                     // tile kt + 1
+        phase_barrier();
+        if (kt + 1 == nk) break;                         // COMP(nk-1) comes after the loop
+        if (wact) compute(fr);                           // COMP(kt)
+        phase_barrier();
+      }
+      if (wact) compute(fr);                             // COMP(nk-1)
+    }
+    // Store this item's outputs (every LDS read of the item except group 1's last
+    // step is done; the next item's tiles go to other stages), then start the next.
+    if (wact) {
+      const GemmProblem pr = cur.second ? p1 : p0;
+      const int Nout = pr.n_out, m0 = cur.m0, rows_valid = cur.rows_valid, col0 = cur.col0;
+#pragma unroll
+      for (int g = 0; g < FM; ++g) {
+        const int rl = wm * (BM / 2) + g * 32 + l32;
+        if (rl >= rows_valid) continue;
+        if (MODE == kSwiGLU) {
+          bf16_t* crow = static_cast<bf16_t*>(pr.out) + (int64_t)(m0 + rl) * Nout;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = col0 + wn * 32 + 8 * q + 4 * half;
+            if (col < Nout) {
+              float h[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) h[j] = silu(acc[0][g][4 * q + j]) * acc[1][g][4 * q + j];
+              *reinterpret_cast<u32x2_t*>(crow + col) = u32x2_t{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])};
+            }
+          }
+        } else {
+          float* crow = static_cast<float*>(pr.out) + (int64_t)(m0 + rl) * Nout;
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int col = col0 + wn * 64 + f * 32 + 8 * q + 4 * half;
+              if (col < Nout) {
+                const f32x16_t& v = acc[f][g];
+                *reinterpret_cast<f32x4_t*>(crow + col) = f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+              }
+            }
+        }
+      }
+    }
+    sb = (sb + nk) & (S - 1);
+    if (more) {
+      cur = nxt;
+      setup(cur, rows, tl);
+      prologue(tl, cur, sb);
+      if (it + 2 * Bx < items) {
+        locate(it + 2 * Bx, nxt);
+        fetch_rows(nxt, rows);
       }
     }
   }
@@ -606,7 +962,7 @@ skinny_gemm_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{};
     for (int c = c0; c < c1; c += kSkinnyBatch) {
-      bf16x8_t av[kSkinnyBatch], bv[NB][kSkinnyBatch];
+      bf16x8_t av[kSkinnyBatch], bv[NB][kSkinnyBatch];  // kDown16: av holds half bits
 #pragma unroll
       for (int j = 0; j < kSkinnyBatch; ++j) {
         const int k = (c + j) * 32 + 8 * kq;  // chunks of 8 are wholly inside or outside k_dim
@@ -619,8 +975,13 @@ skinny_gemm_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
       for (int j = 0; j < kSkinnyBatch; ++j)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], bv[b][j], acc[b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b) {
+          if constexpr (MODE == kDown16)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[j]),
+                                                           bf16x8_to_f16x8(bv[b][j]), acc[b], 0, 0, 0);
+          else
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], bv[b][j], acc[b], 0, 0, 0);
+        }
     }
     if (wave > 0)
 #pragma unroll
@@ -639,7 +1000,7 @@ skinny_gemm_kernel(GemmProblem p0, GemmProblem p1) {
           if (m >= rows_valid) continue;
           const int64_t o = (int64_t)(m0 + m) * Nout + col;
           if constexpr (MODE == kSwiGLU) {
-            static_cast<bf16_t*>(pr.out)[o] = f32_to_bf16(silu(acc[0][i]) * acc[NB - 1][i]);
+            static_cast<_Float16*>(pr.out)[o] = (_Float16)(silu(acc[0][i]) * acc[NB - 1][i]);
           } else {
             static_cast<float*>(pr.out)[o] = acc[0][i];
           }
@@ -734,8 +1095,32 @@ static void launch_variant(const GemmProblem& q0, const GemmProblem& q1, int num
 }
 
 template <int MODE, int ROLE>
+static void launch_pp(const GemmProblem& q0, const GemmProblem& q1, int num_cus, hipStream_t stream) {
+  constexpr int OC = MODE == kSwiGLU ? kPpBN / 2 : kPpBN;
+  auto kern = grouped_gemm_pp_kernel<MODE, ROLE>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kPpLds);
+  const unsigned grid = gemm_grid(q0, q1, kPpBM, OC, num_cus, 1);
+  kern<<<grid, 64 * kPpNW, kPpLds, stream>>>(q0, q1);
+}
+
+// The 256 x 256 ping-pong tiles pay off when every problem of the launch has many
+// rows per group (up to a quarter of a 256-row tile is lost per segment end): at
+// least 512 rows per group if every slot were real (a routed problem's worst case,
+// T min(K, N) rows over N experts; a dense problem's T). Plain forms only.
+static bool use_pp(const GemmProblem& q0, const GemmProblem& q1) {
+  auto ok = [](const GemmProblem& p) {
+    if (p.groups == 0 || p.max_rows <= 0) return true;
+    if (p.k_offsets || p.lda || p.ldb || p.rows_per_group) return false;
+    return p.max_rows / p.groups >= 512;
+  };
+  return ok(q0) && ok(q1);
+}
+
+template <int MODE, int ROLE>
 static void launch_shape(const GemmProblem& q0, const GemmProblem& q1, int num_cus, hipStream_t stream) {
-  launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream);
+  if (use_pp(q0, q1)) launch_pp<MODE, ROLE>(q0, q1, num_cus, stream);
+  else launch_variant<MODE, ROLE, 128, 256, 2, 4, 3, 64>(q0, q1, num_cus, stream);
 }
 
 // Groups of at most this many rows take the skinny kernel (measured at the
@@ -788,6 +1173,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     else launch_skinny<M_, 0>(q0, q1, num_cus, stream);                    \
   } while (0)
       if (op == 0) MOE_SKINNY_DISPATCH(kSwiGLU);
+      else if (op == 2) MOE_SKINNY_DISPATCH(kDown16);
       else MOE_SKINNY_DISPATCH(kPlain);
 #undef MOE_SKINNY_DISPATCH
       return hipGetLastError();
@@ -800,6 +1186,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     else launch_shape<M_, 0>(q0, q1, num_cus, stream);                \
   } while (0)
     if (op == 0) MOE_GEMM_DISPATCH(kSwiGLU);
+    else if (op == 2) MOE_GEMM_DISPATCH(kDown16);
     else MOE_GEMM_DISPATCH(kPlain);
 #undef MOE_GEMM_DISPATCH
   } else {
@@ -808,7 +1195,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
       const int64_t n = p->max_rows * p->n_out;
       const unsigned grid = (unsigned)((n + 255) / 256);
       const float* A = reinterpret_cast<const float*>(p->a);
-      if (op == 0)
+      if (op == 0)  // (op 2, the half-precision down projection, is op 1 for float32)
         grouped_gemm_f32_kernel<kSwiGLU><<<grid, 256, 0, stream>>>(
             A, p->a_rows, p->a_nrows, p->offsets, p->groups, p->max_rows,
             reinterpret_cast<const float*>(p->b0), reinterpret_cast<const float*>(p->b1), p->n_out,
@@ -835,7 +1222,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   GemmProblem g2{static_cast<const bf16_t*>(a.h), nullptr, a.max_rows, a.offsets, a.groups,
                  a.max_rows, static_cast<const bf16_t*>(a.w_down), nullptr, a.d_model, a.d_ff,
                  a.out};
-  return launch_gemm_pair(a.bf16, 1, g2, none, a.num_cus, stream, role);
+  return launch_gemm_pair(a.bf16, 2, g2, none, a.num_cus, stream, role);
 }
 
 }  // namespace moe

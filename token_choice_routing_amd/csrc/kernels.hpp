@@ -113,7 +113,9 @@ struct GemmProblem {
   int rows_per_group;        // > 0: group e owns output rows [e*rpg, (e+1)*rpg) and reads
                              // rows [0, rpg) of a (offsets unused)
 };
-// op 0: out = silu(a b0^T) * (a b1^T); op 1: out = a b0^T. Both problems in one launch.
+// op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
+// float32 out); op 2: out = a b0^T with a in half (the layer's h), float32 out. Both
+// problems in one launch. (float32 layers: op 2 is op 1.)
 // role names the launch in profiles: 0 standalone grouped, 1 standalone single
 // segment, 2 the layer's fused launch, 3 the layer backward.
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,

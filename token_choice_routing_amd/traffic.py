@@ -24,18 +24,24 @@ import sys
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 256 << 20
 
-# bench.py kernel-table names -> kernel-name prefixes (template arguments: mode, role)
+# bench.py kernel-table names -> kernel-name prefixes (GEMM template arguments: mode
+# 0 gate/up, 2 half-precision down; role 0 standalone grouped, 1 standalone single
+# segment, 2 the layer's launches); either GEMM kernel may run a launch
+def _gemm(mode, role):
+    return (f"void moe::grouped_gemm_bf16_kernel<{mode}, {role},", f"void moe::grouped_gemm_pp_kernel<{mode}, {role}>")
+
+
 BENCH_KERNELS = {
-    "gemm_gate_up": "void moe::grouped_gemm_bf16_kernel<0, 0,",
-    "gemm_down": "void moe::grouped_gemm_bf16_kernel<1, 0,",
-    "shared_gate_up": "void moe::grouped_gemm_bf16_kernel<0, 1,",
-    "shared_down": "void moe::grouped_gemm_bf16_kernel<1, 1,",
-    "layer_gate_up": "void moe::grouped_gemm_bf16_kernel<0, 2,",
-    "layer_down": "void moe::grouped_gemm_bf16_kernel<1, 2,",
-    "route": "void moe::route_tile_kernel<false,",
-    "layer_route": "void moe::route_tile_kernel<true,",
-    "gather": "moe::gather_rows_kernel",
-    "combine": "void moe::combine_kernel<",
+    "gate_up_layer": _gemm(0, 2),
+    "down_layer": _gemm(2, 2),
+    "gemm_gate_up": _gemm(0, 0),
+    "gemm_down": _gemm(2, 0),
+    "shared_gate_up": _gemm(0, 1),
+    "shared_down": _gemm(2, 1),
+    "route": ("void moe::route_tile_kernel<false,",),
+    "layer_route": ("void moe::route_tile_kernel<true,",),
+    "gather": ("moe::gather_rows_kernel",),
+    "combine": ("void moe::combine_kernel<",),
 }
 
 
