@@ -31,10 +31,12 @@
 //    step waiting only for its own reads.
 //  * Persistent grid. Each workgroup builds the tile table from the device
 //    offsets (no host round trip for R), and tiles are ordered
-//    (expert, column tile, row tile); each problem's list is cut into 8 contiguous
-//    ranges, one per XCD (workgroups are dispatched round-robin over the 8 XCDs),
-//    so the row tiles that share one expert's weight panel run on the same L2 and
-//    the shared expert's tiles are spread over all XCDs.
+//    (expert, column tile, row tile) for a grouped problem and (row tile, column
+//    tile) for a dense one; each problem's list is cut into 8 contiguous ranges, one
+//    per XCD (workgroups are dispatched round-robin over the 8 XCDs). The tiles an
+//    XCD runs at once then share one expert's weight panel (grouped: the weights are
+//    the larger operand of a segment) or a few activation row panels (dense: the
+//    activations are read about once instead of once per column tile).
 //  * When a range's last round has fewer tiles than the range has workgroups,
 //    those tiles are split by output columns into 2 or 4 sub-tiles, so every
 //    workgroup streams about the same weight bytes. Rows past the segment or
@@ -114,7 +116,7 @@ struct TileTable {
   int klen[kMaxGroups + 1];
 };
 
-// Table of (group, column tile, row tile) over problem 0's groups followed by
+// Table of the tiles of problem 0's groups followed by
 // problem 1's single dense group. Segment e of a grouped problem is [a, b) with
 // a = clamp(offsets[e], 0, max_rows), b = clamp(offsets[e+1], a, max_rows):
 // always inside the buffers, exactly the requested segment for valid offsets.
@@ -180,6 +182,20 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
     if (lane == kWave - 1) tt.prefix[kMaxGroups] = incl;
   }
   __syncthreads();
+}
+
+// Row tile and column tile of tile `local` of a group with mt row tiles and nt
+// column tiles. A dense problem (one group of max_rows rows) runs row-major, a
+// grouped one column-major (all row tiles of one column panel in a row).
+__device__ __forceinline__ void tile_of(const GemmProblem& pr, int local, int mt, int nt,
+                                        int& mtile, int& ntile) {
+  if (pr.groups == 1 && !pr.offsets && pr.rows_per_group <= 0) {
+    mtile = local / nt;
+    ntile = local - mtile * nt;
+  } else {
+    ntile = local / mt;
+    mtile = local - ntile * mt;
+  }
 }
 
 // Workgroups of a tile shape that fit one CU's 160 KB of LDS (stages + tile table);
@@ -270,7 +286,7 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     uint32_t a_end, b_end;  // one past each resource (reads there return zero)
     uint32_t off[J];
   };
-  // Locates work item it (group, column tile, row tile, sub-tile columns), decides
+  // Locates work item it (group, row tile, column tile, sub-tile columns), decides
   // which load instructions fetch something used (A rows before rows_valid, weight
   // rows of the sub-tile's columns; wave-uniform and the same for every K tile, so
   // each stage of the item holds jn of this wavefront's loads) and sets each load's
@@ -301,8 +317,8 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
     w.kofs = tt.kofs[e];
     w.nk = (w.Kdim + BK - 1) / BK;
     const int local = L - tt.prefix[e];
-    const int mt = tt.mt[e];
-    const int ntile = local / mt, mtile = local - ntile * mt;
+    int mtile, ntile;
+    tile_of(pr, local, tt.mt[e], tt.nt[e], mtile, ntile);
     w.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
     w.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - w.m0));
     w.ocp = OC / parts;  // output columns of this item
@@ -678,8 +694,9 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     w.kofs = __builtin_amdgcn_readfirstlane(tt.kofs[e]);
     w.nk = (w.Kdim + BK - 1) / BK;
     const int local = L - __builtin_amdgcn_readfirstlane(tt.prefix[e]);
-    const int mt = __builtin_amdgcn_readfirstlane(tt.mt[e]);
-    const int ntile = local / mt, mtile = local - ntile * mt;
+    int mtile, ntile;
+    tile_of(w.second ? p1 : p0, local, __builtin_amdgcn_readfirstlane(tt.mt[e]),
+            __builtin_amdgcn_readfirstlane(tt.nt[e]), mtile, ntile);
     w.m0 = __builtin_amdgcn_readfirstlane(tt.start[e] + mtile * BM);
     w.rows_valid = __builtin_amdgcn_readfirstlane(min(BM, tt.start[e] + tt.len[e] - w.m0));
     w.parts = parts;
@@ -810,13 +827,18 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int g = 0; g < FM; ++g) acc[f][g] = f32x16_t{};
+    // A computing wavefront runs at raised issue priority, so that on its SIMD the
+    // other group's LDS reads and loads fill the gaps between its MFMAs rather than
+    // delay them (measured +4% on a dense GEMM).
     auto compute = [&](const Frags& fr) {
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int g = 0; g < FM; ++g) acc[f][g] = mfma32<MODE>(fr[ks][f], fr[ks][FN + g], acc[f][g]);
+      __builtin_amdgcn_s_setprio(0);
     };
     // Before the barrier that opens tile kt's first read: this wavefront's loads of
     // tile kt have landed. Loads complete in issue order, and at most the loads of
@@ -940,8 +962,8 @@ skinny_gemm_kernel(GemmProblem p0, GemmProblem p1) {
     const int ge = e >= G0 ? e - G0 : e;
     const int Nout = pr.n_out, Kdim = pr.k_dim;
     const int local = L - tt.prefix[e];
-    const int mt = tt.mt[e];
-    const int ntile = local / mt, mtile = local - ntile * mt;
+    int mtile, ntile;
+    tile_of(pr, local, tt.mt[e], tt.nt[e], mtile, ntile);
     const int m0 = tt.start[e] + mtile * kSkinnyRows;
     const int rows_valid = min(kSkinnyRows, tt.start[e] + tt.len[e] - m0);
     const int n0 = ntile * kSkinnyRows;
