@@ -290,17 +290,17 @@ def roofline(k):
 
 
 def traffic_from_profiles(kernel, workload):
-    """HBM bytes per launch measured with rocprofv3 counters, when a summary for this
-    kernel and workload is committed under profiles/ (else None)."""
+    """(HBM bytes per launch, profiled kernel name) measured with rocprofv3 counters,
+    when a summary for this launch and workload is committed under profiles/ (else
+    None, None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     try:
-        tab = json.load(open(path))
-        ent = tab.get(f"{kernel}@{workload}")
-        return None if ent is None else ent.get("bytes_per_launch")
+        ent = json.load(open(path)).get(f"{kernel}@{workload}")
     except (ValueError, OSError):
-        return None
+        return None, None
+    return (None, None) if ent is None else (ent.get("bytes_per_launch"), ent.get("kernel"))
 
 
 def cpu_baseline(wl_full, budget_s=15.0, Ts=512):
@@ -550,12 +550,13 @@ def main():
     kernels, _ = kernel_table(torch, tcr, layer, args.kernel_iters)
     dom = "gate_up_layer"
     rl = roofline(kernels[dom])
-    rl["kernel"] = ("grouped_gemm_bf16_kernel<0, 2>: the layer's gate/up + SwiGLU launch (routed rows of x "
-                    "read through perm_token, and the shared expert) through moe_expert_gate_up, caches "
-                    "flushed by a 512 MB read before each timed launch")
+    traffic, kname = traffic_from_profiles(dom, cfg.name)
+    rl["kernel"] = (f"{kname or 'grouped GEMM <0, 2>'}: the layer's gate/up + SwiGLU launch (routed rows "
+                    "of x read through perm_token, and the shared expert) through moe_expert_gate_up, "
+                    "caches flushed by a 512 MB read before each timed launch")
     rl["flops_per_launch"] = kernels[dom]["flops"]
     rl["us_per_launch"] = kernels[dom]["us"]
-    rl["traffic"] = traffic_from_profiles(dom, cfg.name)
+    rl["traffic"] = traffic
     line = {
         "metric": "MoE-layer tokens/s + real-expert TFLOP/s (% bf16 MFMA peak) vs rho",
         "value": round(tok_s, 1),

@@ -44,6 +44,9 @@ CASES = {
     # d_model, d_ff and d_ff_shared multiples of 8 but not of 64 or 32: ragged K tiles
     # in every contraction and ragged 64 x 64 tiles in every transpose
     "ragged_dims": dict(T=333, d_model=200, n_experts=12, n_null=4, top_k=3, d_ff=104, d_ff_shared=40),
+    # 512 output rows per expert: the weight gradients take the 256 x 256 ping-pong
+    # tiles (segments of ~150 rows: ragged K ranges of a few 32-wide K tiles)
+    "pp_wgrad": dict(T=640, d_model=512, n_experts=8, n_null=8, top_k=2, d_ff=512, d_ff_shared=512),
 }
 
 
@@ -223,6 +226,21 @@ def test_backward_one_expert_takes_every_slot():
     wl.w_router[3, 0] = 100.0    # expert 3 wins every token
     got, ref = _run_wl(wl, 2e-2, 1e-3)
     assert (ref["fwd"]["topk_idx"][:, 0] == 3).all()
+    _check(cfg, got, ref)
+
+
+def test_backward_empty_expert_ping_pong():
+    """The ping-pong weight-gradient tiles with one expert that receives no rows (an
+    empty K range: its weight gradients are exactly zero) between experts that do."""
+    cfg = Config(name="bwd_pp_empty", dtype="bf16", w_std=None, seed=9, **CASES["pp_wgrad"])
+    wl = generate(cfg)
+    wl.x[:, 0] = 0x3F80          # bf16 1.0 in column 0 of every token
+    wl.w_router[5, 0] = -100.0   # expert 5 loses every token
+    got, ref = _run_wl(wl, 2e-2, 1e-3)
+    off = ref["fwd"]["offsets"]
+    assert off[6] == off[5] and off[-1] > 0
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        assert (got[name][5] == 0).all(), name
     _check(cfg, got, ref)
 
 

@@ -852,9 +852,14 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     // tile k's 32 MFMAs from registers only. Loads are issued only in MEM phases, so the
     // computing group never waits on the address unit.
     Frags fr;
-    wait_tile();
-    phase_barrier();
-    if (grp == 0) {
+    if (nk == 0) {
+      // an empty K range (a weight gradient's segment without rows): the outputs are
+      // zero; the prologue's loads (zero-fills of this wavefront's own stage rows) land
+      // before the next item's loads of the same rows are issued
+      wait_vmcnt<0>();
+    } else if (grp == 0) {
+      wait_tile();
+      phase_barrier();
       for (int kt = 0; kt < nk; ++kt) {
         issue(tl, cur, kt + S - 1, st_of(kt + S - 1));  // MEM(kt)
         if (wact) read_frags(st_of(kt), fr);
@@ -864,6 +869,8 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
         phase_barrier();
       }
     } else {
+      wait_tile();
+      phase_barrier();
       phase_barrier();                                   // phase 0
       for (int kt = 0; kt < nk; ++kt) {
         issue(tl, cur, kt + S - 1, st_of(kt + S - 1));  // MEM(kt)
@@ -1133,8 +1140,7 @@ static void launch_pp(const GemmProblem& q0, const GemmProblem& q1, int num_cus,
 static bool use_pp(const GemmProblem& q0, const GemmProblem& q1) {
   auto ok = [](const GemmProblem& p) {
     if (p.groups == 0 || p.max_rows <= 0) return true;
-    if (p.k_offsets || p.lda || p.ldb || p.rows_per_group) return false;
-    return p.max_rows / p.groups >= 512;
+    return (p.rows_per_group > 0 ? (int64_t)p.rows_per_group : p.max_rows / p.groups) >= 512;
   };
   return ok(q0) && ok(q1);
 }
