@@ -127,10 +127,15 @@ struct BwdWs {
   int S;  // K chunks of the shared expert's weight gradients (its K is all T tokens)
 };
 
-// The shared expert's weight gradients reduce over all T tokens: split into chunks of
-// about 1024 tokens (groups of one GEMM launch, summed in order afterwards), so they
-// spread over the chip like the routed experts' segments.
-inline int shared_splits(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>(32, (T + 1023) / 1024)); }
+// The shared expert's weight gradients reduce over all T tokens: split into chunks
+// (groups of one GEMM launch, summed in order afterwards), so they spread over the
+// chip like the routed experts' segments. Chunks of about 1024 tokens; from 8192
+// tokens on, of about 2048 (8 chunks of 16384 tokens already give 3 rounds of 256
+// tiles at d = 2048, and every chunk costs a float32 partial of the whole gradient).
+inline int shared_splits(int64_t T) {
+  const int64_t chunk = T >= 8192 ? 2048 : 1024;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(T >= 8192 ? 16 : 32, (T + chunk - 1) / chunk));
+}
 
 BwdWs bwd_ws(const moe_dims* d) {
   BwdWs w{};

@@ -321,7 +321,7 @@ router_wgrad_partial_kernel(const float* __restrict__ ds, const bf16_t* __restri
   const int j0 = blockIdx.y * kRouterRows, col = (blockIdx.x * 256 + threadIdx.x) * 2;
   const int64_t t0 = (int64_t)blockIdx.z * chunk, t1 = min<int64_t>(T, t0 + chunk);
   float a0[kRouterRows] = {}, a1[kRouterRows] = {};
-  __shared__ float sds[64][kRouterRows];
+  __shared__ __attribute__((aligned(16))) float sds[64][kRouterRows];
   for (int64_t tb = t0; tb < t1; tb += 64) {
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * kRouterRows; i += 256) {
@@ -365,7 +365,8 @@ router_wgrad_reduce_kernel(const float* __restrict__ part, int chunks, int64_t n
 
 // dx[t] = sum over real slots of dx_perm[p] (slot order) + dx_shared[t] + ds[t] W_r,
 // float32. A workgroup takes 16 tokens x 256 columns, one column per thread: each
-// router row element is read once per 16 tokens, the tokens' ds from LDS.
+// router row element is read once per 16 tokens, the tokens' ds from LDS four router
+// rows at a time (one 16-byte read per token; the rows past N1 are zero).
 constexpr int kScatterTok = 16;
 __global__ void __launch_bounds__(256)
 scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_pos, int K, int64_t R,
@@ -373,11 +374,12 @@ scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__
                   const float* __restrict__ w_router, int N1, int d, int64_t T, float* __restrict__ dx) {
   const int64_t t0 = (int64_t)blockIdx.x * kScatterTok;
   const int nt = (int)min<int64_t>(kScatterTok, T - t0);
-  __shared__ float sds[kScatterTok][260];
+  __shared__ __attribute__((aligned(16))) float sds[kScatterTok][260];
   __shared__ int32_t sp[kScatterTok][MOE_MAX_TOPK];
-  for (int i = threadIdx.x; i < kScatterTok * N1; i += 256) {
-    const int tt = i / N1, j = i - tt * N1;
-    sds[tt][j] = tt < nt ? ds[(t0 + tt) * N1 + j] : 0.0f;
+  const int N4 = (N1 + 3) & ~3;  // <= 260
+  for (int i = threadIdx.x; i < kScatterTok * N4; i += 256) {
+    const int tt = i / N4, j = i - tt * N4;
+    sds[tt][j] = tt < nt && j < N1 ? ds[(t0 + tt) * N1 + j] : 0.0f;
   }
   for (int i = threadIdx.x; i < kScatterTok * K; i += 256) {
     const int tt = i / K, k = i - tt * K;
@@ -388,10 +390,18 @@ scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__
     float acc[kScatterTok];
 #pragma unroll
     for (int tt = 0; tt < kScatterTok; ++tt) acc[tt] = 0.0f;
-    for (int j = 0; j < N1; ++j) {
-      const float w = w_router[(int64_t)j * d + c];
+    for (int j = 0; j < N4; j += 4) {
+      float w[4];
 #pragma unroll
-      for (int tt = 0; tt < kScatterTok; ++tt) acc[tt] += sds[tt][j] * w;
+      for (int q = 0; q < 4; ++q) w[q] = j + q < N1 ? w_router[(int64_t)(j + q) * d + c] : 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < kScatterTok; ++tt) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sds[tt][j]);
+        acc[tt] += v[0] * w[0];
+        acc[tt] += v[1] * w[1];
+        acc[tt] += v[2] * w[2];
+        acc[tt] += v[3] * w[3];
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < kScatterTok; ++tt) {
@@ -415,13 +425,15 @@ __global__ void __launch_bounds__(64) split_offsets_kernel(int64_t rows, int S, 
   for (int s = threadIdx.x; s <= S; s += 64) kofs[s] = (int32_t)min<int64_t>((int64_t)s * chunk, padded);
 }
 
-// out[i] = sum over the S partial matrices in order (deterministic).
+// out[i] = sum over the S partial matrices in order (deterministic), four elements
+// per thread (n is a multiple of 4).
 __global__ void __launch_bounds__(256)
 sum_partials_kernel(const float* __restrict__ part, int S, int64_t n, float* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    float v = 0.0f;
-    for (int s = 0; s < S; ++s) v += part[s * n + i];
-    out[i] = v;
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    f32x4_t v = reinterpret_cast<const f32x4_t*>(part)[i];
+    for (int s = 1; s < S; ++s) v += reinterpret_cast<const f32x4_t*>(part + s * n)[i];
+    reinterpret_cast<f32x4_t*>(out)[i] = v;
   }
 }
 
@@ -538,7 +550,8 @@ hipError_t launch_split_offsets(int64_t rows, int S, int32_t* kofs, hipStream_t 
 
 hipError_t launch_sum_partials(const float* part, int S, int64_t n, float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  sum_partials_kernel<<<grid_for(n), 256, 0, s>>>(part, S, n, out);
+  if (n % 4) return hipErrorInvalidValue;
+  sum_partials_kernel<<<grid_for(n / 4), 256, 0, s>>>(part, S, n, out);
   return hipGetLastError();
 }
 
