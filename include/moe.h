@@ -19,9 +19,14 @@
  *   - Every tensor argument is a DEVICE pointer to a dense row-major buffer,
  *     16-byte aligned. Structs (moe_dims, moe_layer_params, moe_aux_out) live
  *     in host memory and are read during the call only.
- *   - Element type of activations, expert weights, intermediates and outputs:
- *     dims->dtype (MOE_BF16 = bf16 bit patterns, MOE_F32 = float). The router
- *     weight, logits and routing weights are always float32.
+ *   - Element type of activations, expert weights and outputs: dims->dtype
+ *     (MOE_BF16 = bf16 bit patterns, MOE_F32 = float). The router weight, logits
+ *     and routing weights are always float32. The SwiGLU intermediate h is IEEE
+ *     half in a bf16 layer (float in a float32 one): every bf16 activation and
+ *     weight of magnitude in [2^-17, 65504] converts to half exactly, and h's 11
+ *     significant bits keep the error its storage adds to the output well below
+ *     bf16's; h or down-projection weights of magnitude above 65504 are outside
+ *     the supported range (h overflows to infinity, such a weight is clamped).
  *   - Weight layout follows the linear-layer convention [out, in] with the
  *     reduction dimension contiguous: w_gate, w_up [N][d_ff][d_model];
  *     w_down [N][d_model][d_ff]; the router [N+1][d_model], row N = null.
@@ -164,8 +169,10 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, const void
  * bounds; overlapping segments (decreasing offsets) are not meaningful.
  * offsets may be NULL when n_groups == 1 (one segment of max_rows rows).
  * Rows outside the segments are not written.
- * bf16: MFMA with float32 accumulation, h stored as bf16 (the input type of
- * the down projection's MFMA); float32: float FMA throughout.
+ * bf16: MFMA with float32 accumulation; h stored as IEEE half, and the down
+ * projection multiplies it by W_down converted to half (exact for magnitudes in
+ * [2^-17, 65504]; smaller ones truncated toward zero to a multiple of 2^-24) on
+ * the half-precision MFMA; float32: float FMA throughout.
  * bf16 limit: (d_ff + 1) * d_model * 2 bytes (one group's weight matrix plus a
  * row) must fit in 4 GB, else MOE_ERR_UNSUPPORTED.
  * ws: moe_expert_ffn_workspace_bytes() bytes (holds h).
@@ -180,10 +187,12 @@ size_t moe_expert_ffn_workspace_bytes(const moe_dims* dims, int32_t d_ff, int64_
 /*
  * moe_grouped_gemm -- one of the two GEMMs of moe_expert_ffn on its own (same
  * passage and segment rules as moe_expert_ffn; offsets NULL = one segment):
- *   op = MOE_GEMM_GATE_UP: out[p] = silu(b0[e] a_p) * (b1[e] a_p)   out dtype, [rows][n_out]
- *                          a: [rows][k_dim]; b0, b1: [n_groups][n_out][k_dim]
+ *   op = MOE_GEMM_GATE_UP: out[p] = silu(b0[e] a_p) * (b1[e] a_p)   out h, [rows][n_out]
+ *                          a: [rows][k_dim] dtype; b0, b1: [n_groups][n_out][k_dim]
  *   op = MOE_GEMM_DOWN:    out[p] = b0[e] a_p                        out float32, [rows][n_out]
- *                          a: [rows][k_dim] dtype; b0: [n_groups][n_out][k_dim]; b1 unused
+ *                          a: [rows][k_dim] h; b0: [n_groups][n_out][k_dim]; b1 unused
+ * where h is the layer's intermediate type (bf16 dtype: IEEE half bit patterns,
+ * as GATE_UP writes them; float32 dtype: float); b0, b1 are dtype.
  * n_out and k_dim multiples of 8. No workspace.
  * bf16 limit: (n_out + 1) * k_dim * 2 bytes must fit in 4 GB, else
  * MOE_ERR_UNSUPPORTED.
@@ -205,8 +214,8 @@ moe_status moe_grouped_gemm(const moe_dims* dims, int32_t op, int32_t n_groups, 
  * moe_expert_ffn, perm_token entries clamped to [0, T)); w_gate, w_up as in the
  * layer; ws_gate, ws_up: [d_ff_shared][d_model] (ignored when d_ff_shared = 0).
  * h: [T*min(K,N)][d_ff] and hs: [T][d_ff_shared] in the layer's intermediate
- * type (bf16 dtype: bf16; float32 dtype: float32). No workspace. bf16 limits as
- * for moe_layer_forward.
+ * type (bf16 dtype: IEEE half; float32 dtype: float32). No workspace. bf16 limits
+ * as for moe_layer_forward.
  */
 moe_status moe_expert_gate_up(const moe_dims* dims, const void* x, const int32_t* perm_token,
                               const int32_t* offsets, const void* w_gate, const void* w_up,

@@ -206,6 +206,9 @@ def _ffn_run(lengths, d, f, dtype="bf16", seed=0, slack=7, offsets=None):
     ([37, 250, 3, 0, 128], 136, 72),            # K and N tails (not multiples of 64)
     ([64] * 64, 512, 384),
     ([1, 2, 3, 4, 1000, 5], 2048, 1536),
+    # segments ending in a tile of exactly 128 rows (the launch of half-full last
+    # tiles), of 129 rows (a full-tile launch) and a single 128-row segment
+    ([384, 385, 128, 1200], 256, 128),
 ])
 def test_expert_ffn_segments_bf16(lengths, d, f):
     say(f"expert_ffn bf16 lengths={lengths[:8]} d={d} d_ff={f}")
