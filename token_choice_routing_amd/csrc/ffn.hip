@@ -883,8 +883,19 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
       }
       if (wact) compute(fr);                             // COMP(nk-1)
     }
-    // Store this item's outputs (every LDS read of the item except group 1's last
-    // step is done; the next item's tiles go to other stages), then start the next.
+    // Start the next item's first K tiles, then store this item's outputs. Every LDS
+    // read of this item is done (group 1's last step multiplies from registers) and
+    // the next item's tiles go to other stages. Issued first, the loads' latency passes
+    // while the stores drain (loads and stores complete in issue order, so the next
+    // item's first wait still covers both).
+    // (The set-up is computed again after the stores rather than kept: holding its
+    // offsets across the epilogue makes the register allocator spill.)
+    const int sb_next = (sb + nk) & (S - 1);
+    if (more) {
+      Tile t1;
+      setup(nxt, rows, t1);
+      prologue(t1, nxt, sb_next);
+    }
     if (wact) {
       const GemmProblem pr = cur.second ? p1 : p0;
       const int Nout = pr.n_out, m0 = cur.m0, rows_valid = cur.rows_valid, col0 = cur.col0;
@@ -919,11 +930,12 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
         }
       }
     }
-    sb = (sb + nk) & (S - 1);
+    sb = sb_next;
     if (more) {
       cur = nxt;
+#pragma unroll
+      for (int j = 0; j < JA; ++j) rows[j] = opaque_v(rows[j]);
       setup(cur, rows, tl);
-      prologue(tl, cur, sb);
       if (it + 2 * Bx < items) {
         locate(it + 2 * Bx, nxt);
         fetch_rows(nxt, rows);
