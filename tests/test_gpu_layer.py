@@ -222,6 +222,32 @@ def test_decode_token_counts_headline_shape(T):
     check_full(sub_workload(generate(CONFIGS["qwen3_0p6b_rho1"]), np.arange(T)))
 
 
+@pytest.mark.parametrize("N,M,K,T,kind", [
+    (255, 3841, 32, 4, "zero"),   # the size limits: 256 logits, 32 slots (a 256-thread workgroup)
+    (8, 0, 2, 3, "zero"),         # plain top-K, the router's null row unused
+    (16, 4, 8, 4, "zero"),        # 0 < M < K: forced reals
+    (64, 64, 8, 2, "copy"),
+    (16, 16, 4, 1, "constant"),
+])
+def test_few_tokens_route_and_sort_in_one_workgroup(N, M, K, T, kind):
+    """Up to 4 tokens: scoring (float64 dot products), selection, the permutation and
+    the statistics run in one workgroup of one launch; full compare with statistics."""
+    say(f"few tokens N={N} M={M} K={K} T={T} {kind}")
+    check_full(generate(_small(n_experts=N, n_null=M, top_k=K, T=T, null_kind=kind)))
+
+
+def test_few_tokens_infinite_null_bias():
+    """The one-workgroup routing with some tokens' null bias at +inf: their slots are
+    all null, L_z is +inf, the other statistics take the limit."""
+    say("few tokens with +inf null biases")
+    wl = generate(_small(T=4))
+    btok = np.zeros(4, dtype=np.float32)
+    btok[::3] = np.inf
+    wl.null_bias_tok = btok
+    out = check_full(wl)
+    assert (out["n_real"][::3] == 0).all() and np.isinf(out["scalars"][1])
+
+
 @pytest.mark.parametrize("N,M,K,T", [(100, 28, 6, 300), (255, 1, 8, 130), (24, 0, 3, 200)])
 def test_expert_counts_across_router_tilings(N, M, K, T):
     """Full layer where the router spreads a token tile over several scoring

@@ -508,14 +508,18 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   RouteArgs ra{d->T, d->d_model, N, d->n_null, d->top_k, bf16, true, p->x, p->w_router,
                p->null_bias, p->null_bias_tok, nullptr, logits, topk_idx, topk_w, n_real,
                at(L.route), permute_ws, rhist, tstats, d->null_kind};
-  HIP_TRY(launch_route(ra, s));
-
-  // 2. counting sort (histograms already written) + statistics finalisation
+  // 2. counting sort (histograms already written) + statistics finalisation; a few
+  //    tokens take both steps in one workgroup
   AuxTiles af{tstats, rhist, ao.f, ao.P, ao.counts, ao.scalars};
   PermuteArgs pa{d->T, d->top_k, N, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx, nullptr,
                  static_cast<int32_t*>(at(L.counts)), offsets, perm_token, slot_pos, nullptr,
                  permute_ws, true, want_stats ? &af : nullptr};
-  HIP_TRY(launch_permute(pa, s));
+  if (route_small_ok(ra)) {
+    HIP_TRY(launch_route_small(ra, &pa, s));
+  } else {
+    HIP_TRY(launch_route(ra, s));
+    HIP_TRY(launch_permute(pa, s));
+  }
 
   // 3. gate/up + SwiGLU: routed experts read x through perm_token (the gather), and the
   //    shared expert runs in the same launch

@@ -74,6 +74,11 @@ struct PermuteArgs {
 int permute_nchunks(int64_t T);
 size_t permute_ws_bytes(int64_t T, int N);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// A few bf16 tokens: the routing step in one workgroup (launch_route uses it by
+// itself); with pa (fused routing only) that launch also does what launch_permute(*pa)
+// would (permutation and statistics; x_perm is not written).
+bool route_small_ok(const RouteArgs& r);
+hipError_t launch_route_small(const RouteArgs& r, const PermuteArgs* pa, hipStream_t stream);
 
 struct FfnArgs {
   bool bf16;

@@ -47,6 +47,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "aux_final.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -731,6 +732,146 @@ route_from_logits_kernel(RouteKernelArgs a, const float* __restrict__ logits) {
   route_epilogue<FUSED, KMAX, select_threads<KMAX>()>(a, L, ld, nt, t0, blockIdx.x, a.logits_out != nullptr);
 }
 
+// A few tokens (decode-size batches): one workgroup does the whole routing step,
+// which would otherwise be a split-K scoring launch, a selection launch and, in the
+// layer, the permutation's launch, each a few microseconds of latency for little
+// work. Each logit is a float64 dot product of 16 lanes (one DPP row): lane q takes
+// the 8-element chunks q, q + 16, ... of the bf16 token row and the float32 router
+// row (products exact in float64), and the 16 partial sums are added in a fixed
+// tree; the null logit then gets its biases in float64 and every logit is rounded
+// once to float32 (within 1e-6 of the exact value, as the MFMA path). The selection
+// epilogue is the one of the other routing kernels. In the layer (pm.perm_token set)
+// the same workgroup then sorts the tile's slots (per-expert counts, offsets, a
+// stable scatter: thread e walks the slots in order and places expert e's) and
+// finalises the statistics from the single tile's sums.
+// The dot products run on the vector ALUs of one CU in float64, so this pays only
+// for a handful of tokens (measured at the Qwen3-0.6B shape: T = 16 took 125 us
+// against 67 us for the split-K scoring launches).
+constexpr int kSmallT = 4;               // at most this many tokens
+constexpr int64_t kSmallMacs = 1 << 19;  // and T (N + 1) d at most this
+
+struct SmallPermute {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_token;
+  int32_t* slot_pos;
+  AuxTiles aux;  // tstats NULL: no statistics wanted
+};
+
+template <bool FUSED, int KMAX>
+__global__ void __launch_bounds__(select_threads<KMAX>())
+route_small_kernel(RouteKernelArgs a, SmallPermute pm) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int NT = select_threads<KMAX>();
+  constexpr int NG = NT / 16;  // dot products in flight
+  const int N = a.N, d = a.d, ld = N + 1, K = a.K;
+  const int nt = (int)a.T;
+  const EpiLds L = epi_lds(smem_raw, N);
+  float* sl = L.sl;
+  if (FUSED)
+    for (int i = threadIdx.x; i < N + K + 1; i += NT) L.cnt[i] = 0;
+  const int q = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int nchunk = d / 8;
+  for (int item = grp; item < nt * ld; item += NG) {  // uniform over the 16 lanes
+    const int t = item / ld, j = item - t * ld;
+    const bf16_t* xr = a.x + (int64_t)t * d;
+    const float* wr = a.w + (int64_t)j * d;  // row N: the null row
+    double acc = 0.0;
+    // batches of 8 chunks per lane, every load of a batch in flight before its FMAs
+    // (chunks past d are zero)
+    for (int c0 = q; c0 < nchunk; c0 += 16 * 8) {
+      u32x4_t xv[8];
+      f32x4_t w0[8], w1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + 16 * u;
+        const bool in = c < nchunk;
+        xv[u] = in ? *reinterpret_cast<const u32x4_t*>(xr + 8 * c) : u32x4_t{0, 0, 0, 0};
+        w0[u] = in ? *reinterpret_cast<const f32x4_t*>(wr + 8 * c) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        w1[u] = in ? *reinterpret_cast<const f32x4_t*>(wr + 8 * c + 4) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wv[8] = {w0[u][0], w0[u][1], w0[u][2], w0[u][3], w1[u][0], w1[u][1], w1[u][2], w1[u][3]};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc = fma((double)__uint_as_float(xv[u][h] << 16), (double)wv[2 * h], acc);
+          acc = fma((double)__uint_as_float(xv[u][h] & 0xffff0000u), (double)wv[2 * h + 1], acc);
+        }
+      }
+    }
+    acc += dpp_xchg_f64<0>(acc);
+    acc += dpp_xchg_f64<1>(acc);
+    acc += dpp_xchg_f64<2>(acc);
+    acc += dpp_xchg_f64<3>(acc);
+    if (q == 0) {
+      if (j == N) {
+        acc += (double)a.null_bias;
+        if (a.null_bias_tok) acc += (double)a.null_bias_tok[t];
+      }
+      sl[t * ld + j] = (float)acc;
+    }
+  }
+  __syncthreads();
+  route_epilogue<FUSED, KMAX, NT>(a, L, ld, nt, 0, 0, a.logits_out != nullptr);
+  if (!FUSED || !pm.perm_token) return;
+  // the tile's slots in expert order (LDS: slot keys [T K], counts [N], offsets [N + 1])
+  __syncthreads();
+  const int TK = nt * K;
+  int* skey = reinterpret_cast<int*>(smem_raw);
+  int* cnt = skey + TK;
+  int* off = cnt + N;
+  for (int e = threadIdx.x; e < N; e += NT) cnt[e] = 0;
+  __syncthreads();
+  for (int f = threadIdx.x; f < TK; f += NT) {
+    const int v = a.topk_idx[f];
+    const int e = (v >= 0 && v < N) ? v : N;
+    skey[f] = e;
+    if (e < N) atomicAdd(&cnt[e], 1);
+    else pm.slot_pos[f] = -1;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {  // exclusive scan, 4 experts per lane (N <= 256)
+    const int lane = threadIdx.x;
+    int c4[4], local = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * lane + u;
+      c4[u] = e < N ? cnt[e] : 0;
+      local += c4[u];
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * lane + u;
+      if (e < N) off[e] = run;
+      run += c4[u];
+    }
+    if (lane == kWave - 1) off[N] = incl;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= N; e += NT) pm.offsets[e] = off[e];
+  for (int e = threadIdx.x; e < N; e += NT) {
+    pm.counts[e] = cnt[e];
+    int pos = off[e];
+    for (int f = 0; f < TK; ++f)
+      if (skey[f] == e) {
+        pm.perm_token[pos] = f / K;
+        pm.slot_pos[f] = pos;
+        ++pos;
+      }
+  }
+  if (!pm.aux.tstats) return;
+  __syncthreads();  // the LDS is the statistics' scratch from here
+  finalize_tiles(pm.aux, a.chunk_hist, 1, a.T, N, a.M, K, smem_raw);
+}
+
 // 32-expert tiles per scoring workgroup: all of them when N <= 64, else pairs.
 static int route_etw(int N) { return N <= 32 ? 1 : 2; }
 
@@ -783,6 +924,7 @@ static void allow_lds(F* kernel, size_t lds) {
 }
 
 hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
+  if (route_small_ok(r)) return launch_route_small(r, nullptr, stream);
   const int64_t ntt = (r.T + kRouteBT - 1) / kRouteBT;
   const unsigned nblk = (unsigned)ntt;
   const int Np = (r.N + 31) / 32 * 32;
@@ -858,6 +1000,57 @@ hipError_t launch_route(const RouteArgs& r, hipStream_t stream) {
 #undef MOE_SIMT_LAUNCH
 #undef MOE_LOGITS_LAUNCH
 #undef MOE_KMAX_SWITCH
+  return hipGetLastError();
+}
+
+bool route_small_ok(const RouteArgs& r) {
+  return r.bf16 && !r.logits_in && r.T >= 1 && r.T <= kSmallT &&
+         r.T * (int64_t)(r.N + 1) * r.d <= kSmallMacs;
+}
+
+// One launch of route_small_kernel: the routing step, and with pa (fused layer
+// path) also the permutation and the statistics.
+hipError_t launch_route_small(const RouteArgs& r, const PermuteArgs* pa, hipStream_t stream) {
+  if (!route_small_ok(r) || (pa && !r.fused)) return hipErrorInvalidValue;
+  const int Np = (r.N + 31) / 32 * 32;
+  RouteKernelArgs a{static_cast<const bf16_t*>(r.x), r.w_router, r.w_router + (int64_t)r.N * r.d,
+                    r.null_bias, r.null_bias_tok, r.T, r.d, r.N, Np, r.M, r.K, r.logits_out,
+                    r.topk_idx, r.topk_w, r.n_real, r.chunk_hist, r.rhist, r.tstats, 1, 0, nullptr,
+                    r.null_kind};
+  SmallPermute pm{};
+  if (pa) {
+    pm.counts = pa->counts;
+    pm.offsets = pa->offsets;
+    pm.perm_token = pa->perm_token;
+    pm.slot_pos = pa->slot_pos;
+    if (pa->aux) pm.aux = *pa->aux;
+  }
+  const int kmax = r.K <= 2 ? 2 : (r.K <= 8 ? 8 : 32);
+  const int nt_threads = kmax <= 8 ? select_threads<8>() : select_threads<32>();
+  size_t lds = epi_lds_bytes(r.N, r.K, r.fused);
+  if (pa) {
+    lds = std::max(lds, (size_t)(r.T * r.K + 2 * r.N + 1) * sizeof(int));
+    if (pm.aux.tstats) {
+      const int C = r.N + 3, G = finalize_groups(r.N, r.K, nt_threads);
+      lds = std::max(lds, ((size_t)G * C + C + (size_t)(r.N + r.M)) * sizeof(double) +
+                              (size_t)(r.N + r.K + 1) * sizeof(int));
+    }
+  }
+#define MOE_SMALL_LAUNCH(F_, KM_)                                                          \
+  do {                                                                                     \
+    allow_lds(route_small_kernel<F_, KM_>, lds);                                           \
+    route_small_kernel<F_, KM_><<<1, select_threads<KM_>(), lds, stream>>>(a, pm);         \
+  } while (0)
+  if (r.fused) {
+    if (kmax == 2) MOE_SMALL_LAUNCH(true, 2);
+    else if (kmax == 8) MOE_SMALL_LAUNCH(true, 8);
+    else MOE_SMALL_LAUNCH(true, 32);
+  } else {
+    if (kmax == 2) MOE_SMALL_LAUNCH(false, 2);
+    else if (kmax == 8) MOE_SMALL_LAUNCH(false, 8);
+    else MOE_SMALL_LAUNCH(false, 32);
+  }
+#undef MOE_SMALL_LAUNCH
   return hipGetLastError();
 }
 
