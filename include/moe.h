@@ -292,7 +292,11 @@ typedef struct {
  * on `stream` with no host synchronisation. y: [T][d_model] dtype.
  * aux may be NULL; the statistics kernels run only when aux requests
  * counts, f, P or scalars. ws: moe_workspace_bytes(dims, MOE_WS_LAYER) bytes,
- * sized for the worst case of T*min(K,N) real slots.
+ * sized for the worst case of T*min(K,N) real slots. With a shared expert,
+ * zero-output null slots and enough rows per expert for the large GEMM tiles
+ * (T*min(K,N)/N and T both at least 512), the combine is done in the epilogue of
+ * the shared expert's down projection (same arithmetic: float32 fmaf in slot order,
+ * one rounding) and no float32 shared-expert output is kept in the workspace.
  * bf16 limit: (T + 1), (d_ff + 1) and (d_ff_shared + 1) rows of d_model bf16
  * each fit in 4 GB (x is gathered through 32-bit offsets), else
  * MOE_ERR_UNSUPPORTED.

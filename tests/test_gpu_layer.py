@@ -344,3 +344,68 @@ def test_layer_at_the_size_limits():
     cfg = Config(name="limits", T=150, d_model=64, n_experts=255, n_null=3841, top_k=32, d_ff=64,
                  d_ff_shared=32, dtype="bf16", w_std=None, seed=12)
     check_full(generate(cfg))
+
+
+def _fused_shape(**kw):
+    """Shapes whose down projections both take the 256 x 256 tiles (at least 512 rows per
+    expert if every slot were real, and at least 512 tokens), so the layer stores the
+    routed outputs token-major and the shared expert's down projection adds them in its
+    epilogue instead of a separate combine."""
+    base = dict(name="fused_bf16", T=2100, d_model=256, n_experts=4, n_null=4, top_k=2, d_ff=128,
+                d_ff_shared=64, dtype="bf16", w_std=0.05)
+    base.update(kw)
+    return Config(**base)
+
+
+def _workspace(cfg, **kw):
+    from dataclasses import replace
+    return tcr.workspace_bytes(tcr.dims_from_config(replace(cfg, **kw), cfg.T), tcr.MOE_WS_LAYER)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                   # T = 2100: a ragged last tile of 256 tokens
+    dict(T=1100, top_k=8, n_null=8),          # K > N: at most min(K, N) = 4 reals per token
+    dict(T=1100, n_null=0),                   # M = 0: every slot real
+    dict(T=4100, d_model=320, d_ff=96, d_ff_shared=160, n_experts=8, top_k=1, n_null=0),
+])
+def test_shared_down_projection_with_the_combine(kw):
+    """The shared expert's down projection with the combine in its epilogue: full
+    compare against the oracle; a third of the tokens routed to null entirely (+inf
+    null bias) give exactly the shared expert's own output (the standalone FFN, rounded
+    once), as in the path with a separate combine."""
+    cfg = _fused_shape(**kw)
+    say(f"fused combine {kw}")
+    assert _workspace(cfg) < _workspace(cfg, null_kind="copy")   # the fused layout was chosen
+    wl = generate(cfg)
+    out = check_full(wl)
+    if cfg.n_null == 0:          # (the null logit takes no part without null copies)
+        assert (out["n_real"] == cfg.top_k).all()
+        return
+    btok = np.zeros(cfg.T, dtype=np.float32)
+    btok[::3] = np.inf
+    wl.null_bias_tok = btok
+    layer, out = run_layer(wl)
+    nul = np.isinf(btok)
+    assert (out["n_real"][nul] == 0).all() and (out["n_real"][~nul] > 0).any()
+    dims = layer.dims
+    ys = empty((cfg.T, cfg.d_model), torch.float32)
+    ws = empty((tcr.expert_ffn_workspace_bytes(dims, cfg.d_ff_shared, cfg.T),), torch.uint8)
+    tcr.moe_expert_ffn(dims, 1, cfg.d_ff_shared, cfg.T, layer.x, None, layer.ws_gate, layer.ws_up,
+                       layer.ws_down, ys, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["y"][nul], bf16_round(to_host(ys)[nul]))
+    check_routing(wl, out)
+    ref = O.layer_forward(wl, logits=out["logits"].astype(np.float64))
+    assert_layer_close(out["y"], ref["y"], TOL_BF16, True, "y with null-routed tokens")
+
+
+def test_shared_down_projection_with_the_combine_every_token_null():
+    """No routed rows at all (R = 0): the routed down projection has nothing to do and
+    the shared expert's epilogue adds nothing."""
+    cfg = _fused_shape(T=1100)
+    wl = generate(cfg)
+    wl.null_bias_tok = np.full(cfg.T, np.inf, dtype=np.float32)
+    _, out = run_layer(wl)
+    assert out["offsets"][-1] == 0
+    ref = O.layer_forward(wl, logits=out["logits"].astype(np.float64))
+    assert_layer_close(out["y"], ref["y"], TOL_BF16, True, "y, every token null")

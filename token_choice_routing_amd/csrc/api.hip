@@ -80,8 +80,27 @@ int cu_count() {
 // Layer workspace layout (byte offsets, 256-byte aligned pieces).
 struct LayerWs {
   size_t logits, topk_idx, topk_w, n_real, counts, offsets, perm_token, slot_pos, route, permute,
-      h, hs, yp, ys, tstats, rhist, total;
+      h, hs, yp, ys, row_dst, tstats, rhist, total;
 };
+
+// Down projection and combine of the layer. With a shared expert, zero-output null
+// slots and 256 x 256 tiles for both down projections (bf16), the routed outputs are
+// stored token-major (slot k of token t at row t min(K, N) + k) and the shared expert's
+// down projection adds them to its own output in its epilogue: no float32 shared
+// output round trip and no combine launch. Otherwise the two down projections share
+// one launch and the combine kernel follows. The choice depends on the dims alone, so
+// the workspace size does too.
+bool fused_combine(const moe_dims* d) {
+  if (d->dtype != MOE_BF16 || !d->d_ff_shared || d->null_kind != MOE_NULL_ZERO) return false;
+  const int64_t R = max_rows(d);
+  if ((uint64_t)R * (uint64_t)d->d_model * 4u + (1u << 20) >= (1ull << 32)) return false;
+  GemmProblem r2{}, s2{};
+  r2.groups = d->n_experts;
+  r2.max_rows = R;
+  s2.groups = 1;
+  s2.max_rows = d->T;
+  return gemm_pair_uses_pp(r2, GemmProblem{}) && gemm_pair_uses_pp(s2, GemmProblem{});
+}
 
 LayerWs layer_ws(const moe_dims* d) {
   LayerWs w{};
@@ -106,8 +125,10 @@ LayerWs layer_ws(const moe_dims* d) {
   w.permute = take(permute_ws_bytes(T, N));
   w.h = take((size_t)R * d->d_ff * e);
   w.hs = take((size_t)T * d->d_ff_shared * e);
+  const bool fused = fused_combine(d);
   w.yp = take((size_t)R * d->d_model * 4);
-  w.ys = take(d->d_ff_shared ? (size_t)T * d->d_model * 4 : 0);
+  w.ys = take(d->d_ff_shared && !fused ? (size_t)T * d->d_model * 4 : 0);
+  w.row_dst = take(fused ? (size_t)R * 4 : 0);
   const int64_t tiles = permute_nchunks(T);  // 64-token tiles of the router and the sort
   w.tstats = take((size_t)tiles * (N + 3) * 8);
   w.rhist = take((size_t)tiles * (d->top_k + 1) * 4);
@@ -511,9 +532,11 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   // 2. counting sort (histograms already written) + statistics finalisation; a few
   //    tokens take both steps in one workgroup
   AuxTiles af{tstats, rhist, ao.f, ao.P, ao.counts, ao.scalars};
+  const bool fused = fused_combine(d);
+  int32_t* row_dst = fused ? static_cast<int32_t*>(at(L.row_dst)) : nullptr;
   PermuteArgs pa{d->T, d->top_k, N, d->n_null, d->d_model, (int)elt_bytes(d), topk_idx, nullptr,
                  static_cast<int32_t*>(at(L.counts)), offsets, perm_token, slot_pos, nullptr,
-                 permute_ws, true, want_stats ? &af : nullptr};
+                 permute_ws, true, want_stats ? &af : nullptr, row_dst};
   if (route_small_ok(ra)) {
     HIP_TRY(launch_route_small(ra, &pa, s));
   } else {
@@ -535,6 +558,21 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
     s2 = GemmProblem{static_cast<const uint16_t*>(at(L.hs)), nullptr, d->T, nullptr, 1, d->T,
                      static_cast<const uint16_t*>(p->ws_down), nullptr, d->d_model,
                      d->d_ff_shared, at(L.ys)};
+  if (fused) {
+    // routed outputs token-major, then the shared expert's down projection with the
+    // combine in its epilogue (y_t = Ys_t + sum over the token's reals of w yp, in slot
+    // order, rounded once)
+    r2.out_rows = row_dst;
+    HIP_TRY(launch_gemm_pair(bf16, 2, r2, GemmProblem{}, cus, s, 2));
+    s2.out = y;
+    s2.comb_z = static_cast<const float*>(at(L.yp));
+    s2.comb_n = n_real;
+    s2.comb_w = topk_w;
+    s2.comb_k = d->top_k;
+    s2.comb_kr = std::min(d->top_k, N);
+    HIP_TRY(launch_gemm_pair(bf16, 3, s2, GemmProblem{}, cus, s, 2));
+    return MOE_OK;
+  }
   HIP_TRY(launch_gemm_pair(bf16, 2, r2, s2, cus, s, 2));
 
   // 5. weighted combine in slot order, one rounding

@@ -63,13 +63,16 @@ constexpr int kMaxGroups = 512;
 // kDown16: out = h b0^T with h IEEE half (the layer's intermediate) and b0 bf16, each
 //          weight fragment widened to half in registers (exact for |w| >= 2^-17) so the
 //          MFMA runs in half precision; float32 out.
-enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2 };
+// kDownComb: kDown16 for the shared expert of the layer, whose epilogue adds the
+//          token's weighted routed expert outputs (the combine) and stores bf16 y
+//          (256 x 256 tiles only).
+enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3 };
 
 // One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
 // fragment a (bf16 bits, or half bits for kDown16).
 template <int MODE>
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t w, bf16x8_t a, f32x16_t c) {
-  if constexpr (MODE == kDown16)
+  if constexpr (MODE == kDown16 || MODE == kDownComb)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(bf16x8_to_f16x8(w), __builtin_bit_cast(f16x8_t, a), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, c, 0, 0, 0);
@@ -605,6 +608,83 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
 // MFMAs) into the stage tile k - 4 used, which every wavefront has read by then; each
 // wavefront waits for its own loads of tile k before the barrier that opens phase 2k.
 constexpr int kPpBM = 256, kPpBN = 256, kPpBK = 32, kPpS = 4, kPpNW = 8;
+
+// The combine in the epilogue of the shared expert's down projection (kDownComb).
+// The wavefront holds, in acc[f][g], rows rbase + 32 g + l32 (g < 4) of the tile and in
+// each row the four-column groups c0 + 32 f + 8 q + 4 half (f < 2, q < 4) of the shared
+// expert's float32 output. Token row t becomes bf16(acc_t + sum over k < n_t of
+// w_tk z[t kr + k]), each term added with fmaf in slot order, as the standalone combine
+// adds them. One row block at a time, slot after slot while any of its tokens has one
+// left; a lane whose token has none left reads past the buffer's end (zero, no memory
+// access) and keeps its sum. (Two blocks at a time, 16 loads in flight per lane, made
+// the compiler spill.) The loop bound is uniform (a count of votes): a bound the
+// compiler cannot see to be uniform made it spill the K loop's load offsets.
+__device__ __forceinline__ void combine_epilogue(const GemmProblem& pr, int m0, int rows_valid, int rbase, int c0,
+                                                 f32x16_t (&acc)[2][4]) {
+  // (lane values derived here, behind opaque_v, so that nothing of this epilogue is
+  // computed ahead of the K loop and held in registers through it)
+  const int lane = opaque_v((int)threadIdx.x) & (kWave - 1), half = lane >> 5, l32 = lane & 31;
+  const int Nout = pr.n_out, kk = pr.comb_k, kr = pr.comb_kr;
+  const uint32_t z_end = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pr.max_rows * kr * Nout * 4));
+  const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(uniform_ptr(pr.comb_z), z_end);
+  int nk[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int rl = rbase + g * 32 + l32;
+    nk[g] = rl < rows_valid ? min(max(pr.comb_n[m0 + rl], 0), kr) : 0;
+  }
+  const uint32_t cofs = (uint32_t)(c0 + 4 * half) * 4u;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int rl = rbase + g * 32 + l32, tok = m0 + rl;
+    // (k < n_t <= min(K, N) <= K for every row that takes a term, so wrow[k] stays in
+    // the row; rows past the tile's last read the tile's first)
+    const float* wrow = pr.comb_w + (int64_t)(rl < rows_valid ? tok : m0) * kk;
+    const uint32_t zrow = (uint32_t)tok * (uint32_t)kr * (uint32_t)Nout * 4u + cofs;
+    // slots of the block: the most any of its tokens has (a count of wave-wide votes, so
+    // the loop bound is uniform)
+    int nmax = 0;
+    for (int k = 0; k < kr; ++k) nmax += ballot(nk[g] > k) != 0;
+    for (int k = 0; k < nmax; ++k) {
+      const bool on = k < nk[g];
+      const float w = wrow[k];
+      const uint32_t rb = on ? zrow + (uint32_t)k * (uint32_t)Nout * 4u : z_end;
+      f32x4_t z[2][4];
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          z[f][q] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rz, rb + (uint32_t)(f * 32 + 8 * q) * 4u, 0, 0));
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = acc[f][g][4 * q + j];
+            acc[f][g][4 * q + j] = on ? fmaf(w, z[f][q][j], a) : a;
+          }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int rl = rbase + g * 32 + l32;
+    if (rl >= rows_valid) continue;
+    bf16_t* crow = static_cast<bf16_t*>(pr.out) + (int64_t)(m0 + rl) * Nout;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + f * 32 + 8 * q + 4 * half;
+        if (col < Nout) {
+          const f32x16_t& v = acc[f][g];
+          *reinterpret_cast<u32x2_t*>(crow + col) =
+              u32x2_t{pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3])};
+        }
+      }
+  }
+}
+
 constexpr size_t kPpLds = (size_t)kPpS * (kPpBM + kPpBN) * kPpBK * sizeof(bf16_t);  // 128 KB
 
 // SIMD of the calling wavefront within its CU (HW_ID bits 5:4).
@@ -799,6 +879,23 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
       for (int g = 0; g < FM; ++g)
         fr[ks][FN + g] = *reinterpret_cast<const bf16x8_t*>(base + a_lane[ks] + g * kRow32);
     }
+    // half-precision down projections: the weight fragments are widened to half here,
+    // in place, so the MFMA phase needs no registers for converted copies
+    if constexpr (MODE == kDown16 || MODE == kDownComb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) fr[ks][f] = __builtin_bit_cast(bf16x8_t, bf16x8_to_f16x8(fr[ks][f]));
+    }
+  };
+  // One MFMA of a multiplied K tile; the half-precision modes' weight fragments arrive
+  // already widened (read_frags).
+  auto mfma_pp = [](bf16x8_t w, bf16x8_t a, f32x16_t c) {
+    if constexpr (MODE == kDown16 || MODE == kDownComb)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, w), __builtin_bit_cast(f16x8_t, a), c,
+                                                    0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, c, 0, 0, 0);
   };
 
   if (slot >= items) return;
@@ -837,7 +934,7 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int g = 0; g < FM; ++g) acc[f][g] = mfma32<MODE>(fr[ks][f], fr[ks][FN + g], acc[f][g]);
+          for (int g = 0; g < FM; ++g) acc[f][g] = mfma_pp(fr[ks][f], fr[ks][FN + g], acc[f][g]);
       __builtin_amdgcn_s_setprio(0);
     };
     // Before the barrier that opens tile kt's first read: this wavefront's loads of
@@ -896,7 +993,9 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
       setup(nxt, rows, t1);
       prologue(t1, nxt, sb_next);
     }
-    if (wact) {
+    if constexpr (MODE == kDownComb) {
+      if (wact) combine_epilogue(cur.second ? p1 : p0, cur.m0, cur.rows_valid, wm * (BM / 2), cur.col0 + wn * 64, acc);
+    } else if (wact) {
       const GemmProblem pr = cur.second ? p1 : p0;
       const int Nout = pr.n_out, m0 = cur.m0, rows_valid = cur.rows_valid, col0 = cur.col0;
 #pragma unroll
@@ -916,7 +1015,9 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
             }
           }
         } else {
-          float* crow = static_cast<float*>(pr.out) + (int64_t)(m0 + rl) * Nout;
+          // routed rows of the layer go to their token-major slot rows (out_rows)
+          const int64_t orow = pr.out_rows ? (int64_t)pr.out_rows[m0 + rl] : (int64_t)(m0 + rl);
+          float* crow = static_cast<float*>(pr.out) + orow * Nout;
 #pragma unroll
           for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -1194,17 +1295,36 @@ bool gemm_operands_fit(const GemmProblem& p) {
          (!p.rows_per_group || (int64_t)(p.rows_per_group + 1) * a_rb <= 0xFFFFFFFFll);
 }
 
+static bool plain_form(const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; }
+
+static bool skinny_launch(const GemmProblem& q0, const GemmProblem& q1) {
+  return plain_form(q0) && plain_form(q1) &&
+         std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows;
+}
+
+bool gemm_pair_uses_pp(const GemmProblem& p0, const GemmProblem& p1) {
+  const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
+  const GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
+  return (any0 || any1) && !skinny_launch(q0, q1) && use_pp(q0, q1);
+}
+
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
                             int num_cus, hipStream_t stream, int role) {
   const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
   if (!any0 && !any1) return hipSuccess;
   if (bf16 && (!gemm_operands_fit(p0) || !gemm_operands_fit(p1))) return hipErrorInvalidValue;
   if ((any0 ? p0.groups : 0) + (any1 ? p1.groups : 0) > kMaxGroups) return hipErrorInvalidValue;
+  // the output-row redirect and the combine epilogue exist on the 256 x 256 tiles only
+  if ((op == 3 || (any0 && p0.out_rows) || (any1 && p1.out_rows)) && (!bf16 || !gemm_pair_uses_pp(p0, p1)))
+    return hipErrorInvalidValue;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
-    auto plain_form = [](const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; };
-    if (plain_form(q0) && plain_form(q1) &&
-        std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows) {
+    if (op == 3) {
+      if (role == 2) launch_pp<kDownComb, 2>(q0, q1, num_cus, stream);
+      else return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+    if (skinny_launch(q0, q1)) {
 #define MOE_SKINNY_DISPATCH(M_)                                            \
   do {                                                                     \
     if (role == 3) launch_skinny<M_, 3>(q0, q1, num_cus, stream);          \

@@ -70,6 +70,8 @@ struct PermuteArgs {
   int32_t* ws;                    // chunk_hist [nchunks][N]
   bool hist_ready;                // chunk_hist already written (by the fused router)
   const AuxTiles* aux;            // optional statistics finalisation (fused path)
+  int32_t* row_dst;               // optional: row_dst[p] = t min(K, N) + k for the slot (t, k) at p
+                                  // (the token's reals come first, so k < min(K, N))
 };
 int permute_nchunks(int64_t T);
 size_t permute_ws_bytes(int64_t T, int N);
@@ -117,10 +119,21 @@ struct GemmProblem {
   int64_t lda, ldb;          // row strides of a and b0/b1 in elements (0 = k_dim)
   int rows_per_group;        // > 0: group e owns output rows [e*rpg, (e+1)*rpg) and reads
                              // rows [0, rpg) of a (offsets unused)
+  // Layer forward, 256 x 256 tiles only (all zero otherwise):
+  const int32_t* out_rows;   // op 2: row p is stored at output row out_rows[p] (token-major slots)
+  // op 3, the shared expert's down projection with the combine in its epilogue: output
+  // row t (bf16) = acc_t + sum over k < comb_n[t] of comb_w[t][k] * comb_z[t * comb_kr + k],
+  // float32 fmaf in slot order, rounded once.
+  const float* comb_z;       // [rows * comb_kr][n_out] float32 routed expert outputs, token-major
+  const int32_t* comb_n;     // [rows] routed slots of each token (its first slots)
+  const float* comb_w;       // [rows][comb_k] slot weights
+  int comb_k, comb_kr;
 };
 // op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
-// float32 out); op 2: out = a b0^T with a in half (the layer's h), float32 out. Both
-// problems in one launch. (float32 layers: op 2 is op 1.)
+// float32 out); op 2: out = a b0^T with a in half (the layer's h), float32 out; op 3: op 2
+// with the combine epilogue (comb_* fields), bf16 out, on the 256 x 256 tiles only (the
+// launch is refused where gemm_pair_uses_pp is false). Both problems in one launch.
+// (float32 layers: op 2 is op 1.)
 // role names the launch in profiles: 0 standalone grouped, 1 standalone single
 // segment, 2 the layer's fused launch, 3 the layer backward.
 hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const GemmProblem& p1,
@@ -130,6 +143,8 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
 // matrix (a_rows), each plus one row, must fit in 4 GB. False means the launch is
 // refused.
 bool gemm_operands_fit(const GemmProblem& p);
+// Whether a bf16 launch of these problems (plain forms) runs on the 256 x 256 tiles.
+bool gemm_pair_uses_pp(const GemmProblem& p0, const GemmProblem& p1);
 
 // Input check (validate.hip): count[0] = 0; count[0] += non-finite elements of data
 // (bf16 or float32; nan_only: NaN alone, infinities allowed).

@@ -63,7 +63,7 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
                const int32_t* __restrict__ chunk_hist, int nchunks, int64_t max_rows,
                int32_t* __restrict__ perm_token, int32_t* __restrict__ slot_pos,
                int32_t* __restrict__ counts, int32_t* __restrict__ offsets, AuxTiles aux,
-               int64_t T, int M) {
+               int64_t T, int M, int32_t* __restrict__ row_dst) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   constexpr int nw = kPermThreads / kWave;
   const int nkeys = N + 1;
@@ -234,7 +234,13 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
       if (k < N) {
         const int p = wbase[wave * N + k] + lrank[gi];
         slot_pos[f] = p;
-        if (p < max_rows) perm_token[p] = t0 + (int)((unsigned)local / (unsigned)K);  // past capacity: dropped
+        if (p < max_rows) {  // (past capacity: dropped)
+          const int tk = (int)((unsigned)local / (unsigned)K);
+          perm_token[p] = t0 + tk;
+          // token-major destination of the slot's expert output: slot k of token t is
+          // one of its reals, which come first, so k < min(K, N)
+          if (row_dst) row_dst[p] = (t0 + tk) * min(K, N) + (local - tk * K);
+        }
       } else {
         slot_pos[f] = -1;
       }
@@ -307,11 +313,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   if (stats)
     permute_kernel<true><<<grid, kPermThreads, lds, stream>>>(
         a.topk_idx, TK, a.K, a.N, chunk_hist, nchunks, max_rows, a.perm_token, a.slot_pos, a.counts,
-        a.offsets, at, a.T, a.M);
+        a.offsets, at, a.T, a.M, a.row_dst);
   else
     permute_kernel<false><<<grid, kPermThreads, lds, stream>>>(
         a.topk_idx, TK, a.K, a.N, chunk_hist, nchunks, max_rows, a.perm_token, a.slot_pos, a.counts,
-        a.offsets, at, a.T, a.M);
+        a.offsets, at, a.T, a.M, a.row_dst);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.x && a.x_perm) {
