@@ -34,6 +34,7 @@ def _gemm(mode, role):
 BENCH_KERNELS = {
     "gate_up_layer": _gemm(0, 2),
     "down_layer": _gemm(2, 2),
+    "down_combine_layer": ("void moe::grouped_gemm_pp_kernel<3, 2>",),
     "gemm_gate_up": _gemm(0, 0),
     "gemm_down": _gemm(2, 0),
     "shared_gate_up": _gemm(0, 1),
