@@ -91,7 +91,10 @@ def select(logits, N, M, K):
 def decisive_gap(logits, N, M, K):
     """Smallest |v_a - v_b| between a chosen and an unchosen pool entry; a
     routing difference between two implementations at a token is admissible
-    only where this gap is below the flip tolerance."""
+    only where this gap is below the flip tolerance. Where the nearest chosen and
+    unchosen entries are the same infinity (a +inf null logit: its copies are both
+    chosen and left over), no finite change of a logit moves the decision, which the
+    tie rule settles: the gap is taken as infinite."""
     v = _pool(logits, N, M)
     P = N + M
     if K >= P:
@@ -102,7 +105,9 @@ def decisive_gap(logits, N, M, K):
     np.put_along_axis(chosen, topk.astype(np.int64), True, axis=1)
     lo = np.where(chosen, v, np.inf).min(axis=1)
     hi = np.where(~chosen, v, -np.inf).max(axis=1)
-    return np.abs(lo - hi)
+    same_inf = np.isinf(lo) & (lo == hi)
+    gap = np.abs(np.where(same_inf, 0.0, lo) - np.where(same_inf, 0.0, hi))
+    return np.where(same_inf, np.inf, gap)
 
 
 def renorm_weights(logits, topk_idx, N):

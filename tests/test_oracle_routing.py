@@ -169,3 +169,14 @@ def test_decisive_gap_examples():
     assert O.decisive_gap(s, 3, 2, 2)[0] == pytest.approx(0.5)
     s = np.array([[3.0, 1.5, 2.0, 1.5]])           # a real tied with the null
     assert O.decisive_gap(s, 3, 2, 3)[0] == 0.0
+
+
+def test_decisive_gap_with_an_infinite_null_logit():
+    """A +inf null logit: K null copies chosen and further copies left over, all the same
+    infinity; no finite logit change moves the choice (no inf - inf = NaN)."""
+    import warnings
+    s = np.array([[3.0, 1.0, 2.0, np.inf], [3.0, 1.0, 2.0, 1.5]])
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        g = O.decisive_gap(s, 3, 4, 2)
+    assert g[0] == np.inf and g[1] == pytest.approx(1.5)
