@@ -179,4 +179,4 @@ def test_decisive_gap_with_an_infinite_null_logit():
     with warnings.catch_warnings():
         warnings.simplefilter("error")
         g = O.decisive_gap(s, 3, 4, 2)
-    assert g[0] == np.inf and g[1] == pytest.approx(1.5)
+    assert g[0] == np.inf and g[1] == pytest.approx(0.5)   # chosen 3, 2 against the null 1.5
