@@ -49,7 +49,10 @@ __device__ inline void aux_finalize(const AuxFinal& a, int64_t T, int N, int M, 
 // Called by every thread of one workgroup. All three per-tile tables (sums, expert
 // histograms, r histograms) are added column by column in one pass, so their loads
 // are in flight together. LDS: part [G][N + 3], tot [N + 3], terms [N + M] (doubles),
-// then cnt [N] and rsum [K + 1] (ints).
+// then cnt [N] and rsum [K + 1] (ints). BATCH: tiles of one column loaded at a time
+// (32 for the permutation's workgroup, whose columns are long; the one-workgroup
+// router has a single tile and a tight register budget).
+template <int BATCH = 64>
 __device__ inline void finalize_tiles(const AuxTiles& a, const int32_t* __restrict__ chunk_hist, int tiles,
                                int64_t T, int N, int M, int K, unsigned char* lds) {
   const int C = N + 3, R = K + 1, Q = C + N + R;
@@ -63,19 +66,18 @@ __device__ inline void finalize_tiles(const AuxTiles& a, const int32_t* __restri
   for (int i = threadIdx.x; i < N + R; i += blockDim.x) cnt[i] = 0;  // cnt, then rsum
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * Q; idx += blockDim.x) {
-    // item (column q, group g) adds tiles [g per, (g + 1) per) of its column, 16
-    // loads at a time
+    // item (column q, group g) adds tiles [g per, (g + 1) per) of its column, BATCH
+    // loads in flight at a time (the fp64 sums stay in tile order)
     const int q = idx % Q, g = idx / Q;
     const int ta = g * per, tb = min(tiles, (g + 1) * per);
     if (q < C) {
       double sum = 0.0;
-#pragma unroll 2
-      for (int t = ta; t < tb; t += 16) {
-        double v[16];
+      for (int t = ta; t < tb; t += BATCH) {
+        double v[BATCH];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = t + u < tb ? a.tstats[(int64_t)(t + u) * C + q] : 0.0;
+        for (int u = 0; u < BATCH; ++u) v[u] = t + u < tb ? a.tstats[(int64_t)(t + u) * C + q] : 0.0;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) sum += v[u];
+        for (int u = 0; u < BATCH; ++u) sum += v[u];
       }
       part[g * C + q] = sum;
     } else {
@@ -84,13 +86,12 @@ __device__ inline void finalize_tiles(const AuxTiles& a, const int32_t* __restri
       const int col = hist ? q - C : q - C - N, width = hist ? N : R;
       const int32_t* src = hist ? chunk_hist : a.rhist;
       int sum = 0;
-#pragma unroll 2
-      for (int t = ta; t < tb; t += 16) {
-        int v[16];
+      for (int t = ta; t < tb; t += BATCH) {
+        int v[BATCH];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = t + u < tb ? src[(int64_t)(t + u) * width + col] : 0;
+        for (int u = 0; u < BATCH; ++u) v[u] = t + u < tb ? src[(int64_t)(t + u) * width + col] : 0;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) sum += v[u];
+        for (int u = 0; u < BATCH; ++u) sum += v[u];
       }
       if (sum) atomicAdd(&cnt[q - C], sum);  // cnt[col] or rsum[col]
     }

@@ -57,8 +57,14 @@ permute_hist_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int
 // the chunk), so the order is stable (token-major, then k). Workgroup nchunks,
 // when statistics are requested, finalises them from the router's per-tile sums.
 // K groups of 64 slots per chunk; each wavefront takes a contiguous run of groups.
+// With statistics the launch has kStatsThreads per workgroup, for the finalising
+// workgroup (more tile groups summed in parallel, each a shorter chain of loads); the
+// chunk workgroups use their first kPermThreads and end the other wavefronts at once
+// (a workgroup barrier waits only for the wavefronts that have not ended).
+constexpr int kStatsThreads = 1024;
+
 template <bool STATS>
-__global__ void __launch_bounds__(kPermThreads)
+__global__ void __launch_bounds__(STATS ? kStatsThreads : kPermThreads)
 permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
                const int32_t* __restrict__ chunk_hist, int nchunks, int64_t max_rows,
                int32_t* __restrict__ perm_token, int32_t* __restrict__ slot_pos,
@@ -69,9 +75,10 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
   const int nkeys = N + 1;
   const int c = blockIdx.x;
   if (STATS && c == nchunks) {
-    finalize_tiles(aux, chunk_hist, nchunks, T, N, M, K, smem_raw);
+    finalize_tiles<32>(aux, chunk_hist, nchunks, T, N, M, K, smem_raw);
     return;
   }
+  if (STATS && threadIdx.x >= kPermThreads) return;  // whole wavefronts
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int gpw = (K + nw - 1) / nw;  // groups (of 64 slots) per wave
   const int64_t fc = (int64_t)c * kTokChunk * K;
@@ -103,7 +110,7 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
   int* wbase = wcnt + nw * nkeys;
   int* ptot = wbase + nw * N;
   int* ppre = ptot + RP * N;
-  for (int i = threadIdx.x; i < nw * nkeys; i += blockDim.x) wcnt[i] = 0;
+  for (int i = threadIdx.x; i < nw * nkeys; i += kPermThreads) wcnt[i] = 0;
   __syncthreads();
   // rank the slots: the lanes of a wavefront holding the same expert are found with
   // ballots over the key bits; a slot's rank counts the equal keys in lower lanes and
@@ -215,7 +222,7 @@ permute_kernel(const int32_t* __restrict__ topk_idx, int64_t TK, int K, int N,
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nw * N; i += blockDim.x) {
+  for (int i = threadIdx.x; i < nw * N; i += kPermThreads) {
     const int w = i / N, e = i % N;
     int b = cbase[e];
     for (int w2 = 0; w2 < w; ++w2) b += wcnt[w2 * nkeys + e];
@@ -303,7 +310,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   size_t lds = ((size_t)(2 * a.N + 1) + (size_t)nw * (a.N + 1) + (size_t)nw * a.N + (size_t)2 * RP * a.N) *
                sizeof(int);
   if (stats) {
-    const int C = a.N + 3, G = finalize_groups(a.N, a.K, kPermThreads);
+    const int C = a.N + 3, G = finalize_groups(a.N, a.K, kStatsThreads);
     const size_t st = ((size_t)G * C + C + (size_t)(a.N + a.M)) * sizeof(double) +
                       (size_t)(a.N + a.K + 1) * sizeof(int);
     lds = std::max(lds, st);
@@ -311,7 +318,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int64_t max_rows = a.T * (int64_t)std::min(a.K, a.N);
   const unsigned grid = (unsigned)(nchunks + (stats ? 1 : 0));
   if (stats)
-    permute_kernel<true><<<grid, kPermThreads, lds, stream>>>(
+    permute_kernel<true><<<grid, kStatsThreads, lds, stream>>>(
         a.topk_idx, TK, a.K, a.N, chunk_hist, nchunks, max_rows, a.perm_token, a.slot_pos, a.counts,
         a.offsets, at, a.T, a.M, a.row_dst);
   else

@@ -869,7 +869,7 @@ route_small_kernel(RouteKernelArgs a, SmallPermute pm) {
   }
   if (!pm.aux.tstats) return;
   __syncthreads();  // the LDS is the statistics' scratch from here
-  finalize_tiles(pm.aux, a.chunk_hist, 1, a.T, N, a.M, K, smem_raw);
+  finalize_tiles<16>(pm.aux, a.chunk_hist, 1, a.T, N, a.M, K, smem_raw);
 }
 
 // 32-expert tiles per scoring workgroup: all of them when N <= 64, else pairs.
