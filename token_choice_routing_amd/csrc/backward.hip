@@ -403,16 +403,35 @@ scatter_dx_kernel(const float* __restrict__ dx_perm, const int32_t* __restrict__
         acc[tt] += v[3] * w[3];
       }
     }
+    // the slots' rows: four tokens and eight slots at a time, every load issued before
+    // the first add (a load per slot, added in slot order, was a chain of round trips)
 #pragma unroll
-    for (int tt = 0; tt < kScatterTok; ++tt) {
-      if (tt >= nt) break;
-      const int64_t t = t0 + tt;
-      float v = dx_shared ? dx_shared[t * d + c] : 0.0f;
-      for (int k = 0; k < K; ++k) {
-        const int32_t p = sp[tt][k];
-        if (p >= 0 && p < R) v += dx_perm[(int64_t)p * d + c];
+    for (int tg = 0; tg < kScatterTok; tg += 4) {
+      if (tg >= nt) break;
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = (tg + u < nt && dx_shared) ? dx_shared[(t0 + tg + u) * d + c] : 0.0f;
+      for (int k0 = 0; k0 < K; k0 += 8) {
+        float g[4][8];
+        bool on[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int32_t p = (tg + u < nt && k0 + j < K) ? sp[tg + u][k0 + j] : -1;
+            on[u][j] = p >= 0 && p < R;
+            g[u][j] = on[u][j] ? dx_perm[(int64_t)p * d + c] : 0.0f;
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (on[u][j]) v[u] += g[u][j];
       }
-      dx[t * d + c] = v + acc[tt];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (tg + u < nt) dx[(t0 + tg + u) * d + c] = v[u] + acc[tg + u];
     }
   }
 }
