@@ -30,12 +30,19 @@ def _clear(layer):
 @pytest.mark.parametrize("first,second", [
     (("qwen3_0p6b_rho1", 1500), ("qwen3_0p6b_rho1", 333)),
     (("small_null_pool", 900), ("small_null_pool", 1)),
+    # the shared expert's down projection with the combine (2100 tokens), then the
+    # separate combine (600 tokens: too few rows per expert for the large tiles)
+    (("fused_combine", 2100), ("fused_combine", 600)),
 ])
 def test_noalloc_matches_workspace_forward(first, second):
-    small = Config(name="small_null_pool", T=900, d_model=256, n_experts=16, n_null=48, top_k=6,
-                   d_ff=192, d_ff_shared=64, dtype="bf16", w_std=0.05, seed=4)
+    local = {
+        "small_null_pool": Config(name="small_null_pool", T=900, d_model=256, n_experts=16, n_null=48, top_k=6,
+                                  d_ff=192, d_ff_shared=64, dtype="bf16", w_std=0.05, seed=4),
+        "fused_combine": Config(name="fused_combine", T=2100, d_model=256, n_experts=4, n_null=4, top_k=2,
+                                d_ff=128, d_ff_shared=64, dtype="bf16", w_std=0.05, seed=6),
+    }
     for name, T in (first, second):
-        cfg = small if name == "small_null_pool" else CONFIGS[name]
+        cfg = local.get(name) or CONFIGS[name]
         say(f"noalloc {name} T={T}")
         wl = generate(cfg, T=min(T, cfg.T))
         if name == "small_null_pool":
