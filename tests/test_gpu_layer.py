@@ -367,6 +367,8 @@ def _workspace(cfg, **kw):
     dict(T=1100, top_k=8, n_null=8),          # K > N: at most min(K, N) = 4 reals per token
     dict(T=1100, n_null=0),                   # M = 0: every slot real
     dict(T=4100, d_model=320, d_ff=96, d_ff_shared=160, n_experts=8, top_k=1, n_null=0),
+    dict(T=512, n_experts=1, top_k=1, n_null=1),           # one expert, exactly 512 rows of it
+    dict(T=700, d_model=64, d_ff=64, d_ff_shared=32, n_experts=1, top_k=2, n_null=3),  # narrow rows
 ])
 def test_shared_down_projection_with_the_combine(kw):
     """The shared expert's down projection with the combine in its epilogue: full
