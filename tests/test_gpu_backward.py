@@ -47,6 +47,12 @@ CASES = {
     # 512 output rows per expert: the weight gradients take the 256 x 256 ping-pong
     # tiles (segments of ~150 rows: ragged K ranges of a few 32-wide K tiles)
     "pp_wgrad": dict(T=640, d_model=512, n_experts=8, n_null=8, top_k=2, d_ff=512, d_ff_shared=512),
+    # 1024 rows per expert: the data gradients read the weights K-major on the 256 x 256
+    # tiles (W_d for U; W_g then W_u, split at K = d_ff = 160, for da), partial column tiles
+    "kmajor": dict(T=2048, d_model=256, n_experts=4, n_null=4, top_k=2, d_ff=160, d_ff_shared=96),
+    # the same without a shared expert, d_model = 96 (K of U three K tiles, a partial
+    # column tile of da)
+    "kmajor_narrow": dict(T=1536, d_model=96, n_experts=2, n_null=2, top_k=2, d_ff=64, d_ff_shared=0),
 }
 
 

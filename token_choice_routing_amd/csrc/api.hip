@@ -141,6 +141,7 @@ LayerWs layer_ws(const moe_dims* d) {
 // activations transposed per segment for the weight gradients (segments padded to 8
 // columns: Rp = R + 8 N columns at most).
 struct BwdWs {
+  bool km;  // the data gradients read the weights K-major (no transposed copies)
   LayerWs fwd;
   size_t f, g, u, h, dyp, wperm, rslot, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
   size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, kofs_s, part_sd, part_sg, part_su, total;
@@ -158,8 +159,52 @@ inline int shared_splits(int64_t T) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(T >= 8192 ? 16 : 32, (T + chunk - 1) / chunk));
 }
 
+// The backward's data-gradient products U = dy W_d and da = [dg | du] [W_g ; W_u] (and
+// the shared expert's) as K-major weight problems: W_d [N][d][F] is K-major for U (K =
+// d), W_g and W_u [N][F][d] are the two K halves of [W_g ; W_u] (K = 2F).
+struct DgradKm {
+  GemmProblem h3, hs3, a4, as4;
+};
+static DgradKm dgrad_kmajor(const moe_dims* d, const moe_layer_params* p, const void* dy, const int32_t* perm_token,
+                            const int32_t* offsets, const void* dgu, const void* dgus, void* dh, void* dhs,
+                            void* dxp, void* dxs) {
+  const int64_t T = d->T, R = max_rows(d);
+  const int dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared, N = d->n_experts;
+  auto bf = [](const void* q) { return static_cast<const uint16_t*>(q); };
+  DgradKm k{};
+  k.h3 = GemmProblem{bf(dy), perm_token, T, offsets, N, R, bf(p->w_down), nullptr, F, dm, dh};
+  k.h3.b_kmajor = 1;
+  k.h3.k_split = dm;
+  k.a4 = GemmProblem{bf(dgu), nullptr, R, offsets, N, R, bf(p->w_gate), bf(p->w_up), dm, 2 * F, dxp};
+  k.a4.b_kmajor = 1;
+  k.a4.k_split = F;
+  if (Fs) {
+    k.hs3 = GemmProblem{bf(dy), nullptr, T, nullptr, 1, T, bf(p->ws_down), nullptr, Fs, dm, dhs};
+    k.hs3.b_kmajor = 1;
+    k.hs3.k_split = dm;
+    k.as4 = GemmProblem{bf(dgus), nullptr, T, nullptr, 1, T, bf(p->ws_gate), bf(p->ws_up), dm, 2 * Fs, dxs};
+    k.as4.b_kmajor = 1;
+    k.as4.k_split = Fs;
+  }
+  return k;
+}
+// Whether both data-gradient launches of a layer of these dimensions take the K-major
+// form (the launcher's conditions, checked on stand-in pointers).
+static bool dgrad_kmajor_ok(const moe_dims* d) {
+  static const uint16_t stand_in[8] = {};
+  const void* q = stand_in;
+  void* o = const_cast<uint16_t*>(stand_in);
+  moe_layer_params p{};
+  p.w_down = p.w_gate = p.w_up = q;
+  p.ws_down = p.ws_gate = p.ws_up = q;
+  const int32_t* i = reinterpret_cast<const int32_t*>(stand_in);
+  const DgradKm k = dgrad_kmajor(d, &p, q, i, i, q, q, o, o, o, o);
+  return gemm_kmajor_ok(k.h3, k.hs3) && gemm_kmajor_ok(k.a4, k.as4);
+}
+
 BwdWs bwd_ws(const moe_dims* d) {
   BwdWs w{};
+  w.km = dgrad_kmajor_ok(d);
   w.fwd = layer_ws(d);
   const int64_t T = d->T, R = max_rows(d), dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
   const int N = d->n_experts, M = d->n_null;
@@ -180,8 +225,8 @@ BwdWs bwd_ws(const moe_dims* d) {
   w.rslot = take((size_t)R * 4);
   w.dw = take((size_t)T * d->top_k * 4);
   w.ds = take((size_t)T * (N + 1) * 4);
-  w.wdT = take((size_t)N * F * dm * 2);
-  w.wguT = take((size_t)N * dm * 2 * F * 2);
+  w.wdT = w.km ? 0 : take((size_t)N * F * dm * 2);
+  w.wguT = w.km ? 0 : take((size_t)N * dm * 2 * F * 2);
   w.dh = take((size_t)R * F * 4);
   w.dgu = take((size_t)R * 2 * F * 2);
   w.dxp = take((size_t)R * dm * 4);
@@ -198,8 +243,8 @@ BwdWs bwd_ws(const moe_dims* d) {
     w.dhs = take((size_t)T * Fs * 4);
     w.dgus = take((size_t)T * 2 * Fs * 2);
     w.dxs = take((size_t)T * dm * 4);
-    w.wsdT = take((size_t)Fs * dm * 2);
-    w.wsguT = take((size_t)dm * 2 * Fs * 2);
+    w.wsdT = w.km ? 0 : take((size_t)Fs * dm * 2);
+    w.wsguT = w.km ? 0 : take((size_t)dm * 2 * Fs * 2);
     w.xT = take((size_t)dm * w.Tp * 2);
     w.dyT = take((size_t)dm * w.Tp * 2);
     w.hsT = take((size_t)Fs * w.Tp * 2);
@@ -724,14 +769,19 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
   HIP_TRY(launch_slot_rows(dy, slot_pos, topk_w, T, K, (int)dm, R, at(W.dyp), fp(W.wperm), ip(W.rslot), fp(W.dw),
                            s));
 
-  // 5. transposed bf16 weights: W_d^T [N][F][d]; [W_g ; W_u]^T [N][d][2F]
-  HIP_TRY(launch_transpose(p->w_down, N, dm, F, at(W.wdT), dm, 0, F * dm, s));
-  HIP_TRY(launch_transpose(p->w_gate, N, F, dm, at(W.wguT), 2 * F, 0, dm * 2 * F, s));
-  HIP_TRY(launch_transpose(p->w_up, N, F, dm, at(W.wguT), 2 * F, F, dm * 2 * F, s));
-  if (Fs) {
-    HIP_TRY(launch_transpose(p->ws_down, 1, dm, Fs, at(W.wsdT), dm, 0, 0, s));
-    HIP_TRY(launch_transpose(p->ws_gate, 1, Fs, dm, at(W.wsguT), 2 * Fs, 0, 0, s));
-    HIP_TRY(launch_transpose(p->ws_up, 1, Fs, dm, at(W.wsguT), 2 * Fs, Fs, 0, s));
+  // 5. the data gradients' weights: read K-major in place when the launches allow it
+  // (W.km), else transposed copies: W_d^T [N][F][d]; [W_g ; W_u]^T [N][d][2F]
+  const DgradKm km = dgrad_kmajor(d, p, dy, perm_token, offsets, at(W.dgu), Fs ? at(W.dgus) : nullptr, at(W.dh),
+                                  Fs ? at(W.dhs) : nullptr, at(W.dxp), Fs ? at(W.dxs) : nullptr);
+  if (!W.km) {
+    HIP_TRY(launch_transpose(p->w_down, N, dm, F, at(W.wdT), dm, 0, F * dm, s));
+    HIP_TRY(launch_transpose(p->w_gate, N, F, dm, at(W.wguT), 2 * F, 0, dm * 2 * F, s));
+    HIP_TRY(launch_transpose(p->w_up, N, F, dm, at(W.wguT), 2 * F, F, dm * 2 * F, s));
+    if (Fs) {
+      HIP_TRY(launch_transpose(p->ws_down, 1, dm, Fs, at(W.wsdT), dm, 0, 0, s));
+      HIP_TRY(launch_transpose(p->ws_gate, 1, Fs, dm, at(W.wsguT), 2 * Fs, 0, 0, s));
+      HIP_TRY(launch_transpose(p->ws_up, 1, Fs, dm, at(W.wsguT), 2 * Fs, Fs, 0, s));
+    }
   }
 
   // 6. U = dy W_d on the routed rows (dy read through perm_token) and dh_s = dy W_sd;
@@ -744,6 +794,10 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
   if (Fs)
     hs3 = GemmProblem{static_cast<const uint16_t*>(dy), nullptr, T, nullptr, 1, T, bf(W.wsdT), nullptr, (int)Fs,
                       (int)dm, at(W.dhs)};
+  if (W.km) {
+    h3 = km.h3;
+    hs3 = km.hs3;
+  }
   HIP_TRY(launch_gemm_pair(true, 1, h3, hs3, cus, s, 3));
   HIP_TRY(launch_swiglu_bwd_routed(fp(W.g), fp(W.u), fp(W.dh), at(W.h), fp(W.wperm), ip(W.rslot), offsets, N, R,
                                     (int)F, at(W.dgu), fp(W.dw), s));
@@ -756,6 +810,10 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
   if (Fs)
     as4 = GemmProblem{bf(W.dgus), nullptr, T, nullptr, 1, T, bf(W.wsguT), nullptr, (int)dm, (int)(2 * Fs),
                       at(W.dxs)};
+  if (W.km) {
+    a4 = km.a4;
+    as4 = km.as4;
+  }
   HIP_TRY(launch_gemm_pair(true, 1, a4, as4, cus, s, 3));
 
   // 8. dx = sum over the token's slots of da + shared da + ds W_r; dW_r = ds^T x

@@ -66,7 +66,11 @@ constexpr int kMaxGroups = 512;
 // kDownComb: kDown16 for the shared expert of the layer, whose epilogue adds the
 //          token's weighted routed expert outputs (the combine) and stores bf16 y
 //          (256 x 256 tiles only).
-enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3 };
+// kPlainKM: kPlain with K-major weights (GemmProblem::b_kmajor; 256 x 256 tiles only): the
+//          weight tile is staged in LDS as [K][weight rows] and its MFMA fragments are
+//          read with the transposing LDS load (ds_read_b64_tr_b16), so no transposed copy
+//          of the weights is written.
+enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4 };
 
 // One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
 // fragment a (bf16 bits, or half bits for kDown16).
@@ -609,6 +613,47 @@ grouped_gemm_bf16_kernel(GemmProblem p0, GemmProblem p1) {
 // wavefront waits for its own loads of tile k before the barrier that opens phase 2k.
 constexpr int kPpBM = 256, kPpBN = 256, kPpBK = 32, kPpS = 4, kPpNW = 8;
 
+// K-major weight stages (kPlainKM): 1 KB piece i of a stage's weight region holds K rows
+// 2i and 2i + 1 of the tile (BN weight rows of 2 bytes each); lanes 0-31 fill the first.
+__device__ __forceinline__ int kmajor_krow(int i, int lane) { return 2 * i + (lane >> 5); }
+
+// The four bf16 MFMA weight fragments of one K tile (two 16-wide K steps x two 32-row
+// weight blocks) from a K-major weight stage [32 K rows][BN], by transposing LDS reads
+// (ds_read_b64_tr_b16): within each 16-lane block the read gives lane i element i % 4
+// of the 4-element pieces that lanes 4 j + i / 4 (j = 0..3) address, so lanes whose
+// addresses walk K rows (lane / 4) and 4-column steps (lane % 4) each receive one
+// column's four consecutive K values; two reads (K rows + 0..3, + 4..7) make a fragment.
+// a0 / a1: the lane's LDS byte addresses (from the workgroup's LDS base) for weight
+// blocks 0 / 1 at the tile's first K row; the K steps are 16 rows (16 BN 2 bytes) apart.
+// Inline assembly because the compiler, which cannot tell these reads from the
+// buffer->LDS loads still in flight, would otherwise wait for every outstanding load
+// before them; the stage was waited for (and a barrier passed) before this call. All
+// eight reads are issued before one wait for them inside the same statement, so no
+// output register is seen before its read has landed.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+template <int BN>
+__device__ __forceinline__ void kmajor_frags(uint32_t a0, uint32_t a1, bf16x8_t& f00, bf16x8_t& f01,
+                                             bf16x8_t& f10, bf16x8_t& f11) {
+  constexpr int kStep = 16 * BN * 2, kHalf = 4 * BN * 2;
+  s16x4_t r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1), "i"(kHalf), "i"(kStep), "i"(kStep + kHalf));
+  f00 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  f01 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3, 4, 5, 6, 7));
+  f10 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[4], r[5], 0, 1, 2, 3, 4, 5, 6, 7));
+  f11 = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r[6], r[7], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // The combine in the epilogue of the shared expert's down projection (kDownComb).
 // The wavefront holds, in acc[f][g], rows rbase + 32 g + l32 (g < 4) of the tile and in
 // each row the four-column groups c0 + 32 f + 8 q + 4 half (f < 2, q < 4) of the shared
@@ -705,6 +750,8 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
   constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, S = kPpS, NW = kPpNW;
   constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
   constexpr int FM = 4, FN = 2;                      // 32-row blocks per wavefront: activations, weights
+  constexpr bool KM = MODE == kPlainKM;              // K-major weights
+  constexpr bool ROWS = MODE == kDown16 && ROLE == 2; // output rows redirected (out_rows)
   constexpr int CPR = BK / 8, RPI = kWave / CPR;     // 16-byte chunks per row; rows per load instruction
   constexpr int J = (BM + BN) / (RPI * NW);          // load instructions per stage per wavefront (4)
   constexpr int JA = BM / (RPI * NW);                // of which fill activation rows (2)
@@ -803,6 +850,8 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t a_end, b_end;
     uint32_t off[J];
+    uint32_t b_row;  // K-major weights: bytes per K row
+    int k_split;     // K-major weights: K rows read from rb0 (the rest from rb1)
   };
   auto setup = [&](const Where& w, const int (&arow)[JA], Tile& t) {
     const GemmProblem pr = w.second ? p1 : p0;
@@ -812,10 +861,21 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     const int64_t wofs = pr.k_offsets ? (int64_t)w.kofs : (int64_t)w.ge * Nout * ldb;
     const int64_t abase = pr.a_rows ? 0 : w.m0 - (pr.rows_per_group ? (int64_t)w.ge * pr.rows_per_group : 0);
     t.a_end = __builtin_amdgcn_readfirstlane((uint32_t)((pr.a_rows ? pr.a_nrows : w.rows_valid) * a_rb));
-    t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)Nout * b_rb);
     t.ra = buffer_rsrc(uniform_ptr(pr.a + abase * lda + w.kofs), t.a_end);
-    t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + wofs), t.b_end);
-    t.rb1 = buffer_rsrc(uniform_ptr(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs), t.b_end);
+    if constexpr (KM) {
+      // group ge's [k_split][Nout] matrix of b0 and [k_dim - k_split][Nout] matrix of b1;
+      // one end (the larger matrix) serves both, every K row a lane reads being inside its own
+      const int k0 = pr.k_split, k1 = pr.k_dim - pr.k_split;
+      t.b_row = __builtin_amdgcn_readfirstlane((uint32_t)Nout * 2u);
+      t.k_split = __builtin_amdgcn_readfirstlane(k0);
+      t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)max(k0, k1) * t.b_row);
+      t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + (int64_t)w.ge * k0 * Nout), t.b_end);
+      t.rb1 = buffer_rsrc(uniform_ptr(k1 > 0 ? pr.b1 + (int64_t)w.ge * k1 * Nout : pr.b0), t.b_end);
+    } else {
+      t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)Nout * b_rb);
+      t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + wofs), t.b_end);
+      t.rb1 = buffer_rsrc(uniform_ptr(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs), t.b_end);
+    }
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int r = RPI * (wave + NW * j) + lrow;
@@ -824,10 +884,22 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     }
 #pragma unroll
     for (int j = JA; j < J; ++j) {
-      const int r = RPI * (wave + NW * j) + lrow - BM;
-      const int c = MODE == kSwiGLU ? r % OC : r;
-      const int n = w.col0 + c;
-      t.off[j] = (c < ocp && n < Nout ? (uint32_t)n * b_rb : t.b_end) + lk * 2;
+      if constexpr (KM) {
+        // 1 KB piece i of the stage's weight region holds K rows 2i and 2i + 1 (512 bytes
+        // each: 256 weight rows); the lane fills physical 16-byte chunk lane % 32 of its
+        // row with the logical chunk the swizzle of the fragment reads places there (the
+        // 64-byte column groups XOR-ed with k % 4)
+        const int krow = kmajor_krow(wave + NW * (j - JA), lane);
+        const int p16 = lane & 31;
+        const int c = ((p16 & 3) | (((p16 >> 2) ^ (krow & 3)) << 2)) * 8;
+        const int n = w.col0 + c;
+        t.off[j] = c < ocp && n < Nout ? (uint32_t)krow * t.b_row + (uint32_t)n * 2u : t.b_end;
+      } else {
+        const int r = RPI * (wave + NW * j) + lrow - BM;
+        const int c = MODE == kSwiGLU ? r % OC : r;
+        const int n = w.col0 + c;
+        t.off[j] = (c < ocp && n < Nout ? (uint32_t)n * b_rb : t.b_end) + lk * 2;
+      }
     }
   };
   // This wavefront's J loads of K tile kt into stage st. Chunks past the K range,
@@ -841,6 +913,16 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     const bool in = kt < w.nk && (int)(kt * BK + lk) < w.Kdim;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      if (KM && j >= JA) {
+        // K rows [kt BK, kt BK + BK) of the weights: from rb0 below k_split, else rb1
+        // (k_split and k_dim are multiples of BK, so a tile is whole and never straddles)
+        const int kg = kt * BK;
+        const bool second = kg >= t.k_split;
+        const uint32_t kbw = (uint32_t)(second ? kg - t.k_split : kg) * t.b_row;
+        buffer_load_lds16(second ? t.rb1 : t.rb0, kt < w.nk ? t.off[j] + kbw : t.b_end,
+                          smem + st * STAGE + RPI * (wave + NW * j) * BK);
+        continue;
+      }
       const bool up = MODE == kSwiGLU && j >= JA && RPI * (wave + NW * j) - BM >= OC;
       const uint32_t end = j < JA ? t.a_end : t.b_end;
       buffer_load_lds16(j < JA ? t.ra : up ? t.rb1 : t.rb0, in ? t.off[j] + kb : end,
@@ -864,13 +946,37 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     a_lane[ks] = (uint32_t)lds_off<BK>(wm * (BM / 2) + l32, ks * 2 + half) * 2;
-    b_lane[ks] = (uint32_t)(BM * BK + lds_off<BK>((MODE == kSwiGLU ? wn * 32 : wn * 64) + l32, ks * 2 + half)) * 2;
+    if constexpr (KM) {
+      // K-major weight region [BK][BN]: here b_lane[f] is the lane's transposing-read
+      // address of weight block f (rows wn 64 + 32 f ...), K step and half folded into
+      // immediates (their K offsets are multiples of 4, so the swizzle term k % 4 is the
+      // lane's own). Lane l of each 16-lane block b addresses K row 8 (b / 2) + (l % 16) / 4
+      // and weight rows 16 (b % 2) + 4 (l % 4) .. + 3 of the block; the read hands lane l
+      // the four K values of weight row l % 32 (the MFMA's fragment layout).
+      const int s16 = lane & 15;
+      const int kl = 8 * (lane >> 5) + (s16 >> 2), nl = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+      const int chunk = 2 * wn + ks;  // the wavefront's 32-row weight block ks
+      b_lane[ks] = (uint32_t)(BM * BK + kl * BN + ((chunk ^ (kl & 3)) * 32) + nl) * 2;
+    } else {
+      b_lane[ks] = (uint32_t)(BM * BK + lds_off<BK>((MODE == kSwiGLU ? wn * 32 : wn * 64) + l32, ks * 2 + half)) * 2;
+    }
   }
   constexpr uint32_t kRow32 = 32 * BK * 2;                                   // bytes between 32-row blocks
   constexpr uint32_t kWStep = MODE == kSwiGLU ? (BN / 2) * BK * 2 : kRow32;  // gate -> up, or block -> block
   typedef bf16x8_t Frags[2][FN + FM];  // per 16-wide K step: FN weight fragments, then FM activation ones
   auto read_frags = [&](int st, Frags& fr) {
     const char* base = reinterpret_cast<const char*>(smem) + st * (STAGE * 2);
+    if constexpr (KM) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int g = 0; g < FM; ++g)
+          fr[ks][FN + g] = *reinterpret_cast<const bf16x8_t*>(base + a_lane[ks] + g * kRow32);
+      // LDS byte address of the stage (the dynamic LDS follows the static tile table)
+      const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)base);
+      kmajor_frags<BN>(sb + b_lane[0], sb + b_lane[1], fr[0][0], fr[0][1], fr[1][0], fr[1][1]);
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -1015,8 +1121,10 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
             }
           }
         } else {
-          // routed rows of the layer go to their token-major slot rows (out_rows)
-          const int64_t orow = pr.out_rows ? (int64_t)pr.out_rows[m0 + rl] : (int64_t)(m0 + rl);
+          // routed rows of the layer go to their token-major slot rows (out_rows; compiled
+          // only into the layer's down projection launch, since the load's wait would
+          // also wait for the next item's first tiles, issued just before)
+          const int64_t orow = ROWS && pr.out_rows ? (int64_t)pr.out_rows[m0 + rl] : (int64_t)(m0 + rl);
           float* crow = static_cast<float*>(pr.out) + orow * Nout;
 #pragma unroll
           for (int f = 0; f < FN; ++f)
@@ -1290,16 +1398,32 @@ static void launch_skinny(const GemmProblem& q0, const GemmProblem& q1, int num_
 bool gemm_operands_fit(const GemmProblem& p) {
   if (p.groups == 0 || p.max_rows <= 0) return true;
   const int64_t a_rb = (p.lda ? p.lda : p.k_dim) * 2, b_rb = (p.ldb ? p.ldb : p.k_dim) * 2;
-  return (int64_t)(p.n_out + 1) * b_rb <= 0xFFFFFFFFll &&
+  const int64_t b_bytes = p.b_kmajor ? (int64_t)(std::max(p.k_split, p.k_dim - p.k_split) + 1) * p.n_out * 2
+                                     : (int64_t)(p.n_out + 1) * b_rb;
+  return b_bytes <= 0xFFFFFFFFll &&
          (!p.a_rows || (p.a_nrows + 1) * a_rb <= 0xFFFFFFFFll) &&
          (!p.rows_per_group || (int64_t)(p.rows_per_group + 1) * a_rb <= 0xFFFFFFFFll);
 }
 
 static bool plain_form(const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; }
 
+// A K-major weight problem (op 1) the 256 x 256 kernel takes: plain form otherwise,
+// whole 8-column chunks per row, whole K tiles, the b0 / b1 boundary on a K tile boundary.
+static bool kmajor_ok(const GemmProblem& p) {
+  if (p.groups == 0 || p.max_rows <= 0) return true;
+  return p.b_kmajor && plain_form(p) && !p.out_rows && p.n_out % 8 == 0 && p.k_split > 0 &&
+         p.k_split % kPpBK == 0 && p.k_dim % kPpBK == 0 && p.k_split <= p.k_dim &&
+         (p.k_split < p.k_dim) == (p.b1 != nullptr);
+}
+
 static bool skinny_launch(const GemmProblem& q0, const GemmProblem& q1) {
   return plain_form(q0) && plain_form(q1) &&
          std::max(rows_per_group_bound(q0), rows_per_group_bound(q1)) <= kSkinnyMaxRows;
+}
+
+bool gemm_kmajor_ok(const GemmProblem& p0, const GemmProblem& p1) {
+  const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
+  return (!any0 || kmajor_ok(p0)) && (!any1 || kmajor_ok(p1)) && gemm_pair_uses_pp(p0, p1);
 }
 
 bool gemm_pair_uses_pp(const GemmProblem& p0, const GemmProblem& p1) {
@@ -1314,11 +1438,20 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   if (!any0 && !any1) return hipSuccess;
   if (bf16 && (!gemm_operands_fit(p0) || !gemm_operands_fit(p1))) return hipErrorInvalidValue;
   if ((any0 ? p0.groups : 0) + (any1 ? p1.groups : 0) > kMaxGroups) return hipErrorInvalidValue;
-  // the output-row redirect and the combine epilogue exist on the 256 x 256 tiles only
-  if ((op == 3 || (any0 && p0.out_rows) || (any1 && p1.out_rows)) && (!bf16 || !gemm_pair_uses_pp(p0, p1)))
-    return hipErrorInvalidValue;
+  // the output-row redirect (the layer's down projection launch) and the combine
+  // epilogue exist on the 256 x 256 tiles only
+  const bool redirect = (any0 && p0.out_rows) || (any1 && p1.out_rows);
+  if ((op == 3 || redirect) && (!bf16 || !gemm_pair_uses_pp(p0, p1))) return hipErrorInvalidValue;
+  if (redirect && (op != 2 || role != 2)) return hipErrorInvalidValue;
+  const bool km = (any0 && p0.b_kmajor) || (any1 && p1.b_kmajor);
+  if (km && (!bf16 || op != 1 || !gemm_kmajor_ok(p0, p1))) return hipErrorInvalidValue;
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
+    if (km) {
+      if (role == 3) launch_pp<kPlainKM, 3>(q0, q1, num_cus, stream);
+      else launch_pp<kPlainKM, 0>(q0, q1, num_cus, stream);
+      return hipGetLastError();
+    }
     if (op == 3) {
       if (role == 2) launch_pp<kDownComb, 2>(q0, q1, num_cus, stream);
       else return hipErrorInvalidValue;

@@ -120,7 +120,7 @@ struct GemmProblem {
   int rows_per_group;        // > 0: group e owns output rows [e*rpg, (e+1)*rpg) and reads
                              // rows [0, rpg) of a (offsets unused)
   // Layer forward, 256 x 256 tiles only (all zero otherwise):
-  const int32_t* out_rows;   // op 2: row p is stored at output row out_rows[p] (token-major slots)
+  const int32_t* out_rows;   // op 2, role 2: row p is stored at output row out_rows[p] (token-major slots)
   // op 3, the shared expert's down projection with the combine in its epilogue: output
   // row t (bf16) = acc_t + sum over k < comb_n[t] of comb_w[t][k] * comb_z[t * comb_kr + k],
   // float32 fmaf in slot order, rounded once.
@@ -128,9 +128,17 @@ struct GemmProblem {
   const int32_t* comb_n;     // [rows] routed slots of each token (its first slots)
   const float* comb_w;       // [rows][comb_k] slot weights
   int comb_k, comb_kr;
+  // K-major weights (op 1 on 256 x 256 tiles only): group e's weights are b0's matrix
+  // e of [k_split][n_out] for K rows [0, k_split) and, when k_split < k_dim, b1's matrix
+  // e of [k_dim - k_split][n_out] for the rest: B[n][k] = b0[e][k][n] (b1[e][k -
+  // k_split][n]). A row-major weight [n_out][k_dim] of the other modes is the transpose
+  // of this layout; the backward's data gradients read the forward's weights this way.
+  // n_out a multiple of 8, k_split and k_dim multiples of 32.
+  int b_kmajor, k_split;
 };
 // op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
-// float32 out); op 2: out = a b0^T with a in half (the layer's h), float32 out; op 3: op 2
+// float32 out; with b_kmajor set in both problems, B read from K-major b0 / b1, 256 x 256
+// tiles only); op 2: out = a b0^T with a in half (the layer's h), float32 out; op 3: op 2
 // with the combine epilogue (comb_* fields), bf16 out, on the 256 x 256 tiles only (the
 // launch is refused where gemm_pair_uses_pp is false). Both problems in one launch.
 // (float32 layers: op 2 is op 1.)
@@ -145,6 +153,8 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
 bool gemm_operands_fit(const GemmProblem& p);
 // Whether a bf16 launch of these problems (plain forms) runs on the 256 x 256 tiles.
 bool gemm_pair_uses_pp(const GemmProblem& p0, const GemmProblem& p1);
+// Whether an op 1 launch of these K-major weight problems is taken (else it is refused).
+bool gemm_kmajor_ok(const GemmProblem& p0, const GemmProblem& p1);
 
 // Input check (validate.hip): count[0] = 0; count[0] += non-finite elements of data
 // (bf16 or float32; nan_only: NaN alone, infinities allowed).
