@@ -53,6 +53,9 @@ CASES = {
     # the same without a shared expert, d_model = 96 (K of U three K tiles, a partial
     # column tile of da)
     "kmajor_narrow": dict(T=1536, d_model=96, n_experts=2, n_null=2, top_k=2, d_ff=64, d_ff_shared=0),
+    # weight gradients with both operands K-major (at least 512 output rows per group) on
+    # ragged tiles: 520 and 544 rows (partial row and column tiles), segments of ~300 rows
+    "kmajor_wgrad_ragged": dict(T=600, d_model=520, n_experts=4, n_null=4, top_k=2, d_ff=544, d_ff_shared=520),
 }
 
 

@@ -141,9 +141,10 @@ LayerWs layer_ws(const moe_dims* d) {
 // activations transposed per segment for the weight gradients (segments padded to 8
 // columns: Rp = R + 8 N columns at most).
 struct BwdWs {
-  bool km;  // the data gradients read the weights K-major (no transposed copies)
+  bool km;   // the data gradients read the weights K-major (no transposed copies)
+  bool km2;  // the weight gradients read both operands K-major (no transposed segments)
   LayerWs fwd;
-  size_t f, g, u, h, dyp, wperm, rslot, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart;
+  size_t f, g, u, h, dyp, wperm, rslot, dw, ds, wdT, wguT, dh, dgu, dxp, kofs, xpT, dypT, hT, dguT, rpart, xp;
   size_t gs, us, hs, dhs, dgus, dxs, wsdT, wsguT, xT, dyT, hsT, dgusT, kofs_s, part_sd, part_sg, part_su, total;
   int64_t Rp, Tp;
   int S;  // K chunks of the shared expert's weight gradients (its K is all T tokens)
@@ -202,9 +203,56 @@ static bool dgrad_kmajor_ok(const moe_dims* d) {
   return gemm_kmajor_ok(k.h3, k.hs3) && gemm_kmajor_ok(k.a4, k.as4);
 }
 
+// The weight gradients dW_d = dY^T h, [dW_g ; dW_u] = [dg | du]^T x_perm (and the
+// shared expert's, per token chunk) with both operands K-major: K = the rows of a
+// segment (chunk) of the row-major sources, which are then read in place (x_perm:
+// the routed rows of x gathered in expert order).
+struct WgradKm {
+  GemmProblem wd, wsd, wg, wu, wsg, wsu;
+};
+static WgradKm wgrad_kmajor(const moe_dims* d, int S, const int32_t* offsets, const int32_t* kofs_s, const void* dyp,
+                            const void* h, const void* dgu, const void* xp, const void* dy, const void* hs,
+                            const void* dgus, const void* x, float* dw_down, float* dw_gate, float* dw_up,
+                            float* part_sd, float* part_sg, float* part_su) {
+  const int64_t T = d->T, R = max_rows(d);
+  const int dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared, N = d->n_experts;
+  auto bf = [](const void* q) { return static_cast<const uint16_t*>(q); };
+  auto km = [](GemmProblem g) {
+    g.a_kmajor = 1;
+    g.b_kmajor = 1;
+    return g;
+  };
+  WgradKm k{};
+  // fields: a, a_rows, a_nrows, offsets, groups, max_rows, b0, b1, n_out, k_dim, out, k_offsets, lda, ldb, rows_per_group
+  k.wd = km(GemmProblem{bf(dyp), nullptr, R, nullptr, N, (int64_t)N * dm, bf(h), nullptr, F, (int)R, dw_down,
+                        offsets, dm, F, dm});
+  k.wg = km(GemmProblem{bf(dgu), nullptr, R, nullptr, N, (int64_t)N * F, bf(xp), nullptr, dm, (int)R, dw_gate,
+                        offsets, 2 * F, dm, F});
+  k.wu = km(GemmProblem{bf(dgu) + F, nullptr, R, nullptr, N, (int64_t)N * F, bf(xp), nullptr, dm, (int)R, dw_up,
+                        offsets, 2 * F, dm, F});
+  if (Fs) {
+    k.wsd = km(GemmProblem{bf(dy), nullptr, T, nullptr, S, (int64_t)S * dm, bf(hs), nullptr, Fs, (int)T, part_sd,
+                           kofs_s, dm, Fs, dm});
+    k.wsg = km(GemmProblem{bf(dgus), nullptr, T, nullptr, S, (int64_t)S * Fs, bf(x), nullptr, dm, (int)T, part_sg,
+                           kofs_s, 2 * Fs, dm, Fs});
+    k.wsu = km(GemmProblem{bf(dgus) + Fs, nullptr, T, nullptr, S, (int64_t)S * Fs, bf(x), nullptr, dm, (int)T,
+                           part_su, kofs_s, 2 * Fs, dm, Fs});
+  }
+  return k;
+}
+static bool wgrad_kmajor_ok(const moe_dims* d) {
+  static const uint16_t stand_in[8] = {};
+  const void* q = stand_in;
+  float* o = reinterpret_cast<float*>(const_cast<uint16_t*>(stand_in));
+  const int32_t* i = reinterpret_cast<const int32_t*>(stand_in);
+  const WgradKm k = wgrad_kmajor(d, shared_splits(d->T), i, i, q, q, q, q, q, q, q, q, o, o, o, o, o, o);
+  return gemm_kmajor_ok(k.wd, k.wsd) && gemm_kmajor_ok(k.wg, k.wu) && gemm_kmajor_ok(k.wsg, k.wsu);
+}
+
 BwdWs bwd_ws(const moe_dims* d) {
   BwdWs w{};
   w.km = dgrad_kmajor_ok(d);
+  w.km2 = wgrad_kmajor_ok(d);
   w.fwd = layer_ws(d);
   const int64_t T = d->T, R = max_rows(d), dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
   const int N = d->n_experts, M = d->n_null;
@@ -231,10 +279,11 @@ BwdWs bwd_ws(const moe_dims* d) {
   w.dgu = take((size_t)R * 2 * F * 2);
   w.dxp = take((size_t)R * dm * 4);
   w.kofs = take((size_t)(N + 1) * 4);
-  w.xpT = take((size_t)dm * w.Rp * 2);
-  w.dypT = take((size_t)dm * w.Rp * 2);
-  w.hT = take((size_t)F * w.Rp * 2);
-  w.dguT = take((size_t)2 * F * w.Rp * 2);
+  w.xpT = w.km2 ? 0 : take((size_t)dm * w.Rp * 2);
+  w.dypT = w.km2 ? 0 : take((size_t)dm * w.Rp * 2);
+  w.hT = w.km2 ? 0 : take((size_t)F * w.Rp * 2);
+  w.dguT = w.km2 ? 0 : take((size_t)2 * F * w.Rp * 2);
+  w.xp = w.km2 ? take((size_t)R * dm * 2) : 0;
   w.rpart = take(router_wgrad_ws_bytes(T, N + 1, (int)dm));
   if (Fs) {
     w.gs = take((size_t)T * Fs * 4);
@@ -245,10 +294,10 @@ BwdWs bwd_ws(const moe_dims* d) {
     w.dxs = take((size_t)T * dm * 4);
     w.wsdT = w.km ? 0 : take((size_t)Fs * dm * 2);
     w.wsguT = w.km ? 0 : take((size_t)dm * 2 * Fs * 2);
-    w.xT = take((size_t)dm * w.Tp * 2);
-    w.dyT = take((size_t)dm * w.Tp * 2);
-    w.hsT = take((size_t)Fs * w.Tp * 2);
-    w.dgusT = take((size_t)2 * Fs * w.Tp * 2);
+    w.xT = w.km2 ? 0 : take((size_t)dm * w.Tp * 2);
+    w.dyT = w.km2 ? 0 : take((size_t)dm * w.Tp * 2);
+    w.hsT = w.km2 ? 0 : take((size_t)Fs * w.Tp * 2);
+    w.dgusT = w.km2 ? 0 : take((size_t)2 * Fs * w.Tp * 2);
     w.S = shared_splits(T);
     w.kofs_s = take((size_t)(w.S + 1) * 4);
     w.part_sd = take((size_t)w.S * dm * Fs * 4);
@@ -821,7 +870,27 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
                             (int)dm, T, gr->dx, s));
   HIP_TRY(launch_router_wgrad(fp(W.ds), p->x, T, N + 1, (int)dm, fp(W.rpart), gr->dw_router, s));
 
-  // 9. weight gradients: activations transposed per segment, K = the segment's rows
+  // 9. weight gradients, K = the rows of a segment: both operands read K-major in place
+  // when the launches allow it (W.km2), else transposed per segment
+  if (W.km2) {
+    const int S = W.S;
+    int32_t* kofs_s = Fs ? ip(W.kofs_s) : nullptr;
+    HIP_TRY(launch_gather_slots(p->x, perm_token, T, offsets, N, R, (int)dm, at(W.xp), s));
+    if (Fs) HIP_TRY(launch_split_offsets(T, S, kofs_s, s));
+    const WgradKm k = wgrad_kmajor(d, S, offsets, kofs_s, at(W.dyp), at(W.h), at(W.dgu), at(W.xp), dy,
+                                   Fs ? at(W.hs) : nullptr, Fs ? at(W.dgus) : nullptr, p->x, gr->dw_down,
+                                   gr->dw_gate, gr->dw_up, Fs ? fp(W.part_sd) : nullptr,
+                                   Fs ? fp(W.part_sg) : nullptr, Fs ? fp(W.part_su) : nullptr);
+    HIP_TRY(launch_gemm_pair(true, 1, k.wd, k.wsd, cus, s, 3));
+    if (Fs) HIP_TRY(launch_sum_partials(fp(W.part_sd), S, dm * Fs, gr->dws_down, s));
+    HIP_TRY(launch_gemm_pair(true, 1, k.wg, k.wu, cus, s, 3));
+    if (Fs) {
+      HIP_TRY(launch_gemm_pair(true, 1, k.wsg, k.wsu, cus, s, 3));
+      HIP_TRY(launch_sum_partials(fp(W.part_sg), S, Fs * dm, gr->dws_gate, s));
+      HIP_TRY(launch_sum_partials(fp(W.part_su), S, Fs * dm, gr->dws_up, s));
+    }
+    return MOE_OK;
+  }
   int32_t* kofs = ip(W.kofs);
   HIP_TRY(launch_pad_offsets(offsets, N, R, kofs, s));
   HIP_TRY(launch_transpose_segments(p->x, perm_token, T, offsets, kofs, N, R, dm, at(W.xpT), W.Rp, s));

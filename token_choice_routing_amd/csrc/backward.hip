@@ -460,6 +460,20 @@ unsigned grid_for(int64_t n, int per = 256) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + per - 1) / per, 8192));
 }
 
+// out[p] = x[perm_token[p]] (rows of d bf16) for the real slots p < offsets[G] (at
+// most R): the routed token rows in expert order.
+__global__ void __launch_bounds__(256)
+gather_slots_kernel(const bf16_t* __restrict__ x, const int32_t* __restrict__ perm_token, int64_t T,
+                    const int32_t* __restrict__ offsets, int G, int64_t R, int d, bf16_t* __restrict__ out) {
+  const int64_t cpr = d / 8;
+  const int64_t n = min<int64_t>(max<int64_t>((int64_t)offsets[G], 0), R) * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t p = i / cpr, c = i - p * cpr;
+    const int64_t t = min<int64_t>(max<int64_t>((int64_t)perm_token[p], 0), T - 1);
+    *reinterpret_cast<u32x4_t*>(out + p * d + 8 * c) = *reinterpret_cast<const u32x4_t*>(x + t * d + 8 * c);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_transpose(const void* in, int64_t batches, int64_t R, int64_t C, void* out, int64_t ldo,
@@ -483,6 +497,14 @@ hipError_t launch_transpose_segments(const void* src, const int32_t* src_rows, i
   const dim3 grid((unsigned)((C + kTile - 1) / kTile), (unsigned)((ld + kTile - 1) / kTile));
   transpose_segments_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(src), src_rows, src_nrows,
                                                  offsets, kofs, G, rows, C, static_cast<bf16_t*>(dst), ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_slots(const void* x, const int32_t* perm_token, int64_t T, const int32_t* offsets, int G,
+                               int64_t R, int d, void* out, hipStream_t s) {
+  if (R <= 0 || T <= 0) return hipSuccess;
+  gather_slots_kernel<<<grid_for(R * (d / 8)), 256, 0, s>>>(static_cast<const bf16_t*>(x), perm_token, T, offsets, G,
+                                                             R, d, static_cast<bf16_t*>(out));
   return hipGetLastError();
 }
 

@@ -70,7 +70,9 @@ constexpr int kMaxGroups = 512;
 //          weight tile is staged in LDS as [K][weight rows] and its MFMA fragments are
 //          read with the transposing LDS load (ds_read_b64_tr_b16), so no transposed copy
 //          of the weights is written.
-enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4 };
+// kPlainKM2: kPlainKM whose activation operand is K-major too (GemmProblem::a_kmajor, the
+//          weight-gradient form: K = rows of both source matrices), read the same way.
+enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4, kPlainKM2 = 5 };
 
 // One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
 // fragment a (bf16 bits, or half bits for kDown16).
@@ -142,9 +144,9 @@ __device__ void build_tile_table(TileTable& tt, const GemmProblem& p0, const Gem
         const GemmProblem pr = e < G0 ? p0 : p1;
         const int ge = e < G0 ? e : e - G0;
         kl = pr.k_dim;
-        if (pr.k_offsets) {
-          ko = pr.k_offsets[ge];
-          kl = max(0, pr.k_offsets[ge + 1] - ko);
+        if (pr.k_offsets) {  // clamped to [0, k_dim] as the segments are to [0, max_rows]
+          ko = min(max(pr.k_offsets[ge], 0), pr.k_dim);
+          kl = min(max(pr.k_offsets[ge + 1], ko), pr.k_dim) - ko;
         }
         if (pr.rows_per_group > 0) {
           const int64_t a = min<int64_t>((int64_t)ge * pr.rows_per_group, pr.max_rows);
@@ -631,6 +633,53 @@ __device__ __forceinline__ int kmajor_krow(int i, int lane) { return 2 * i + (la
 // eight reads are issued before one wait for them inside the same statement, so no
 // output register is seen before its read has landed.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t kmajor_pair(s16x4_t lo, s16x4_t hi) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// All twelve fragments of a K tile when both operands are K-major ([32 K rows][256],
+// fragment layout [K step][two weight blocks, then four activation blocks]): addresses
+// b0, b1 of the weight blocks and a0..a3 of the activation blocks, as kmajor_frags.
+template <int BM>
+__device__ __forceinline__ void kmajor_frags_all(uint32_t b0, uint32_t b1, uint32_t a0, uint32_t a1, uint32_t a2,
+                                                 uint32_t a3, bf16x8_t (&fr)[2][6]) {
+  static_assert(BM == 256, "offsets below: K step 16 rows (8192 bytes), half 4 rows (2048)");
+  s16x4_t r[24];  // [K step][half][block]
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %24\n\t"
+      "ds_read_b64_tr_b16 %1, %25\n\t"
+      "ds_read_b64_tr_b16 %2, %26\n\t"
+      "ds_read_b64_tr_b16 %3, %27\n\t"
+      "ds_read_b64_tr_b16 %4, %28\n\t"
+      "ds_read_b64_tr_b16 %5, %29\n\t"
+      "ds_read_b64_tr_b16 %6, %24 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %7, %25 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %26 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %9, %27 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %28 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %11, %29 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %12, %24 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %13, %25 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %14, %26 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %15, %27 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %16, %28 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %17, %29 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %18, %24 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %19, %25 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %20, %26 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %21, %27 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %22, %28 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %23, %29 offset:10240\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+        "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17]), "=&v"(r[18]), "=&v"(r[19]), "=&v"(r[20]), "=&v"(r[21]),
+        "=&v"(r[22]), "=&v"(r[23])
+      : "v"(b0), "v"(b1), "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int blk = 0; blk < 6; ++blk) fr[ks][blk] = kmajor_pair(r[12 * ks + blk], r[12 * ks + 6 + blk]);
+}
 template <int BN>
 __device__ __forceinline__ void kmajor_frags(uint32_t a0, uint32_t a1, bf16x8_t& f00, bf16x8_t& f01,
                                              bf16x8_t& f10, bf16x8_t& f11) {
@@ -750,7 +799,8 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
   constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, S = kPpS, NW = kPpNW;
   constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
   constexpr int FM = 4, FN = 2;                      // 32-row blocks per wavefront: activations, weights
-  constexpr bool KM = MODE == kPlainKM;              // K-major weights
+  constexpr bool KM = MODE == kPlainKM || MODE == kPlainKM2;  // K-major weights
+  constexpr bool KMA = MODE == kPlainKM2;                      // and K-major activations
   constexpr bool ROWS = MODE == kDown16 && ROLE == 2; // output rows redirected (out_rows)
   constexpr int CPR = BK / 8, RPI = kWave / CPR;     // 16-byte chunks per row; rows per load instruction
   constexpr int J = (BM + BN) / (RPI * NW);          // load instructions per stage per wavefront (4)
@@ -852,6 +902,7 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     uint32_t off[J];
     uint32_t b_row;  // K-major weights: bytes per K row
     int k_split;     // K-major weights: K rows read from rb0 (the rest from rb1)
+    uint32_t a_row;  // K-major activations: bytes per K row
   };
   auto setup = [&](const Where& w, const int (&arow)[JA], Tile& t) {
     const GemmProblem pr = w.second ? p1 : p0;
@@ -860,17 +911,35 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     const uint32_t a_rb = (uint32_t)lda * 2, b_rb = (uint32_t)ldb * 2;
     const int64_t wofs = pr.k_offsets ? (int64_t)w.kofs : (int64_t)w.ge * Nout * ldb;
     const int64_t abase = pr.a_rows ? 0 : w.m0 - (pr.rows_per_group ? (int64_t)w.ge * pr.rows_per_group : 0);
-    t.a_end = __builtin_amdgcn_readfirstlane((uint32_t)((pr.a_rows ? pr.a_nrows : w.rows_valid) * a_rb));
-    t.ra = buffer_rsrc(uniform_ptr(pr.a + abase * lda + w.kofs), t.a_end);
+    if constexpr (KMA) {
+      // rows [kofs, kofs + klen) of the [rows][lda] activation source are the item's K;
+      // its output rows are the columns abase + ... (rows past klen read zero)
+      t.a_row = __builtin_amdgcn_readfirstlane(a_rb);
+      t.a_end = __builtin_amdgcn_readfirstlane((uint32_t)w.Kdim * a_rb);
+      t.ra = buffer_rsrc(uniform_ptr(pr.a + (int64_t)w.kofs * lda), t.a_end);
+    } else {
+      t.a_end = __builtin_amdgcn_readfirstlane((uint32_t)((pr.a_rows ? pr.a_nrows : w.rows_valid) * a_rb));
+      t.ra = buffer_rsrc(uniform_ptr(pr.a + abase * lda + w.kofs), t.a_end);
+    }
     if constexpr (KM) {
-      // group ge's [k_split][Nout] matrix of b0 and [k_dim - k_split][Nout] matrix of b1;
-      // one end (the larger matrix) serves both, every K row a lane reads being inside its own
-      const int k0 = pr.k_split, k1 = pr.k_dim - pr.k_split;
-      t.b_row = __builtin_amdgcn_readfirstlane((uint32_t)Nout * 2u);
-      t.k_split = __builtin_amdgcn_readfirstlane(k0);
-      t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)max(k0, k1) * t.b_row);
-      t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + (int64_t)w.ge * k0 * Nout), t.b_end);
-      t.rb1 = buffer_rsrc(uniform_ptr(k1 > 0 ? pr.b1 + (int64_t)w.ge * k1 * Nout : pr.b0), t.b_end);
+      if (pr.k_offsets) {
+        // weight-gradient form: rows [kofs, kofs + klen) of the one [rows][ldb] matrix b0
+        // (rows past klen read zero; no second matrix)
+        t.b_row = __builtin_amdgcn_readfirstlane(b_rb);
+        t.k_split = 0x7fffffff;
+        t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)w.Kdim * b_rb);
+        t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + (int64_t)w.kofs * ldb), t.b_end);
+        t.rb1 = t.rb0;
+      } else {
+        // group ge's [k_split][Nout] matrix of b0 and [k_dim - k_split][Nout] matrix of b1;
+        // one end (the larger matrix) serves both, every K row a lane reads being inside its own
+        const int k0 = pr.k_split, k1 = pr.k_dim - pr.k_split;
+        t.b_row = __builtin_amdgcn_readfirstlane((uint32_t)Nout * 2u);
+        t.k_split = __builtin_amdgcn_readfirstlane(k0);
+        t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)max(k0, k1) * t.b_row);
+        t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + (int64_t)w.ge * k0 * Nout), t.b_end);
+        t.rb1 = buffer_rsrc(uniform_ptr(k1 > 0 ? pr.b1 + (int64_t)w.ge * k1 * Nout : pr.b0), t.b_end);
+      }
     } else {
       t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)Nout * b_rb);
       t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + wofs), t.b_end);
@@ -878,9 +947,18 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     }
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
-      const int r = RPI * (wave + NW * j) + lrow;
-      const int64_t row = pr.a_rows ? min<int64_t>(max<int64_t>(arow[j], 0), pr.a_nrows - 1) : r;
-      t.off[j] = (r >= w.rows_valid ? t.a_end : (uint32_t)row * a_rb) + lk * 2;
+      if constexpr (KMA) {
+        // piece i of the activation region: K rows 2i, 2i + 1 of 256 output rows each,
+        // swizzled as the weight region
+        const int krow = kmajor_krow(wave + NW * j, lane);
+        const int p16 = lane & 31;
+        const int c = ((p16 & 3) | (((p16 >> 2) ^ (krow & 3)) << 2)) * 8;
+        t.off[j] = c < w.rows_valid ? (uint32_t)krow * a_rb + (uint32_t)(abase + c) * 2u : t.a_end;
+      } else {
+        const int r = RPI * (wave + NW * j) + lrow;
+        const int64_t row = pr.a_rows ? min<int64_t>(max<int64_t>(arow[j], 0), pr.a_nrows - 1) : r;
+        t.off[j] = (r >= w.rows_valid ? t.a_end : (uint32_t)row * a_rb) + lk * 2;
+      }
     }
 #pragma unroll
     for (int j = JA; j < J; ++j) {
@@ -913,6 +991,12 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     const bool in = kt < w.nk && (int)(kt * BK + lk) < w.Kdim;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      if (KMA && j < JA) {
+        // K rows [kt BK, kt BK + BK) of the activation source (past klen: zero)
+        buffer_load_lds16(t.ra, kt < w.nk ? t.off[j] + (uint32_t)(kt * BK) * t.a_row : t.a_end,
+                          smem + st * STAGE + RPI * (wave + NW * j) * BK);
+        continue;
+      }
       if (KM && j >= JA) {
         // K rows [kt BK, kt BK + BK) of the weights: from rb0 below k_split, else rb1
         // (k_split and k_dim are multiples of BK, so a tile is whole and never straddles)
@@ -942,10 +1026,21 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
   // activation block and the first weight block; the other blocks of the same K step
   // are whole 32-row strides further on (the swizzle term (row / 4) % 4 repeats every
   // 32 rows), so they fold into the LDS reads' immediate offsets.
-  uint32_t a_lane[2], b_lane[2];
+  uint32_t a_lane[KMA ? 4 : 2], b_lane[2];
+  if constexpr (KMA) {
+    // K-major activation region [BK][BM]: a_lane[g] addresses the wavefront's 32-row
+    // block g (rows wm BM / 2 + 32 g ...) as b_lane does the weight blocks below
+    const int s16 = lane & 15;
+    const int kl = 8 * (lane >> 5) + (s16 >> 2), nl = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = 4 * wm + g;
+      a_lane[g] = (uint32_t)(kl * BM + ((chunk ^ (kl & 3)) * 32) + nl) * 2;
+    }
+  }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    a_lane[ks] = (uint32_t)lds_off<BK>(wm * (BM / 2) + l32, ks * 2 + half) * 2;
+    if constexpr (!KMA) a_lane[ks] = (uint32_t)lds_off<BK>(wm * (BM / 2) + l32, ks * 2 + half) * 2;
     if constexpr (KM) {
       // K-major weight region [BK][BN]: here b_lane[f] is the lane's transposing-read
       // address of weight block f (rows wn 64 + 32 f ...), K step and half folded into
@@ -966,7 +1061,13 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
   typedef bf16x8_t Frags[2][FN + FM];  // per 16-wide K step: FN weight fragments, then FM activation ones
   auto read_frags = [&](int st, Frags& fr) {
     const char* base = reinterpret_cast<const char*>(smem) + st * (STAGE * 2);
-    if constexpr (KM) {
+    if constexpr (KMA) {
+      // LDS byte address of the stage (the dynamic LDS follows the static tile table)
+      const uint32_t sb = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)base);
+      kmajor_frags_all<BM>(sb + b_lane[0], sb + b_lane[1], sb + a_lane[0], sb + a_lane[1], sb + a_lane[2],
+                           sb + a_lane[3], fr);
+      return;
+    } else if constexpr (KM) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1398,6 +1499,7 @@ static void launch_skinny(const GemmProblem& q0, const GemmProblem& q1, int num_
 bool gemm_operands_fit(const GemmProblem& p) {
   if (p.groups == 0 || p.max_rows <= 0) return true;
   const int64_t a_rb = (p.lda ? p.lda : p.k_dim) * 2, b_rb = (p.ldb ? p.ldb : p.k_dim) * 2;
+  if (p.a_kmajor) return true;  // the K-major weight-gradient form checks its own offsets
   const int64_t b_bytes = p.b_kmajor ? (int64_t)(std::max(p.k_split, p.k_dim - p.k_split) + 1) * p.n_out * 2
                                      : (int64_t)(p.n_out + 1) * b_rb;
   return b_bytes <= 0xFFFFFFFFll &&
@@ -1407,13 +1509,22 @@ bool gemm_operands_fit(const GemmProblem& p) {
 
 static bool plain_form(const GemmProblem& p) { return !p.k_offsets && !p.lda && !p.ldb && !p.rows_per_group; }
 
-// A K-major weight problem (op 1) the 256 x 256 kernel takes: plain form otherwise,
-// whole 8-column chunks per row, whole K tiles, the b0 / b1 boundary on a K tile boundary.
+// A K-major problem (op 1) the 256 x 256 kernel takes. Weights only: plain form
+// otherwise, whole 8-column chunks per row, whole K tiles, the b0 / b1 boundary on a K
+// tile boundary. Both operands (the weight-gradient form): per-group K ranges
+// (k_offsets) of two row-major sources with 16-byte rows and 8-column chunks, their
+// byte offsets (up to twice the K extent, the past-the-end reads included) within 4 GB.
 static bool kmajor_ok(const GemmProblem& p) {
   if (p.groups == 0 || p.max_rows <= 0) return true;
-  return p.b_kmajor && plain_form(p) && !p.out_rows && p.n_out % 8 == 0 && p.k_split > 0 &&
-         p.k_split % kPpBK == 0 && p.k_dim % kPpBK == 0 && p.k_split <= p.k_dim &&
-         (p.k_split < p.k_dim) == (p.b1 != nullptr);
+  if (!p.b_kmajor || p.out_rows || p.n_out % 8 != 0) return false;
+  if (p.a_kmajor) {
+    const int64_t reach = 2 * (int64_t)p.k_dim + kPpBK;
+    return p.k_offsets && !p.a_rows && !p.offsets && !p.b1 && p.rows_per_group > 0 && p.rows_per_group % 8 == 0 &&
+           p.lda >= p.rows_per_group && p.lda % 8 == 0 && p.ldb >= p.n_out && p.ldb % 8 == 0 &&
+           reach * p.lda * 2 <= 0xFFFFFFFFll && reach * p.ldb * 2 <= 0xFFFFFFFFll;
+  }
+  return plain_form(p) && p.k_split > 0 && p.k_split % kPpBK == 0 && p.k_dim % kPpBK == 0 &&
+         p.k_split <= p.k_dim && (p.k_split < p.k_dim) == (p.b1 != nullptr);
 }
 
 static bool skinny_launch(const GemmProblem& q0, const GemmProblem& q1) {
@@ -1423,6 +1534,7 @@ static bool skinny_launch(const GemmProblem& q0, const GemmProblem& q1) {
 
 bool gemm_kmajor_ok(const GemmProblem& p0, const GemmProblem& p1) {
   const bool any0 = p0.groups > 0 && p0.max_rows > 0, any1 = p1.groups > 0 && p1.max_rows > 0;
+  if (any0 && any1 && p0.a_kmajor != p1.a_kmajor) return false;
   return (!any0 || kmajor_ok(p0)) && (!any1 || kmajor_ok(p1)) && gemm_pair_uses_pp(p0, p1);
 }
 
@@ -1448,8 +1560,13 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   if (bf16) {
     GemmProblem q0 = any0 ? p0 : GemmProblem{}, q1 = any1 ? p1 : GemmProblem{};
     if (km) {
-      if (role == 3) launch_pp<kPlainKM, 3>(q0, q1, num_cus, stream);
-      else launch_pp<kPlainKM, 0>(q0, q1, num_cus, stream);
+      if ((any0 && p0.a_kmajor) || (any1 && p1.a_kmajor)) {
+        if (role == 3) launch_pp<kPlainKM2, 3>(q0, q1, num_cus, stream);
+        else launch_pp<kPlainKM2, 0>(q0, q1, num_cus, stream);
+      } else {
+        if (role == 3) launch_pp<kPlainKM, 3>(q0, q1, num_cus, stream);
+        else launch_pp<kPlainKM, 0>(q0, q1, num_cus, stream);
+      }
       return hipGetLastError();
     }
     if (op == 3) {

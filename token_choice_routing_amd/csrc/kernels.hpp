@@ -134,7 +134,12 @@ struct GemmProblem {
   // k_split][n]). A row-major weight [n_out][k_dim] of the other modes is the transpose
   // of this layout; the backward's data gradients read the forward's weights this way.
   // n_out a multiple of 8, k_split and k_dim multiples of 32.
+  // With a_kmajor too (the weight-gradient form, k_offsets and rows_per_group set): group
+  // e reduces over rows [k_offsets[e], k_offsets[e+1]) of two row-major sources, A[m][k]
+  // = a[k][m0 + m] (row stride lda, m0 the group-relative output row) and B[n][k] =
+  // b0[k][n] (row stride ldb); k_dim bounds the rows of either.
   int b_kmajor, k_split;
+  int a_kmajor;
 };
 // op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
 // float32 out; with b_kmajor set in both problems, B read from K-major b0 / b1, 256 x 256
@@ -173,6 +178,9 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int G, int64_t rows, int32
 hipError_t launch_transpose_segments(const void* src, const int32_t* src_rows, int64_t src_nrows,
                                      const int32_t* offsets, const int32_t* kofs, int G, int64_t rows,
                                      int64_t C, void* dst, int64_t ld, hipStream_t s);
+// out[p] = x[perm_token[p]] (bf16 rows of d, d a multiple of 8) for p < offsets[G] (at most R).
+hipError_t launch_gather_slots(const void* x, const int32_t* perm_token, int64_t T, const int32_t* offsets, int G,
+                               int64_t R, int d, void* out, hipStream_t s);
 hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offsets, int G, int64_t rows, int F,
                            void* h, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
