@@ -799,14 +799,31 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
                  nullptr, permute_ws, true, &af};
   HIP_TRY(launch_permute(pa, s));
 
-  // 3. expert pre-activations g = x W_g^T, u = x W_u^T (float32) and h = silu(g) u
+  // 3. expert pre-activations g = x W_g^T, u = x W_u^T (float32) and h = silu(g) u (bf16):
+  // routed and shared in one launch whose epilogue keeps g and u and writes h, when the
+  // 256 x 256 tiles take both; else g and u by plain GEMMs and h by its own kernel
+  GemmProblem gk{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate),
+                 static_cast<const uint16_t*>(p->w_up), (int)F, (int)dm, at(W.h)};
+  gk.keep_g = fp(W.g);
+  gk.keep_u = fp(W.u);
+  GemmProblem gsk{};
+  if (Fs) {
+    gsk = GemmProblem{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_gate),
+                      static_cast<const uint16_t*>(p->ws_up), (int)Fs, (int)dm, at(W.hs)};
+    gsk.keep_g = fp(W.gs);
+    gsk.keep_u = fp(W.us);
+  }
+  const bool keep = gemm_pair_uses_pp(gk, gsk);
+  if (keep) HIP_TRY(launch_gemm_pair(true, 4, gk, gsk, cus, s, 3));
   GemmProblem g1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate), nullptr,
                  (int)F, (int)dm, at(W.g)};
   GemmProblem u1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_up), nullptr,
                  (int)F, (int)dm, at(W.u)};
-  HIP_TRY(launch_gemm_pair(true, 1, g1, u1, cus, s, 3));
-  HIP_TRY(launch_swiglu_h(fp(W.g), fp(W.u), offsets, N, R, (int)F, at(W.h), s));
-  if (Fs) {
+  if (!keep) {
+    HIP_TRY(launch_gemm_pair(true, 1, g1, u1, cus, s, 3));
+    HIP_TRY(launch_swiglu_h(fp(W.g), fp(W.u), offsets, N, R, (int)F, at(W.h), s));
+  }
+  if (Fs && !keep) {
     GemmProblem gs{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_gate), nullptr, (int)Fs,
                    (int)dm, at(W.gs)};
     GemmProblem us{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_up), nullptr, (int)Fs,

@@ -72,7 +72,9 @@ constexpr int kMaxGroups = 512;
 //          of the weights is written.
 // kPlainKM2: kPlainKM whose activation operand is K-major too (GemmProblem::a_kmajor, the
 //          weight-gradient form: K = rows of both source matrices), read the same way.
-enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4, kPlainKM2 = 5 };
+// kSwiGLUKeep: kSwiGLU for the backward's recompute (256 x 256 tiles only): the epilogue
+//          stores g and u (float32, keep_g / keep_u) and h = silu(g) u as bf16.
+enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4, kPlainKM2 = 5, kSwiGLUKeep = 6 };
 
 // One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
 // fragment a (bf16 bits, or half bits for kDown16).
@@ -797,7 +799,8 @@ template <int MODE, int ROLE>
 __global__ void __launch_bounds__(64 * kPpNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
   constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, S = kPpS, NW = kPpNW;
-  constexpr int OC = MODE == kSwiGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr bool SW = MODE == kSwiGLU || MODE == kSwiGLUKeep;  // gate and up weight halves
+  constexpr int OC = SW ? BN / 2 : BN;  // output columns per tile
   constexpr int FM = 4, FN = 2;                      // 32-row blocks per wavefront: activations, weights
   constexpr bool KM = MODE == kPlainKM || MODE == kPlainKM2;  // K-major weights
   constexpr bool KMA = MODE == kPlainKM2;                      // and K-major activations
@@ -943,7 +946,7 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
     } else {
       t.b_end = __builtin_amdgcn_readfirstlane((uint32_t)Nout * b_rb);
       t.rb0 = buffer_rsrc(uniform_ptr(pr.b0 + wofs), t.b_end);
-      t.rb1 = buffer_rsrc(uniform_ptr(MODE == kSwiGLU ? pr.b1 + wofs : pr.b0 + wofs), t.b_end);
+      t.rb1 = buffer_rsrc(uniform_ptr(SW ? pr.b1 + wofs : pr.b0 + wofs), t.b_end);
     }
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
@@ -974,7 +977,7 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
         t.off[j] = c < ocp && n < Nout ? (uint32_t)krow * t.b_row + (uint32_t)n * 2u : t.b_end;
       } else {
         const int r = RPI * (wave + NW * j) + lrow - BM;
-        const int c = MODE == kSwiGLU ? r % OC : r;
+        const int c = SW ? r % OC : r;
         const int n = w.col0 + c;
         t.off[j] = (c < ocp && n < Nout ? (uint32_t)n * b_rb : t.b_end) + lk * 2;
       }
@@ -1007,7 +1010,7 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
                           smem + st * STAGE + RPI * (wave + NW * j) * BK);
         continue;
       }
-      const bool up = MODE == kSwiGLU && j >= JA && RPI * (wave + NW * j) - BM >= OC;
+      const bool up = SW && j >= JA && RPI * (wave + NW * j) - BM >= OC;
       const uint32_t end = j < JA ? t.a_end : t.b_end;
       buffer_load_lds16(j < JA ? t.ra : up ? t.rb1 : t.rb0, in ? t.off[j] + kb : end,
                         smem + st * STAGE + RPI * (wave + NW * j) * BK);
@@ -1053,11 +1056,11 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
       const int chunk = 2 * wn + ks;  // the wavefront's 32-row weight block ks
       b_lane[ks] = (uint32_t)(BM * BK + kl * BN + ((chunk ^ (kl & 3)) * 32) + nl) * 2;
     } else {
-      b_lane[ks] = (uint32_t)(BM * BK + lds_off<BK>((MODE == kSwiGLU ? wn * 32 : wn * 64) + l32, ks * 2 + half)) * 2;
+      b_lane[ks] = (uint32_t)(BM * BK + lds_off<BK>((SW ? wn * 32 : wn * 64) + l32, ks * 2 + half)) * 2;
     }
   }
   constexpr uint32_t kRow32 = 32 * BK * 2;                                   // bytes between 32-row blocks
-  constexpr uint32_t kWStep = MODE == kSwiGLU ? (BN / 2) * BK * 2 : kRow32;  // gate -> up, or block -> block
+  constexpr uint32_t kWStep = SW ? (BN / 2) * BK * 2 : kRow32;  // gate -> up, or block -> block
   typedef bf16x8_t Frags[2][FN + FM];  // per 16-wide K step: FN weight fragments, then FM activation ones
   auto read_frags = [&](int st, Frags& fr) {
     const char* base = reinterpret_cast<const char*>(smem) + st * (STAGE * 2);
@@ -1219,6 +1222,23 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) h[j] = silu(acc[0][g][4 * q + j]) * acc[1][g][4 * q + j];
               *reinterpret_cast<u32x2_t*>(crow + col) = u32x2_t{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])};
+            }
+          }
+        } else if (MODE == kSwiGLUKeep) {
+          const int64_t ro = (int64_t)(m0 + rl) * Nout;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = col0 + wn * 32 + 8 * q + 4 * half;
+            if (col < Nout) {
+              const f32x4_t gv{acc[0][g][4 * q], acc[0][g][4 * q + 1], acc[0][g][4 * q + 2], acc[0][g][4 * q + 3]};
+              const f32x4_t uv{acc[1][g][4 * q], acc[1][g][4 * q + 1], acc[1][g][4 * q + 2], acc[1][g][4 * q + 3]};
+              *reinterpret_cast<f32x4_t*>(pr.keep_g + ro + col) = gv;
+              *reinterpret_cast<f32x4_t*>(pr.keep_u + ro + col) = uv;
+              float h[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) h[j] = silu(gv[j]) * uv[j];
+              *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(pr.out) + ro + col) =
+                  u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
             }
           }
         } else {
@@ -1553,7 +1573,10 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
   // the output-row redirect (the layer's down projection launch) and the combine
   // epilogue exist on the 256 x 256 tiles only
   const bool redirect = (any0 && p0.out_rows) || (any1 && p1.out_rows);
-  if ((op == 3 || redirect) && (!bf16 || !gemm_pair_uses_pp(p0, p1))) return hipErrorInvalidValue;
+  if ((op == 3 || op == 4 || redirect) && (!bf16 || !gemm_pair_uses_pp(p0, p1))) return hipErrorInvalidValue;
+  if (op == 4 && ((any0 && (!p0.keep_g || !p0.keep_u || p0.n_out % 4)) || (any1 && (!p1.keep_g || !p1.keep_u ||
+                                                                                   p1.n_out % 4))))
+    return hipErrorInvalidValue;
   if (redirect && (op != 2 || role != 2)) return hipErrorInvalidValue;
   const bool km = (any0 && p0.b_kmajor) || (any1 && p1.b_kmajor);
   if (km && (!bf16 || op != 1 || !gemm_kmajor_ok(p0, p1))) return hipErrorInvalidValue;
@@ -1571,6 +1594,11 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     }
     if (op == 3) {
       if (role == 2) launch_pp<kDownComb, 2>(q0, q1, num_cus, stream);
+      else return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+    if (op == 4) {
+      if (role == 3) launch_pp<kSwiGLUKeep, 3>(q0, q1, num_cus, stream);
       else return hipErrorInvalidValue;
       return hipGetLastError();
     }

@@ -140,12 +140,18 @@ struct GemmProblem {
   // b0[k][n] (row stride ldb); k_dim bounds the rows of either.
   int b_kmajor, k_split;
   int a_kmajor;
+  // op 4 (the backward's recompute of op 0, 256 x 256 tiles only): g = a b0^T and u =
+  // a b1^T stored as float32 [max_rows][n_out] here, and out = bf16 silu(g) u.
+  float* keep_g;
+  float* keep_u;
 };
 // op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
 // float32 out; with b_kmajor set in both problems, B read from K-major b0 / b1, 256 x 256
 // tiles only); op 2: out = a b0^T with a in half (the layer's h), float32 out; op 3: op 2
 // with the combine epilogue (comb_* fields), bf16 out, on the 256 x 256 tiles only (the
-// launch is refused where gemm_pair_uses_pp is false). Both problems in one launch.
+// launch is refused where gemm_pair_uses_pp is false); op 4: op 0 keeping g and u
+// (keep_g / keep_u) with h in bf16 (256 x 256 tiles, role 3 only). Both problems in one
+// launch.
 // (float32 layers: op 2 is op 1.)
 // role names the launch in profiles: 0 standalone grouped, 1 standalone single
 // segment, 2 the layer's fused launch, 3 the layer backward.
