@@ -82,7 +82,11 @@ def _router_case(T, d, N, M, K, dtype, seed):
 @pytest.mark.parametrize("T,d,N,M,K,dtype", [
     (1000, 1024, 64, 64, 4, "bf16"), (777, 2048, 64, 192, 8, "bf16"), (300, 200, 40, 8, 3, "bf16"),
     (130, 24, 8, 8, 2, "bf16"), (256, 64, 8, 8, 2, "f32"), (65, 1032, 100, 0, 6, "bf16"),
-    (1, 512, 64, 64, 8, "bf16")])
+    (1, 512, 64, 64, 8, "bf16"),
+    # from 128 token tiles on, one workgroup per tile scores and selects (eight
+    # wavefronts for up to 8 slots): ragged token tails, a K tail, experts past N
+    (8200, 2048, 64, 192, 8, "bf16"), (8250, 200, 40, 8, 3, "bf16"), (8192, 1024, 64, 0, 2, "bf16"),
+    (8193, 512, 64, 64, 16, "bf16")])
 def test_route_gemm_logits_and_flip_rule(T, d, N, M, K, dtype):
     say(f"route GEMM T={T} d={d} N={N} M={M} K={K} {dtype}")
     xs, xv, w, b, btok = _router_case(T, d, N, M, K, dtype, T + d)
