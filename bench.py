@@ -451,7 +451,8 @@ def decode_sweep(torch, base, main_layer, steps):
 def backward_bench(torch, layers, steps, warmup):
     """moe_layer_backward (gradients of <dy, y> + 2e-2 L_bal + 1e-3 L_z, routing and
     expert pre-activations recomputed from x) on each layer, timed with events on the
-    current stream. TFLOP/s are counted on the gradient contractions of the real
+    current stream; beside it the training pair moe_layer_forward_train +
+    moe_layer_backward_saved (the forward keeps that state, the backward reads it). TFLOP/s are counted on the gradient contractions of the real
     slots and the shared expert (2 x the forward's: data and weight gradients,
     12 d d_ff per row); the recomputation (the forward's gate/up for routed rows and
     for the shared expert) is reported as executed FLOPs beside them."""
@@ -474,13 +475,35 @@ def backward_bench(torch, layers, steps, warmup):
         fwd_ms, _ = time_layer(torch, layer, steps, 2)  # also fills the holder's offsets
         R = int(layer.offsets[-1].item())
         d, F, Fs, T = cfg.d_model, cfg.d_ff, cfg.d_ff_shared, layer.T
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            a.record(s)
+            for _ in range(steps):
+                fn()
+            b.record(s)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        # the training pair: a forward that keeps its routing and pre-activations, and the
+        # backward that reads them instead of recomputing (each timed alone, then as a step)
+        train_fwd_ms = timed(lambda: layer.forward_train())
+        saved_ms = timed(lambda: layer.backward_saved(dy, 2e-2, 1e-3))
+        train_step_ms = timed(lambda: (layer.forward_train(), layer.backward_saved(dy, 2e-2, 1e-3)))
         useful = 12.0 * d * F * R + 12.0 * d * Fs * T
         executed = useful + 4.0 * d * F * R + 4.0 * d * Fs * T
         out.append({"workload": cfg.name, "T": T, "real_slots": R, "ms": round(ms, 4),
                     "forward_ms": round(fwd_ms, 4), "tokens_per_s": round(T / ms * 1e3, 1),
                     "grad_tflops": round(useful / ms / 1e9, 2),
                     "grad_mfma_frac": round(useful / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-                    "executed_tflops": round(executed / ms / 1e9, 2)})
+                    "executed_tflops": round(executed / ms / 1e9, 2),
+                    "saved": {"forward_train_ms": round(train_fwd_ms, 4), "backward_saved_ms": round(saved_ms, 4),
+                              "train_step_ms": round(train_step_ms, 4),
+                              "stateless_step_ms": round(fwd_ms + ms, 4),
+                              "grad_tflops": round(useful / saved_ms / 1e9, 2),
+                              "grad_mfma_frac": round(useful / saved_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}})
         log(f"  backward {cfg.name}: {out[-1]}")
     return out
 

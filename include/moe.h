@@ -359,6 +359,32 @@ moe_status moe_layer_backward(const moe_dims* dims, const moe_layer_params* para
                               size_t ws_bytes, moe_stream stream);
 
 /*
+ * moe_layer_forward_train / moe_layer_backward_saved -- the same forward and backward
+ * for a training step that keeps the forward's state instead of recomputing it (the
+ * paper review, section 4 "training configuration", trains the layer; which state a
+ * step keeps is not fixed by the pages).
+ * moe_layer_forward_train computes y exactly as moe_layer_forward does (bit for bit)
+ * and leaves in ws -- moe_workspace_bytes(dims, MOE_WS_BACKWARD) bytes, the backward's
+ * workspace -- the routing (logits, selection, weights), the permutation, the pool
+ * counts f and the expert pre-activations g, u (float32) and h = silu(g) u (bf16), routed
+ * and shared. aux may ask for P, counts and scalars only (its other pointers must be
+ * NULL: MOE_ERR_ARG; the routing outputs stay in ws). Same limits as moe_layer_backward
+ * (bf16, MOE_NULL_ZERO).
+ * moe_layer_backward_saved then returns what moe_layer_backward returns for the same
+ * inputs and dy (bit for bit), reading that state from ws instead of recomputing it: ws
+ * must be the workspace of a moe_layer_forward_train call with the same dims, params
+ * and x, with nothing written to it in between (not checked; the ws memory of the pair
+ * is the caller's). Saves the recompute (routing, permutation and one gate/up GEMM);
+ * the forward instead stores g and u (8 bytes per row and column) next to h.
+ * All enqueued on `stream`; no host synchronisation.
+ */
+moe_status moe_layer_forward_train(const moe_dims* dims, const moe_layer_params* params, void* y,
+                                   const moe_aux_out* aux, void* ws, size_t ws_bytes, moe_stream stream);
+moe_status moe_layer_backward_saved(const moe_dims* dims, const moe_layer_params* params, const void* dy,
+                                    float alpha, float beta, const moe_layer_grads* grads, void* ws,
+                                    size_t ws_bytes, moe_stream stream);
+
+/*
  * moe_validate_inputs -- optional check of the layer's inputs, not part of the
  * forward: NaN or +-inf anywhere in x, the router, the expert and shared-expert
  * weights or the constant vector, and NaN in null_bias / null_bias_tok (an

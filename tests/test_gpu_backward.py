@@ -259,3 +259,61 @@ def test_backward_at_the_size_limits():
                  d_ff_shared=32, dtype="bf16", w_std=None, seed=12)
     got, ref = _run_wl(generate(cfg), 2e-2, 1e-3)
     _check(cfg, got, ref)
+
+
+# moe_layer_forward_train + moe_layer_backward_saved against moe_layer_forward +
+# moe_layer_backward, bit for bit: the gate/up launch keeping g and u on the 256 x 256
+# tiles with the fused combine after it (keep_fused), on those tiles without a shared
+# expert (the down projections and the combine launch), and off them (plain GEMMs for g
+# and u, the layer's own gate/up for the half-precision h)
+TRAIN_CASES = {
+    "small": CASES["nullpool_shared"],
+    "keep_fused": dict(T=4096, d_model=256, n_experts=8, n_null=8, top_k=2, d_ff=256, d_ff_shared=256),
+    "keep_no_shared": dict(T=2048, d_model=256, n_experts=4, n_null=4, top_k=2, d_ff=160, d_ff_shared=0),
+}
+
+
+@pytest.mark.parametrize("case", list(TRAIN_CASES))
+def test_forward_train_and_backward_saved_match_the_stateless_pair(case):
+    cfg = Config(name=f"train_{case}", dtype="bf16", w_std=None, seed=3, **TRAIN_CASES[case])
+    say(f"  training pair {case} T={cfg.T} d={cfg.d_model} N={cfg.n_experts} Fs={cfg.d_ff_shared}")
+    wl = generate(cfg)
+    layer = MoeLayer(wl)
+    layer.forward()
+    y_ref = layer.y.clone()
+    aux_ref = {k: getattr(layer, k).clone() for k in ("counts", "P", "scalars")}
+    rng = np.random.default_rng(11)
+    dy = to_device(bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32)))
+    g_ref = {k: v.clone() for k, v in layer.backward(dy, 2e-2, 1e-3).items() if v is not None}
+    layer.y.zero_()
+    for k in aux_ref:
+        getattr(layer, k).zero_()
+    layer.forward_train()
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y, y_ref), "forward_train y differs from the forward's"
+    for k, v in aux_ref.items():
+        assert torch.equal(getattr(layer, k), v), k
+    for v in layer.grads.values():
+        if v is not None:
+            v.fill_(float("nan"))
+    layer.backward_saved(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    for k, v in g_ref.items():
+        assert torch.equal(layer.grads[k], v), k
+    # a second backward from the same state gives the same gradients (it reads the state
+    # only)
+    layer.backward_saved(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    for k, v in g_ref.items():
+        assert torch.equal(layer.grads[k], v), k
+
+
+def test_forward_train_refuses_routing_outputs():
+    from token_choice_routing_amd import AuxOut, MoeError, moe_layer_forward_train
+    cfg = Config(name="train_refuse", dtype="bf16", w_std=None, seed=3, **CASES["topk_m0"])
+    layer = MoeLayer(generate(cfg))
+    layer._backward_buffers()
+    bad = AuxOut(layer.logits.data_ptr(), None, None, None, None, None, None, None, None)
+    with pytest.raises(MoeError):
+        moe_layer_forward_train(layer.dims, layer.params, layer.y, bad, layer.ws_bwd)
+

@@ -84,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_layer_forward_noalloc": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P],
         "moe_layer_backward": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(LayerGrads), _P, ctypes.c_size_t, _P],
+        "moe_layer_forward_train": [D, ctypes.POINTER(LayerParams), _P, ctypes.POINTER(AuxOut), _P,
+                                    ctypes.c_size_t, _P],
+        "moe_layer_backward_saved": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_float, ctypes.c_float,
+                                     ctypes.POINTER(LayerGrads), _P, ctypes.c_size_t, _P],
         "moe_validate_inputs": [D, ctypes.POINTER(LayerParams), _P, ctypes.c_size_t, _P],
     }
     for name, args in sig.items():
@@ -252,6 +256,24 @@ def moe_layer_backward(dims, params: LayerParams, dy, alpha: float, beta: float,
     _check(load_library().moe_layer_backward(ctypes.byref(dims), ctypes.byref(params), _ptr(dy),
                                               float(alpha), float(beta), ctypes.byref(grads), wp, wb,
                                               _stream(stream)), "moe_layer_backward")
+
+
+def moe_layer_forward_train(dims, params: LayerParams, y, aux: AuxOut = None, ws=None, stream=None):
+    """The layer forward that leaves its routing and expert pre-activations in ws (the
+    backward's workspace) for moe_layer_backward_saved."""
+    wp, wb = _ws(ws)
+    _check(load_library().moe_layer_forward_train(ctypes.byref(dims), ctypes.byref(params), _ptr(y),
+                                                   ctypes.byref(aux) if aux is not None else None, wp, wb,
+                                                   _stream(stream)), "moe_layer_forward_train")
+
+
+def moe_layer_backward_saved(dims, params: LayerParams, dy, alpha: float, beta: float, grads: LayerGrads,
+                             ws=None, stream=None):
+    """moe_layer_backward from the state a moe_layer_forward_train call left in ws."""
+    wp, wb = _ws(ws)
+    _check(load_library().moe_layer_backward_saved(ctypes.byref(dims), ctypes.byref(params), _ptr(dy),
+                                                    float(alpha), float(beta), ctypes.byref(grads), wp, wb,
+                                                    _stream(stream)), "moe_layer_backward_saved")
 
 
 def moe_validate_inputs(dims, params: LayerParams, ws, stream=None) -> bool:

@@ -563,6 +563,11 @@ moe_status moe_aux_stats(const moe_dims* d, const float* logits, const int32_t* 
   return MOE_OK;
 }
 
+static moe_status layer_down_combine(const moe_dims* d, const moe_layer_params* p, void* y, const LayerWs& L,
+                                     uint8_t* base, const int32_t* offsets, const int32_t* slot_pos,
+                                     const float* topk_w, const int32_t* n_real, const int32_t* row_dst,
+                                     hipStream_t s);
+
 moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void* y,
                              const moe_aux_out* aux, void* ws, size_t ws_bytes,
                              moe_stream stream) {
@@ -615,7 +620,6 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   const bool want_stats = ao.counts || ao.f || ao.P || ao.scalars;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = d->dtype == MOE_BF16;
-  const int64_t R = max_rows(d);
   const int N = d->n_experts;
   MOE_TRY(no_pending_error());
 
@@ -640,10 +644,25 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
 
   // 3. gate/up + SwiGLU: routed experts read x through perm_token (the gather), and the
   //    shared expert runs in the same launch
-  const int cus = cu_count();
   HIP_TRY(launch_layer_gate_up(d, p->x, perm_token, offsets, p->w_gate, p->w_up, p->ws_gate, p->ws_up,
                                at(L.h), at(L.hs), s));
 
+  return layer_down_combine(d, p, y, L, base, offsets, slot_pos, topk_w, n_real, row_dst, s);
+}
+
+// Steps 4-5 of the layer forward: the down projections (routed and shared, from the
+// half-precision h and hs in L) and the weighted combine into y, or, with fused = a
+// row_dst, the routed outputs token-major and the combine in the shared expert's
+// down projection.
+static moe_status layer_down_combine(const moe_dims* d, const moe_layer_params* p, void* y, const LayerWs& L,
+                                     uint8_t* base, const int32_t* offsets, const int32_t* slot_pos,
+                                     const float* topk_w, const int32_t* n_real, const int32_t* row_dst,
+                                     hipStream_t s) {
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  const bool bf16 = d->dtype == MOE_BF16, fused = row_dst != nullptr;
+  const int64_t R = max_rows(d);
+  const int N = d->n_experts;
+  const int cus = cu_count();
   // 4. down projection, routed and shared, float32 outputs
   GemmProblem r2{static_cast<const uint16_t*>(at(L.h)), nullptr, R, offsets, N, R,
                  static_cast<const uint16_t*>(p->w_down), nullptr, d->d_model, d->d_ff, at(L.yp)};
@@ -733,13 +752,12 @@ moe_status moe_validate_inputs(const moe_dims* d, const moe_layer_params* p, voi
   return host ? MOE_ERR_NONFINITE : MOE_OK;
 }
 
-moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,
-                              float beta, const moe_layer_grads* gr, void* ws, size_t ws_bytes,
-                              moe_stream stream) {
-  MOE_TRY(check_dims(d));
-  if (!p || !gr) return MOE_ERR_ARG;
+// Checks shared by the backward entry points and the training forward: dims, the
+// layer's parameters and the backward workspace.
+static moe_status check_backward_args(const moe_dims* d, const moe_layer_params* p, const BwdWs& W, void* ws,
+                                      size_t ws_bytes) {
+  if (!p) return MOE_ERR_ARG;
   if (d->dtype != MOE_BF16 || d->null_kind != MOE_NULL_ZERO) return MOE_ERR_UNSUPPORTED;
-  const BwdWs W = bwd_ws(d);
   const int64_t T = d->T, dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
   // bf16 operands at 32-bit byte offsets (transposed activations: rows of Rp columns)
   if (!fits_4g(T, dm) || !fits_4g(2 * F, dm) || !fits_4g(2 * std::max<int64_t>(F, Fs), W.Rp) ||
@@ -755,50 +773,43 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     MOE_TRY(need(p->ws_gate));
     MOE_TRY(need(p->ws_up));
     MOE_TRY(need(p->ws_down));
-    MOE_TRY(need(gr->dws_gate));
-    MOE_TRY(need(gr->dws_up));
-    MOE_TRY(need(gr->dws_down));
   }
-  MOE_TRY(need(dy));
-  MOE_TRY(need(gr->dx));
-  MOE_TRY(need(gr->dw_router));
-  MOE_TRY(need(gr->dw_gate));
-  MOE_TRY(need(gr->dw_up));
-  MOE_TRY(need(gr->dw_down));
   if (!ws || ws_bytes < W.total) return MOE_ERR_WORKSPACE;
   MOE_TRY(need(ws));
-  if (T == 0) return MOE_OK;
+  return MOE_OK;
+}
 
-  uint8_t* base = static_cast<uint8_t*>(ws);
+// The layer state the backward works from, written into the backward workspace:
+// routing (logits, selection, weights), the permutation, the pool counts f, and the
+// expert pre-activations g, u (float32) and h (bf16), routed and shared. With fwd set
+// (the training forward) also the half-precision h and hs of the layer forward's
+// layout, the row redirect of the fused combine, and the caller's statistics outputs
+// (P, counts, scalars).
+static moe_status backward_state(const moe_dims* d, const moe_layer_params* p, const BwdWs& W, uint8_t* base,
+                                 hipStream_t s, const moe_aux_out* fwd) {
   auto at = [&](size_t off) { return static_cast<void*>(base + off); };
   auto fp = [&](size_t off) { return static_cast<float*>(at(off)); };
   auto ip = [&](size_t off) { return static_cast<int32_t*>(at(off)); };
   const LayerWs& L = W.fwd;
-  float* logits = fp(L.logits);
-  int32_t* topk_idx = ip(L.topk_idx);
-  float* topk_w = fp(L.topk_w);
-  int32_t* offsets = ip(L.offsets);
-  int32_t* perm_token = ip(L.perm_token);
-  int32_t* slot_pos = ip(L.slot_pos);
-  int32_t* permute_ws = ip(L.permute);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = d->T, dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
   const int64_t R = max_rows(d);
   const int N = d->n_experts, M = d->n_null, K = d->top_k;
   const int cus = cu_count();
   const uint16_t* x16 = static_cast<const uint16_t*>(p->x);
-  auto bf = [&](size_t off) { return static_cast<const uint16_t*>(at(off)); };
-  MOE_TRY(no_pending_error());
-
-  // 1-2. the forward's routing, permutation and pool counts f, recomputed
+  int32_t* offsets = ip(L.offsets);
+  int32_t* perm_token = ip(L.perm_token);
+  int32_t* permute_ws = ip(L.permute);
+  // 1-2. routing, permutation and pool counts f
   RouteArgs ra{T, d->d_model, N, M, K, true, true, p->x, p->w_router, p->null_bias, p->null_bias_tok,
-               nullptr, logits, topk_idx, topk_w, ip(L.n_real), at(L.route), permute_ws, ip(L.rhist),
-               static_cast<double*>(at(L.tstats)), d->null_kind};
+               nullptr, fp(L.logits), ip(L.topk_idx), fp(L.topk_w), ip(L.n_real), at(L.route), permute_ws,
+               ip(L.rhist), static_cast<double*>(at(L.tstats)), d->null_kind};
   HIP_TRY(launch_route(ra, s));
-  AuxTiles af{static_cast<double*>(at(L.tstats)), ip(L.rhist), fp(W.f), nullptr, nullptr, nullptr};
-  PermuteArgs pa{T, K, N, M, d->d_model, 2, topk_idx, nullptr, ip(L.counts), offsets, perm_token, slot_pos,
-                 nullptr, permute_ws, true, &af};
+  AuxTiles af{static_cast<double*>(at(L.tstats)), ip(L.rhist), fp(W.f), fwd ? fwd->P : nullptr,
+              fwd ? fwd->counts : nullptr, fwd ? fwd->scalars : nullptr};
+  int32_t* row_dst = fwd && fused_combine(d) ? ip(L.row_dst) : nullptr;
+  PermuteArgs pa{T, K, N, M, d->d_model, 2, ip(L.topk_idx), nullptr, ip(L.counts), offsets, perm_token,
+                 ip(L.slot_pos), nullptr, permute_ws, true, &af, row_dst};
   HIP_TRY(launch_permute(pa, s));
-
   // 3. expert pre-activations g = x W_g^T, u = x W_u^T (float32) and h = silu(g) u (bf16):
   // routed and shared in one launch whose epilogue keeps g and u and writes h, when the
   // 256 x 256 tiles take both; else g and u by plain GEMMs and h by its own kernel
@@ -814,7 +825,16 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     gsk.keep_u = fp(W.us);
   }
   const bool keep = gemm_pair_uses_pp(gk, gsk);
-  if (keep) HIP_TRY(launch_gemm_pair(true, 4, gk, gsk, cus, s, 3));
+  if (keep && fwd) {
+    // the forward's half-precision h (and hs) from the same epilogue: bit for bit what the
+    // layer forward's gate/up launch writes
+    gk.keep_h16 = at(L.h);
+    if (Fs) gsk.keep_h16 = at(L.hs);
+  }
+  if (keep) HIP_TRY(launch_gemm_pair(true, 4, gk, gsk, cus, s, fwd ? 2 : 3));
+  if (!keep && fwd)
+    HIP_TRY(launch_layer_gate_up(d, p->x, perm_token, offsets, p->w_gate, p->w_up, p->ws_gate, p->ws_up, at(L.h),
+                                 at(L.hs), s));
   GemmProblem g1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate), nullptr,
                  (int)F, (int)dm, at(W.g)};
   GemmProblem u1{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_up), nullptr,
@@ -831,6 +851,53 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     HIP_TRY(launch_gemm_pair(true, 1, gs, us, cus, s, 3));
     HIP_TRY(launch_swiglu_h(fp(W.gs), fp(W.us), nullptr, 1, T, (int)Fs, at(W.hs), s));
   }
+  return MOE_OK;
+}
+
+// The backward from the state in the workspace: recomputed first (recompute), or left
+// there by moe_layer_forward_train.
+static moe_status layer_backward(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,
+                                 float beta, const moe_layer_grads* gr, void* ws, size_t ws_bytes, moe_stream stream,
+                                 bool recompute) {
+  MOE_TRY(check_dims(d));
+  if (!p || !gr) return MOE_ERR_ARG;
+  const BwdWs W = bwd_ws(d);
+  MOE_TRY(check_backward_args(d, p, W, ws, ws_bytes));
+  const int64_t T = d->T, dm = d->d_model, F = d->d_ff, Fs = d->d_ff_shared;
+  if (Fs) {
+    MOE_TRY(need(gr->dws_gate));
+    MOE_TRY(need(gr->dws_up));
+    MOE_TRY(need(gr->dws_down));
+  }
+  MOE_TRY(need(dy));
+  MOE_TRY(need(gr->dx));
+  MOE_TRY(need(gr->dw_router));
+  MOE_TRY(need(gr->dw_gate));
+  MOE_TRY(need(gr->dw_up));
+  MOE_TRY(need(gr->dw_down));
+  if (T == 0) return MOE_OK;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  auto fp = [&](size_t off) { return static_cast<float*>(at(off)); };
+  auto ip = [&](size_t off) { return static_cast<int32_t*>(at(off)); };
+  const LayerWs& L = W.fwd;
+  float* logits = fp(L.logits);
+  int32_t* topk_idx = ip(L.topk_idx);
+  float* topk_w = fp(L.topk_w);
+  int32_t* offsets = ip(L.offsets);
+  int32_t* perm_token = ip(L.perm_token);
+  int32_t* slot_pos = ip(L.slot_pos);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t R = max_rows(d);
+  const int N = d->n_experts, M = d->n_null, K = d->top_k;
+  const int cus = cu_count();
+  auto bf = [&](size_t off) { return static_cast<const uint16_t*>(at(off)); };
+  MOE_TRY(no_pending_error());
+
+  // 1-3. routing, permutation, pool counts and expert pre-activations
+  if (recompute) MOE_TRY(backward_state(d, p, W, base, s, nullptr));
+
   // 4. per real slot: its expert row's dY = g dy (bf16, for dW_down), g and slot index
   HIP_TRY(launch_slot_rows(dy, slot_pos, topk_w, T, K, (int)dm, R, at(W.dyp), fp(W.wperm), ip(W.rslot), fp(W.dw),
                            s));
@@ -948,6 +1015,45 @@ moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, cons
     HIP_TRY(launch_sum_partials(fp(W.part_su), S, Fs * dm, gr->dws_up, s));
   }
   return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,
+                              float beta, const moe_layer_grads* gr, void* ws, size_t ws_bytes,
+                              moe_stream stream) {
+  return layer_backward(d, p, dy, alpha, beta, gr, ws, ws_bytes, stream, true);
+}
+
+moe_status moe_layer_backward_saved(const moe_dims* d, const moe_layer_params* p, const void* dy, float alpha,
+                                    float beta, const moe_layer_grads* gr, void* ws, size_t ws_bytes,
+                                    moe_stream stream) {
+  return layer_backward(d, p, dy, alpha, beta, gr, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_layer_forward_train(const moe_dims* d, const moe_layer_params* p, void* y, const moe_aux_out* aux,
+                                   void* ws, size_t ws_bytes, moe_stream stream) {
+  MOE_TRY(check_dims(d));
+  if (!p) return MOE_ERR_ARG;
+  const BwdWs W = bwd_ws(d);
+  MOE_TRY(check_backward_args(d, p, W, ws, ws_bytes));
+  MOE_TRY(need(y));
+  moe_aux_out ao{};
+  if (aux) ao = *aux;
+  // the routing outputs and f stay in the workspace (the backward reads them there)
+  if (ao.logits || ao.topk_idx || ao.topk_w || ao.n_real || ao.offsets || ao.f) return MOE_ERR_ARG;
+  MOE_TRY(maybe(ao.P));
+  MOE_TRY(maybe(ao.counts));
+  MOE_TRY(maybe(ao.scalars));
+  if (d->T == 0) return MOE_OK;
+  MOE_TRY(no_pending_error());
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(backward_state(d, p, W, base, s, &ao));
+  const LayerWs& L = W.fwd;
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  return layer_down_combine(d, p, y, L, base, static_cast<const int32_t*>(at(L.offsets)),
+                            static_cast<const int32_t*>(at(L.slot_pos)), static_cast<const float*>(at(L.topk_w)),
+                            static_cast<const int32_t*>(at(L.n_real)),
+                            fused_combine(d) ? static_cast<const int32_t*>(at(L.row_dst)) : nullptr, s);
 }
 
 }  // extern "C"

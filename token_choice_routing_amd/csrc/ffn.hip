@@ -1239,6 +1239,9 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
               for (int j = 0; j < 4; ++j) h[j] = silu(gv[j]) * uv[j];
               *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(pr.out) + ro + col) =
                   u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+              if (pr.keep_h16)
+                *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(pr.keep_h16) + ro + col) =
+                    u32x2_t{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])};
             }
           }
         } else {
@@ -1599,6 +1602,7 @@ hipError_t launch_gemm_pair(bool bf16, int op, const GemmProblem& p0, const Gemm
     }
     if (op == 4) {
       if (role == 3) launch_pp<kSwiGLUKeep, 3>(q0, q1, num_cus, stream);
+      else if (role == 2) launch_pp<kSwiGLUKeep, 2>(q0, q1, num_cus, stream);
       else return hipErrorInvalidValue;
       return hipGetLastError();
     }

@@ -144,6 +144,9 @@ struct GemmProblem {
   // a b1^T stored as float32 [max_rows][n_out] here, and out = bf16 silu(g) u.
   float* keep_g;
   float* keep_u;
+  // op 4, optional: h also stored as IEEE half here (the forward's down-projection input,
+  // bit for bit what op 0 writes), for a forward that keeps its pre-activations
+  void* keep_h16;
 };
 // op 0: out = silu(a b0^T) * (a b1^T) (bf16 a, half out); op 1: out = a b0^T (bf16 a,
 // float32 out; with b_kmajor set in both problems, B read from K-major b0 / b1, 256 x 256

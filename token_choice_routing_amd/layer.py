@@ -5,7 +5,8 @@ import numpy as np
 import torch
 
 from . import (AuxOut, LayerGrads, LayerParams, MOE_BF16, MOE_WS_BACKWARD, MOE_WS_LAYER, dims_from_config,
-               moe_layer_backward, moe_layer_forward, workspace_bytes)
+               moe_layer_backward, moe_layer_backward_saved, moe_layer_forward, moe_layer_forward_train,
+               workspace_bytes)
 
 
 def to_device(a, device="cuda"):
@@ -79,9 +80,7 @@ class MoeLayer:
 
     GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down")
 
-    def backward(self, dy, alpha=0.0, beta=0.0, stream=None):
-        """Gradients of <dy, y> + alpha L_bal + beta L_z (float32 device tensors,
-        allocated on the first call and reused)."""
+    def _backward_buffers(self):
         if getattr(self, "grads", None) is None:
             cfg, dev, f32 = self.cfg, self.x.device, torch.float32
             N, d, F, Fs = cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
@@ -93,8 +92,29 @@ class MoeLayer:
             self.grads_struct = LayerGrads(*(p(self.grads[k]) for k in self.GRADS))
             self.ws_bwd = torch.empty((max(workspace_bytes(self.dims, MOE_WS_BACKWARD), 256),),
                                       dtype=torch.uint8, device=dev)
+            self.aux_train = AuxOut(None, None, None, None, None, p(self.counts), None, p(self.P),
+                                    p(self.scalars))
+
+    def backward(self, dy, alpha=0.0, beta=0.0, stream=None):
+        """Gradients of <dy, y> + alpha L_bal + beta L_z (float32 device tensors,
+        allocated on the first call and reused)."""
+        self._backward_buffers()
         moe_layer_backward(self.dims, self.params, dy, alpha, beta, self.grads_struct, self.ws_bwd,
                            stream=stream)
+        return self.grads
+
+    def forward_train(self, stream=None):
+        """The forward that keeps its routing and pre-activations in the backward's
+        workspace (counts, P and scalars are written too; the routing outputs are not)."""
+        self._backward_buffers()
+        moe_layer_forward_train(self.dims, self.params, self.y, self.aux_train, self.ws_bwd, stream=stream)
+        return self.y
+
+    def backward_saved(self, dy, alpha=0.0, beta=0.0, stream=None):
+        """backward() from the state of the last forward_train() call."""
+        self._backward_buffers()
+        moe_layer_backward_saved(self.dims, self.params, dy, alpha, beta, self.grads_struct, self.ws_bwd,
+                                 stream=stream)
         return self.grads
 
     def validate(self):
