@@ -779,6 +779,28 @@ static moe_status check_backward_args(const moe_dims* d, const moe_layer_params*
   return MOE_OK;
 }
 
+// Whether the expert pre-activations come from the keep-mode launch (g and u stored in
+// IEEE half) rather than plain GEMMs (float32): the 256 x 256 tiles take the routed and
+// the shared gate/up problems (a function of the dims).
+static bool keep_preacts(const moe_dims* d) {
+  static const int32_t one = 1;  // a non-null row index and offsets pointer for the shape test
+  GemmProblem r{}, sh{};
+  r.a_rows = &one;
+  r.a_nrows = d->T;
+  r.offsets = &one;
+  r.groups = d->n_experts;
+  r.max_rows = max_rows(d);
+  r.n_out = d->d_ff;
+  r.k_dim = d->d_model;
+  if (d->d_ff_shared) {
+    sh.groups = 1;
+    sh.max_rows = d->T;
+    sh.n_out = d->d_ff_shared;
+    sh.k_dim = d->d_model;
+  }
+  return gemm_pair_uses_pp(r, sh);
+}
+
 // The layer state the backward works from, written into the backward workspace:
 // routing (logits, selection, weights), the permutation, the pool counts f, and the
 // expert pre-activations g, u (float32) and h (bf16), routed and shared. With fwd set
@@ -815,16 +837,17 @@ static moe_status backward_state(const moe_dims* d, const moe_layer_params* p, c
   // 256 x 256 tiles take both; else g and u by plain GEMMs and h by its own kernel
   GemmProblem gk{x16, perm_token, T, offsets, N, R, static_cast<const uint16_t*>(p->w_gate),
                  static_cast<const uint16_t*>(p->w_up), (int)F, (int)dm, at(W.h)};
-  gk.keep_g = fp(W.g);
-  gk.keep_u = fp(W.u);
+  gk.keep_g = at(W.g);
+  gk.keep_u = at(W.u);
   GemmProblem gsk{};
   if (Fs) {
     gsk = GemmProblem{x16, nullptr, T, nullptr, 1, T, static_cast<const uint16_t*>(p->ws_gate),
                       static_cast<const uint16_t*>(p->ws_up), (int)Fs, (int)dm, at(W.hs)};
-    gsk.keep_g = fp(W.gs);
-    gsk.keep_u = fp(W.us);
+    gsk.keep_g = at(W.gs);
+    gsk.keep_u = at(W.us);
   }
-  const bool keep = gemm_pair_uses_pp(gk, gsk);
+  // (the same test as gemm_pair_uses_pp(gk, gsk); the gradient step reads g and u by it)
+  const bool keep = keep_preacts(d);
   if (keep && fwd) {
     // the forward's half-precision h (and hs) from the same epilogue: bit for bit what the
     // layer forward's gate/up launch writes
@@ -932,9 +955,10 @@ static moe_status layer_backward(const moe_dims* d, const moe_layer_params* p, c
     hs3 = km.hs3;
   }
   HIP_TRY(launch_gemm_pair(true, 1, h3, hs3, cus, s, 3));
-  HIP_TRY(launch_swiglu_bwd_routed(fp(W.g), fp(W.u), fp(W.dh), at(W.h), fp(W.wperm), ip(W.rslot), offsets, N, R,
+  const bool g16 = keep_preacts(d);
+  HIP_TRY(launch_swiglu_bwd_routed(at(W.g), at(W.u), g16, fp(W.dh), at(W.h), fp(W.wperm), ip(W.rslot), offsets, N, R,
                                     (int)F, at(W.dgu), fp(W.dw), s));
-  if (Fs) HIP_TRY(launch_swiglu_bwd(fp(W.gs), fp(W.us), fp(W.dhs), nullptr, 1, T, (int)Fs, at(W.dgus), s));
+  if (Fs) HIP_TRY(launch_swiglu_bwd(at(W.gs), at(W.us), g16, fp(W.dhs), nullptr, 1, T, (int)Fs, at(W.dgus), s));
   HIP_TRY(launch_router_bwd(logits, topk_idx, topk_w, fp(W.dw), fp(W.f), T, N, M, K, alpha, beta, fp(W.ds), s));
 
   // 7. da = [dg | du] [W_g ; W_u]: routed rows and shared rows (float32)

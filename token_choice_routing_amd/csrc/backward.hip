@@ -163,15 +163,17 @@ swiglu_h_kernel(const float* __restrict__ g, const float* __restrict__ u, const 
 
 // SwiGLU backward: dgu[p][j] = dh u silu'(g), dgu[p][F + j] = dh silu(g), bf16, with
 // silu'(z) = sigma(z) (1 + z (1 - sigma(z))).
+// (GT: float, or _Float16 for the keep-mode GEMM's g and u)
+template <typename GT>
 __global__ void __launch_bounds__(256)
-swiglu_bwd_kernel(const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ dh,
+swiglu_bwd_kernel(const GT* __restrict__ g, const GT* __restrict__ u, const float* __restrict__ dh,
                   const int32_t* offsets, int G, int64_t rows, int F, bf16_t* __restrict__ dgu) {
   const int64_t n = live_rows(offsets, G, rows) * F;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t p = i / F, j = i - p * F;
-    const float z = g[i], sg = 1.0f / (1.0f + __expf(-z));
+    const float z = (float)g[i], sg = 1.0f / (1.0f + __expf(-z));
     const float d = dh[i];
-    dgu[p * 2 * F + j] = f32_to_bf16(d * u[i] * (sg * (1.0f + z * (1.0f - sg))));
+    dgu[p * 2 * F + j] = f32_to_bf16(d * (float)u[i] * (sg * (1.0f + z * (1.0f - sg))));
     dgu[p * 2 * F + F + j] = f32_to_bf16(d * z * sg);
   }
 }
@@ -219,8 +221,21 @@ slot_rows_kernel(const bf16_t* __restrict__ dy, const int32_t* __restrict__ slot
 // (so Y_p is never recomputed), written to dw[row_slot[p]] (float32, lanes add in a
 // fixed order), and with dh = topk_w U_p the SwiGLU backward as in swiglu_bwd_kernel.
 // 4 elements per lane and step (F is a multiple of 8).
+// four consecutive g or u values as float32 (GT float, or _Float16)
+template <typename GT>
+__device__ __forceinline__ f32x4_t load4(const GT* p) {
+  if constexpr (sizeof(GT) == 4) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  } else {
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    const f16x4_t v = *reinterpret_cast<const f16x4_t*>(p);
+    return f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+}
+
+template <typename GT>
 __global__ void __launch_bounds__(256)
-swiglu_bwd_routed_kernel(const float* __restrict__ g, const float* __restrict__ u, const float* __restrict__ U,
+swiglu_bwd_routed_kernel(const GT* __restrict__ g, const GT* __restrict__ u, const float* __restrict__ U,
                          const bf16_t* __restrict__ h, const float* __restrict__ w_perm,
                          const int32_t* __restrict__ row_slot, const int32_t* offsets, int G, int64_t rows,
                          int F, bf16_t* __restrict__ dgu, float* __restrict__ dw) {
@@ -232,8 +247,8 @@ swiglu_bwd_routed_kernel(const float* __restrict__ g, const float* __restrict__ 
   float acc = 0.0f;
   for (int j = lane * 4; j < F; j += kWave * 4) {
     const f32x4_t uu = *reinterpret_cast<const f32x4_t*>(U + o + j);
-    const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(g + o + j);
-    const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(u + o + j);
+    const f32x4_t gg = load4(g + o + j);
+    const f32x4_t vv = load4(u + o + j);
     const u32x2_t hh = *reinterpret_cast<const u32x2_t*>(h + o + j);
     float dg[4], du[4];
 #pragma unroll
@@ -515,10 +530,16 @@ hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offset
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
+hipError_t launch_swiglu_bwd(const void* g, const void* u, bool g16, const float* dh, const int32_t* offsets, int G,
                              int64_t rows, int F, void* dgu, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  swiglu_bwd_kernel<<<grid_for(rows * F), 256, 0, s>>>(g, u, dh, offsets, G, rows, F, static_cast<bf16_t*>(dgu));
+  if (g16)
+    swiglu_bwd_kernel<_Float16><<<grid_for(rows * F), 256, 0, s>>>(
+        static_cast<const _Float16*>(g), static_cast<const _Float16*>(u), dh, offsets, G, rows, F,
+        static_cast<bf16_t*>(dgu));
+  else
+    swiglu_bwd_kernel<float><<<grid_for(rows * F), 256, 0, s>>>(
+        static_cast<const float*>(g), static_cast<const float*>(u), dh, offsets, G, rows, F, static_cast<bf16_t*>(dgu));
   return hipGetLastError();
 }
 
@@ -532,12 +553,18 @@ hipError_t launch_slot_rows(const void* dy, const int32_t* slot_pos, const float
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd_routed(const float* g, const float* u, const float* U, const void* h,
+hipError_t launch_swiglu_bwd_routed(const void* g, const void* u, bool g16, const float* U, const void* h,
                                     const float* w_perm, const int32_t* row_slot, const int32_t* offsets, int G,
                                     int64_t rows, int F, void* dgu, float* dw, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  swiglu_bwd_routed_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
-      g, u, U, static_cast<const bf16_t*>(h), w_perm, row_slot, offsets, G, rows, F, static_cast<bf16_t*>(dgu), dw);
+  if (g16)
+    swiglu_bwd_routed_kernel<_Float16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+        static_cast<const _Float16*>(g), static_cast<const _Float16*>(u), U, static_cast<const bf16_t*>(h), w_perm,
+        row_slot, offsets, G, rows, F, static_cast<bf16_t*>(dgu), dw);
+  else
+    swiglu_bwd_routed_kernel<float><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+        static_cast<const float*>(g), static_cast<const float*>(u), U, static_cast<const bf16_t*>(h), w_perm,
+        row_slot, offsets, G, rows, F, static_cast<bf16_t*>(dgu), dw);
   return hipGetLastError();
 }
 

@@ -73,7 +73,8 @@ constexpr int kMaxGroups = 512;
 // kPlainKM2: kPlainKM whose activation operand is K-major too (GemmProblem::a_kmajor, the
 //          weight-gradient form: K = rows of both source matrices), read the same way.
 // kSwiGLUKeep: kSwiGLU for the backward's recompute (256 x 256 tiles only): the epilogue
-//          stores g and u (float32, keep_g / keep_u) and h = silu(g) u as bf16.
+//          stores g and u (IEEE half, keep_g / keep_u) and h = silu(g) u as bf16 (from the
+//          float32 g and u).
 enum { kSwiGLU = 0, kPlain = 1, kDown16 = 2, kDownComb = 3, kPlainKM = 4, kPlainKM2 = 5, kSwiGLUKeep = 6 };
 
 // One 32x32x16 MFMA step: the weight fragment w (bf16 bits) and the activation
@@ -1232,8 +1233,10 @@ grouped_gemm_pp_kernel(GemmProblem p0, GemmProblem p1) {
             if (col < Nout) {
               const f32x4_t gv{acc[0][g][4 * q], acc[0][g][4 * q + 1], acc[0][g][4 * q + 2], acc[0][g][4 * q + 3]};
               const f32x4_t uv{acc[1][g][4 * q], acc[1][g][4 * q + 1], acc[1][g][4 * q + 2], acc[1][g][4 * q + 3]};
-              *reinterpret_cast<f32x4_t*>(pr.keep_g + ro + col) = gv;
-              *reinterpret_cast<f32x4_t*>(pr.keep_u + ro + col) = uv;
+              *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(pr.keep_g) + ro + col) =
+                  u32x2_t{pack_f16x2(gv[0], gv[1]), pack_f16x2(gv[2], gv[3])};
+              *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(pr.keep_u) + ro + col) =
+                  u32x2_t{pack_f16x2(uv[0], uv[1]), pack_f16x2(uv[2], uv[3])};
               float h[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j) h[j] = silu(gv[j]) * uv[j];

@@ -142,8 +142,8 @@ struct GemmProblem {
   int a_kmajor;
   // op 4 (the backward's recompute of op 0, 256 x 256 tiles only): g = a b0^T and u =
   // a b1^T stored as float32 [max_rows][n_out] here, and out = bf16 silu(g) u.
-  float* keep_g;
-  float* keep_u;
+  void* keep_g;  // IEEE half [max_rows][n_out]
+  void* keep_u;
   // op 4, optional: h also stored as IEEE half here (the forward's down-projection input,
   // bit for bit what op 0 writes), for a forward that keeps its pre-activations
   void* keep_h16;
@@ -153,7 +153,7 @@ struct GemmProblem {
 // tiles only); op 2: out = a b0^T with a in half (the layer's h), float32 out; op 3: op 2
 // with the combine epilogue (comb_* fields), bf16 out, on the 256 x 256 tiles only (the
 // launch is refused where gemm_pair_uses_pp is false); op 4: op 0 keeping g and u
-// (keep_g / keep_u) with h in bf16 (256 x 256 tiles, role 3 only). Both problems in one
+// (keep_g / keep_u, IEEE half) with h in bf16 (256 x 256 tiles, roles 2 and 3). Both problems in one
 // launch.
 // (float32 layers: op 2 is op 1.)
 // role names the launch in profiles: 0 standalone grouped, 1 standalone single
@@ -192,7 +192,8 @@ hipError_t launch_gather_slots(const void* x, const int32_t* perm_token, int64_t
                                int64_t R, int d, void* out, hipStream_t s);
 hipError_t launch_swiglu_h(const float* g, const float* u, const int32_t* offsets, int G, int64_t rows, int F,
                            void* h, hipStream_t s);
-hipError_t launch_swiglu_bwd(const float* g, const float* u, const float* dh, const int32_t* offsets, int G,
+// g and u: float32, or IEEE half when g16 (the keep-mode GEMM's).
+hipError_t launch_swiglu_bwd(const void* g, const void* u, bool g16, const float* dh, const int32_t* offsets, int G,
                              int64_t rows, int F, void* dgu, hipStream_t s);
 // Real slot (t, k) at row p: dy_perm[p] = topk_w dy_t (bf16), w_perm[p] = topk_w,
 // row_slot[p] = t K + k; null slots: dw[t][k] = 0.
@@ -201,7 +202,7 @@ hipError_t launch_slot_rows(const void* dy, const int32_t* slot_pos, const float
                             hipStream_t s);
 // Routed rows from U = dy W_d: dw[row_slot[p]] = <U_p, h_p>, and the SwiGLU backward
 // of dh = w_perm U into dgu (as launch_swiglu_bwd).
-hipError_t launch_swiglu_bwd_routed(const float* g, const float* u, const float* U, const void* h,
+hipError_t launch_swiglu_bwd_routed(const void* g, const void* u, bool g16, const float* U, const void* h,
                                     const float* w_perm, const int32_t* row_slot, const int32_t* offsets, int G,
                                     int64_t rows, int F, void* dgu, float* dw, hipStream_t s);
 hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* dw,
