@@ -650,10 +650,10 @@ moe_status moe_layer_forward(const moe_dims* d, const moe_layer_params* p, void*
   return layer_down_combine(d, p, y, L, base, offsets, slot_pos, topk_w, n_real, row_dst, s);
 }
 
-// Steps 4-5 of the layer forward: the down projections (routed and shared, from the
-// half-precision h and hs in L) and the weighted combine into y, or, with fused = a
-// row_dst, the routed outputs token-major and the combine in the shared expert's
-// down projection.
+// Steps 4-5 of the layer forward: the down projections (routed and shared, from h and
+// hs in L: IEEE half in bf16 layers, float32 in float32 ones) and the weighted combine
+// into y, or, given a row_dst (the fused combine), the routed outputs token-major and
+// the combine in the shared expert's down projection.
 static moe_status layer_down_combine(const moe_dims* d, const moe_layer_params* p, void* y, const LayerWs& L,
                                      uint8_t* base, const int32_t* offsets, const int32_t* slot_pos,
                                      const float* topk_w, const int32_t* n_real, const int32_t* row_dst,
