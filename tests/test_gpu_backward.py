@@ -316,6 +316,27 @@ def test_forward_train_and_backward_saved_match_the_stateless_pair(case, null_bi
         assert torch.equal(layer.grads[k], v), k
 
 
+def test_training_pair_full_size_headline_shape():
+    """The training pair at the Qwen3-1.7B rho = 0.25 shape (16384 tokens, 64 experts,
+    K = 8 of 64 + 192, shared expert): y and every gradient equal the stateless pair's."""
+    from workloads import CONFIGS
+    cfg = CONFIGS["qwen3_1p7b_rho0p25"]
+    say(f"  training pair full size {cfg.name}")
+    layer = MoeLayer(generate(cfg))
+    layer.forward(aux=False)
+    y_ref = layer.y.clone()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    dy = torch.randn((layer.T, cfg.d_model), generator=g, device="cuda").to(torch.bfloat16)
+    g_ref = {k: v.clone() for k, v in layer.backward(dy, 2e-2, 1e-3).items() if v is not None}
+    layer.forward_train()
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y, y_ref)
+    layer.backward_saved(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    for k, v in g_ref.items():
+        assert torch.equal(layer.grads[k], v), k
+
+
 def test_forward_train_refuses_routing_outputs():
     from token_choice_routing_amd import AuxOut, MoeError, moe_layer_forward_train
     cfg = Config(name="train_refuse", dtype="bf16", w_std=None, seed=3, **CASES["topk_m0"])
