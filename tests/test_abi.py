@@ -193,6 +193,51 @@ def test_backward_argument_checks(lib):
     assert call(_dims(T=0)) == MOE_OK
 
 
+def test_training_pair_argument_checks(lib):
+    """moe_layer_forward_train and moe_layer_backward_saved refuse what the backward does
+    not cover and bad pointers or workspaces like moe_layer_backward, before anything is
+    launched; the training forward also refuses the aux routing outputs and f (they stay
+    in the workspace). T = 0 is a no-op for both."""
+    big = 1 << 40
+    p = tcr.LayerParams(FAKE, FAKE, 0.0, None, FAKE, FAKE, FAKE, None, None, None)
+    d = _dims()
+    need = tcr.workspace_bytes(d, tcr.MOE_WS_BACKWARD)
+
+    def fwd(d, params=p, y=FAKE, aux=None, ws=FAKE, nbytes=big):
+        return lib.moe_layer_forward_train(ctypes.byref(d), ctypes.byref(params) if params else None, y,
+                                           ctypes.byref(aux) if aux else None, ws, ctypes.c_size_t(nbytes), None)
+
+    assert fwd(_dims(dtype=MOE_F32)) == MOE_ERR_UNSUPPORTED
+    assert fwd(_dims(null_kind=tcr.MOE_NULL_COPY)) == MOE_ERR_UNSUPPORTED
+    assert fwd(d, params=None) == MOE_ERR_ARG
+    assert fwd(d, y=None) == MOE_ERR_ARG
+    assert fwd(d, y=MIS) == MOE_ERR_ALIGN
+    assert fwd(d, nbytes=need - 1) == MOE_ERR_WORKSPACE
+    assert fwd(d, ws=None, nbytes=need) == MOE_ERR_WORKSPACE
+    for name in ("logits", "topk_idx", "topk_w", "n_real", "offsets", "f"):
+        a = tcr.AuxOut()
+        setattr(a, name, FAKE)
+        assert fwd(d, aux=a) == MOE_ERR_ARG, name
+    a = tcr.AuxOut()
+    a.P = MIS
+    assert fwd(d, aux=a) == MOE_ERR_ALIGN
+    assert fwd(_dims(T=0)) == MOE_OK
+
+    grads = tcr.LayerGrads(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None)
+
+    def bwd(d, dy=FAKE, g=grads, ws=FAKE, nbytes=big):
+        return lib.moe_layer_backward_saved(ctypes.byref(d), ctypes.byref(p), dy, ctypes.c_float(0.02),
+                                            ctypes.c_float(0.001), ctypes.byref(g) if g else None, ws,
+                                            ctypes.c_size_t(nbytes), None)
+
+    assert bwd(_dims(dtype=MOE_F32)) == MOE_ERR_UNSUPPORTED
+    assert bwd(d, g=None) == MOE_ERR_ARG
+    assert bwd(d, dy=None) == MOE_ERR_ARG
+    assert bwd(d, dy=MIS) == MOE_ERR_ALIGN
+    assert bwd(d, nbytes=need - 1) == MOE_ERR_WORKSPACE
+    assert bwd(_dims(T=0)) == MOE_OK
+
+
 def test_binding_refuses_host_and_strided_tensors():
     """The binding passes device addresses only: a host tensor or a strided view would be
     read as a dense device array, so it is refused before the call."""
