@@ -305,6 +305,52 @@ def test_layer_forward_and_backward_replay_in_a_hip_graph():
     del graph
 
 
+def test_training_pair_replays_in_a_hip_graph():
+    """moe_layer_forward_train + moe_layer_backward_saved enqueue only kernels as well:
+    captured in one HIP graph (on the 256 x 256 keep launch with the fused combine), every
+    replay with eager calls in between gives the stateless pair's y and gradients."""
+    from workloads.configs import Config
+    say("forward_train + backward_saved captured in a HIP graph")
+    cfg = Config(name="graph_train", T=4096, d_model=256, n_experts=8, n_null=8, top_k=2, d_ff=256,
+                 d_ff_shared=256, dtype="bf16", w_std=None, seed=4)
+    layer = MoeLayer(generate(cfg))
+    rng = np.random.default_rng(2)
+    dy = to_device(bf16_round(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32)))
+    layer.forward()
+    grads = layer.backward(dy, 2e-2, 1e-3)
+    torch.cuda.synchronize()
+    ref_y = layer.y.clone()
+    ref_g = {k: v.clone() for k, v in grads.items() if v is not None}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward_train(stream=side)
+        layer.backward_saved(dy, 2e-2, 1e-3, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        layer.forward_train(stream=cs)
+        layer.backward_saved(dy, 2e-2, 1e-3, stream=cs)
+    torch.cuda.synchronize()
+    for i in range(3):
+        layer.y.zero_()
+        for v in grads.values():
+            if v is not None:
+                v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, ref_y), f"replay {i}: y"
+        for k, v in ref_g.items():
+            assert torch.equal(grads[k], v), f"replay {i}: {k}"
+        layer.forward()                 # eager work between replays
+        layer.backward(dy, 2e-2, 1e-3)
+        torch.cuda.synchronize()
+    del graph
+
+
 def test_validate_inputs_finds_nan_and_inf():
     """moe_validate_inputs: a clean layer passes; a NaN in x, an infinity in an expert
     weight or in the router, or a NaN null bias is found; an infinite per-token null
